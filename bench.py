@@ -1,0 +1,234 @@
+"""MoE-layer forward throughput on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic tokens:
+router -> selection -> routing map -> dispatch -> expert FFNs (grouped GEMM)
+-> combine -> balance statistics, every stage a call into libmoe_dispatch.so
+on one HIP stream, inputs and weights resident in HBM.
+
+Default workload: expert choice, bf16, n = 4096 tokens, d = 2048, 64 experts,
+capacity factor 2 (128 tokens per expert), GELU experts d -> 4096 -> d.
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+
+Prints one JSON line: tokens/s over exactly K timed steps, the roofline of the
+dominant step (the expert FFN call), per-stage times, and the CPU oracle's
+throughput on the same workload for reference.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix cores, TFLOP/s
+FP32_PEAK_TFLOPS = 157.3
+STAGES = ("router", "select", "build_map", "dispatch", "expert_ffn", "combine", "balance_stats")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expert_ffn_traffic.json")
+
+
+def algorithmic(cfg, k, M):
+    """Compulsory HBM bytes and FLOPs of each stage (each tensor touched once)."""
+    b = 2 if cfg.dtype == "bf16" else 4
+    n, d, E, f = cfg.n, cfg.d, cfg.E, cfg.f
+    w1r = 2 * f if cfg.act == "swiglu" else f
+    flops_ffn = 2.0 * M * d * w1r + 2.0 * M * f * d
+    bytes_ffn = E * (w1r * d + d * f) * b + M * d * b + 2 * M * f * b + M * d * b
+    if cfg.shared_f:
+        sr = 2 * cfg.shared_f if cfg.act == "swiglu" else cfg.shared_f
+        flops_ffn += 2.0 * n * d * sr + 2.0 * n * cfg.shared_f * d
+        bytes_ffn += (sr * d + d * cfg.shared_f) * b + n * d * b + 2 * n * cfg.shared_f * b + n * d * b
+    ec = cfg.direction == "ec"
+    return {
+        "router": dict(bytes=n * d * b + d * E * b + 4 * n * E * (2 if ec else 1), flops=2.0 * n * d * E),
+        "select": dict(bytes=4 * n * E + 8 * (E * k if ec else n * k), flops=0.0),
+        "build_map": dict(bytes=8 * M + 16 * M + 4 * n, flops=0.0),
+        "dispatch": dict(bytes=2 * M * d * b, flops=0.0),
+        "expert_ffn": dict(bytes=bytes_ffn, flops=flops_ffn),
+        "combine": dict(bytes=M * d * b + 2 * n * d * b + (n * d * b if cfg.shared_f else 0), flops=2.0 * M * d),
+        "balance_stats": dict(bytes=4 * n * E, flops=0.0),
+    }
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for name in ("grouped_gemm.hip", "device_common.hpp", "kernels.hpp"):
+        with open(os.path.join(ROOT, "sparse_expert_dispatch_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(cfg, inp, w1_host, w2_host):
+    """The CPU oracle, as it is, on one full forward of the same workload."""
+    import threadpoolctl
+    from oracle import moe_oracle as O
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    t0 = time.perf_counter()
+    O.forward(cfg, dict(inp, w1=w1_host, w2=w2_host))
+    dt = time.perf_counter() - t0
+    return {"value": cfg.n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"one full layer forward of the same workload (n={cfg.n}), {dt:.2f} s "
+                      f"of host time, numpy/OpenBLAS float64"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2, the headline one)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    from sparse_expert_dispatch_amd import _native as N
+    from sparse_expert_dispatch_amd import workloads as W
+    from sparse_expert_dispatch_amd.layer import MoELayer, to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    N.lib()
+    cfg = W.FULL_CONFIGS[args.config]
+    print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
+    inp = W.gen_inputs(cfg)
+    w1_host, w2_host = inp.pop("w1"), inp.pop("w2")
+    weights = {"wg": to_device(inp["wg"]), "w1": to_device(w1_host), "w2": to_device(w2_host),
+               "logit_offset": to_device(inp.get("logit_offset")),
+               "sel_bias": to_device(inp.get("sel_bias"))}
+    if cfg.shared_f:
+        weights["shared_w1"] = to_device(inp["shared_w1"])
+        weights["shared_w2"] = to_device(inp["shared_w2"])
+    x = to_device(inp["x"])
+    layer = MoELayer(cfg, weights)
+    stream = torch.cuda.current_stream()
+
+    if args.calib_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step(ev=None):
+        if ev is None:
+            layer.forward(x, residual=True)
+            return
+        ev[0].record(stream)
+        w = layer.w
+        tc = layer.rcfg.dir == N.MOE_TOKEN_CHOICE
+        N.moe_router(x, w["wg"], w.get("logit_offset"), layer.rcfg, layer.logits, None,
+                     None if tc else layer.scores_t, layer.ws_router)
+        ev[1].record(stream)
+        N.moe_select(layer.logits, None if tc else layer.scores_t, w.get("sel_bias"), layer.rcfg,
+                     layer.sel_idx, layer.sel_gate, layer.ws_route)
+        ev[2].record(stream)
+        N.moe_build_map(layer.sel_idx, layer.sel_gate, layer.rcfg, layer.map, layer.ws_route)
+        ev[3].record(stream)
+        N.moe_dispatch(x, layer.map, layer.x_perm)
+        ev[4].record(stream)
+        N.moe_expert_ffn(layer.x_perm, layer.map.expert_offset, w["w1"], w["w2"], layer.act,
+                         layer.y_perm, layer.ws_ffn)
+        if layer.shared:
+            N.moe_expert_ffn(x, layer.shared_offsets, w["shared_w1"], w["shared_w2"], layer.act,
+                             layer.shared_out, layer.ws_shared)
+        ev[5].record(stream)
+        layer.combine(x, residual=True)
+        ev[6].record(stream)
+        layer.balance_stats()
+        ev[7].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    print(f"[bench] timed {args.steps} steps in {elapsed:.4f}s", file=sys.stderr, flush=True)
+
+    stage_ms = {s: [] for s in STAGES}
+    for ev in events:
+        for j, s in enumerate(STAGES):
+            stage_ms[s].append(ev[j].elapsed_time(ev[j + 1]))
+    k = layer.k
+    M = int(layer.map.n_kept.item())
+    alg = algorithmic(cfg, k, M)
+    stages = {}
+    for s in STAGES:
+        ms = float(np.mean(stage_ms[s]))
+        a = alg[s]
+        stages[s] = {"us": round(ms * 1e3, 2), "GB/s": round(a["bytes"] / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(a["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if a["flops"]:
+            stages[s]["TFLOP/s"] = round(a["flops"] / (ms * 1e-3) / 1e12, 1)
+    ffn_ms = float(np.mean(stage_ms["expert_ffn"]))
+    ffn = alg["expert_ffn"]
+    intensity = ffn["flops"] / ffn["bytes"]
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        if tr.get("source_hash") == source_hash() and tr.get("workload") == cfg.name:
+            traffic = tr.get("bytes_per_launch")
+    if intensity < ridge or cfg.dtype != "bf16":
+        achieved = ffn["bytes"] / (ffn_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+    else:
+        achieved = ffn["flops"] / (ffn_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
+    roofline["kernel"] = "moe_expert_ffn (grouped GEMM: up projection + activation, down projection)"
+    roofline["algorithmic_bytes"] = int(ffn["bytes"])
+    roofline["flops"] = ffn["flops"]
+    roofline["avg_us"] = round(ffn_ms * 1e3, 2)
+
+    ms_per_step = elapsed / args.steps * 1e3
+    line = {
+        "metric": "MoE-layer fwd tokens/sec at 1 MI355X; % peak HBM (route/dispatch) & MFMA (experts)",
+        "value": round(cfg.n * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded normals; random-init weights of the stated shapes)",
+        "config": {"workload": cfg.name, "n": cfg.n, "d": cfg.d, "E": cfg.E, "f": cfg.f, "act": cfg.act,
+                   "direction": cfg.direction, "k": k, "kept_assignments": M,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "stages": stages,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, w1_host, w2_host)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,231 @@
+/*
+ * moe_dispatch.h -- C ABI of a Mixture-of-Experts layer forward on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (MoE-routing pages: page 2 "Expert choice routing", section "The
+ * math"; page 5 "MoE routing strategies explained", strategies 1-6):
+ *
+ *   S = softmax(X W_g)  or  sigmoid(X W_g)              moe_router
+ *   token choice: each token keeps its top-k experts;   moe_select
+ *   expert choice: each expert keeps its top-k tokens
+ *   capacity / routing map (P = onehot(I))              moe_build_map
+ *   X_in[e] = P[e] X                                    moe_dispatch
+ *   Y[e] = Expert_e(X_in[e])                            moe_expert_ffn
+ *   out = residual + shared + scatter_add(G * Y, I)     moe_combine
+ *   load-balance loss, z-loss, MaxVio                   moe_balance_stats
+ *
+ * Conventions common to every call:
+ *  - Tensor arguments are DEVICE pointers owned by the caller.  The library
+ *    allocates no device memory; calls that need scratch space take a
+ *    caller-owned workspace (`ws`, `ws_bytes`) whose size the *_workspace_size
+ *    queries give.  Configuration structs are HOST pointers, read during the
+ *    call only.
+ *  - Every call validates its arguments on the host before touching the GPU
+ *    and returns MOE_ERR_INVALID_ARG (bad shape, null pointer, k > E, ...),
+ *    MOE_ERR_UNSUPPORTED (a valid request this build does not implement) or
+ *    MOE_ERR_WORKSPACE (workspace too small) without any device work.  A HIP
+ *    launch failure returns MOE_ERR_LAUNCH.  moe_last_error() returns a
+ *    thread-local message for the last non-OK status.  No exception or abort
+ *    crosses the ABI.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *    void*; NULL = the default stream).  Results are valid once the stream
+ *    has synchronised.  No call synchronises the host with the device: sizes
+ *    that depend on routing (per-expert counts, kept assignments) stay on the
+ *    device, and host-side buffer sizes use the bounds below.
+ *  - Layouts are row-major.  bf16 tensors are raw bfloat16 bit patterns
+ *    (uint16) rounded to nearest-even; fp32 tensors are IEEE float.  Expert
+ *    weights are K-contiguous: W1 [E, f, d] (SwiGLU: [E, 2f, d], gate rows
+ *    first, then up rows), W2 [E, d, f].  The router weight keeps the pages'
+ *    [d, E] layout.
+ *  - Inputs must be finite.  Results are deterministic: the same inputs give
+ *    the same bits on every run (no floating-point atomics).
+ */
+#ifndef MOE_DISPATCH_H
+#define MOE_DISPATCH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status_t;
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_LAUNCH = 4
+};
+
+enum { MOE_F32 = 0, MOE_BF16 = 1 };               /* element type           */
+enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 };        /* router score function  */
+enum { MOE_TOKEN_CHOICE = 0, MOE_EXPERT_CHOICE = 1 };
+enum { MOE_GELU = 0, MOE_SWIGLU = 1 };            /* expert activation      */
+
+#define MOE_NSTATS 8
+/* moe_balance_stats output, in this order:
+ *  0 lb_loss   = lb_coef * E * sum_e f_e * P_e  (f_e: share of chosen
+ *                assignments before drops; P_e: mean normalised score)
+ *  1 z_loss    = z_coef * mean_t logsumexp(z_t)^2
+ *  2 max_vio   = (max_e load_e - mean load) / mean load, load = kept rows
+ *  3 max_load_share = max_e load_e / total kept (router-collapse flag)
+ *  4 kept assignments         5 dropped assignments
+ *  6 tokens with no kept expert (dropped entirely / selected by no expert)
+ *  7 largest number of experts any token kept                            */
+
+/* Routing configuration (host struct). */
+typedef struct {
+  int32_t n;          /* tokens                                            */
+  int32_t d;          /* model dimension                                   */
+  int32_t E;          /* experts                                           */
+  int32_t k;          /* token choice: experts per token; expert choice:
+                         tokens per expert (see moe_ec_k)                  */
+  int32_t dir;        /* MOE_TOKEN_CHOICE | MOE_EXPERT_CHOICE              */
+  int32_t score;      /* MOE_SOFTMAX | MOE_SIGMOID (token choice only)     */
+  int32_t n_group;    /* group-limited routing: contiguous expert groups;
+                         1 = no group limit                                */
+  int32_t topk_group; /* groups kept per token (1 <= topk_group <= n_group) */
+  int32_t group_topm; /* group score = sum of the group's top-m keys, 1..4  */
+  int32_t norm_topk;  /* 1: renormalise gates over the k selected experts  */
+  int32_t capacity;   /* token choice: slots per expert; -1 = dropless     */
+} moe_route_cfg_t;
+
+/* Routing map (host struct of caller-owned device buffers; M_max =
+ * moe_max_slots(cfg)).  Slots are expert-major: expert e owns slots
+ * expert_offset[e] .. expert_offset[e+1]-1, filled in arrival order. */
+typedef struct {
+  int32_t *expert_count;  /* [E]   assignments chosen per expert (pre-drop) */
+  int32_t *expert_offset; /* [E+1] exclusive prefix of kept rows per expert */
+  int32_t *slot_token;    /* [M_max] token of each slot                      */
+  float   *slot_gate;     /* [M_max] gate of each slot                       */
+  int32_t *assign_slot;   /* token choice [n,k]: slot of (token, rank), -1 =
+                             dropped; expert choice [E,k]: slot of I[e,j]   */
+  int32_t *token_offset;  /* [n+1] token-side CSR over token_slot            */
+  int32_t *token_slot;    /* [M_max] each token's kept slots, rank order
+                             (token choice) or ascending expert (expert c.) */
+  int32_t *n_kept;        /* [1]   kept assignments = expert_offset[E]       */
+} moe_route_map_t;
+
+/* ---- sizes (pure host functions, no GPU needed) ---------------------- */
+
+/* Tokens per expert under expert choice, k = n c / E (page 1 "Who picks
+ * whom"; page 2 "A worked example"), rounded half up.  Returns -1 on
+ * invalid input (n, E <= 0, c <= 0). */
+int32_t moe_ec_k(int32_t n, double c, int32_t E);
+
+/* Per-expert capacity under token choice: cf * k * n / E (the balanced load
+ * times the capacity factor; page 5 strategy 2 states it for k = 1), rounded
+ * half up, computed in double as ((cf * k) * n) / E.  -1 on invalid input. */
+int32_t moe_tc_capacity(int32_t n, int32_t k, int32_t E, double cf);
+
+/* Upper bound on kept assignments: token choice n*k (capacity-limited:
+ * min(n*k, E*capacity)); expert choice E*k.  -1 on invalid cfg. */
+int64_t moe_max_slots(const moe_route_cfg_t *cfg);
+
+/* Workspace for moe_router (`dtype` of X and W_g). */
+moe_status_t moe_router_workspace_size(const moe_route_cfg_t *cfg, int32_t dtype, size_t *bytes);
+/* Workspace shared by moe_select, moe_build_map and moe_balance_stats. */
+moe_status_t moe_route_workspace_size(const moe_route_cfg_t *cfg, size_t *bytes);
+/* Workspace for moe_expert_ffn with M_max rows and hidden size f. */
+moe_status_t moe_ffn_workspace_size(int64_t M_max, int32_t E, int32_t d, int32_t f, int32_t act,
+                                    int32_t dtype, size_t *bytes);
+
+/* ---- the layer --------------------------------------------------------- */
+
+/* Router (page 2 "The math": S = softmax(X W_g), W_g: [d, E]; page 5
+ * strategy 4: a sigmoid per expert instead).  Logits Z = X W_g accumulated
+ * in fp32 (bf16 inputs on the matrix cores), plus logit_offset[e] when
+ * given, written to logits [n,E] fp32.  Optional outputs: scores [n,E] and
+ * scores_t [E,n] (the transpose, the column-contiguous layout expert choice
+ * selects from), both fp32, computed with the library's specified exp
+ * (Cody-Waite reduction, degree-7 Taylor polynomial, single fp32 operations,
+ * no fused multiply-add), a halving-stride tree sum over experts and IEEE
+ * division, so equal logits give equal score bits on any conforming device.
+ * X [n,d] and W_g [d,E] in `dtype`; logit_offset [E] fp32 or NULL.
+ * Any shape; bf16 with d % 64 == 0 and E % 16 == 0 runs on the matrix cores
+ * (X and W_g 16-byte aligned), other shapes on a scalar fp32 kernel. */
+moe_status_t moe_router(const void *X, const void *Wg, int32_t dtype, const float *logit_offset,
+                        const moe_route_cfg_t *cfg, float *logits, float *scores, float *scores_t,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/* Selection.
+ * Token choice (page 2 "Token-choice and its load-balance headache"; page 5
+ * strategies 1, 2, 4, 5): every token keeps its k best experts, in rank
+ * order, lower expert index first on equal keys.  Key = the logit (softmax
+ * is monotone within a row) or sigmoid(z) + sel_bias[e] (sel_bias [E] fp32
+ * or NULL; the bias enters the choice only).  With n_group > 1 the experts
+ * form n_group contiguous groups, each scored by the sum of its top
+ * group_topm keys, and only the topk_group best groups (lower index on ties)
+ * stay eligible.  Gates: softmax over the k selected logits when norm_topk,
+ * else the full-row softmax probability; sigmoid: the raw sigmoid scores,
+ * renormalised over the k when norm_topk.  Output sel_idx [n,k] int32,
+ * sel_gate [n,k] fp32.
+ * Expert choice (page 2 "The transposed selection"): every expert keeps the
+ * k tokens with the highest softmax score in its column, lower token index
+ * first on equal scores; I [E,k] int32 in ascending token order, G [E,k] =
+ * S[I, e].  scores_t [E,n] from moe_router is used when given, else it is
+ * recomputed from `logits` into the workspace.  n <= 2^24. */
+moe_status_t moe_select(const float *logits, const float *scores_t, const float *sel_bias,
+                        const moe_route_cfg_t *cfg, int32_t *sel_idx, float *sel_gate, void *ws,
+                        size_t ws_bytes, void *stream);
+
+/* Routing map.  Token choice: assignments arrive in token order and, within
+ * a token, in rank order; an assignment is kept iff fewer than `capacity`
+ * earlier arrivals went to its expert (page 1 "Dropped tokens flow in
+ * opposite directions": tokens arriving after the buffer fills skip the
+ * expert and ride the residual); capacity -1 keeps all (dropless).
+ * Expert choice: slot e*k + j holds I[e,j].  Fills every field of `map`;
+ * kept slots are expert-major and in arrival order within an expert. */
+moe_status_t moe_build_map(const int32_t *sel_idx, const float *sel_gate, const moe_route_cfg_t *cfg,
+                           const moe_route_map_t *map, void *ws, size_t ws_bytes, void *stream);
+
+/* Dispatch X_in = P X (page 2 "The math"): X_perm[s] = X[slot_token[s]]
+ * for s < n_kept (read on the device); rows n_kept..M_max-1 are left
+ * untouched.  X [n,d], X_perm [M_max,d] in `dtype`. */
+moe_status_t moe_dispatch(const void *X, int32_t dtype, int32_t n, int32_t d,
+                          const moe_route_map_t *map, int64_t M_max, void *X_perm, void *stream);
+
+/* Expert FFNs as one grouped GEMM (page 2 "The math": Y[e] =
+ * Expert_e(X_in[e]) on dense per-expert batches).  Rows
+ * expert_offset[e] .. expert_offset[e+1]-1 (device array [E+1]) of X_perm
+ * go through expert e: GELU: Y = gelu(X W1_e^T) W2_e^T; SwiGLU:
+ * Y = (silu(X Wg_e^T) * (X Wu_e^T)) W2_e^T.  bf16: fp32 accumulation on the
+ * matrix cores, the hidden activation rounded to bf16, d % 64 == 0 and
+ * f % 64 == 0.  fp32: fp32 throughout, any shape.  The always-on shared
+ * expert of page 5 strategy 3 is the same call with E = 1 and offsets
+ * {0, n}.  Rows >= expert_offset[E] of Y_perm are left untouched. */
+moe_status_t moe_expert_ffn(const void *X_perm, int32_t dtype, const int32_t *expert_offset,
+                            int32_t E, int32_t d, int32_t f, int32_t act, const void *W1,
+                            const void *W2, int64_t M_max, void *Y_perm, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* Combine out = scatter_add(G * Y, I) (page 2 "The math"), the gate applied
+ * to the expert output: for every token, out = residual + shared_out + sum
+ * of slot_gate[s] * Y_perm[s] over its token_slot list, in list order, fp32
+ * accumulation and one rounding to `dtype`.  residual and shared_out [n,d]
+ * are optional (NULL = 0).  A token with no kept slot and no shared expert
+ * gets its residual back bit for bit (page 1: dropped tokens pass through on
+ * the residual stream).  out [n,d]; must not alias the inputs. */
+moe_status_t moe_combine(const void *Y_perm, int32_t dtype, const moe_route_map_t *map, int32_t n,
+                         int32_t d, const void *residual, const void *shared_out, void *out,
+                         void *stream);
+
+/* Balance statistics (page 1 "What each direction guarantees": load-balance
+ * loss coefficient 0.01, router z-loss 0.001; page 4 "Pitfalls": monitor
+ * per-expert counts, one expert at 80% of traffic means collapse; page 5
+ * TL;DR: MaxVio).  Writes stats [MOE_NSTATS] fp32 (layout above) and, when
+ * non-NULL, hist [E+1] int32 = number of tokens keeping 0..E experts.
+ * Reads logits [n,E] and the map from moe_build_map. */
+moe_status_t moe_balance_stats(const float *logits, const moe_route_map_t *map,
+                               const moe_route_cfg_t *cfg, float lb_coef, float z_coef, float *stats,
+                               int32_t *hist, void *ws, size_t ws_bytes, void *stream);
+
+const char *moe_status_string(moe_status_t status);
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_DISPATCH_H */

@@ -360,18 +360,20 @@ def silu(h: np.ndarray) -> np.ndarray:
     return h / (1.0 + np.exp(-h))
 
 
-def expert_forward(xe: np.ndarray, w1: np.ndarray, w2: np.ndarray, act: str) -> np.ndarray:
-    """One expert FFN in float64: GELU: gelu(x W1^T) W2^T; SwiGLU:
-    (silu(x Wg^T) * (x Wu^T)) W2^T with W1 = [Wg; Wu] (gate rows first)."""
+def expert_hidden(xe: np.ndarray, w1: np.ndarray, act: str) -> np.ndarray:
+    """The expert's hidden activation in float64: GELU: gelu(x W1^T);
+    SwiGLU: silu(x Wg^T) * (x Wu^T) with W1 = [Wg; Wu] (gate rows first)."""
     x = widen(xe) if xe.dtype == np.uint16 else np.asarray(xe, dtype=np.float64)
     W1 = widen(w1)
-    W2 = widen(w2)
     if act == "gelu":
-        h = gelu(x @ W1.T)
-    else:
-        f = W1.shape[0] // 2
-        h = silu(x @ W1[:f].T) * (x @ W1[f:].T)
-    return h @ W2.T
+        return gelu(x @ W1.T)
+    f = W1.shape[0] // 2
+    return silu(x @ W1[:f].T) * (x @ W1[f:].T)
+
+
+def expert_forward(xe: np.ndarray, w1: np.ndarray, w2: np.ndarray, act: str) -> np.ndarray:
+    """One expert FFN in float64: hidden activation, then h W2^T."""
+    return expert_hidden(xe, w1, act) @ widen(w2).T
 
 
 def expert_ffn(x_perm: np.ndarray, expert_offset: np.ndarray, w1_of, w2_of, act: str,

@@ -1,0 +1,290 @@
+"""ctypes binding of libmoe_dispatch.so (the C ABI in include/moe_dispatch.h).
+
+Argument marshalling only: every function here checks tensor placement,
+dtype and contiguity, turns tensors into raw device pointers and calls the
+library, which does all the work in its HIP kernels.  PyTorch supplies device
+memory and the current stream.  There is no fallback: if the library is not
+built, or a call fails, an exception says so.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libmoe_dispatch.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SOFTMAX, MOE_SIGMOID = 0, 1
+MOE_TOKEN_CHOICE, MOE_EXPERT_CHOICE = 0, 1
+MOE_GELU, MOE_SWIGLU = 0, 1
+MOE_NSTATS = 8
+STAT_NAMES = ("lb_loss", "z_loss", "max_vio", "max_load_share", "n_kept", "n_dropped",
+              "tokens_without_expert", "max_experts_per_token")
+
+EXPORTED = ("moe_ec_k", "moe_tc_capacity", "moe_max_slots", "moe_router_workspace_size",
+            "moe_route_workspace_size", "moe_ffn_workspace_size", "moe_router", "moe_select",
+            "moe_build_map", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_balance_stats",
+            "moe_status_string", "moe_last_error")
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({detail})")
+        self.status = status
+
+
+class RouteCfg(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in
+                ("n", "d", "E", "k", "dir", "score", "n_group", "topk_group", "group_topm",
+                 "norm_topk", "capacity")]
+
+
+class RouteMapC(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in
+                ("expert_count", "expert_offset", "slot_token", "slot_gate", "assign_slot",
+                 "token_offset", "token_slot", "n_kept")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m sparse_expert_dispatch_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, F32, F64 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                                 ctypes.c_float, ctypes.c_double)
+    CFG = ctypes.POINTER(RouteCfg)
+    MAP = ctypes.POINTER(RouteMapC)
+    SZP = ctypes.POINTER(ctypes.c_size_t)
+    sig = {
+        "moe_ec_k": (I32, [I32, F64, I32]),
+        "moe_tc_capacity": (I32, [I32, I32, I32, F64]),
+        "moe_max_slots": (I64, [CFG]),
+        "moe_router_workspace_size": (I32, [CFG, I32, SZP]),
+        "moe_route_workspace_size": (I32, [CFG, SZP]),
+        "moe_ffn_workspace_size": (I32, [I64, I32, I32, I32, I32, I32, SZP]),
+        "moe_router": (I32, [P, P, I32, P, CFG, P, P, P, P, SZ, P]),
+        "moe_select": (I32, [P, P, P, CFG, P, P, P, SZ, P]),
+        "moe_build_map": (I32, [P, P, CFG, MAP, P, SZ, P]),
+        "moe_dispatch": (I32, [P, I32, I32, I32, MAP, I64, P, P]),
+        "moe_expert_ffn": (I32, [P, I32, P, I32, I32, I32, I32, P, P, I64, P, P, SZ, P]),
+        "moe_combine": (I32, [P, I32, MAP, I32, I32, P, P, P, P]),
+        "moe_balance_stats": (I32, [P, MAP, CFG, F32, F32, P, P, P, SZ, P]),
+        "moe_status_string": (ctypes.c_char_p, [I32]),
+        "moe_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+# ---------------------------------------------------------------- marshalling helpers
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtypes=None) -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return t.data_ptr()
+
+
+_BF16_STORAGE = (torch.bfloat16, torch.uint16, torch.int16)
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype in _BF16_STORAGE:
+        return MOE_BF16
+    raise TypeError(f"unsupported element type {t.dtype} (float32 or bfloat16)")
+
+
+def _elem_dtypes(code: int):
+    return _F32 if code == MOE_F32 else _BF16_STORAGE
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        L = lib()
+        raise MoEError(status, where, f"{L.moe_status_string(status).decode()}: "
+                                      f"{L.moe_last_error().decode()}")
+
+
+def make_cfg(n, d, E, k, direction=MOE_TOKEN_CHOICE, score=MOE_SOFTMAX, n_group=1, topk_group=1,
+             group_topm=1, norm_topk=1, capacity=-1) -> RouteCfg:
+    return RouteCfg(int(n), int(d), int(E), int(k), int(direction), int(score), int(n_group),
+                    int(topk_group), int(group_topm), int(norm_topk), int(capacity))
+
+
+class RouteMap:
+    """Device buffers of a routing map (allocated with torch)."""
+
+    FIELDS = ("expert_count", "expert_offset", "slot_token", "slot_gate", "assign_slot",
+              "token_offset", "token_slot", "n_kept")
+
+    def __init__(self, cfg: RouteCfg, device="cuda"):
+        M = moe_max_slots(cfg)
+        n, E, k = cfg.n, cfg.E, cfg.k
+        i32 = dict(dtype=torch.int32, device=device)
+        self.M_max = M
+        self.expert_count = torch.empty(E, **i32)
+        self.expert_offset = torch.empty(E + 1, **i32)
+        self.slot_token = torch.empty(M, **i32)
+        self.slot_gate = torch.empty(M, dtype=torch.float32, device=device)
+        self.assign_slot = torch.empty((n, k) if cfg.dir == MOE_TOKEN_CHOICE else (E, k), **i32)
+        self.token_offset = torch.empty(n + 1, **i32)
+        self.token_slot = torch.empty(M, **i32)
+        self.n_kept = torch.empty(1, **i32)
+
+    def c(self) -> RouteMapC:
+        return RouteMapC(*[getattr(self, f).data_ptr() for f in self.FIELDS])
+
+
+# ---------------------------------------------------------------- the C ABI, one to one
+
+def moe_ec_k(n: int, c: float, E: int) -> int:
+    return lib().moe_ec_k(int(n), float(c), int(E))
+
+
+def moe_tc_capacity(n: int, k: int, E: int, cf: float) -> int:
+    return lib().moe_tc_capacity(int(n), int(k), int(E), float(cf))
+
+
+def moe_max_slots(cfg: RouteCfg) -> int:
+    v = lib().moe_max_slots(ctypes.byref(cfg))
+    if v < 0:
+        _check(MOE_ERR_INVALID_ARG, "moe_max_slots")
+    return v
+
+
+def moe_router_workspace_size(cfg: RouteCfg, dtype: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().moe_router_workspace_size(ctypes.byref(cfg), int(dtype), ctypes.byref(out)),
+           "moe_router_workspace_size")
+    return out.value
+
+
+def moe_route_workspace_size(cfg: RouteCfg) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().moe_route_workspace_size(ctypes.byref(cfg), ctypes.byref(out)),
+           "moe_route_workspace_size")
+    return out.value
+
+
+def moe_ffn_workspace_size(M_max: int, E: int, d: int, f: int, act: int, dtype: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().moe_ffn_workspace_size(int(M_max), int(E), int(d), int(f), int(act), int(dtype),
+                                        ctypes.byref(out)), "moe_ffn_workspace_size")
+    return out.value
+
+
+def _ws(ws: Optional[torch.Tensor]):
+    if ws is None:
+        return None, 0
+    return _ptr(ws, "ws"), ws.numel() * ws.element_size()
+
+
+def moe_router(x, wg, logit_offset, cfg: RouteCfg, logits, scores=None, scores_t=None, ws=None,
+               stream=None):
+    code = dtype_code(x)
+    w, wb = _ws(ws)
+    _check(lib().moe_router(_ptr(x, "x", _elem_dtypes(code)), _ptr(wg, "wg", _elem_dtypes(code)), code,
+                            _ptr(logit_offset, "logit_offset", _F32), ctypes.byref(cfg),
+                            _ptr(logits, "logits", _F32), _ptr(scores, "scores", _F32),
+                            _ptr(scores_t, "scores_t", _F32), w, wb, _stream(stream)), "moe_router")
+
+
+def moe_select(logits, scores_t, sel_bias, cfg: RouteCfg, sel_idx, sel_gate, ws=None, stream=None):
+    w, wb = _ws(ws)
+    _check(lib().moe_select(_ptr(logits, "logits", _F32), _ptr(scores_t, "scores_t", _F32),
+                            _ptr(sel_bias, "sel_bias", _F32), ctypes.byref(cfg),
+                            _ptr(sel_idx, "sel_idx", _I32), _ptr(sel_gate, "sel_gate", _F32), w, wb,
+                            _stream(stream)), "moe_select")
+
+
+def moe_build_map(sel_idx, sel_gate, cfg: RouteCfg, rmap: RouteMap, ws=None, stream=None):
+    w, wb = _ws(ws)
+    cm = rmap.c()
+    _check(lib().moe_build_map(_ptr(sel_idx, "sel_idx", _I32), _ptr(sel_gate, "sel_gate", _F32),
+                               ctypes.byref(cfg), ctypes.byref(cm), w, wb, _stream(stream)),
+           "moe_build_map")
+
+
+def moe_dispatch(x, rmap: RouteMap, x_perm, stream=None):
+    code = dtype_code(x)
+    n, d = x.shape
+    cm = rmap.c()
+    _check(lib().moe_dispatch(_ptr(x, "x", _elem_dtypes(code)), code, int(n), int(d), ctypes.byref(cm),
+                              int(x_perm.shape[0]), _ptr(x_perm, "x_perm", _elem_dtypes(code)),
+                              _stream(stream)), "moe_dispatch")
+
+
+def moe_expert_ffn(x_perm, expert_offset, w1, w2, act: int, y_perm, ws, stream=None):
+    code = dtype_code(x_perm)
+    E = expert_offset.numel() - 1
+    d = x_perm.shape[1]
+    f = w2.shape[-1]
+    w, wb = _ws(ws)
+    _check(lib().moe_expert_ffn(_ptr(x_perm, "x_perm", _elem_dtypes(code)), code,
+                                _ptr(expert_offset, "expert_offset", _I32), int(E), int(d), int(f),
+                                int(act), _ptr(w1, "w1", _elem_dtypes(code)),
+                                _ptr(w2, "w2", _elem_dtypes(code)), int(x_perm.shape[0]),
+                                _ptr(y_perm, "y_perm", _elem_dtypes(code)), w, wb, _stream(stream)),
+           "moe_expert_ffn")
+
+
+def moe_combine(y_perm, rmap: RouteMap, n: int, residual, shared_out, out, stream=None):
+    code = dtype_code(y_perm)
+    cm = rmap.c()
+    _check(lib().moe_combine(_ptr(y_perm, "y_perm", _elem_dtypes(code)), code, ctypes.byref(cm),
+                             int(n), int(out.shape[1]), _ptr(residual, "residual", _elem_dtypes(code)),
+                             _ptr(shared_out, "shared_out", _elem_dtypes(code)),
+                             _ptr(out, "out", _elem_dtypes(code)), _stream(stream)), "moe_combine")
+
+
+def moe_balance_stats(logits, rmap: RouteMap, cfg: RouteCfg, lb_coef, z_coef, stats, hist=None,
+                      ws=None, stream=None):
+    w, wb = _ws(ws)
+    cm = rmap.c()
+    _check(lib().moe_balance_stats(_ptr(logits, "logits", _F32), ctypes.byref(cm), ctypes.byref(cfg),
+                                   float(lb_coef), float(z_coef), _ptr(stats, "stats", _F32),
+                                   _ptr(hist, "hist", _I32), w, wb, _stream(stream)),
+           "moe_balance_stats")
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()

@@ -1,0 +1,304 @@
+// C ABI of the MoE-layer forward: host-side validation, workspace sizing and
+// launches.  Every entry point checks its arguments before the first HIP
+// call, so argument errors are reported (and testable) without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/moe_dispatch.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status_t fail(moe_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+moe_status_t launched(hipError_t err, const char* what) {
+  if (err != hipSuccess) return fail(MOE_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(err));
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE(cond, ...)                                          \
+  do {                                                              \
+    if (!(cond)) return fail(MOE_ERR_INVALID_ARG, __VA_ARGS__);     \
+  } while (0)
+#define SUPPORTED(cond, ...)                                        \
+  do {                                                              \
+    if (!(cond)) return fail(MOE_ERR_UNSUPPORTED, __VA_ARGS__);     \
+  } while (0)
+
+moe_status_t check_cfg(const moe_route_cfg_t* c) {
+  REQUIRE(c != nullptr, "cfg is NULL");
+  REQUIRE(c->n > 0 && c->d > 0 && c->E > 0 && c->k > 0, "n, d, E, k must be positive (n=%d d=%d E=%d k=%d)",
+          c->n, c->d, c->E, c->k);
+  REQUIRE(c->dir == MOE_TOKEN_CHOICE || c->dir == MOE_EXPERT_CHOICE, "dir must be 0 or 1");
+  REQUIRE(c->score == MOE_SOFTMAX || c->score == MOE_SIGMOID, "score must be 0 or 1");
+  REQUIRE(c->norm_topk == 0 || c->norm_topk == 1, "norm_topk must be 0 or 1");
+  SUPPORTED(c->E <= moe::kMaxExperts, "E=%d exceeds the supported %d experts", c->E, moe::kMaxExperts);
+  if (c->dir == MOE_TOKEN_CHOICE) {
+    REQUIRE(c->k <= c->E, "token choice needs k <= E (k=%d E=%d)", c->k, c->E);
+    SUPPORTED(c->k <= 64, "token choice supports k <= 64 (k=%d)", c->k);
+    REQUIRE((int64_t)c->n * c->k <= INT32_MAX, "n*k overflows int32");
+    REQUIRE(c->n_group >= 1 && c->E % c->n_group == 0, "E=%d must be a multiple of n_group=%d", c->E,
+            c->n_group);
+    SUPPORTED(c->n_group <= 64, "n_group <= 64");
+    REQUIRE(c->topk_group >= 1 && c->topk_group <= c->n_group, "need 1 <= topk_group <= n_group");
+    REQUIRE(c->group_topm >= 1 && c->group_topm <= c->E / c->n_group,
+            "need 1 <= group_topm <= experts per group");
+    SUPPORTED(c->group_topm <= 4, "group_topm <= 4");
+    REQUIRE(c->k <= c->topk_group * (c->E / c->n_group),
+            "k=%d exceeds the experts of the %d kept groups", c->k, c->topk_group);
+    REQUIRE(c->capacity >= -1, "capacity must be >= -1 (-1 = dropless)");
+  } else {
+    REQUIRE(c->k <= c->n, "expert choice needs k <= n (k=%d n=%d)", c->k, c->n);
+    SUPPORTED(c->score == MOE_SOFTMAX, "expert choice selects on softmax scores");
+    SUPPORTED(c->n_group == 1, "expert choice has no group limit");
+    SUPPORTED(c->n <= (1 << 24), "expert choice supports n <= 2^24");
+    REQUIRE((int64_t)c->E * c->k <= INT32_MAX, "E*k overflows int32");
+  }
+  return MOE_OK;
+}
+
+moe_status_t check_map(const moe_route_map_t* m) {
+  REQUIRE(m != nullptr, "map is NULL");
+  REQUIRE(m->expert_count && m->expert_offset && m->slot_token && m->slot_gate && m->assign_slot &&
+              m->token_offset && m->token_slot && m->n_kept,
+          "every routing-map buffer must be non-NULL");
+  return MOE_OK;
+}
+
+moe::MapPtrs map_ptrs(const moe_route_map_t* m) {
+  return moe::MapPtrs{m->expert_count, m->expert_offset, m->slot_token, m->slot_gate,
+                      m->assign_slot,  m->token_offset,  m->token_slot, m->n_kept};
+}
+
+size_t route_ws(const moe_route_cfg_t* c) {
+  size_t b = moe::map_workspace_bytes(c->dir, c->n, c->E, c->k);
+  const size_t s = moe::stats_workspace_bytes(c->n, c->E);
+  if (s > b) b = s;
+  if (c->dir == MOE_EXPERT_CHOICE) {
+    const size_t e = moe::select_ec_workspace_bytes(c->n, c->E);
+    if (e > b) b = e;
+  }
+  return b;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_ec_k(int32_t n, double c, int32_t E) {
+  if (n <= 0 || E <= 0 || !(c > 0.0)) return -1;
+  const double v = std::floor((double)n * c / (double)E + 0.5);
+  return v > (double)INT32_MAX ? -1 : (int32_t)v;
+}
+
+int32_t moe_tc_capacity(int32_t n, int32_t k, int32_t E, double cf) {
+  if (n <= 0 || k <= 0 || E <= 0 || !(cf >= 0.0)) return -1;
+  const double v = std::floor(cf * (double)k * (double)n / (double)E + 0.5);
+  return v > (double)INT32_MAX ? -1 : (int32_t)v;
+}
+
+int64_t moe_max_slots(const moe_route_cfg_t* cfg) {
+  if (check_cfg(cfg) != MOE_OK) return -1;
+  if (cfg->dir == MOE_EXPERT_CHOICE) return (int64_t)cfg->E * cfg->k;
+  const int64_t nk = (int64_t)cfg->n * cfg->k;
+  if (cfg->capacity < 0) return nk;
+  const int64_t cap = (int64_t)cfg->E * cfg->capacity;
+  return cap < nk ? cap : nk;
+}
+
+moe_status_t moe_router_workspace_size(const moe_route_cfg_t* cfg, int32_t dtype, size_t* bytes) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  REQUIRE(bytes != nullptr, "bytes is NULL");
+  REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, "dtype must be MOE_F32 or MOE_BF16");
+  *bytes = moe::router_workspace_bytes(cfg->n, cfg->d, cfg->E, dtype);
+  return MOE_OK;
+}
+
+moe_status_t moe_route_workspace_size(const moe_route_cfg_t* cfg, size_t* bytes) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  REQUIRE(bytes != nullptr, "bytes is NULL");
+  *bytes = route_ws(cfg);
+  return MOE_OK;
+}
+
+moe_status_t moe_ffn_workspace_size(int64_t M_max, int32_t E, int32_t d, int32_t f, int32_t act,
+                                    int32_t dtype, size_t* bytes) {
+  REQUIRE(bytes != nullptr, "bytes is NULL");
+  REQUIRE(M_max > 0 && E > 0 && d > 0 && f > 0, "M_max, E, d, f must be positive");
+  REQUIRE(act == MOE_GELU || act == MOE_SWIGLU, "act must be MOE_GELU or MOE_SWIGLU");
+  REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, "dtype must be MOE_F32 or MOE_BF16");
+  *bytes = moe::ffn_workspace_bytes(M_max, E, d, f, act, dtype);
+  return MOE_OK;
+}
+
+moe_status_t moe_router(const void* X, const void* Wg, int32_t dtype, const float* logit_offset,
+                        const moe_route_cfg_t* cfg, float* logits, float* scores, float* scores_t,
+                        void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  REQUIRE(X && Wg && logits, "X, Wg and logits must be non-NULL");
+  REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, "dtype must be MOE_F32 or MOE_BF16");
+  if (dtype == MOE_BF16 && cfg->d % 64 == 0 && cfg->E % 16 == 0)   // the matrix-core path
+    REQUIRE(aligned16(X) && aligned16(Wg), "X and Wg must be 16-byte aligned");
+  const size_t need = moe::router_workspace_bytes(cfg->n, cfg->d, cfg->E, dtype);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "router needs %zu workspace bytes, got %zu", need, ws_bytes);
+  return launched(moe::launch_router(X, Wg, dtype, logit_offset, cfg->n, cfg->d, cfg->E, cfg->score,
+                                     logits, scores, scores_t, ws, as_stream(stream)),
+                  "moe_router");
+}
+
+moe_status_t moe_select(const float* logits, const float* scores_t, const float* sel_bias,
+                        const moe_route_cfg_t* cfg, int32_t* sel_idx, float* sel_gate, void* ws,
+                        size_t ws_bytes, void* stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  REQUIRE(sel_idx && sel_gate, "sel_idx and sel_gate must be non-NULL");
+  if (cfg->dir == MOE_TOKEN_CHOICE) {
+    REQUIRE(logits, "logits must be non-NULL");
+    moe::SelectArgs a{cfg->n, cfg->E, cfg->k, cfg->score, cfg->n_group, cfg->topk_group,
+                      cfg->group_topm, cfg->norm_topk};
+    return launched(moe::launch_select_tc(logits, sel_bias, a, sel_idx, sel_gate, as_stream(stream)),
+                    "moe_select");
+  }
+  REQUIRE(logits || scores_t, "expert choice needs logits or scores_t");
+  if (!scores_t) {
+    const size_t need = moe::select_ec_workspace_bytes(cfg->n, cfg->E);
+    if (!ws || ws_bytes < need)
+      return fail(MOE_ERR_WORKSPACE, "select needs %zu workspace bytes, got %zu", need, ws_bytes);
+  }
+  return launched(moe::launch_select_ec(logits, scores_t, cfg->n, cfg->E, cfg->k, sel_idx, sel_gate,
+                                        ws, as_stream(stream)),
+                  "moe_select");
+}
+
+moe_status_t moe_build_map(const int32_t* sel_idx, const float* sel_gate, const moe_route_cfg_t* cfg,
+                           const moe_route_map_t* map, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  st = check_map(map);
+  if (st != MOE_OK) return st;
+  REQUIRE(sel_idx && sel_gate, "sel_idx and sel_gate must be non-NULL");
+  const size_t need = moe::map_workspace_bytes(cfg->dir, cfg->n, cfg->E, cfg->k);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "build_map needs %zu workspace bytes, got %zu", need, ws_bytes);
+  const moe::MapPtrs m = map_ptrs(map);
+  if (cfg->dir == MOE_TOKEN_CHOICE)
+    return launched(moe::launch_build_map_tc(sel_idx, sel_gate, cfg->n, cfg->E, cfg->k, cfg->capacity, m,
+                                             ws, as_stream(stream)),
+                    "moe_build_map");
+  return launched(moe::launch_build_map_ec(sel_idx, sel_gate, cfg->n, cfg->E, cfg->k, m, ws,
+                                           as_stream(stream)),
+                  "moe_build_map");
+}
+
+moe_status_t moe_dispatch(const void* X, int32_t dtype, int32_t n, int32_t d, const moe_route_map_t* map,
+                          int64_t M_max, void* X_perm, void* stream) {
+  REQUIRE(X && X_perm, "X and X_perm must be non-NULL");
+  REQUIRE(map && map->slot_token && map->n_kept, "map->slot_token and map->n_kept must be non-NULL");
+  REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, "dtype must be MOE_F32 or MOE_BF16");
+  REQUIRE(n > 0 && d > 0 && M_max > 0, "n, d, M_max must be positive");
+  REQUIRE(M_max <= (int64_t)INT32_MAX * 4, "M_max too large");
+  const int eb = dtype == MOE_BF16 ? 2 : 4;
+  if (((int64_t)d * eb) % 16 == 0)
+    REQUIRE(aligned16(X) && aligned16(X_perm), "X and X_perm must be 16-byte aligned");
+  return launched(moe::launch_dispatch(X, eb, n, d, map->slot_token, map->n_kept, M_max, X_perm,
+                                       as_stream(stream)),
+                  "moe_dispatch");
+}
+
+moe_status_t moe_expert_ffn(const void* X_perm, int32_t dtype, const int32_t* expert_offset, int32_t E,
+                            int32_t d, int32_t f, int32_t act, const void* W1, const void* W2,
+                            int64_t M_max, void* Y_perm, void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(X_perm && expert_offset && W1 && W2 && Y_perm, "tensor arguments must be non-NULL");
+  REQUIRE(E > 0 && d > 0 && f > 0 && M_max > 0, "E, d, f, M_max must be positive");
+  REQUIRE(act == MOE_GELU || act == MOE_SWIGLU, "act must be MOE_GELU or MOE_SWIGLU");
+  REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, "dtype must be MOE_F32 or MOE_BF16");
+  REQUIRE(M_max <= INT32_MAX, "M_max must fit in int32");
+  if (dtype == MOE_BF16) {
+    SUPPORTED(d % 64 == 0 && f % 64 == 0, "bf16 expert FFN needs d %% 64 == 0 and f %% 64 == 0 (d=%d f=%d)",
+              d, f);
+    REQUIRE(aligned16(X_perm) && aligned16(W1) && aligned16(W2) && aligned16(Y_perm),
+            "bf16 tensors must be 16-byte aligned");
+  }
+  const size_t need = moe::ffn_workspace_bytes(M_max, E, d, f, act, dtype);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "expert_ffn needs %zu workspace bytes, got %zu", need, ws_bytes);
+  REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
+  return launched(moe::launch_expert_ffn(X_perm, dtype, expert_offset, E, d, f, act, W1, W2, M_max,
+                                         Y_perm, ws, as_stream(stream)),
+                  "moe_expert_ffn");
+}
+
+moe_status_t moe_combine(const void* Y_perm, int32_t dtype, const moe_route_map_t* map, int32_t n,
+                         int32_t d, const void* residual, const void* shared_out, void* out,
+                         void* stream) {
+  REQUIRE(Y_perm && out, "Y_perm and out must be non-NULL");
+  REQUIRE(map && map->token_offset && map->token_slot && map->slot_gate,
+          "map->token_offset, token_slot and slot_gate must be non-NULL");
+  REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, "dtype must be MOE_F32 or MOE_BF16");
+  REQUIRE(n > 0 && d > 0, "n, d must be positive");
+  REQUIRE(out != Y_perm && out != residual && out != shared_out, "out must not alias an input");
+  const int vec = dtype == MOE_BF16 ? 8 : 4;
+  if (d % vec == 0)
+    REQUIRE(aligned16(Y_perm) && aligned16(out) && (!residual || aligned16(residual)) &&
+                (!shared_out || aligned16(shared_out)),
+            "tensors must be 16-byte aligned");
+  return launched(moe::launch_combine(Y_perm, dtype, map->token_offset, map->token_slot, map->slot_gate, n,
+                                      d, residual, shared_out, out, as_stream(stream)),
+                  "moe_combine");
+}
+
+moe_status_t moe_balance_stats(const float* logits, const moe_route_map_t* map,
+                               const moe_route_cfg_t* cfg, float lb_coef, float z_coef, float* stats,
+                               int32_t* hist, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  REQUIRE(logits && stats, "logits and stats must be non-NULL");
+  REQUIRE(map && map->expert_count && map->expert_offset && map->token_offset,
+          "map->expert_count, expert_offset and token_offset must be non-NULL");
+  const size_t need = moe::stats_workspace_bytes(cfg->n, cfg->E);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "balance_stats needs %zu workspace bytes, got %zu", need, ws_bytes);
+  return launched(moe::launch_balance_stats(logits, map_ptrs(map), cfg->n, cfg->E, cfg->k, cfg->dir,
+                                            cfg->score, lb_coef, z_coef, stats, hist, ws,
+                                            as_stream(stream)),
+                  "moe_balance_stats");
+}
+
+const char* moe_status_string(moe_status_t status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// Internal launch interface between the C ABI layer (api.cpp) and the HIP
+// kernels.  Launchers enqueue on `stream` and return hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxExperts = 512;      // experts per layer
+constexpr int kMaxExpertRegs = kMaxExperts / 64;
+
+#ifdef __HIPCC__
+// Halving-stride tree sum of a zero-padded power-of-two row of length P
+// held as lane l, register j -> element l + 64 j.  Passes with a stride of
+// 64 s elements are in-register (j += s); the last six are across lanes.
+// Returns the sum in every lane; `row` is not modified.
+template <int R>
+__device__ __forceinline__ float row_tree_sum(const float (&row)[R], int P) {
+#pragma clang fp contract(off)
+  float t[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) t[j] = row[j];
+#pragma unroll
+  for (int s = R / 2; s >= 1; s >>= 1) {
+    if (s < (P >> 6)) {
+#pragma unroll
+      for (int j = 0; j < s; ++j) t[j] = t[j] + t[j + s];
+    }
+  }
+  float v = t[0];
+  const int Pw = P < 64 ? P : 64;
+  for (int s = Pw >> 1; s >= 1; s >>= 1) v = v + __shfl_down(v, s, 64);
+  return __shfl(v, 0, 64);
+}
+#endif
+
+// router.hip
+size_t router_workspace_bytes(int n, int d, int E, int dtype);
+hipError_t launch_router(const void* X, const void* Wg, int dtype, const float* offset, int n, int d,
+                         int E, int score, float* logits, float* scores, float* scores_t, void* ws,
+                         hipStream_t stream);
+
+// Scores (and/or their transpose) from finished logits: the router's
+// epilogue on its own; `logits` may be NULL.
+hipError_t launch_router_finalize(const float* partial, int nsplit, int n, int E, const float* offset,
+                                  int score, float* logits, float* scores, float* scores_t,
+                                  hipStream_t stream);
+
+// select.hip
+struct SelectArgs {
+  int n, E, k, score, n_group, topk_group, group_topm, norm_topk;
+};
+hipError_t launch_select_tc(const float* logits, const float* bias, const SelectArgs& a, int32_t* idx,
+                            float* gate, hipStream_t stream);
+size_t select_ec_workspace_bytes(int n, int E);
+hipError_t launch_select_ec(const float* logits, const float* scores_t, int n, int E, int k,
+                            int32_t* I, float* G, void* ws, hipStream_t stream);
+
+// route_map.hip
+struct MapPtrs {
+  int32_t* expert_count;
+  int32_t* expert_offset;
+  int32_t* slot_token;
+  float* slot_gate;
+  int32_t* assign_slot;
+  int32_t* token_offset;
+  int32_t* token_slot;
+  int32_t* n_kept;
+};
+size_t map_workspace_bytes(int dir, int n, int E, int k);
+hipError_t launch_build_map_tc(const int32_t* idx, const float* gate, int n, int E, int k,
+                               int capacity, const MapPtrs& m, void* ws, hipStream_t stream);
+hipError_t launch_build_map_ec(const int32_t* I, const float* G, int n, int E, int k,
+                               const MapPtrs& m, void* ws, hipStream_t stream);
+
+// permute.hip
+hipError_t launch_dispatch(const void* X, int elem_bytes, int n, int d, const int32_t* slot_token,
+                           const int32_t* n_kept, int64_t M_max, void* X_perm, hipStream_t stream);
+hipError_t launch_combine(const void* Y, int dtype, const int32_t* token_offset,
+                          const int32_t* token_slot, const float* slot_gate, int n, int d,
+                          const void* residual, const void* shared, void* out, hipStream_t stream);
+
+// grouped_gemm.hip
+size_t ffn_workspace_bytes(int64_t M_max, int E, int d, int f, int act, int dtype);
+hipError_t launch_expert_ffn(const void* X_perm, int dtype, const int32_t* expert_offset, int E,
+                             int d, int f, int act, const void* W1, const void* W2, int64_t M_max,
+                             void* Y_perm, void* ws, hipStream_t stream);
+
+// stats.hip
+size_t stats_workspace_bytes(int n, int E);
+hipError_t launch_balance_stats(const float* logits, const MapPtrs& m, int n, int E, int k, int dir,
+                                int score, float lb_coef, float z_coef, float* stats, int32_t* hist,
+                                void* ws, hipStream_t stream);
+
+}  // namespace moe

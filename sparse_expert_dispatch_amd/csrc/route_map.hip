@@ -1,0 +1,268 @@
+// Routing map: per-expert counts and offsets, the capacity rule in token
+// arrival order, the expert-major slot table, and the token-side lists the
+// combine walks.
+//
+// MoE-routing pages: page 1 "Token choice vs expert choice routing",
+// section "Dropped tokens flow in opposite directions" (a fixed per-expert
+// buffer; tokens arriving after it fills skip the expert and pass through
+// on the residual; dropless computes every assignment); page 5 "MoE routing
+// strategies explained", strategy 2 (overflow tokens skip the layer through
+// the residual connection); page 2 "Expert choice routing", section "The
+// math" (P = onehot(I): slot e*k + j carries token I[e, j]).
+//
+// Token choice runs as a stable counting sort of the n*k arrivals by expert:
+//  1. chunk histograms (LDS integer atomics; counts are order-free),
+//  2. one workgroup turns them into per-chunk starting positions per expert
+//     (a scan over chunks in chunk order) and expert offsets of the kept
+//     rows (a scan over experts),
+//  3. one wave per chunk walks its arrivals in order, 64 at a time: lanes
+//     with the same expert find each other with one ballot per expert-id
+//     bit, their rank inside the wave is a popcount, and a per-expert LDS
+//     counter carries the running position across iterations.  A position
+//     below the capacity is kept; its slot is offset[e] + position.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int kMapChunk = 1024;      // arrivals per chunk
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(256) void map_chunk_hist_kernel(const int32_t* __restrict__ idx,
+                                                             int64_t M, int E,
+                                                             int32_t* __restrict__ chunk_hist) {
+  extern __shared__ int sh[];
+  for (int e = threadIdx.x; e < E; e += 256) sh[e] = 0;
+  __syncthreads();
+  const int64_t a0 = (int64_t)blockIdx.x * kMapChunk;
+  for (int i = threadIdx.x; i < kMapChunk; i += 256) {
+    const int64_t a = a0 + i;
+    if (a < M) {
+      const int e = idx[a];
+      if ((unsigned)e < (unsigned)E) atomicAdd(&sh[e], 1);   // out-of-range ids are dropped
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) chunk_hist[(size_t)blockIdx.x * E + e] = sh[e];
+}
+
+// One workgroup: thread e scans expert e's chunk counts in chunk order; then
+// a workgroup scan over experts of the kept counts gives the slot offsets.
+__global__ __launch_bounds__(kScanThreads) void map_scan_kernel(
+    const int32_t* __restrict__ chunk_hist, int nchunks, int E, int capacity,
+    int32_t* __restrict__ chunk_base, int32_t* __restrict__ expert_count,
+    int32_t* __restrict__ expert_offset, int32_t* __restrict__ n_kept) {
+  __shared__ int scratch[kScanThreads / 64];
+  const int e = threadIdx.x;
+  int kept = 0;
+  if (e < E) {
+    int run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = chunk_hist[(size_t)c * E + e];
+      chunk_base[(size_t)c * E + e] = run;
+      run += v;
+    }
+    expert_count[e] = run;
+    kept = capacity < 0 ? run : min(run, capacity);
+  }
+  int total = 0;
+  const int off = block_exclusive_scan<kScanThreads>(kept, scratch, &total);
+  if (e < E) expert_offset[e] = off;
+  if (e == 0) {
+    expert_offset[E] = total;
+    *n_kept = total;
+  }
+}
+
+__global__ __launch_bounds__(64) void map_scatter_kernel(
+    const int32_t* __restrict__ idx, const float* __restrict__ gate, int64_t M, int k, int E,
+    int nbits, int capacity, const int32_t* __restrict__ chunk_base,
+    const int32_t* __restrict__ expert_offset, int32_t* __restrict__ slot_token,
+    float* __restrict__ slot_gate, int32_t* __restrict__ assign_slot) {
+  extern __shared__ int cnt[];
+  const int lane = threadIdx.x;
+  const int c = blockIdx.x;
+  for (int e = lane; e < E; e += 64) cnt[e] = chunk_base[(size_t)c * E + e];
+  __syncthreads();
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  const int64_t a0 = (int64_t)c * kMapChunk;
+  for (int it = 0; it < kMapChunk; it += 64) {
+    const int64_t a = a0 + it + lane;
+    const bool inrange = a < M;
+    const int e_raw = inrange ? idx[a] : 0;
+    const bool valid = inrange && (unsigned)e_raw < (unsigned)E;
+    const int e = valid ? e_raw : 0;
+    uint64_t match = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      match &= bit ? bal : ~bal;
+    }
+    // every lane reads its expert's running position before any lane of
+    // this wave updates it (the update below depends on the value read)
+    const int base = valid ? cnt[e] : 0;
+    const int rank = __popcll(match & lt_mask);
+    const int pos = base + rank;
+    const bool last = valid && (match >> lane) == 1ull;
+    if (last) cnt[e] = base + __popcll(match);
+    if (inrange) {
+      int32_t s = -1;
+      if (valid && (capacity < 0 || pos < capacity)) {
+        s = expert_offset[e] + pos;
+        slot_token[s] = (int32_t)(a / k);
+        slot_gate[s] = gate[a];
+      }
+      assign_slot[a] = s;
+    }
+  }
+}
+
+// Token-side lists.  One workgroup: each thread owns a contiguous run of
+// tokens, counts their kept assignments, and a workgroup scan turns the
+// counts into token_offset.
+template <int DIR>
+__global__ __launch_bounds__(kScanThreads) void token_offsets_kernel(
+    const int32_t* __restrict__ assign_slot, const uint32_t* __restrict__ mask, int n, int k, int W,
+    int32_t* __restrict__ token_offset) {
+  __shared__ int scratch[kScanThreads / 64];
+  const int seg = (n + kScanThreads - 1) / kScanThreads;
+  const int t0 = min(n, (int)threadIdx.x * seg), t1 = min(n, t0 + seg);
+  auto count = [&](int t) {
+    int c = 0;
+    if (DIR == 0) {
+      for (int r = 0; r < k; ++r) c += assign_slot[(size_t)t * k + r] >= 0 ? 1 : 0;
+    } else {
+      for (int w = 0; w < W; ++w) c += __popc(mask[(size_t)t * W + w]);
+    }
+    return c;
+  };
+  int sum = 0;
+  for (int t = t0; t < t1; ++t) sum += count(t);
+  int total = 0;
+  int run = block_exclusive_scan<kScanThreads>(sum, scratch, &total);
+  for (int t = t0; t < t1; ++t) {
+    token_offset[t] = run;
+    run += count(t);
+  }
+  if (threadIdx.x == 0) token_offset[n] = total;
+}
+
+__global__ __launch_bounds__(256) void token_fill_tc_kernel(const int32_t* __restrict__ assign_slot,
+                                                            const int32_t* __restrict__ token_offset,
+                                                            int n, int k,
+                                                            int32_t* __restrict__ token_slot) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= n) return;
+  int q = token_offset[t];
+  for (int r = 0; r < k; ++r) {
+    const int s = assign_slot[(size_t)t * k + r];
+    if (s >= 0) token_slot[q++] = s;
+  }
+}
+
+// ---------------------------------------------------------------- expert choice
+
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p, int64_t count,
+                                                       uint32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < count) p[i] = v;
+}
+
+__global__ __launch_bounds__(256) void ec_slots_kernel(const int32_t* __restrict__ I,
+                                                       const float* __restrict__ G, int n, int E, int k,
+                                                       int W, MapPtrs m, uint32_t* __restrict__ mask) {
+  const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (s >= (int64_t)E * k) return;
+  const int e = (int)(s / k);
+  const int t = I[s];
+  m.slot_token[s] = t;
+  m.slot_gate[s] = G[s];
+  m.assign_slot[s] = (int32_t)s;
+  if ((unsigned)t < (unsigned)n) atomicOr(&mask[(size_t)t * W + (e >> 5)], 1u << (e & 31));
+  if (s - (int64_t)e * k == 0) {
+    m.expert_count[e] = k;
+    m.expert_offset[e] = e * k;
+    if (e == E - 1) {
+      m.expert_offset[E] = E * k;
+      *m.n_kept = E * k;
+    }
+  }
+}
+
+// A token's experts in ascending expert order; the slot of (token t,
+// expert e) is e*k + j with I[e, j] = t, found by binary search in the
+// ascending row I[e, :].
+__global__ __launch_bounds__(256) void token_fill_ec_kernel(const int32_t* __restrict__ I,
+                                                            const uint32_t* __restrict__ mask,
+                                                            const int32_t* __restrict__ token_offset,
+                                                            int n, int k, int W,
+                                                            int32_t* __restrict__ token_slot) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= n) return;
+  int q = token_offset[t];
+  for (int w = 0; w < W; ++w) {
+    uint32_t bits = mask[(size_t)t * W + w];
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      const int e = 32 * w + b;
+      const int32_t* row = I + (size_t)e * k;
+      int lo = 0, hi = k;             // first j with row[j] >= t
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (row[mid] < t) lo = mid + 1; else hi = mid;
+      }
+      token_slot[q++] = e * k + lo;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- host side
+
+static int chunks_of(int64_t M) { return (int)((M + kMapChunk - 1) / kMapChunk); }
+
+size_t map_workspace_bytes(int dir, int n, int E, int k) {
+  if (dir == 0) return (size_t)2 * chunks_of((int64_t)n * k) * E * sizeof(int32_t);
+  return (size_t)n * ((E + 31) / 32) * sizeof(uint32_t);
+}
+
+hipError_t launch_build_map_tc(const int32_t* idx, const float* gate, int n, int E, int k,
+                               int capacity, const MapPtrs& m, void* ws, hipStream_t stream) {
+  const int64_t M = (int64_t)n * k;
+  const int nch = chunks_of(M);
+  int32_t* chunk_hist = static_cast<int32_t*>(ws);
+  int32_t* chunk_base = chunk_hist + (size_t)nch * E;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  hipLaunchKernelGGL(map_chunk_hist_kernel, dim3(nch), dim3(256), E * sizeof(int), stream, idx, M, E,
+                     chunk_hist);
+  hipLaunchKernelGGL(map_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, chunk_hist, nch, E,
+                     capacity, chunk_base, m.expert_count, m.expert_offset, m.n_kept);
+  hipLaunchKernelGGL(map_scatter_kernel, dim3(nch), dim3(64), E * sizeof(int), stream, idx, gate, M,
+                     k, E, nbits, capacity, chunk_base, m.expert_offset, m.slot_token, m.slot_gate,
+                     m.assign_slot);
+  hipLaunchKernelGGL(token_offsets_kernel<0>, dim3(1), dim3(kScanThreads), 0, stream, m.assign_slot,
+                     nullptr, n, k, 0, m.token_offset);
+  hipLaunchKernelGGL(token_fill_tc_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, m.assign_slot,
+                     m.token_offset, n, k, m.token_slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_map_ec(const int32_t* I, const float* G, int n, int E, int k,
+                               const MapPtrs& m, void* ws, hipStream_t stream) {
+  const int W = (E + 31) / 32;
+  uint32_t* mask = static_cast<uint32_t*>(ws);
+  const int64_t words = (int64_t)n * W;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
+                     mask, words, 0u);
+  const int64_t M = (int64_t)E * k;
+  hipLaunchKernelGGL(ec_slots_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, stream, I, G, n,
+                     E, k, W, m, mask);
+  hipLaunchKernelGGL(token_offsets_kernel<1>, dim3(1), dim3(kScanThreads), 0, stream, nullptr, mask, n,
+                     k, W, m.token_offset);
+  hipLaunchKernelGGL(token_fill_ec_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, I, mask,
+                     m.token_offset, n, k, W, m.token_slot);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,121 @@
+"""MoELayer: the layer forward as a sequence of the library's calls.
+
+Allocation and sequencing only.  Every step (router, selection, routing
+map, dispatch, expert FFNs, combine, statistics) is one call into
+libmoe_dispatch.so on the current stream; no arithmetic happens here.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _native as N
+
+
+def _bytes(n: int, device) -> torch.Tensor:
+    # float64 storage keeps workspaces 256-byte aligned and non-empty
+    return torch.empty(max(1, (int(n) + 7) // 8), dtype=torch.float64, device=device)
+
+
+class MoELayer:
+    """One MoE layer with device-resident weights.
+
+    `cfg` carries the layer's shape and routing options (the fields of
+    sparse_expert_dispatch_amd.workloads.MoEConfig); `weights` holds device
+    tensors wg [d,E], w1 [E, f|2f, d], w2 [E, d, f] and optionally
+    logit_offset [E], sel_bias [E], shared_w1, shared_w2.  bf16 tensors may be
+    torch.bfloat16 or raw uint16 bit patterns."""
+
+    def __init__(self, cfg, weights: dict, device="cuda"):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.w = weights
+        n, d, E = cfg.n, cfg.d, cfg.E
+        tc = cfg.direction == "tc"
+        self.k = cfg.k if tc else N.moe_ec_k(n, cfg.c, E)
+        cap = -1
+        if tc and cfg.capacity_factor is not None:
+            cap = N.moe_tc_capacity(n, self.k, E, cfg.capacity_factor)
+        self.capacity = cap
+        self.rcfg = N.make_cfg(n, d, E, self.k,
+                               N.MOE_TOKEN_CHOICE if tc else N.MOE_EXPERT_CHOICE,
+                               N.MOE_SOFTMAX if cfg.score == "softmax" else N.MOE_SIGMOID,
+                               cfg.n_group, cfg.topk_group, cfg.group_topm, int(cfg.norm_topk), cap)
+        self.dtype_code = N.MOE_BF16 if cfg.dtype == "bf16" else N.MOE_F32
+        self.act = N.MOE_SWIGLU if cfg.act == "swiglu" else N.MOE_GELU
+        edt = torch.bfloat16 if self.dtype_code == N.MOE_BF16 else torch.float32
+        dev = self.device
+        f32 = dict(dtype=torch.float32, device=dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.M_max = N.moe_max_slots(self.rcfg)
+        self.logits = torch.empty((n, E), **f32)
+        self.scores_t = torch.empty((E, n), **f32) if not tc else None
+        sel_shape = (n, self.k) if tc else (E, self.k)
+        self.sel_idx = torch.empty(sel_shape, **i32)
+        self.sel_gate = torch.empty(sel_shape, **f32)
+        self.map = N.RouteMap(self.rcfg, dev)
+        self.x_perm = torch.empty((self.M_max, d), dtype=edt, device=dev)
+        self.y_perm = torch.empty((self.M_max, d), dtype=edt, device=dev)
+        self.out = torch.empty((n, d), dtype=edt, device=dev)
+        self.stats = torch.empty(N.MOE_NSTATS, **f32)
+        self.hist = torch.empty(E + 1, **i32)
+        self.ws_router = _bytes(N.moe_router_workspace_size(self.rcfg, self.dtype_code), dev)
+        self.ws_route = _bytes(N.moe_route_workspace_size(self.rcfg), dev)
+        self.ws_ffn = _bytes(N.moe_ffn_workspace_size(self.M_max, E, d, cfg.f, self.act,
+                                                      self.dtype_code), dev)
+        self.shared = bool(getattr(cfg, "shared_f", 0))
+        if self.shared:
+            self.shared_out = torch.empty((n, d), dtype=edt, device=dev)
+            self.shared_offsets = torch.tensor([0, n], **i32)
+            self.ws_shared = _bytes(N.moe_ffn_workspace_size(n, 1, d, cfg.shared_f, self.act,
+                                                             self.dtype_code), dev)
+
+    # The stages, in order; each is one library call.
+    def route(self, x, stream=None):
+        w = self.w
+        tc = self.rcfg.dir == N.MOE_TOKEN_CHOICE
+        N.moe_router(x, w["wg"], w.get("logit_offset"), self.rcfg, self.logits, None,
+                     None if tc else self.scores_t, self.ws_router, stream)
+        N.moe_select(self.logits, None if tc else self.scores_t, w.get("sel_bias"), self.rcfg,
+                     self.sel_idx, self.sel_gate, self.ws_route, stream)
+        N.moe_build_map(self.sel_idx, self.sel_gate, self.rcfg, self.map, self.ws_route, stream)
+
+    def experts(self, x, stream=None):
+        w = self.w
+        N.moe_dispatch(x, self.map, self.x_perm, stream)
+        N.moe_expert_ffn(self.x_perm, self.map.expert_offset, w["w1"], w["w2"], self.act,
+                         self.y_perm, self.ws_ffn, stream)
+        if self.shared:
+            N.moe_expert_ffn(x, self.shared_offsets, w["shared_w1"], w["shared_w2"], self.act,
+                             self.shared_out, self.ws_shared, stream)
+
+    def combine(self, x, residual: bool = True, stream=None):
+        N.moe_combine(self.y_perm, self.map, self.cfg.n, x if residual else None,
+                      self.shared_out if self.shared else None, self.out, stream)
+
+    def balance_stats(self, stream=None):
+        N.moe_balance_stats(self.logits, self.map, self.rcfg, self.cfg.lb_coef, self.cfg.z_coef,
+                            self.stats, self.hist, self.ws_route, stream)
+
+    def forward(self, x: torch.Tensor, residual: bool = True, stats: bool = True,
+                stream=None) -> torch.Tensor:
+        """out = residual + shared expert + gate-weighted routed experts.
+        Results (and every intermediate) stay in this object's buffers."""
+        self.route(x, stream)
+        self.experts(x, stream)
+        self.combine(x, residual, stream)
+        if stats:
+            self.balance_stats(stream)
+        return self.out
+
+
+def to_device(a, device="cuda") -> Optional[torch.Tensor]:
+    """numpy array (float32, int32, or bf16 as uint16) -> device tensor
+    (bf16 bit patterns become torch.bfloat16 without any conversion)."""
+    import numpy as np
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)

@@ -1,0 +1,249 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI
+(via the Python binding), bring every stage's result back, and compare it
+with the CPU oracle run on the same seeded inputs.
+
+Selection, routing maps, drop sets and permutations must match bit for bit
+given the device's fp32 logits (the oracle is run with those logits
+injected).  Logits must match within 1e-5 relative to each row's largest
+magnitude.  Expert outputs and layer outputs in bf16 must match within
+max-abs 2e-2 x RMS of the oracle's value; fp32 layers within 1e-4 x RMS."""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+from oracle import moe_oracle as O
+from sparse_expert_dispatch_amd import _native as N
+from sparse_expert_dispatch_amd.layer import MoELayer, to_device
+
+LOGIT_RTOL = 1e-5
+BF16_TOL = 2e-2
+F32_TOL = 1e-4
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def widen(a: np.ndarray) -> np.ndarray:
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def upload(cfg, inp: dict) -> dict:
+    w = {"wg": to_device(inp["wg"]), "w1": to_device(inp["w1"]), "w2": to_device(inp["w2"]),
+         "logit_offset": to_device(inp.get("logit_offset")), "sel_bias": to_device(inp.get("sel_bias"))}
+    if cfg.shared_f:
+        w["shared_w1"] = to_device(inp["shared_w1"])
+        w["shared_w2"] = to_device(inp["shared_w2"])
+    return w
+
+
+def run_gpu(cfg, inp: dict, weights=None) -> dict:
+    """Run every stage on the GPU; return host copies of all results."""
+    w = weights if weights is not None else upload(cfg, inp)
+    x = to_device(inp["x"])
+    layer = MoELayer(cfg, w)
+    layer.route(x)
+    layer.experts(x)
+    layer.combine(x, residual=False)
+    branch = layer.out.clone()
+    layer.combine(x, residual=True)
+    layer.balance_stats()
+    torch.cuda.synchronize()
+    m = layer.map
+    r = dict(logits=host(layer.logits), sel_idx=host(layer.sel_idx), sel_gate=host(layer.sel_gate),
+             n_kept=int(host(m.n_kept)[0]), M_max=layer.M_max, k=layer.k, capacity=layer.capacity,
+             expert_count=host(m.expert_count), expert_offset=host(m.expert_offset),
+             slot_token=host(m.slot_token), slot_gate=host(m.slot_gate),
+             assign_slot=host(m.assign_slot), token_offset=host(m.token_offset),
+             token_slot=host(m.token_slot), x_perm=host(layer.x_perm), y_perm=host(layer.y_perm),
+             branch=host(branch), out=host(layer.out), stats=host(layer.stats), hist=host(layer.hist))
+    if layer.scores_t is not None:
+        r["scores_t"] = host(layer.scores_t)
+    if layer.shared:
+        r["shared"] = host(layer.shared_out)
+    r["layer"] = layer
+    return r
+
+
+def check_logits(z_gpu: np.ndarray, z_ref: np.ndarray):
+    err = np.abs(z_gpu.astype(np.float64) - z_ref.astype(np.float64)).max(axis=1)
+    scale = np.abs(z_ref.astype(np.float64)).max(axis=1)
+    bad = err > LOGIT_RTOL * scale
+    assert not bad.any(), f"logit rows off: {np.where(bad)[0][:5]}, worst rel " \
+                          f"{(err / np.maximum(scale, 1e-30)).max():.3g}"
+
+
+def max_rel_rms(got: np.ndarray, ref: np.ndarray) -> float:
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = np.sqrt((ref ** 2).mean())
+    return float(np.abs(got - ref).max() / rms) if rms > 0 else float(np.abs(got - ref).max())
+
+
+def check_expert_rows(y_dev: np.ndarray, xe: np.ndarray, w1: np.ndarray, w2: np.ndarray, act: str,
+                      bf16: bool, what: str):
+    """Device expert outputs against the oracle, element by element, within
+    the bound of the device's arithmetic.  bf16: the hidden activation and
+    the output are each rounded once to bf16 (relative error <= 2^-8), so
+    |y_dev - y| <= 2^-8 |y| + 2^-8 (|h| |W2|^T), with 5% slack for the fp32
+    accumulations and the activation functions.  fp32: 1e-4 x RMS."""
+    h = O.expert_hidden(xe, w1, act)
+    W2 = widen(w2)
+    y = h @ W2.T
+    got = widen(y_dev)
+    if not bf16:
+        err = max_rel_rms(got, y)
+        assert err <= F32_TOL, f"{what}: max-abs / RMS = {err:.3g}"
+        return
+    u = 2.0 ** -8
+    bound = 1.05 * (u * np.abs(y) + u * (np.abs(h) @ np.abs(W2).T)) + 1e-6 * np.sqrt((y ** 2).mean())
+    excess = np.abs(got - y) - bound
+    assert excess.max() <= 0, f"{what}: error exceeds the rounding bound by {excess.max():.3g} " \
+                              f"(max-abs / RMS {max_rel_rms(got, y):.3g})"
+
+
+def check_map(g: dict, ref_map: dict):
+    nk = int(ref_map["n_kept"])
+    assert g["n_kept"] == nk
+    for key in ("expert_count", "expert_offset", "assign_slot", "token_offset"):
+        assert np.array_equal(g[key], ref_map[key]), key
+    for key in ("slot_token", "slot_gate", "token_slot"):
+        got = g[key][:nk]
+        want = ref_map[key][:nk]
+        if key == "slot_gate":
+            assert np.array_equal(got.view(np.uint32), want.astype(np.float32).view(np.uint32)), key
+        else:
+            assert np.array_equal(got, want), key
+
+
+def compare_all(cfg, inp: dict, g: dict, full_ffn: bool = True, sample_tokens=None):
+    """Stage-by-stage comparison of a GPU run `g` with the oracle."""
+    t0 = time.time()
+    z_ref = O.router_logits(inp["x"], inp["wg"], inp.get("logit_offset"))
+    check_logits(g["logits"], z_ref)
+    z = g["logits"]
+    bf16 = cfg.dtype == "bf16"
+    tol = BF16_TOL if bf16 else F32_TOL
+
+    if cfg.direction == "tc":
+        idx, gate = O.select_token_choice(z, cfg.k, cfg.score, inp.get("sel_bias"), cfg.n_group,
+                                          cfg.topk_group, cfg.group_topm, cfg.norm_topk)
+        cap = O.tc_capacity(cfg.n, cfg.k, cfg.E, cfg.capacity_factor)
+        assert g["capacity"] == (cap if cfg.capacity_factor is not None else -1)
+        rmap = O.build_map_token_choice(idx, gate, cfg.E, None if cfg.capacity_factor is None else cap)
+        k = cfg.k
+    else:
+        k = O.ec_k(cfg.n, cfg.c, cfg.E)
+        assert g["k"] == k
+        S = O.softmax_rows(z)
+        assert np.array_equal(g["scores_t"].view(np.uint32), S.T.copy().view(np.uint32)), "scores_t"
+        idx, gate = O.select_expert_choice(z, k)
+        rmap = O.build_map_expert_choice(idx, gate, cfg.n)
+    assert np.array_equal(g["sel_idx"], idx), "selection"
+    assert np.array_equal(g["sel_gate"].view(np.uint32), gate.view(np.uint32)), "gates"
+    check_map(g, rmap)
+    nk = rmap["n_kept"]
+    assert np.array_equal(g["x_perm"][:nk], inp["x"][rmap["slot_token"]]), "dispatch"
+    log(f"  routing exact ({time.time() - t0:.1f}s)")
+
+    w1_of = lambda e: inp["w1"][e]
+    w2_of = lambda e: inp["w2"][e]
+    shared = None
+    if full_ffn:
+        y_ref = O.expert_ffn(inp["x"][rmap["slot_token"]], rmap["expert_offset"], w1_of, w2_of, cfg.act)
+        off = rmap["expert_offset"]
+        for e in range(cfg.E):
+            a, b = int(off[e]), int(off[e + 1])
+            if b > a:
+                check_expert_rows(g["y_perm"][a:b], inp["x"][rmap["slot_token"][a:b]], w1_of(e),
+                                  w2_of(e), cfg.act, bf16, f"expert {e}")
+        if cfg.shared_f:
+            shared = O.expert_forward(inp["x"], inp["shared_w1"], inp["shared_w2"], cfg.act)
+            check_expert_rows(g["shared"], inp["x"], inp["shared_w1"], inp["shared_w2"], cfg.act, bf16,
+                              "shared expert")
+        branch = O.combine(y_ref, rmap["slot_gate"], rmap["token_offset"], rmap["token_slot"], cfg.n,
+                           None, shared)
+        tokens = np.arange(cfg.n)
+    else:
+        # sampled tokens: each one's branch from its own experts, the expert
+        # outputs computed one expert at a time for all sampled rows it owns
+        tokens = np.asarray(sample_tokens)
+        pairs = {}                                   # expert -> [(i, slot)]
+        for i, t in enumerate(tokens):
+            for q in range(rmap["token_offset"][t], rmap["token_offset"][t + 1]):
+                s = int(rmap["token_slot"][q])
+                e = int(np.searchsorted(rmap["expert_offset"], s, side="right") - 1)
+                pairs.setdefault(e, []).append((i, s))
+        yrows = {}
+        for e, lst in sorted(pairs.items()):
+            xe = inp["x"][[tokens[i] for i, _ in lst]]
+            ys = O.expert_forward(xe, w1_of(e), w2_of(e), cfg.act)
+            slots = [s for _, s in lst]
+            check_expert_rows(g["y_perm"][slots], xe, w1_of(e), w2_of(e), cfg.act, bf16, f"expert {e}")
+            for (i, s), y in zip(lst, ys):
+                yrows[s] = y
+        shared_rows = None
+        if cfg.shared_f:
+            shared_rows = O.expert_forward(inp["x"][tokens], inp["shared_w1"], inp["shared_w2"], cfg.act)
+            check_expert_rows(g["shared"][tokens], inp["x"][tokens], inp["shared_w1"], inp["shared_w2"],
+                              cfg.act, bf16, "shared expert")
+        branch = np.zeros((len(tokens), cfg.d))
+        for i, t in enumerate(tokens):
+            for q in range(rmap["token_offset"][t], rmap["token_offset"][t + 1]):
+                s = int(rmap["token_slot"][q])
+                branch[i] += float(rmap["slot_gate"][s]) * yrows[s]
+            if shared_rows is not None:
+                branch[i] += shared_rows[i]
+    # combine on its own: the device's expert outputs summed by the oracle;
+    # the only difference left is one rounding of the fp32 sum to `dtype`
+    gb = widen(g["branch"][tokens])
+    y_dev = widen(g["y_perm"])
+    sh_dev = widen(g["shared"]) if cfg.shared_f else None
+    comb = np.zeros((len(tokens), cfg.d))
+    for i, t in enumerate(tokens):
+        for q in range(rmap["token_offset"][t], rmap["token_offset"][t + 1]):
+            s = int(rmap["token_slot"][q])
+            comb[i] += float(rmap["slot_gate"][s]) * y_dev[s]
+        if sh_dev is not None:
+            comb[i] += sh_dev[t]
+    ulp = 2.0 ** -8 if bf16 else 2.0 ** -22
+    cerr = np.abs(gb - comb) - ulp * np.abs(comb)
+    assert cerr.max() <= 1e-6 * np.sqrt((comb ** 2).mean()) + 1e-30, \
+        f"combine: worst excess {cerr.max():.3g}"
+    # the layer against the oracle end to end (the tolerance is relative to
+    # the RMS of the layer output, residual included)
+    res = widen(inp["x"][tokens])
+    out_ref = branch + res
+    rms_out = np.sqrt((out_ref ** 2).mean())
+    err_out = np.abs(widen(g["out"][tokens]) - out_ref).max() / rms_out
+    err_branch = np.abs(gb - branch).max() / rms_out
+    log(f"  max-abs / RMS(out): out {err_out:.3g}, branch {err_branch:.3g}; "
+        f"branch vs RMS(branch) {max_rel_rms(gb, branch):.3g}")
+    assert err_out <= tol, f"layer output: max-abs / RMS(out) = {err_out:.3g}"
+    assert err_branch <= tol, f"layer branch: max-abs / RMS(out) = {err_branch:.3g}"
+    # tokens with no kept expert (and no shared expert) ride the residual bit for bit
+    if not cfg.shared_f:
+        empty = tokens[np.diff(rmap["token_offset"])[tokens] == 0]
+        assert np.array_equal(g["out"][empty], inp["x"][empty]), "residual pass-through"
+    log(f"  outputs within tolerance ({time.time() - t0:.1f}s)")
+
+    st_ref, hist_ref = O.balance_stats(z, rmap, cfg.direction, k, cfg.score, cfg.lb_coef, cfg.z_coef)
+    st = g["stats"].astype(np.float64)
+    for i in range(4):
+        assert abs(st[i] - st_ref[i]) <= 1e-4 * max(abs(st_ref[i]), 1e-6), \
+            f"{O.STAT_NAMES[i]}: {st[i]} vs {st_ref[i]}"
+    assert np.array_equal(st[4:], st_ref[4:]), (st[4:], st_ref[4:])
+    assert np.array_equal(g["hist"], hist_ref)
+    return rmap

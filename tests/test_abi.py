@@ -1,0 +1,145 @@
+"""The C ABI on the host: the library loads, exports every declared entry
+point, sizes agree with the pages' worked examples and with the oracle, and
+bad arguments are rejected before any GPU work.  CPU only (no kernel runs:
+every call here fails validation or is a pure host function)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sparse_expert_dispatch_amd as M
+from sparse_expert_dispatch_amd import _native as N
+from oracle import moe_oracle as O
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moe_dispatch.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(N.LIB_PATH):
+        pytest.fail(f"{N.LIB_PATH} not built (run python -m sparse_expert_dispatch_amd.build)")
+    return N.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) == 15
+    for name in names:
+        assert hasattr(L, name), name
+    assert sorted(N.EXPORTED) == names
+
+
+def test_sizes_match_worked_examples_and_oracle(L):
+    assert M.moe_ec_k(4096, 2.0, 64) == 128          # page 1 "Who picks whom"
+    assert M.moe_ec_k(1024, 2.0, 8) == 256           # page 2 "A worked example"
+    assert M.moe_tc_capacity(16384, 1, 128, 1.25) == 160
+    assert M.moe_tc_capacity(256, 2, 8, 1.25) == 80
+    rng = np.random.default_rng(0)
+    for _ in range(2000):
+        n, E, k = int(rng.integers(1, 20000)), int(rng.integers(1, 300)), int(rng.integers(1, 9))
+        c = float(rng.choice([0.5, 1.0, 1.25, 2.0, 3.3]))
+        assert M.moe_ec_k(n, c, E) == O.ec_k(n, c, E)
+        assert M.moe_tc_capacity(n, k, E, c) == O.tc_capacity(n, k, E, c)
+    assert M.moe_ec_k(0, 2.0, 8) == -1 and M.moe_tc_capacity(10, 0, 8, 1.0) == -1
+
+
+def test_max_slots(L):
+    cfg = N.make_cfg(256, 64, 8, 2, capacity=80)
+    assert M.moe_max_slots(cfg) == 512
+    cfg = N.make_cfg(256, 64, 8, 2, capacity=40)
+    assert M.moe_max_slots(cfg) == 320
+    cfg = N.make_cfg(4096, 2048, 64, 128, direction=N.MOE_EXPERT_CHOICE)
+    assert M.moe_max_slots(cfg) == 8192
+
+
+FAKE = 0x10000   # a non-NULL, 16-byte aligned address that is never dereferenced
+
+
+def _router(L, cfg, dtype=N.MOE_BF16, x=FAKE, ws=None, wsb=0):
+    return L.moe_router(x, FAKE, dtype, None, ctypes.byref(cfg), FAKE, None, None, ws, wsb, None)
+
+
+@pytest.mark.parametrize("bad, status", [
+    (dict(n=0), N.MOE_ERR_INVALID_ARG),
+    (dict(k=9), N.MOE_ERR_INVALID_ARG),                       # k > E
+    (dict(E=600, k=2), N.MOE_ERR_UNSUPPORTED),                 # beyond 512 experts
+    (dict(n_group=3), N.MOE_ERR_INVALID_ARG),                  # E % n_group
+    (dict(n_group=4, topk_group=5), N.MOE_ERR_INVALID_ARG),
+    (dict(n_group=4, topk_group=1, k=3), N.MOE_ERR_INVALID_ARG),   # k > experts in kept groups
+    (dict(capacity=-2), N.MOE_ERR_INVALID_ARG),
+    (dict(score=7), N.MOE_ERR_INVALID_ARG),
+    (dict(group_topm=0), N.MOE_ERR_INVALID_ARG),
+])
+def test_config_validation(L, bad, status):
+    kw = dict(n=256, d=64, E=8, k=2)
+    kw.update(bad)
+    n, d, E, k = kw.pop("n"), kw.pop("d"), kw.pop("E"), kw.pop("k")
+    cfg = N.make_cfg(n, d, E, k, **kw)
+    assert _router(L, cfg, N.MOE_F32) == status
+    assert L.moe_last_error().decode() != ""
+
+
+def test_expert_choice_validation(L):
+    cfg = N.make_cfg(100, 64, 8, 101, direction=N.MOE_EXPERT_CHOICE)      # k > n
+    assert _router(L, cfg, N.MOE_F32) == N.MOE_ERR_INVALID_ARG
+    cfg = N.make_cfg(100, 64, 8, 10, direction=N.MOE_EXPERT_CHOICE, score=N.MOE_SIGMOID)
+    assert _router(L, cfg, N.MOE_F32) == N.MOE_ERR_UNSUPPORTED
+
+
+def test_null_pointers_and_unsupported_shapes(L):
+    cfg = N.make_cfg(256, 64, 8, 2)
+    assert _router(L, cfg, N.MOE_F32, x=None) == N.MOE_ERR_INVALID_ARG
+    cfg = N.make_cfg(256, 128, 16, 2)                     # misaligned bf16 input
+    assert _router(L, cfg, N.MOE_BF16, x=FAKE + 2) == N.MOE_ERR_INVALID_ARG
+    # expert FFN: bf16 shapes and workspace
+    st = L.moe_expert_ffn(FAKE, N.MOE_BF16, FAKE, 8, 100, 128, N.MOE_GELU, FAKE, FAKE, 64, FAKE,
+                          FAKE, 1 << 30, None)
+    assert st == N.MOE_ERR_UNSUPPORTED
+    st = L.moe_expert_ffn(FAKE, N.MOE_BF16, FAKE, 8, 128, 128, N.MOE_GELU, FAKE, FAKE, 64, FAKE,
+                          FAKE, 16, None)
+    assert st == N.MOE_ERR_WORKSPACE
+    st = L.moe_expert_ffn(FAKE, N.MOE_BF16, None, 8, 128, 128, N.MOE_GELU, FAKE, FAKE, 64, FAKE,
+                          FAKE, 1 << 30, None)
+    assert st == N.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_checks(L):
+    cfg = N.make_cfg(4096, 2048, 64, 128, direction=N.MOE_EXPERT_CHOICE)
+    need = M.moe_route_workspace_size(cfg)
+    assert need >= 4096 * 64 * 4
+    cm = N.RouteMapC(*([FAKE] * 8))
+    assert L.moe_build_map(FAKE, FAKE, ctypes.byref(cfg), ctypes.byref(cm), FAKE, 8, None) == \
+        N.MOE_ERR_WORKSPACE
+    cm_bad = N.RouteMapC(*([FAKE] * 7 + [0]))
+    assert L.moe_build_map(FAKE, FAKE, ctypes.byref(cfg), ctypes.byref(cm_bad), FAKE, need, None) == \
+        N.MOE_ERR_INVALID_ARG
+    # select without precomputed scores needs the transpose workspace
+    assert L.moe_select(FAKE, None, None, ctypes.byref(cfg), FAKE, FAKE, FAKE, 8, None) == \
+        N.MOE_ERR_WORKSPACE
+    assert L.moe_balance_stats(FAKE, ctypes.byref(cm), ctypes.byref(cfg), 0.01, 0.001, FAKE, None,
+                               FAKE, 4, None) == N.MOE_ERR_WORKSPACE
+    # combine output must not alias an input
+    assert L.moe_combine(FAKE, N.MOE_BF16, ctypes.byref(cm), 16, 64, None, None, FAKE, None) == \
+        N.MOE_ERR_INVALID_ARG
+
+
+def test_status_strings(L):
+    assert M.moe_status_string(0) == "ok"
+    assert M.moe_status_string(3) == "workspace too small"
+    assert M.moe_status_string(99) == "unknown status"
+
+
+def test_python_binding_refuses_cpu_tensors(L):
+    import torch
+    cfg = N.make_cfg(16, 64, 8, 2)
+    x = torch.zeros(16, 64)
+    with pytest.raises(ValueError):
+        M.moe_router(x, torch.zeros(64, 8), None, cfg, torch.zeros(16, 8))

@@ -102,9 +102,13 @@ typedef struct {
   float   *slot_gate;     /* [M_max] gate of each slot                       */
   int32_t *assign_slot;   /* token choice [n,k]: slot of (token, rank), -1 =
                              dropped; expert choice [E,k]: slot of I[e,j]   */
-  int32_t *token_offset;  /* [n+1] token-side CSR over token_slot            */
-  int32_t *token_slot;    /* [M_max] each token's kept slots, rank order
-                             (token choice) or ascending expert (expert c.) */
+  int32_t *token_offset;  /* [n+1] token t's list is token_slot[token_offset[t]
+                             .. token_offset[t+1]-1]                        */
+  int32_t *token_slot;    /* [moe_token_list_len] token choice: the token's k
+                             slots in rank order, -1 where dropped
+                             (token_offset[t] = t*k); expert choice: the
+                             slots of the experts that picked the token, in
+                             ascending expert order                         */
   int32_t *n_kept;        /* [1]   kept assignments = expert_offset[E]       */
 } moe_route_map_t;
 
@@ -123,6 +127,11 @@ int32_t moe_tc_capacity(int32_t n, int32_t k, int32_t E, double cf);
 /* Upper bound on kept assignments: token choice n*k (capacity-limited:
  * min(n*k, E*capacity)); expert choice E*k.  -1 on invalid cfg. */
 int64_t moe_max_slots(const moe_route_cfg_t *cfg);
+
+/* Length of the token-side list (map->token_slot): n*k under token choice
+ * (dropped assignments keep a -1 entry), E*k under expert choice.  -1 on
+ * invalid cfg. */
+int64_t moe_token_list_len(const moe_route_cfg_t *cfg);
 
 /* Workspace for moe_router (`dtype` of X and W_g). */
 moe_status_t moe_router_workspace_size(const moe_route_cfg_t *cfg, int32_t dtype, size_t *bytes);

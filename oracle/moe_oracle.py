@@ -309,14 +309,12 @@ def build_map_token_choice(idx: np.ndarray, gate: np.ndarray, E: int, capacity: 
                 slot_token[s] = t
                 slot_gate[s] = gate_l[t][r]
                 assign_slot[t, r] = s
-    # token-side lists: a token's kept slots in rank order
-    kept_mask = assign_slot >= 0
-    token_offset = np.zeros(n + 1, dtype=np.int64)
-    token_offset[1:] = np.cumsum(kept_mask.sum(axis=1))
-    token_slot = assign_slot[kept_mask].astype(np.int32)   # row-major = (token, rank) order
+    # token-side lists: token t's k assignments in rank order, -1 where dropped
+    token_offset = (np.arange(n + 1, dtype=np.int64) * k).astype(np.int32)
+    token_slot = assign_slot.reshape(-1).copy()
     return dict(expert_count=count.astype(np.int32), expert_offset=offset.astype(np.int32),
                 slot_token=slot_token, slot_gate=slot_gate, assign_slot=assign_slot,
-                token_offset=token_offset.astype(np.int32), token_slot=token_slot, n_kept=M)
+                token_offset=token_offset, token_slot=token_slot, n_kept=M)
 
 
 def build_map_expert_choice(I: np.ndarray, G: np.ndarray, n: int):
@@ -405,7 +403,8 @@ def combine(y_perm: np.ndarray, slot_gate: np.ndarray, token_offset: np.ndarray,
     for t in range(n):
         for q in range(int(token_offset[t]), int(token_offset[t + 1])):
             s = int(token_slot[q])
-            branch[t] += float(slot_gate[s]) * y_perm[s]
+            if s >= 0:                          # -1: an assignment dropped at capacity
+                branch[t] += float(slot_gate[s]) * y_perm[s]
     out = branch
     if shared is not None:
         out = out + np.asarray(shared, dtype=np.float64)
@@ -457,7 +456,9 @@ def balance_stats(z: np.ndarray, rmap: dict, direction: str, k: int, score: str,
     max_vio = float((load.max() - mean_load) / mean_load) if mean_load > 0 else 0.0
     n_kept = int(rmap["n_kept"])
     total = n * k if direction == "tc" else E * k
-    per_tok = np.diff(rmap["token_offset"].astype(np.int64))
+    kept_entry = (rmap["token_slot"] >= 0).astype(np.int64)
+    per_tok = np.array([kept_entry[a:b].sum() for a, b in
+                        zip(rmap["token_offset"][:-1], rmap["token_offset"][1:])], dtype=np.int64)
     hist = np.bincount(per_tok, minlength=E + 1)[:E + 1].astype(np.int64)
     stats = np.array([lb, zl, max_vio, float(load.max()) / max(n_kept, 1), n_kept,
                       total - n_kept, int((per_tok == 0).sum()), int(per_tok.max(initial=0))],

@@ -11,4 +11,4 @@ from ._native import (  # noqa: F401
     MOE_SOFTMAX, MOE_SWIGLU, MOE_TOKEN_CHOICE, STAT_NAMES, MoEError, RouteCfg, RouteMap, lib,
     make_cfg, moe_balance_stats, moe_build_map, moe_combine, moe_dispatch, moe_ec_k, moe_expert_ffn,
     moe_ffn_workspace_size, moe_last_error, moe_max_slots, moe_route_workspace_size, moe_router,
-    moe_router_workspace_size, moe_select, moe_status_string, moe_tc_capacity)
+    moe_router_workspace_size, moe_select, moe_status_string, moe_tc_capacity, moe_token_list_len)

@@ -26,7 +26,8 @@ MOE_NSTATS = 8
 STAT_NAMES = ("lb_loss", "z_loss", "max_vio", "max_load_share", "n_kept", "n_dropped",
               "tokens_without_expert", "max_experts_per_token")
 
-EXPORTED = ("moe_ec_k", "moe_tc_capacity", "moe_max_slots", "moe_router_workspace_size",
+EXPORTED = ("moe_ec_k", "moe_tc_capacity", "moe_max_slots", "moe_token_list_len",
+            "moe_router_workspace_size",
             "moe_route_workspace_size", "moe_ffn_workspace_size", "moe_router", "moe_select",
             "moe_build_map", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_balance_stats",
             "moe_status_string", "moe_last_error")
@@ -71,6 +72,7 @@ def lib() -> ctypes.CDLL:
         "moe_ec_k": (I32, [I32, F64, I32]),
         "moe_tc_capacity": (I32, [I32, I32, I32, F64]),
         "moe_max_slots": (I64, [CFG]),
+        "moe_token_list_len": (I64, [CFG]),
         "moe_router_workspace_size": (I32, [CFG, I32, SZP]),
         "moe_route_workspace_size": (I32, [CFG, SZP]),
         "moe_ffn_workspace_size": (I32, [I64, I32, I32, I32, I32, I32, SZP]),
@@ -163,7 +165,7 @@ class RouteMap:
         self.slot_gate = torch.empty(M, dtype=torch.float32, device=device)
         self.assign_slot = torch.empty((n, k) if cfg.dir == MOE_TOKEN_CHOICE else (E, k), **i32)
         self.token_offset = torch.empty(n + 1, **i32)
-        self.token_slot = torch.empty(M, **i32)
+        self.token_slot = torch.empty(moe_token_list_len(cfg), **i32)
         self.n_kept = torch.empty(1, **i32)
 
     def c(self) -> RouteMapC:
@@ -184,6 +186,13 @@ def moe_max_slots(cfg: RouteCfg) -> int:
     v = lib().moe_max_slots(ctypes.byref(cfg))
     if v < 0:
         _check(MOE_ERR_INVALID_ARG, "moe_max_slots")
+    return v
+
+
+def moe_token_list_len(cfg: RouteCfg) -> int:
+    v = lib().moe_token_list_len(ctypes.byref(cfg))
+    if v < 0:
+        _check(MOE_ERR_INVALID_ARG, "moe_token_list_len")
     return v
 
 

@@ -126,6 +126,11 @@ int64_t moe_max_slots(const moe_route_cfg_t* cfg) {
   return cap < nk ? cap : nk;
 }
 
+int64_t moe_token_list_len(const moe_route_cfg_t* cfg) {
+  if (check_cfg(cfg) != MOE_OK) return -1;
+  return cfg->dir == MOE_EXPERT_CHOICE ? (int64_t)cfg->E * cfg->k : (int64_t)cfg->n * cfg->k;
+}
+
 moe_status_t moe_router_workspace_size(const moe_route_cfg_t* cfg, int32_t dtype, size_t* bytes) {
   moe_status_t st = check_cfg(cfg);
   if (st != MOE_OK) return st;
@@ -277,7 +282,7 @@ moe_status_t moe_balance_stats(const float* logits, const moe_route_map_t* map,
   moe_status_t st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   REQUIRE(logits && stats, "logits and stats must be non-NULL");
-  REQUIRE(map && map->expert_count && map->expert_offset && map->token_offset,
+  REQUIRE(map && map->expert_count && map->expert_offset && map->token_offset && map->token_slot,
           "map->expert_count, expert_offset and token_offset must be non-NULL");
   const size_t need = moe::stats_workspace_bytes(cfg->n, cfg->E);
   if (!ws || ws_bytes < need)

@@ -10,14 +10,46 @@
 // token).
 //
 // Both kernels are pure HBM streams: one wave per row, 16-byte loads and
-// stores, every byte read or written once.  The combine is a gather rather
-// than a scatter: each token walks its own slot list (token_offset /
-// token_slot) in a fixed order and accumulates in fp32, so there are no
-// floating-point atomics and the result is bitwise reproducible.
+// stores, every byte read or written once.  Each wave issues all the loads
+// of a row (or of a batch of rows) before it consumes any, so one memory
+// round trip covers them.  The combine is a gather rather than a scatter:
+// each token walks its own slot list in a fixed order and accumulates in
+// fp32, so there are no floating-point atomics and the result is bitwise
+// reproducible.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kCopyUnroll = 8;   // 16-byte chunks per lane in flight (8 KB per wave)
+
+__global__ __launch_bounds__(256) void dispatch_vec_kernel(const char* __restrict__ X, int64_t row_bytes,
+                                                           const int32_t* __restrict__ slot_token,
+                                                           const int32_t* __restrict__ n_kept,
+                                                           int64_t M_max, char* __restrict__ Xp) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t rows = min((int64_t)*n_kept, M_max);
+  if (row >= rows) return;
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(X + (int64_t)slot_token[row] * row_bytes);
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(Xp + row * row_bytes);
+  const int64_t nv = row_bytes / 16;
+  for (int64_t base = 0; base < nv; base += 64 * kCopyUnroll) {
+    u32x4_t v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = base + u * 64 + lane;
+      if (i < nv) v[u] = src[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = base + u * 64 + lane;
+      if (i < nv) dst[i] = v[u];
+    }
+  }
+}
 
 template <typename V>
 __global__ __launch_bounds__(256) void dispatch_kernel(const char* __restrict__ X, int64_t row_bytes,
@@ -42,8 +74,8 @@ hipError_t launch_dispatch(const void* X, int elem_bytes, int n, int d, const in
   const char* src = static_cast<const char*>(X);
   char* dst = static_cast<char*>(X_perm);
   if (row_bytes % 16 == 0)
-    hipLaunchKernelGGL(dispatch_kernel<uint4>, grid, block, 0, stream, src, row_bytes, slot_token,
-                       n_kept, M_max, dst);
+    hipLaunchKernelGGL(dispatch_vec_kernel, grid, block, 0, stream, src, row_bytes, slot_token, n_kept,
+                       M_max, dst);
   else if (row_bytes % 4 == 0)
     hipLaunchKernelGGL(dispatch_kernel<uint32_t>, grid, block, 0, stream, src, row_bytes, slot_token,
                        n_kept, M_max, dst);
@@ -55,90 +87,158 @@ hipError_t launch_dispatch(const void* X, int elem_bytes, int n, int d, const in
 
 // ---------------------------------------------------------------- combine
 
+// 16 bytes of a row: 4 fp32 or 8 bf16 values.
 template <typename T> struct Elem;
 template <> struct Elem<float> {
-  static constexpr int kVec = 4;                       // elements per 16-byte access
-  MOE_DEV static void load(const float* p, float* v) {
-    const float4 q = *reinterpret_cast<const float4*>(p);
-    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  static constexpr int kVec = 4;
+  MOE_DEV static void unpack(const u32x4_t& r, float* v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(r[i]);
   }
-  MOE_DEV static void store(float* p, const float* v) {
-    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  MOE_DEV static u32x4_t pack(const float* v) {
+    return u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                   __float_as_uint(v[3])};
   }
   MOE_DEV static float one(const float* p) { return *p; }
   MOE_DEV static void put(float* p, float v) { *p = v; }
 };
 template <> struct Elem<bf16_t> {
   static constexpr int kVec = 8;
-  MOE_DEV static void load(const bf16_t* p, float* v) {
-    const uint4 q = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  MOE_DEV static void unpack(const u32x4_t& r, float* v) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      v[2 * i] = __uint_as_float(r[i] << 16);
+      v[2 * i + 1] = __uint_as_float(r[i] & 0xFFFF0000u);
     }
   }
-  MOE_DEV static void store(bf16_t* p, const float* v) {
-    uint4 q;
-    q.x = pack_bf16x2(v[0], v[1]);
-    q.y = pack_bf16x2(v[2], v[3]);
-    q.z = pack_bf16x2(v[4], v[5]);
-    q.w = pack_bf16x2(v[6], v[7]);
-    *reinterpret_cast<uint4*>(p) = q;
+  MOE_DEV static u32x4_t pack(const float* v) {
+    return u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                   pack_bf16x2(v[6], v[7])};
   }
   MOE_DEV static float one(const bf16_t* p) { return bf16_to_f32(*p); }
   MOE_DEV static void put(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 };
 
 // One wave per token.  acc = residual; acc += shared; then acc += g * y for
-// the token's slots in list order; one rounding at the store.
-template <typename T, bool kVecPath>
-__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Y,
-                                                      const int32_t* __restrict__ token_offset,
-                                                      const int32_t* __restrict__ token_slot,
-                                                      const float* __restrict__ slot_gate, int n,
-                                                      int d, const T* __restrict__ residual,
-                                                      const T* __restrict__ shared, T* __restrict__ out) {
-  constexpr int V = kVecPath ? Elem<T>::kVec : 1;
+// the token's slots in list order (negative entries are dropped
+// assignments); one rounding at the store.  The token's slot list and gates
+// are loaded once (lane q holds entry q) and read back with readlane; the
+// rows of kSlotBatch slots are loaded together before they are added.
+constexpr int kChunks = 4;      // 16-byte chunks per lane per column pass
+constexpr int kSlotBatch = 4;   // expert rows in flight per wave
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_vec_kernel(const T* __restrict__ Y,
+                                                          const int32_t* __restrict__ token_offset,
+                                                          const int32_t* __restrict__ token_slot,
+                                                          const float* __restrict__ slot_gate, int n,
+                                                          int d, const T* __restrict__ residual,
+                                                          const T* __restrict__ shared,
+                                                          T* __restrict__ out) {
+  constexpr int V = Elem<T>::kVec;
+  const int lane = threadIdx.x & 63;
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (t >= n) return;
+  const int q0 = token_offset[t], q1 = token_offset[t + 1];
+  const size_t rowoff = (size_t)t * d;
+  // the first 64 list entries live in registers for every column pass;
+  // longer lists (a token picked by more than 64 experts) reload the rest
+  const int cnt0 = min(64, q1 - q0);
+  const int s0 = lane < cnt0 ? token_slot[q0 + lane] : -1;
+  const float g0 = s0 >= 0 ? slot_gate[s0] : 0.f;
+  for (int col0 = 0; col0 < d; col0 += 64 * V * kChunks) {
+    float acc[kChunks][V];
+    bool ok[kChunks];
+    u32x4_t rres[kChunks], rsh[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int col = col0 + (c * 64 + lane) * V;
+      ok[c] = col < d;
+      if (ok[c] && residual) rres[c] = *reinterpret_cast<const u32x4_t*>(residual + rowoff + col);
+      if (ok[c] && shared) rsh[c] = *reinterpret_cast<const u32x4_t*>(shared + rowoff + col);
+    }
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      if (ok[c] && residual) {
+        Elem<T>::unpack(rres[c], acc[c]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[c][i] = 0.f;
+      }
+      if (ok[c] && shared) {
+        float sh[V];
+        Elem<T>::unpack(rsh[c], sh);
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[c][i] += sh[i];
+      }
+    }
+    for (int w0 = q0; w0 < q1; w0 += 64) {
+      const int cnt = min(64, q1 - w0);
+      int my_s = s0;
+      float my_g = g0;
+      if (w0 != q0) {
+        my_s = lane < cnt ? token_slot[w0 + lane] : -1;
+        my_g = my_s >= 0 ? slot_gate[my_s] : 0.f;
+      }
+      for (int qb = 0; qb < cnt; qb += kSlotBatch) {
+        u32x4_t ry[kSlotBatch][kChunks];
+        int sb[kSlotBatch];
+        float gb[kSlotBatch];
+#pragma unroll
+        for (int b = 0; b < kSlotBatch; ++b) {
+          const int q = qb + b;
+          sb[b] = q < cnt ? __builtin_amdgcn_readlane(my_s, q) : -1;
+          gb[b] = q < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_g), q)) : 0.f;
+          const T* yrow = Y + (size_t)(sb[b] < 0 ? 0 : sb[b]) * d;
+#pragma unroll
+          for (int c = 0; c < kChunks; ++c)
+            if (ok[c] && sb[b] >= 0)
+              ry[b][c] = *reinterpret_cast<const u32x4_t*>(yrow + col0 + (c * 64 + lane) * V);
+        }
+#pragma unroll
+        for (int b = 0; b < kSlotBatch; ++b) {
+          if (sb[b] < 0) continue;
+#pragma unroll
+          for (int c = 0; c < kChunks; ++c) {
+            if (!ok[c]) continue;
+            float y[V];
+            Elem<T>::unpack(ry[b][c], y);
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[c][i] = fmaf(gb[b], y[i], acc[c][i]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c)
+      if (ok[c])
+        *reinterpret_cast<u32x4_t*>(out + rowoff + col0 + (c * 64 + lane) * V) = Elem<T>::pack(acc[c]);
+  }
+}
+
+// Scalar path for rows that are not a whole number of 16-byte chunks.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_scalar_kernel(const T* __restrict__ Y,
+                                                             const int32_t* __restrict__ token_offset,
+                                                             const int32_t* __restrict__ token_slot,
+                                                             const float* __restrict__ slot_gate, int n,
+                                                             int d, const T* __restrict__ residual,
+                                                             const T* __restrict__ shared,
+                                                             T* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= n) return;
   const int q0 = token_offset[t], q1 = token_offset[t + 1];
   const size_t rowoff = (size_t)t * d;
-  for (int c = lane * V; c < d; c += 64 * V) {
-    float acc[V];
-    if (kVecPath) {
-      if (residual) {
-        Elem<T>::load(residual + rowoff + c, acc);
-      } else {
-#pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] = 0.f;
-      }
-      if (shared) {
-        float s[V];
-        Elem<T>::load(shared + rowoff + c, s);
-#pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] += s[i];
-      }
-      for (int q = q0; q < q1; ++q) {
-        const int s = token_slot[q];
-        const float g = slot_gate[s];
-        float y[V];
-        Elem<T>::load(Y + (size_t)s * d + c, y);
-#pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] = fmaf(g, y[i], acc[i]);
-      }
-      Elem<T>::store(out + rowoff + c, acc);
-    } else {
-      float a = residual ? Elem<T>::one(residual + rowoff + c) : 0.f;
-      if (shared) a += Elem<T>::one(shared + rowoff + c);
-      for (int q = q0; q < q1; ++q) {
-        const int s = token_slot[q];
-        a = fmaf(slot_gate[s], Elem<T>::one(Y + (size_t)s * d + c), a);
-      }
-      Elem<T>::put(out + rowoff + c, a);
+  for (int c = lane; c < d; c += 64) {
+    float a = residual ? Elem<T>::one(residual + rowoff + c) : 0.f;
+    if (shared) a += Elem<T>::one(shared + rowoff + c);
+    for (int q = q0; q < q1; ++q) {
+      const int s = token_slot[q];
+      if (s < 0) continue;
+      a = fmaf(slot_gate[s], Elem<T>::one(Y + (size_t)s * d + c), a);
     }
+    Elem<T>::put(out + rowoff + c, a);
   }
 }
 
@@ -148,15 +248,13 @@ hipError_t launch_combine(const void* Y, int dtype, const int32_t* token_offset,
   const dim3 grid((n + 3) / 4), block(256);
   if (dtype == 1) {
     typedef bf16_t T;
-    const bool vec = d % 8 == 0;
-    auto k = vec ? combine_kernel<T, true> : combine_kernel<T, false>;
+    auto k = d % 8 == 0 ? combine_vec_kernel<T> : combine_scalar_kernel<T>;
     hipLaunchKernelGGL(k, grid, block, 0, stream, static_cast<const T*>(Y), token_offset, token_slot,
                        slot_gate, n, d, static_cast<const T*>(residual),
                        static_cast<const T*>(shared), static_cast<T*>(out));
   } else {
     typedef float T;
-    const bool vec = d % 4 == 0;
-    auto k = vec ? combine_kernel<T, true> : combine_kernel<T, false>;
+    auto k = d % 4 == 0 ? combine_vec_kernel<T> : combine_scalar_kernel<T>;
     hipLaunchKernelGGL(k, grid, block, 0, stream, static_cast<const T*>(Y), token_offset, token_slot,
                        slot_gate, n, d, static_cast<const T*>(residual),
                        static_cast<const T*>(shared), static_cast<T*>(out));

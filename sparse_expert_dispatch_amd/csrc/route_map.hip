@@ -74,11 +74,12 @@ __global__ __launch_bounds__(kScanThreads) void map_scan_kernel(
   }
 }
 
+// Token choice also writes the token-side lists: token t's entries are its
+// k assignments in rank order (token_offset[t] = t*k), -1 for a dropped one.
 __global__ __launch_bounds__(64) void map_scatter_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ gate, int64_t M, int k, int E,
     int nbits, int capacity, const int32_t* __restrict__ chunk_base,
-    const int32_t* __restrict__ expert_offset, int32_t* __restrict__ slot_token,
-    float* __restrict__ slot_gate, int32_t* __restrict__ assign_slot) {
+    const int32_t* __restrict__ expert_offset, MapPtrs m) {
   extern __shared__ int cnt[];
   const int lane = threadIdx.x;
   const int c = blockIdx.x;
@@ -86,6 +87,7 @@ __global__ __launch_bounds__(64) void map_scatter_kernel(
   __syncthreads();
   const uint64_t lt_mask = (1ull << lane) - 1ull;
   const int64_t a0 = (int64_t)c * kMapChunk;
+  if (c == 0 && lane == 0) m.token_offset[M / k] = (int32_t)M;
   for (int it = 0; it < kMapChunk; it += 64) {
     const int64_t a = a0 + it + lane;
     const bool inrange = a < M;
@@ -109,58 +111,22 @@ __global__ __launch_bounds__(64) void map_scatter_kernel(
       int32_t s = -1;
       if (valid && (capacity < 0 || pos < capacity)) {
         s = expert_offset[e] + pos;
-        slot_token[s] = (int32_t)(a / k);
-        slot_gate[s] = gate[a];
+        m.slot_token[s] = (int32_t)(a / k);
+        m.slot_gate[s] = gate[a];
       }
-      assign_slot[a] = s;
+      m.assign_slot[a] = s;
+      m.token_slot[a] = s;
+      if (a % k == 0) m.token_offset[a / k] = (int32_t)a;
     }
-  }
-}
-
-// Token-side lists.  One workgroup: each thread owns a contiguous run of
-// tokens, counts their kept assignments, and a workgroup scan turns the
-// counts into token_offset.
-template <int DIR>
-__global__ __launch_bounds__(kScanThreads) void token_offsets_kernel(
-    const int32_t* __restrict__ assign_slot, const uint32_t* __restrict__ mask, int n, int k, int W,
-    int32_t* __restrict__ token_offset) {
-  __shared__ int scratch[kScanThreads / 64];
-  const int seg = (n + kScanThreads - 1) / kScanThreads;
-  const int t0 = min(n, (int)threadIdx.x * seg), t1 = min(n, t0 + seg);
-  auto count = [&](int t) {
-    int c = 0;
-    if (DIR == 0) {
-      for (int r = 0; r < k; ++r) c += assign_slot[(size_t)t * k + r] >= 0 ? 1 : 0;
-    } else {
-      for (int w = 0; w < W; ++w) c += __popc(mask[(size_t)t * W + w]);
-    }
-    return c;
-  };
-  int sum = 0;
-  for (int t = t0; t < t1; ++t) sum += count(t);
-  int total = 0;
-  int run = block_exclusive_scan<kScanThreads>(sum, scratch, &total);
-  for (int t = t0; t < t1; ++t) {
-    token_offset[t] = run;
-    run += count(t);
-  }
-  if (threadIdx.x == 0) token_offset[n] = total;
-}
-
-__global__ __launch_bounds__(256) void token_fill_tc_kernel(const int32_t* __restrict__ assign_slot,
-                                                            const int32_t* __restrict__ token_offset,
-                                                            int n, int k,
-                                                            int32_t* __restrict__ token_slot) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= n) return;
-  int q = token_offset[t];
-  for (int r = 0; r < k; ++r) {
-    const int s = assign_slot[(size_t)t * k + r];
-    if (s >= 0) token_slot[q++] = s;
   }
 }
 
 // ---------------------------------------------------------------- expert choice
+// Token t's list holds the slots of the experts that picked it, in
+// ascending expert order.  A bit mask [n][ceil(E/32)] records who picked
+// whom (integer atomics, order-free); a token's list length is the popcount
+// of its row, the offsets are a workgroup scan, and the position of (t, e)
+// in t's list is the popcount of t's bits below e.
 
 __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p, int64_t count,
                                                        uint32_t v) {
@@ -189,32 +155,40 @@ __global__ __launch_bounds__(256) void ec_slots_kernel(const int32_t* __restrict
   }
 }
 
-// A token's experts in ascending expert order; the slot of (token t,
-// expert e) is e*k + j with I[e, j] = t, found by binary search in the
-// ascending row I[e, :].
-__global__ __launch_bounds__(256) void token_fill_ec_kernel(const int32_t* __restrict__ I,
+// One workgroup: each thread owns a contiguous run of tokens; their list
+// lengths are summed, scanned across the workgroup, and written back as
+// offsets.
+__global__ __launch_bounds__(kScanThreads) void ec_token_offsets_kernel(
+    const uint32_t* __restrict__ mask, int n, int W, int32_t* __restrict__ token_offset) {
+  __shared__ int scratch[kScanThreads / 64];
+  const int seg = (n + kScanThreads - 1) / kScanThreads;
+  const int t0 = min(n, (int)threadIdx.x * seg), t1 = min(n, t0 + seg);
+  int sum = 0;
+  for (int64_t i = (int64_t)t0 * W; i < (int64_t)t1 * W; ++i) sum += __popc(mask[i]);
+  int total = 0;
+  int run = block_exclusive_scan<kScanThreads>(sum, scratch, &total);
+  for (int t = t0; t < t1; ++t) {
+    token_offset[t] = run;
+    for (int w = 0; w < W; ++w) run += __popc(mask[(size_t)t * W + w]);
+  }
+  if (threadIdx.x == 0) token_offset[n] = total;
+}
+
+__global__ __launch_bounds__(256) void ec_token_fill_kernel(const int32_t* __restrict__ I,
                                                             const uint32_t* __restrict__ mask,
                                                             const int32_t* __restrict__ token_offset,
-                                                            int n, int k, int W,
+                                                            int n, int E, int k, int W,
                                                             int32_t* __restrict__ token_slot) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= n) return;
-  int q = token_offset[t];
-  for (int w = 0; w < W; ++w) {
-    uint32_t bits = mask[(size_t)t * W + w];
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      bits &= bits - 1u;
-      const int e = 32 * w + b;
-      const int32_t* row = I + (size_t)e * k;
-      int lo = 0, hi = k;             // first j with row[j] >= t
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (row[mid] < t) lo = mid + 1; else hi = mid;
-      }
-      token_slot[q++] = e * k + lo;
-    }
-  }
+  const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (s >= (int64_t)E * k) return;
+  const int e = (int)(s / k);
+  const int t = I[s];
+  if ((unsigned)t >= (unsigned)n) return;
+  const uint32_t* row = mask + (size_t)t * W;
+  int before = 0;
+  for (int w = 0; w < (e >> 5); ++w) before += __popc(row[w]);
+  before += __popc(row[e >> 5] & ((1u << (e & 31)) - 1u));
+  token_slot[token_offset[t] + before] = (int32_t)s;
 }
 
 // ---------------------------------------------------------------- host side
@@ -239,12 +213,7 @@ hipError_t launch_build_map_tc(const int32_t* idx, const float* gate, int n, int
   hipLaunchKernelGGL(map_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, chunk_hist, nch, E,
                      capacity, chunk_base, m.expert_count, m.expert_offset, m.n_kept);
   hipLaunchKernelGGL(map_scatter_kernel, dim3(nch), dim3(64), E * sizeof(int), stream, idx, gate, M,
-                     k, E, nbits, capacity, chunk_base, m.expert_offset, m.slot_token, m.slot_gate,
-                     m.assign_slot);
-  hipLaunchKernelGGL(token_offsets_kernel<0>, dim3(1), dim3(kScanThreads), 0, stream, m.assign_slot,
-                     nullptr, n, k, 0, m.token_offset);
-  hipLaunchKernelGGL(token_fill_tc_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, m.assign_slot,
-                     m.token_offset, n, k, m.token_slot);
+                     k, E, nbits, capacity, chunk_base, m.expert_offset, m);
   return hipGetLastError();
 }
 
@@ -256,12 +225,12 @@ hipError_t launch_build_map_ec(const int32_t* I, const float* G, int n, int E, i
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
                      mask, words, 0u);
   const int64_t M = (int64_t)E * k;
-  hipLaunchKernelGGL(ec_slots_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, stream, I, G, n,
-                     E, k, W, m, mask);
-  hipLaunchKernelGGL(token_offsets_kernel<1>, dim3(1), dim3(kScanThreads), 0, stream, nullptr, mask, n,
-                     k, W, m.token_offset);
-  hipLaunchKernelGGL(token_fill_ec_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, I, mask,
-                     m.token_offset, n, k, W, m.token_slot);
+  const dim3 grid((unsigned)((M + 255) / 256));
+  hipLaunchKernelGGL(ec_slots_kernel, grid, dim3(256), 0, stream, I, G, n, E, k, W, m, mask);
+  hipLaunchKernelGGL(ec_token_offsets_kernel, dim3(1), dim3(kScanThreads), 0, stream, mask, n, W,
+                     m.token_offset);
+  hipLaunchKernelGGL(ec_token_fill_kernel, grid, dim3(256), 0, stream, I, mask, m.token_offset, n, E,
+                     k, W, m.token_slot);
   return hipGetLastError();
 }
 

@@ -22,15 +22,23 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 constexpr int kRouterRows = 64;    // rows per workgroup (16 per wave)
 constexpr int kRouterBK = 64;      // K per LDS stage
 constexpr int kRouterCols = 256;   // expert columns per workgroup
 constexpr int kRouterLdsStride = kRouterBK + 8;   // bf16 elements per LDS row (padding skews banks)
+constexpr int kRouterMaxItems = kRouterBK * kRouterCols / 8 / 256;   // 16-byte W_g loads per thread
 
+// Software pipeline: while the matrix cores work on K stage s (A fragments
+// in registers, the W_g stage in LDS buffer s % 2), the next stage's A
+// fragments and W_g rows are already loading into registers; they are
+// written (transposed) to the other LDS buffer after the MFMAs, so one
+// barrier per stage suffices.
 __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ Wg, int n, int d, int E, int k_per_split,
     float* __restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) bf16_t sB[kRouterCols * kRouterLdsStride];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[2][kRouterCols * kRouterLdsStride];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -40,7 +48,9 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
   const int ncols = min(kRouterCols, E - c0);     // multiple of 16
   const int nt = ncols >> 4;                       // 16-column tiles
   const int kbeg = split * k_per_split;
-  const int kend = kbeg + k_per_split;
+  const int nk = k_per_split / kRouterBK;
+  const int per_row = ncols >> 3;                  // 8-column chunks per K row
+  const int items = kRouterBK * per_row;
 
   f32x4_t acc[16];
 #pragma unroll
@@ -49,34 +59,63 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
   // A fragment source: row (lane % 16), 8 K values at (lane / 16) * 8.
   int arow = row0 + (lane & 15);
   if (arow > n - 1) arow = n - 1;                  // tail rows are computed but never stored
-  const bf16_t* aptr = X + (size_t)arow * d + ((lane >> 4) << 3);
+  const bf16_t* aptr = X + (size_t)arow * d + kbeg + ((lane >> 4) << 3);
 
-  for (int k0 = kbeg; k0 < kend; k0 += kRouterBK) {
-    // Prefetch this wave's A fragments for the two 32-wide K steps.
-    bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(aptr + k0);
-    bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(aptr + k0 + 32);
-    // Stage W_g[k0 .. k0+64, c0 .. c0+ncols] transposed into LDS.
-    const int per_row = ncols >> 3;                // 8-column chunks per K row
-    for (int item = tid; item < kRouterBK * per_row; item += 256) {
-      const int kk = item / per_row;
-      const int cc = (item - kk * per_row) << 3;
-      const uint4 v = *reinterpret_cast<const uint4*>(Wg + (size_t)(k0 + kk) * E + c0 + cc);
-      const bf16_t* pv = reinterpret_cast<const bf16_t*>(&v);
+  u32x4_t wreg[kRouterMaxItems];
+  auto load_w = [&](int k0) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sB[(cc + i) * kRouterLdsStride + kk] = pv[i];
+    for (int i = 0; i < kRouterMaxItems; ++i) {
+      const int item = tid + 256 * i;
+      if (item < items) {
+        const int kk = item / per_row;
+        const int cc = (item - kk * per_row) << 3;
+        wreg[i] = *reinterpret_cast<const u32x4_t*>(Wg + (size_t)(k0 + kk) * E + c0 + cc);
+      }
+    }
+  };
+  auto store_w = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kRouterMaxItems; ++i) {
+      const int item = tid + 256 * i;
+      if (item < items) {
+        const int kk = item / per_row;
+        const int cc = (item - kk * per_row) << 3;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          sB[buf][(cc + 2 * h) * kRouterLdsStride + kk] = (bf16_t)(wreg[i][h] & 0xFFFFu);
+          sB[buf][(cc + 2 * h + 1) * kRouterLdsStride + kk] = (bf16_t)(wreg[i][h] >> 16);
+        }
+      }
+    }
+  };
+
+  load_w(kbeg);
+  bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(aptr);
+  bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(aptr + 32);
+  store_w(0);
+  for (int s = 0; s < nk; ++s) {
+    const int cur = s & 1;
+    const bool more = s + 1 < nk;
+    bf16x8_t na0 = a0, na1 = a1;
+    if (more) {
+      load_w(kbeg + (s + 1) * kRouterBK);
+      na0 = *reinterpret_cast<const bf16x8_t*>(aptr + (s + 1) * kRouterBK);
+      na1 = *reinterpret_cast<const bf16x8_t*>(aptr + (s + 1) * kRouterBK + 32);
     }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (j < nt) {
-        const bf16_t* bp = sB + (j * 16 + (lane & 15)) * kRouterLdsStride + ((lane >> 4) << 3);
+        const bf16_t* bp = sB[cur] + (j * 16 + (lane & 15)) * kRouterLdsStride + ((lane >> 4) << 3);
         bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(bp);
         bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(bp + 32);
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[j], 0, 0, 0);
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[j], 0, 0, 0);
       }
     }
-    __syncthreads();
+    if (more) store_w(cur ^ 1);
+    a0 = na0;
+    a1 = na1;
   }
   // C fragment: lane holds column (lane % 16), rows (lane / 16) * 4 + r.
   float* out = partial + (size_t)split * n * E;
@@ -113,23 +152,29 @@ __global__ __launch_bounds__(256) void router_gemm_scalar_kernel(const T* __rest
 
 static bool router_uses_mfma(int dtype, int d, int E) { return dtype == 1 && d % 64 == 0 && E % 16 == 0; }
 
-// Finalize: one wave per row; lane l holds experts l + 64 j.  Sums the split
-// partials in split order, adds the offset, writes the logits and (on
-// request) the specified scores, row-major and/or transposed (the transpose
-// goes through an LDS tile so the [E, n] stores stay coalesced).
-__global__ __launch_bounds__(256) void router_finalize_kernel(
+// Finalize: 16 rows per workgroup, one wave per row at a time; lane l holds
+// experts l + 64 j.  Sums the split partials in split order, adds the
+// offset, writes the logits and (on request) the specified scores,
+// row-major and/or transposed.  The transpose goes through an LDS tile with
+// an odd row stride (E + 1 floats), so both the row-wise writes and the
+// column-wise reads are free of bank conflicts and the [E, n] stores are
+// 64-byte runs.
+constexpr int kFinRows = 16;
+
+__global__ __launch_bounds__(1024) void router_finalize_kernel(
     const float* partial, int nsplit, int n, int E, const float* __restrict__ offset, int score,
     float* logits, float* __restrict__ scores, float* __restrict__ scores_t) {
   // `partial` and `logits` may be the same buffer (single K-slice): each
   // element is read and then written by the same thread.
 #pragma clang fp contract(off)
-  extern __shared__ float sT[];   // [64 rows][E] when scores_t is requested
+  extern __shared__ float sT[];   // [kFinRows][E + 1] when scores_t is requested
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nj = (E + 63) >> 6;
   const int P = next_pow2(E);
-  const int blk_row0 = blockIdx.x * 64;
-  for (int rr = wave; rr < 64; rr += 4) {
+  const int ld = E + 1;
+  const int blk_row0 = blockIdx.x * kFinRows;
+  for (int rr = wave; rr < kFinRows; rr += 16) {
     const int row = blk_row0 + rr;
     if (row >= n) break;
     float z[kMaxExpertRegs];
@@ -169,16 +214,16 @@ __global__ __launch_bounds__(256) void router_finalize_kernel(
       const int e = lane + 64 * j;
       if (j < nj && e < E) {
         if (scores) scores[(size_t)row * E + e] = p[j];
-        if (scores_t) sT[rr * E + e] = p[j];
+        if (scores_t) sT[rr * ld + e] = p[j];
       }
     }
   }
   if (!scores_t) return;
   __syncthreads();
-  const int rows = min(64, n - blk_row0);
-  for (int item = threadIdx.x; item < E * 64; item += 256) {
-    const int e = item >> 6, rr = item & 63;
-    if (rr < rows) scores_t[(size_t)e * n + blk_row0 + rr] = sT[rr * E + e];
+  const int rows = min(kFinRows, n - blk_row0);
+  for (int item = threadIdx.x; item < E * kFinRows; item += 1024) {
+    const int e = item / kFinRows, rr = item % kFinRows;
+    if (rr < rows) scores_t[(size_t)e * n + blk_row0 + rr] = sT[rr * ld + e];
   }
 }
 
@@ -233,13 +278,13 @@ hipError_t launch_router(const void* X, const void* Wg, int dtype, const float* 
 hipError_t launch_router_finalize(const float* partial, int nsplit, int n, int E, const float* offset,
                                   int score, float* logits, float* scores, float* scores_t,
                                   hipStream_t stream) {
-  const size_t lds = scores_t ? (size_t)64 * E * sizeof(float) : 0;
+  const size_t lds = scores_t ? (size_t)kFinRows * (E + 1) * sizeof(float) : 0;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&router_finalize_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(router_finalize_kernel, dim3((n + 63) / 64), dim3(256), lds, stream, partial,
+  hipLaunchKernelGGL(router_finalize_kernel, dim3((n + kFinRows - 1) / kFinRows), dim3(1024), lds, stream, partial,
                      nsplit, n, E, offset, score, logits, scores, scores_t);
   return hipGetLastError();
 }

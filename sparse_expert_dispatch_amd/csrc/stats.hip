@@ -15,32 +15,41 @@
 //   max_vio = (max_e load_e - mean load) / mean load,  load = kept rows,
 // plus kept / dropped counts and the experts-per-token histogram.
 //
-// Deterministic: per-block partial sums in a fixed order, then one
-// workgroup reduces them in block order; integers use order-free atomics.
+// Two kernels.  The row kernel (16 tokens per workgroup, one per wave) adds up
+// each block's normalised scores, squared log-sum-exps and experts-per-token
+// histogram; the final kernel (one workgroup) reduces the block partials in
+// a fixed order, so the floats are reproducible bit for bit.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 
-constexpr int kStatRows = 64;   // rows per block (16 per wave)
+constexpr int kStatRows = 16;   // rows per block, one per wave
 
-__global__ __launch_bounds__(256) void stats_rows_kernel(const float* __restrict__ logits, int n,
-                                                         int E, int score, float* __restrict__ part_P,
-                                                         float* __restrict__ part_Z) {
+__global__ __launch_bounds__(1024) void stats_rows_kernel(const float* __restrict__ logits,
+                                                         const int32_t* __restrict__ token_offset,
+                                                         const int32_t* __restrict__ token_slot,
+                                                         int n, int E, int score,
+                                                         float* __restrict__ part_P,
+                                                         float* __restrict__ part_Z,
+                                                         int32_t* __restrict__ part_H) {
 #pragma clang fp contract(off)
-  __shared__ float sP[4][kMaxExperts];
-  __shared__ float sZ[4];
+  __shared__ float sP[kStatRows][kMaxExperts];
+  __shared__ float sZ[kStatRows];
+  __shared__ int sH[kMaxExperts + 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nj = (E + 63) >> 6;
   const int P2 = next_pow2(E);
+  for (int i = threadIdx.x; i <= E; i += 1024) sH[i] = 0;
+  __syncthreads();
   float accP[kMaxExpertRegs];
 #pragma unroll
   for (int j = 0; j < kMaxExpertRegs; ++j) accP[j] = 0.f;
   float accZ = 0.f;
-  for (int r = 0; r < kStatRows / 4; ++r) {
-    const int row = blockIdx.x * kStatRows + wave * (kStatRows / 4) + r;
-    if (row >= n) break;
+  {
+    const int row = blockIdx.x * kStatRows + wave;
+    if (row >= n) goto done;
     float z[kMaxExpertRegs];
     float m = -__builtin_huge_valf();
 #pragma unroll
@@ -49,6 +58,12 @@ __global__ __launch_bounds__(256) void stats_rows_kernel(const float* __restrict
       z[j] = (j < nj && e < E) ? logits[(size_t)row * E + e] : 0.f;
       if (j < nj && e < E) m = fmaxf(m, z[j]);
     }
+    // kept experts of this token: its list entries that are not drops
+    const int q0 = token_offset[row], q1 = token_offset[row + 1];
+    int kept = 0;
+    for (int q = q0; q < q1; q += 64)
+      kept += __popcll(__ballot(q + lane < q1 && token_slot[q + lane] >= 0));
+    if (lane == 0) atomicAdd(&sH[min(kept, E)], 1);
     m = wave_max_f32(m);
     float t[kMaxExpertRegs], u[kMaxExpertRegs];
 #pragma unroll
@@ -64,6 +79,7 @@ __global__ __launch_bounds__(256) void stats_rows_kernel(const float* __restrict
     const float lse = m + logf(s_exp);
     accZ = accZ + lse * lse;
   }
+done:
 #pragma unroll
   for (int j = 0; j < kMaxExpertRegs; ++j) {
     const int e = lane + 64 * j;
@@ -71,124 +87,140 @@ __global__ __launch_bounds__(256) void stats_rows_kernel(const float* __restrict
   }
   if (lane == 0) sZ[wave] = accZ;
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256)
-    part_P[(size_t)blockIdx.x * E + e] = ((sP[0][e] + sP[1][e]) + sP[2][e]) + sP[3][e];
-  if (threadIdx.x == 0) part_Z[blockIdx.x] = ((sZ[0] + sZ[1]) + sZ[2]) + sZ[3];
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    float v = sP[0][e];
+    for (int w = 1; w < kStatRows; ++w) v = v + sP[w][e];
+    part_P[(size_t)blockIdx.x * E + e] = v;
+  }
+  for (int i = threadIdx.x; i <= E; i += 1024) part_H[(size_t)blockIdx.x * (E + 1) + i] = sH[i];
+  if (threadIdx.x == 0) {
+    float v = sZ[0];
+    for (int w = 1; w < kStatRows; ++w) v = v + sZ[w];
+    part_Z[blockIdx.x] = v;
+  }
 }
 
 constexpr int kFinThreads = 1024;
 
+// Column sums of a [nb][cols] partial table, in a fixed order: thread group
+// g (of G = kFinThreads / cols rounded up to a power of two) sums rows g,
+// g + G, ...; the G group sums are then added in group order.  Result in
+// out_lds[0 .. cols).
+template <typename T>
+MOE_DEV void fixed_order_column_sums(const T* __restrict__ part, int nb, int cols, T* red,
+                                     T* out_lds) {
+#pragma clang fp contract(off)
+  int cp = 32;
+  while (cp < cols) cp <<= 1;
+  const int groups = kFinThreads / cp;
+  const int tid = threadIdx.x;
+  const int g = tid / cp, c = tid % cp;
+  T s = 0;
+  if (c < cols && g < groups) {
+#pragma unroll 8
+    for (int b = g; b < nb; b += groups) s = s + part[(size_t)b * cols + c];
+  }
+  red[tid] = s;
+  __syncthreads();
+  if (tid < cols) {
+    T v = 0;
+    for (int q = 0; q < groups; ++q) v = v + red[q * cp + tid];
+    out_lds[tid] = v;
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(kFinThreads) void stats_final_kernel(
-    const float* __restrict__ part_P, const float* __restrict__ part_Z, int nblocks, int n, int E,
-    int k, int dir, float lb_coef, float z_coef, const int32_t* __restrict__ expert_count,
-    const int32_t* __restrict__ expert_offset, const int32_t* __restrict__ token_offset,
+    const float* __restrict__ part_P, const float* __restrict__ part_Z,
+    const int32_t* __restrict__ part_H, int nblocks, int n, int E, int k, int dir, float lb_coef,
+    float z_coef, const int32_t* __restrict__ expert_count, const int32_t* __restrict__ expert_offset,
     float* __restrict__ stats, int32_t* __restrict__ hist) {
 #pragma clang fp contract(off)
   __shared__ float red[kFinThreads];
   __shared__ int ired[kFinThreads];
-  __shared__ int shist[kMaxExperts + 1];
+  __shared__ float sPe[kMaxExperts];
+  __shared__ float sZ[1];
+  __shared__ int sH[kMaxExperts + 1];
+  __shared__ int wred[kFinThreads / 64][2];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
 
-  // total chosen assignments (exact integer)
-  ired[tid] = tid < E ? expert_count[tid] : 0;
-  __syncthreads();
-  for (int s = kFinThreads / 2; s >= 1; s >>= 1) {
-    if (tid < s) ired[tid] += ired[tid + s];
-    __syncthreads();
-  }
-  const int chosen_total = ired[0];
-  __syncthreads();
+  fixed_order_column_sums<float>(part_P, nblocks, E, red, sPe);
+  fixed_order_column_sums<float>(part_Z, nblocks, 1, red, sZ);
+  fixed_order_column_sums<int>(part_H, nblocks, E + 1, ired, sH);
 
-  // f_e * P_e, reduced by a fixed tree over experts
-  float fp = 0.f;
-  if (tid < E) {
-    float pe = 0.f;
-    for (int b = 0; b < nblocks; ++b) pe = pe + part_P[(size_t)b * E + tid];
-    pe = pe / (float)n;
-    const float fe = (float)expert_count[tid] / (float)chosen_total;
-    fp = fe * pe;
+  // chosen total and largest kept load
+  int chosen = 0, maxload = 0;
+  for (int e = tid; e < E; e += kFinThreads) {
+    chosen += expert_count[e];
+    maxload = max(maxload, expert_offset[e + 1] - expert_offset[e]);
   }
-  red[tid] = fp;
-  __syncthreads();
-  for (int s = kFinThreads / 2; s >= 1; s >>= 1) {
-    if (tid < s) red[tid] = red[tid] + red[tid + s];
-    __syncthreads();
+  for (int o = 32; o >= 1; o >>= 1) {
+    chosen += __shfl_xor(chosen, o, 64);
+    maxload = max(maxload, __shfl_xor(maxload, o, 64));
   }
-  const float sum_fp = red[0];
-  __syncthreads();
-
-  // z-loss partials, fixed tree over blocks (nblocks may exceed the thread count)
-  float zp = 0.f;
-  for (int b = tid; b < nblocks; b += kFinThreads) zp = zp + part_Z[b];
-  red[tid] = zp;
-  __syncthreads();
-  for (int s = kFinThreads / 2; s >= 1; s >>= 1) {
-    if (tid < s) red[tid] = red[tid] + red[tid + s];
-    __syncthreads();
+  if (lane == 0) {
+    wred[wave][0] = chosen;
+    wred[wave][1] = maxload;
   }
-  const float sum_z = red[0];
   __syncthreads();
-
-  // maximum kept load
-  ired[tid] = tid < E ? expert_offset[tid + 1] - expert_offset[tid] : 0;
-  __syncthreads();
-  for (int s = kFinThreads / 2; s >= 1; s >>= 1) {
-    if (tid < s) ired[tid] = max(ired[tid], ired[tid + s]);
-    __syncthreads();
+  int ch = 0, ml = 0;
+  for (int w = 0; w < kFinThreads / 64; ++w) {
+    ch += wred[w][0];
+    ml = max(ml, wred[w][1]);
   }
-  const int max_load = ired[0];
-  __syncthreads();
-
-  // experts-per-token histogram and its maximum
-  for (int i = tid; i <= E; i += kFinThreads) shist[i] = 0;
-  __syncthreads();
-  int my_max = 0;
-  for (int t = tid; t < n; t += kFinThreads) {
-    const int c = token_offset[t + 1] - token_offset[t];
-    atomicAdd(&shist[min(c, E)], 1);
-    my_max = max(my_max, c);
-  }
-  ired[tid] = my_max;
-  __syncthreads();
-  for (int s = kFinThreads / 2; s >= 1; s >>= 1) {
-    if (tid < s) ired[tid] = max(ired[tid], ired[tid + s]);
-    __syncthreads();
-  }
-  const int max_per_token = ired[0];
   if (hist)
-    for (int i = tid; i <= E; i += kFinThreads) hist[i] = shist[i];
-
+    for (int i = tid; i <= E; i += kFinThreads) hist[i] = sH[i];
+  // sum_e f_e P_e by a halving tree over experts
+  const int P = next_pow2(E);
+  if (tid < P) red[tid] = tid < E ? ((float)expert_count[tid] / (float)ch) * (sPe[tid] / (float)n) : 0.f;
+  __syncthreads();
+  for (int s = P >> 1; s >= 1; s >>= 1) {
+    if (tid < s) red[tid] = red[tid] + red[tid + s];
+    __syncthreads();
+  }
   if (tid == 0) {
+    int mt = 0;
+    for (int i = E; i >= 0; --i)
+      if (sH[i] > 0) {
+        mt = i;
+        break;
+      }
     const int n_kept = expert_offset[E];
     const int total = dir == 0 ? n * k : E * k;
     const float mean_load = (float)n_kept / (float)E;
-    stats[0] = lb_coef * (float)E * sum_fp;
-    stats[1] = z_coef * (sum_z / (float)n);
-    stats[2] = mean_load > 0.f ? ((float)max_load - mean_load) / mean_load : 0.f;
-    stats[3] = n_kept > 0 ? (float)max_load / (float)n_kept : 0.f;
+    stats[0] = lb_coef * (float)E * red[0];
+    stats[1] = z_coef * (sZ[0] / (float)n);
+    stats[2] = mean_load > 0.f ? ((float)ml - mean_load) / mean_load : 0.f;
+    stats[3] = n_kept > 0 ? (float)ml / (float)n_kept : 0.f;
     stats[4] = (float)n_kept;
     stats[5] = (float)(total - n_kept);
-    stats[6] = (float)shist[0];
-    stats[7] = (float)max_per_token;
+    stats[6] = (float)sH[0];
+    stats[7] = (float)mt;
   }
 }
 
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 size_t stats_workspace_bytes(int n, int E) {
   const size_t nb = (size_t)(n + kStatRows - 1) / kStatRows;
-  return nb * E * sizeof(float) + nb * sizeof(float);
+  return align256(nb * E * sizeof(float)) + align256(nb * sizeof(float)) +
+         align256(nb * (E + 1) * sizeof(int32_t));
 }
 
 hipError_t launch_balance_stats(const float* logits, const MapPtrs& m, int n, int E, int k, int dir,
                                 int score, float lb_coef, float z_coef, float* stats, int32_t* hist,
                                 void* ws, hipStream_t stream) {
   const int nb = (n + kStatRows - 1) / kStatRows;
-  float* part_P = static_cast<float*>(ws);
-  float* part_Z = part_P + (size_t)nb * E;
-  hipLaunchKernelGGL(stats_rows_kernel, dim3(nb), dim3(256), 0, stream, logits, n, E, score, part_P,
-                     part_Z);
-  hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(kFinThreads), 0, stream, part_P, part_Z, nb, n,
-                     E, k, dir, lb_coef, z_coef, m.expert_count, m.expert_offset, m.token_offset,
-                     stats, hist);
+  char* w = static_cast<char*>(ws);
+  float* part_P = reinterpret_cast<float*>(w);
+  float* part_Z = reinterpret_cast<float*>(w + align256((size_t)nb * E * sizeof(float)));
+  int32_t* part_H = reinterpret_cast<int32_t*>(w + align256((size_t)nb * E * sizeof(float)) +
+                                               align256((size_t)nb * sizeof(float)));
+  hipLaunchKernelGGL(stats_rows_kernel, dim3(nb), dim3(1024), 0, stream, logits, m.token_offset,
+                     m.token_slot, n, E, score, part_P, part_Z, part_H);
+  hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(kFinThreads), 0, stream, part_P, part_Z, part_H,
+                     nb, n, E, k, dir, lb_coef, z_coef, m.expert_count, m.expert_offset, stats, hist);
   return hipGetLastError();
 }
 

@@ -78,6 +78,12 @@ def run_gpu(cfg, inp: dict, weights=None) -> dict:
     return r
 
 
+def kept_slots(rmap: dict, t: int) -> list:
+    """Token t's kept slots, in its list order (negative entries are drops)."""
+    a, b = int(rmap["token_offset"][t]), int(rmap["token_offset"][t + 1])
+    return [int(s) for s in rmap["token_slot"][a:b] if s >= 0]
+
+
 def check_logits(z_gpu: np.ndarray, z_ref: np.ndarray):
     err = np.abs(z_gpu.astype(np.float64) - z_ref.astype(np.float64)).max(axis=1)
     scale = np.abs(z_ref.astype(np.float64)).max(axis=1)
@@ -120,8 +126,9 @@ def check_map(g: dict, ref_map: dict):
     for key in ("expert_count", "expert_offset", "assign_slot", "token_offset"):
         assert np.array_equal(g[key], ref_map[key]), key
     for key in ("slot_token", "slot_gate", "token_slot"):
-        got = g[key][:nk]
-        want = ref_map[key][:nk]
+        ln = nk if key != "token_slot" else int(ref_map["token_offset"][-1])
+        got = g[key][:ln]
+        want = ref_map[key][:ln]
         if key == "slot_gate":
             assert np.array_equal(got.view(np.uint32), want.astype(np.float32).view(np.uint32)), key
         else:
@@ -182,8 +189,7 @@ def compare_all(cfg, inp: dict, g: dict, full_ffn: bool = True, sample_tokens=No
         tokens = np.asarray(sample_tokens)
         pairs = {}                                   # expert -> [(i, slot)]
         for i, t in enumerate(tokens):
-            for q in range(rmap["token_offset"][t], rmap["token_offset"][t + 1]):
-                s = int(rmap["token_slot"][q])
+            for s in kept_slots(rmap, t):
                 e = int(np.searchsorted(rmap["expert_offset"], s, side="right") - 1)
                 pairs.setdefault(e, []).append((i, s))
         yrows = {}
@@ -201,8 +207,7 @@ def compare_all(cfg, inp: dict, g: dict, full_ffn: bool = True, sample_tokens=No
                               cfg.act, bf16, "shared expert")
         branch = np.zeros((len(tokens), cfg.d))
         for i, t in enumerate(tokens):
-            for q in range(rmap["token_offset"][t], rmap["token_offset"][t + 1]):
-                s = int(rmap["token_slot"][q])
+            for s in kept_slots(rmap, t):
                 branch[i] += float(rmap["slot_gate"][s]) * yrows[s]
             if shared_rows is not None:
                 branch[i] += shared_rows[i]
@@ -213,8 +218,7 @@ def compare_all(cfg, inp: dict, g: dict, full_ffn: bool = True, sample_tokens=No
     sh_dev = widen(g["shared"]) if cfg.shared_f else None
     comb = np.zeros((len(tokens), cfg.d))
     for i, t in enumerate(tokens):
-        for q in range(rmap["token_offset"][t], rmap["token_offset"][t + 1]):
-            s = int(rmap["token_slot"][q])
+        for s in kept_slots(rmap, t):
             comb[i] += float(rmap["slot_gate"][s]) * y_dev[s]
         if sh_dev is not None:
             comb[i] += sh_dev[t]
@@ -235,7 +239,7 @@ def compare_all(cfg, inp: dict, g: dict, full_ffn: bool = True, sample_tokens=No
     assert err_branch <= tol, f"layer branch: max-abs / RMS(out) = {err_branch:.3g}"
     # tokens with no kept expert (and no shared expert) ride the residual bit for bit
     if not cfg.shared_f:
-        empty = tokens[np.diff(rmap["token_offset"])[tokens] == 0]
+        empty = np.array([t for t in tokens if not kept_slots(rmap, t)], dtype=np.int64)
         assert np.array_equal(g["out"][empty], inp["x"][empty]), "residual pass-through"
     log(f"  outputs within tolerance ({time.time() - t0:.1f}s)")
 

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for name in names:
         assert hasattr(L, name), name
     assert sorted(N.EXPORTED) == names
@@ -56,8 +56,10 @@ def test_max_slots(L):
     assert M.moe_max_slots(cfg) == 512
     cfg = N.make_cfg(256, 64, 8, 2, capacity=40)
     assert M.moe_max_slots(cfg) == 320
+    assert M.moe_token_list_len(cfg) == 512
     cfg = N.make_cfg(4096, 2048, 64, 128, direction=N.MOE_EXPERT_CHOICE)
     assert M.moe_max_slots(cfg) == 8192
+    assert M.moe_token_list_len(cfg) == 8192
 
 
 FAKE = 0x10000   # a non-NULL, 16-byte aligned address that is never dereferenced

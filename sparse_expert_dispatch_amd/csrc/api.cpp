@@ -243,6 +243,7 @@ moe_status_t moe_expert_ffn(const void* X_perm, int32_t dtype, const int32_t* ex
   REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, "dtype must be MOE_F32 or MOE_BF16");
   REQUIRE(M_max <= INT32_MAX, "M_max must fit in int32");
   if (dtype == MOE_BF16) {
+    SUPPORTED(E <= moe::kMaxExperts, "bf16 expert FFN supports E <= %d (E=%d)", moe::kMaxExperts, E);
     SUPPORTED(d % 64 == 0 && f % 64 == 0, "bf16 expert FFN needs d %% 64 == 0 and f %% 64 == 0 (d=%d f=%d)",
               d, f);
     REQUIRE(aligned16(X_perm) && aligned16(W1) && aligned16(W2) && aligned16(Y_perm),

@@ -37,35 +37,68 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 64
+#endif
 constexpr int kBM = 128;
-constexpr int kBK = 64;
+constexpr int kBK = MOE_GEMM_BK;             // K per stage
 constexpr int kLdsStride = kBK + 8;          // bf16 per LDS row
 constexpr int kTileElems = 128 * kLdsStride; // one 128-row operand tile
 constexpr int kGemmThreads = 256;
 constexpr int kXcds = 8;
+#ifndef MOE_GEMM_PREFETCH
+#define MOE_GEMM_PREFETCH 1
+#endif
+constexpr int kPrefetch = MOE_GEMM_PREFETCH;   // K stages in flight in registers
+#ifndef MOE_GEMM_V2
+#define MOE_GEMM_V2 0
+#endif
+#ifndef MOE_GEMM_ORDER
+#define MOE_GEMM_ORDER -1                        // tile order: -1 by shape, 0 N inner, 1 M inner
+#endif
 
 enum { kEpiNone = 0, kEpiGelu = 1, kEpiSwiglu = 2 };
 
-MOE_DEV float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
-MOE_DEV float silu_f(float x) { return x / (1.0f + expf(-x)); }
+// GELU x * Phi(x) with erf from Abramowitz & Stegun formula 7.1.26
+// (|error| <= 1.5e-7 over the real line, far below the bf16 rounding of the
+// result): erf(z) = 1 - (a1 t + ... + a5 t^5) exp(-z^2), t = 1 / (1 + p z),
+// z >= 0, odd extension for z < 0.
+MOE_DEV float gelu_f(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __frcp_rn(1.0f + 0.3275911f * z);
+  const float poly =
+      t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  const float erf_z = 1.0f - poly * __expf(-z * z);
+  const float erf_x = x < 0.f ? -erf_z : erf_z;
+  return 0.5f * x * (1.0f + erf_x);
+}
+MOE_DEV float silu_f(float x) { return x * __frcp_rn(1.0f + __expf(-x)); }
 
-// Tile list: tile_off[e] = sum over e' < e of ceil(m_e' / kBM).
-__global__ __launch_bounds__(1024) void tile_plan_kernel(const int32_t* __restrict__ expert_offset,
-                                                         int E, int32_t* __restrict__ tile_off) {
-  __shared__ int scratch[16];
-  const int e = threadIdx.x;
-  int v = 0;
-  for (int base = 0; base < E; base += 1024) {
-    // E <= 1024 in practice; the loop keeps the kernel correct beyond that
-    const int ee = base + e;
-    const int m = ee < E ? expert_offset[ee + 1] - expert_offset[ee] : 0;
-    const int tiles = (m + kBM - 1) / kBM;
-    int total = 0;
-    const int ex = block_exclusive_scan<1024>(tiles, scratch, &total);
-    if (ee < E) tile_off[ee] = v + ex;
-    v += total;
+// Tile list, built by every workgroup in LDS at kernel start (no separate
+// launch, no host synchronisation): tile_off[e] = sum over e' < e of
+// ceil(m_e' / kBM), tile_off[E] = all M tiles.  E <= kMaxExperts.
+MOE_DEV void block_tile_plan(const int32_t* __restrict__ expert_offset, int E, int32_t* tile_off) {
+  __shared__ int scratch[kGemmThreads / 64];
+  constexpr int kPer = (kMaxExperts + kGemmThreads - 1) / kGemmThreads;
+  const int e0 = threadIdx.x * kPer;
+  int cnt[kPer];
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = e0 + i;
+    const int m = e < E ? expert_offset[e + 1] - expert_offset[e] : 0;
+    cnt[i] = (m + kBM - 1) / kBM;
+    sum += cnt[i];
   }
-  if (e == 0) tile_off[E] = v;
+  int total = 0;
+  int run = block_exclusive_scan<kGemmThreads>(sum, scratch, &total);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (e0 + i < E) tile_off[e0 + i] = run;
+    run += cnt[i];
+  }
+  if (threadIdx.x == 0) tile_off[E] = total;
+  __syncthreads();
 }
 
 template <bool kDual>
@@ -80,11 +113,18 @@ MOE_DEV int b_row_of(int r, int n0, int N) {
 template <bool kDual, int kEpi>
 __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
-    const int32_t* __restrict__ expert_offset, const int32_t* __restrict__ tile_off, int E, int N,
-    int K, bf16_t* __restrict__ C) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][kTileElems];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][kTileElems];
+    const int32_t* __restrict__ expert_offset, int E, int N, int K, int mt_inner,
+    bf16_t* __restrict__ C) {
+  // LDS: A and B K-stages, double buffered; reused for the output tile.
+  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * kTileElems];
+  __shared__ int32_t tile_off[kMaxExperts + 1];
+  block_tile_plan(expert_offset, E, tile_off);
   constexpr int kBNout = kDual ? 64 : 128;
+  constexpr int kLoads = kBK / 16;                 // 16-byte loads per thread per operand and stage
+  constexpr int kChunksRow = kBK / 8;              // 16-byte chunks per operand row
+  constexpr int kRowsPass = kGemmThreads / kChunksRow;
+  constexpr int kCStride = kBNout + 8;             // bf16 per output-tile row in LDS
+  static_assert(128 * kCStride <= 4 * kTileElems, "output tile must fit the LDS stages");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -96,36 +136,70 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
   const int per_xcd_blocks = gridDim.x / kXcds;
   const int64_t lo = n_tiles * xcd / kXcds, hi = n_tiles * (xcd + 1) / kXcds;
   const int64_t nbrows = kDual ? 2 * (int64_t)N : (int64_t)N;
+  const int ld_row = tid / kChunksRow;
+  const int ld_chunk = (tid % kChunksRow) * 8;
+  const int nk = K / kBK;
 
-  // global->LDS copy assignment: thread covers rows (tid / 8) + 32 i, 16-byte chunk tid % 8
-  const int ld_row = tid >> 3;
-  const int ld_chunk = (tid & 7) << 3;
-
-  for (int64_t t = lo + blockIdx.x / kXcds; t < hi; t += per_xcd_blocks) {
-    const int mt = (int)(t / ntn);
-    const int nt = (int)(t - (int64_t)mt * ntn);
-    // expert owning M tile mt: last e with tile_off[e] <= mt
+  // Per-tile state: output placement and the global sources of this
+  // thread's 16-byte staging loads.
+  int row_base = 0, m_valid = 0, n0 = 0;
+  const bf16_t* a_src[kLoads];
+  const bf16_t* b_src[kLoads];
+  auto setup = [&](int64_t t) {
+    // expert owning tile t: expert e holds tiles [tile_off[e] * ntn, tile_off[e+1] * ntn)
     int e_lo = 0, e_hi = E - 1;
     while (e_lo < e_hi) {
       const int mid = (e_lo + e_hi + 1) >> 1;
-      if (tile_off[mid] <= mt) e_lo = mid; else e_hi = mid - 1;
+      if ((int64_t)tile_off[mid] * ntn <= t) e_lo = mid; else e_hi = mid - 1;
     }
     const int e = e_lo;
-    const int row_base = expert_offset[e] + (mt - tile_off[e]) * kBM;
-    const int m_valid = min(kBM, expert_offset[e + 1] - row_base);
-    const int n0 = nt * kBNout;
+    const int mtiles = tile_off[e + 1] - tile_off[e];
+    const int local = (int)(t - (int64_t)tile_off[e] * ntn);
+    // weight-streaming shapes walk an expert's M tiles innermost (its weight
+    // slice is fetched once and the other M tiles hit L2); shapes with many
+    // rows per expert walk N innermost (the A panel stays in L2)
+    const int mloc = mt_inner ? local % mtiles : local / ntn;
+    const int nt = mt_inner ? local / mtiles : local % ntn;
+    row_base = expert_offset[e] + mloc * kBM;
+    m_valid = min(kBM, expert_offset[e + 1] - row_base);
+    n0 = nt * kBNout;
     const bf16_t* Be = B + (size_t)e * nbrows * K;
-
-    const bf16_t* a_src[4];
-    const bf16_t* b_src[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = ld_row + 32 * i;
-      const int ra = row_base + min(r, m_valid - 1);      // tail rows re-read the last valid row
-      a_src[i] = A + (size_t)ra * K + ld_chunk;
+    for (int i = 0; i < kLoads; ++i) {
+      const int r = ld_row + kRowsPass * i;
+      a_src[i] = A + (size_t)(row_base + min(r, m_valid - 1)) * K + ld_chunk;   // tail rows re-read
       b_src[i] = Be + (size_t)b_row_of<kDual>(r, n0, N) * K + ld_chunk;
     }
+  };
+  u32x4_t ra[kLoads], rb[kLoads];
+  auto load_stage = [&](int st) {
+    const int koff = st * kBK;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      ra[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + koff);
+      rb[i] = *reinterpret_cast<const u32x4_t*>(b_src[i] + koff);
+    }
+  };
+  auto store_stage = [&](int buf) {
+    bf16_t* sA = smem + buf * kTileElems;
+    bf16_t* sB = smem + (2 + buf) * kTileElems;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      *reinterpret_cast<u32x4_t*>(&sA[(ld_row + kRowsPass * i) * kLdsStride + ld_chunk]) = ra[i];
+      *reinterpret_cast<u32x4_t*>(&sB[(ld_row + kRowsPass * i) * kLdsStride + ld_chunk]) = rb[i];
+    }
+  };
 
+  int64_t t = lo + blockIdx.x / kXcds;
+  if (t >= hi) return;
+  setup(t);
+  load_stage(0);
+  while (true) {
+    // K pipeline: LDS double buffer; the next stage's global loads are in
+    // flight while the matrix cores work on the current one.
+    store_stage(0);
+    if (nk > 1) load_stage(1);
+    __syncthreads();
     f32x16_t acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -133,34 +207,10 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    u32x4_t ra[4], rb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4_t*>(a_src[i]);
-      rb[i] = *reinterpret_cast<const u32x4_t*>(b_src[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4_t*>(&sA[0][(ld_row + 32 * i) * kLdsStride + ld_chunk]) = ra[i];
-      *reinterpret_cast<u32x4_t*>(&sB[0][(ld_row + 32 * i) * kLdsStride + ld_chunk]) = rb[i];
-    }
-    __syncthreads();
-
-    const int nk = K / kBK;
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        const int koff = (kt + 1) * kBK;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ra[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + koff);
-          rb[i] = *reinterpret_cast<const u32x4_t*>(b_src[i] + koff);
-        }
-      }
-      const bf16_t* pa = sA[cur];
-      const bf16_t* pb = sB[cur];
+      const bf16_t* pa = smem + cur * kTileElems;
+      const bf16_t* pb = smem + (2 + cur) * kTileElems;
 #pragma unroll
       for (int s = 0; s < kBK / 16; ++s) {
         const int kc = s * 16 + ((lane >> 5) << 3);
@@ -179,37 +229,225 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
           for (int j = 0; j < 2; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
-      if (more) {
-        const int nxt = cur ^ 1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *reinterpret_cast<u32x4_t*>(&sA[nxt][(ld_row + 32 * i) * kLdsStride + ld_chunk]) = ra[i];
-          *reinterpret_cast<u32x4_t*>(&sB[nxt][(ld_row + 32 * i) * kLdsStride + ld_chunk]) = rb[i];
-        }
+      if (kt + 1 < nk) {
+        store_stage(cur ^ 1);
+        if (kt + 2 < nk) load_stage(kt + 2);
       }
       __syncthreads();
     }
 
-    // Epilogue.  32x32 accumulator layout: lane holds column (lane % 32),
-    // element v -> row (v / 4) * 8 + (lane / 32) * 4 + v % 4.
+    // The next tile's first K stage starts loading before this tile's
+    // epilogue, so HBM stays busy across the tile boundary.
+    const int c_row_base = row_base, c_m_valid = m_valid, c_n0 = n0;
+    const int64_t tn = t + per_xcd_blocks;
+    if (tn < hi) {
+      setup(tn);
+      load_stage(0);
+    }
+
+    // Epilogue: activation, bf16 rounding, then the tile goes through LDS
+    // so that global stores are whole 16-byte chunks of output rows.
+    // 32x32 accumulator layout: lane holds column (lane % 32), element v ->
+    // row (v / 4) * 8 + (lane / 32) * 4 + v % 4.
+    bf16_t* sC = smem;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = wm * 64 + i * 32 + (v >> 2) * 8 + ((lane >> 5) << 2) + (v & 3);
-        if (r >= m_valid) continue;
-        bf16_t* crow = C + (size_t)(row_base + r) * N + n0;
         if (kDual) {
           const float g = acc[i][0][v], u = acc[i][1][v];
-          crow[wn * 32 + (lane & 31)] = f32_to_bf16(silu_f(g) * u);
+          sC[r * kCStride + wn * 32 + (lane & 31)] = f32_to_bf16(silu_f(g) * u);
         } else {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            const int col = wn * 64 + j * 32 + (lane & 31);
-            if (n0 + col >= N) continue;
             float x = acc[i][j][v];
             if (kEpi == kEpiGelu) x = gelu_f(x);
-            crow[col] = f32_to_bf16(x);
+            sC[r * kCStride + wn * 64 + j * 32 + (lane & 31)] = f32_to_bf16(x);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int kOutChunksRow = kBNout / 8;
+    for (int q = tid; q < 128 * kOutChunksRow; q += kGemmThreads) {
+      const int r = q / kOutChunksRow, c = (q % kOutChunksRow) * 8;
+      if (r < c_m_valid && c_n0 + c < N)
+        *reinterpret_cast<u32x4_t*>(C + (size_t)(c_row_base + r) * N + c_n0 + c) =
+            *reinterpret_cast<const u32x4_t*>(sC + r * kCStride + c);
+    }
+    __syncthreads();
+    if (tn >= hi) break;
+    t = tn;
+  }
+}
+
+// ---------------------------------------------------------------- weight-streaming kernel
+// Workgroup tile 128 rows x 256 weight rows (GELU / plain: 256 output
+// columns; SwiGLU: 128 outputs from 128 gate and 128 up rows).  Each wave
+// owns 64 weight rows and all 128 token rows: its B fragments (weights) go
+// straight from global memory into registers in the MFMA operand layout, so
+// weights never touch LDS; only the A panel (token rows, shared by the four
+// waves) is staged through a double-buffered LDS tile.  Per 16-wide K step
+// a wave issues 4 LDS reads and 8 v_mfma_f32_32x32x16_bf16 (4 x 2 tiles of
+// 32 x 32, 128 accumulators in AGPRs).  The next K stage's weights and A
+// rows are loading while the current one is multiplied.
+constexpr int kV2BN = 256;                 // weight rows per workgroup
+
+template <bool kDual, int kEpi>
+__global__ __launch_bounds__(kGemmThreads) void grouped_gemm_ws_kernel(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
+    const int32_t* __restrict__ expert_offset, int E, int N, int K, int mt_inner,
+    bf16_t* __restrict__ C) {
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2][128 * kLdsStride];
+  __shared__ int32_t tile_off[kMaxExperts + 1];
+  block_tile_plan(expert_offset, E, tile_off);
+  constexpr int kBNout = kDual ? kV2BN / 2 : kV2BN;   // output columns per workgroup
+  constexpr int kWaveCols = kBNout / 4;               // output columns per wave (64 or 32)
+  static_assert(kBK == 64, "the weight-streaming kernel stages K in steps of 64");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int ntn = (N + kBNout - 1) / kBNout;
+  const int64_t n_tiles = (int64_t)tile_off[E] * ntn;
+  const int xcd = blockIdx.x % kXcds;
+  const int per_xcd_blocks = gridDim.x / kXcds;
+  const int64_t lo = n_tiles * xcd / kXcds, hi = n_tiles * (xcd + 1) / kXcds;
+  const int64_t nbrows = kDual ? 2 * (int64_t)N : (int64_t)N;
+  const int ld_row = tid >> 3;               // A staging: rows tid/8 + 32 i, chunk tid % 8
+  const int ld_chunk = (tid & 7) << 3;
+
+  for (int64_t t = lo + blockIdx.x / kXcds; t < hi; t += per_xcd_blocks) {
+    int e_lo = 0, e_hi = E - 1;
+    while (e_lo < e_hi) {
+      const int mid = (e_lo + e_hi + 1) >> 1;
+      if ((int64_t)tile_off[mid] * ntn <= t) e_lo = mid; else e_hi = mid - 1;
+    }
+    const int e = e_lo;
+    const int mtiles = tile_off[e + 1] - tile_off[e];
+    const int local = (int)(t - (int64_t)tile_off[e] * ntn);
+    const int mloc = mt_inner ? local % mtiles : local / ntn;
+    const int nt = mt_inner ? local / mtiles : local % ntn;
+    const int row_base = expert_offset[e] + mloc * kBM;
+    const int m_valid = min(kBM, expert_offset[e + 1] - row_base);
+    const int n0 = nt * kBNout;
+    const int wc0 = n0 + wave * kWaveCols;               // this wave's first output column
+    const bool wave_live = wc0 < N;
+    const bf16_t* Be = B + (size_t)e * nbrows * K;
+
+    const bf16_t* a_src[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = ld_row + 32 * i;
+      a_src[i] = A + (size_t)(row_base + min(r, m_valid - 1)) * K + ld_chunk;
+    }
+    // B fragment rows of this lane: column group j of the wave's 64 rows
+    const int kl = (lane >> 5) << 3;                      // K offset of the lane's 8 values
+    const bf16_t* b_src[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      int wrow;
+      if (kDual) wrow = (j == 0 ? 0 : N) + min(wc0, N - 32) + (lane & 31);
+      else wrow = min(wc0 + j * 32, N - 32) + (lane & 31);
+      b_src[j] = Be + (size_t)wrow * K + kl;
+    }
+
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    const int nk = K / kBK;
+    u32x4_t ra[4];
+    bf16x8_t bq[2][4][2];                                  // [buffer][k step][column group]
+    auto load_a = [&](int st) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + st * kBK);
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4_t*>(&sA[buf][(ld_row + 32 * i) * kLdsStride + ld_chunk]) = ra[i];
+    };
+    auto load_b = [&](int st, int q) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          bq[q][s][j] = *reinterpret_cast<const bf16x8_t*>(b_src[j] + st * kBK + s * 16);
+    };
+    auto mma_stage = [&](int buf, int q) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8_t af[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          af[i] = *reinterpret_cast<const bf16x8_t*>(&sA[buf][(i * 32 + (lane & 31)) * kLdsStride + s * 16 + kl]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bq[q][s][j], acc[i][j], 0, 0, 0);
+      }
+    };
+
+    load_a(0);
+    load_b(0, 0);
+    store_a(0);
+    if (nk > 1) {
+      load_a(1);
+      load_b(1, 1);
+    }
+    __syncthreads();
+    // two stages per trip so the register buffers have compile-time indices
+    for (int kt = 0; kt < nk; kt += 2) {
+      mma_stage(0, 0);
+      if (kt + 1 < nk) {
+        store_a(1);
+        if (kt + 2 < nk) {
+          load_a(kt + 2);
+          load_b(kt + 2, 0);
+        }
+      }
+      __syncthreads();
+      if (kt + 1 >= nk) break;
+      mma_stage(1, 1);
+      if (kt + 2 < nk) {
+        store_a(0);
+        if (kt + 3 < nk) {
+          load_a(kt + 3);
+          load_b(kt + 3, 1);
+        }
+      }
+      __syncthreads();
+    }
+
+    // Epilogue: accumulator element v of tile (i, j) is row
+    // i*32 + (v/4)*8 + (lane/32)*4 + v%4, column (lane % 32) of group j.
+    if (wave_live) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = i * 32 + (v >> 2) * 8 + ((lane >> 5) << 2) + (v & 3);
+          if (r >= m_valid) continue;
+          bf16_t* crow = C + (size_t)(row_base + r) * N;
+          if (kDual) {
+            const float g = acc[i][0][v], u = acc[i][1][v];
+            crow[wc0 + (lane & 31)] = f32_to_bf16(silu_f(g) * u);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int col = wc0 + j * 32 + (lane & 31);
+              if (col >= N) continue;
+              float x = acc[i][j][v];
+              if (kEpi == kEpiGelu) x = gelu_f(x);
+              crow[col] = f32_to_bf16(x);
+            }
           }
         }
       }
@@ -271,46 +509,59 @@ __global__ __launch_bounds__(256) void ffn_down_f32_kernel(const float* __restri
 
 // ---------------------------------------------------------------- host side
 
+#if MOE_GEMM_V2
+#define MOE_GEMM_KERNEL grouped_gemm_ws_kernel
+#else
+#define MOE_GEMM_KERNEL grouped_gemm_bf16_kernel
+#endif
+
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t ffn_workspace_bytes(int64_t M_max, int E, int d, int f, int act, int dtype) {
   (void)d;
   (void)act;
   const size_t elem = dtype == 1 ? 2 : 4;
-  return align256((size_t)(E + 1) * sizeof(int32_t)) + align256((size_t)M_max * f * elem);
+  return align256((size_t)M_max * f * elem);
 }
 
-static int persistent_blocks() {
-  static int blocks = 0;
-  if (!blocks) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    blocks = ((2 * cus + kXcds - 1) / kXcds) * kXcds;   // two workgroups per CU, multiple of 8
-  }
-  return blocks;
+// Persistent grid: as many workgroups as fit on the device at once (so every
+// one of them is resident and walks its share of the tile list), rounded
+// down to a multiple of the XCD count.
+template <typename Kern>
+static int persistent_blocks(Kern kernel) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel),
+                                                   kGemmThreads, 0) != hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  return ((per_cu * cus) / kXcds) * kXcds;
 }
 
 hipError_t launch_expert_ffn(const void* X_perm, int dtype, const int32_t* expert_offset, int E,
                              int d, int f, int act, const void* W1, const void* W2, int64_t M_max,
                              void* Y_perm, void* ws, hipStream_t stream) {
   char* w = static_cast<char*>(ws);
-  int32_t* tile_off = reinterpret_cast<int32_t*>(w);
-  void* H = w + align256((size_t)(E + 1) * sizeof(int32_t));
+  void* H = w;
   if (dtype == 1) {
-    hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(1024), 0, stream, expert_offset, E, tile_off);
-    const int blocks = persistent_blocks();
+    static const int blocks = persistent_blocks(MOE_GEMM_KERNEL<false, kEpiNone>);
     const bf16_t* x = static_cast<const bf16_t*>(X_perm);
     bf16_t* h = static_cast<bf16_t*>(H);
+    // few rows per expert: the GEMMs stream weights, walk M tiles innermost
+#if MOE_GEMM_ORDER < 0
+    const int mt_inner = M_max <= (int64_t)E * 4 * kBM ? 1 : 0;
+#else
+    const int mt_inner = MOE_GEMM_ORDER;
+#endif
     if (act == 1)
-      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<true, kEpiSwiglu>), dim3(blocks), dim3(kGemmThreads),
-                         0, stream, x, static_cast<const bf16_t*>(W1), expert_offset, tile_off, E, f, d, h);
+      hipLaunchKernelGGL((MOE_GEMM_KERNEL<true, kEpiSwiglu>), dim3(blocks), dim3(kGemmThreads), 0, stream,
+                         x, static_cast<const bf16_t*>(W1), expert_offset, E, f, d, mt_inner, h);
     else
-      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, kEpiGelu>), dim3(blocks), dim3(kGemmThreads),
-                         0, stream, x, static_cast<const bf16_t*>(W1), expert_offset, tile_off, E, f, d, h);
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<false, kEpiNone>), dim3(blocks), dim3(kGemmThreads), 0,
-                       stream, h, static_cast<const bf16_t*>(W2), expert_offset, tile_off, E, d, f,
+      hipLaunchKernelGGL((MOE_GEMM_KERNEL<false, kEpiGelu>), dim3(blocks), dim3(kGemmThreads), 0, stream,
+                         x, static_cast<const bf16_t*>(W1), expert_offset, E, f, d, mt_inner, h);
+    hipLaunchKernelGGL((MOE_GEMM_KERNEL<false, kEpiNone>), dim3(blocks), dim3(kGemmThreads), 0, stream, h,
+                       static_cast<const bf16_t*>(W2), expert_offset, E, d, f, mt_inner,
                        static_cast<bf16_t*>(Y_perm));
   } else {
     const int64_t up = M_max * f, down = M_max * d;

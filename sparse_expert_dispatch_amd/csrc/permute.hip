@@ -124,8 +124,14 @@ template <> struct Elem<bf16_t> {
 // assignments); one rounding at the store.  The token's slot list and gates
 // are loaded once (lane q holds entry q) and read back with readlane; the
 // rows of kSlotBatch slots are loaded together before they are added.
-constexpr int kChunks = 4;      // 16-byte chunks per lane per column pass
-constexpr int kSlotBatch = 4;   // expert rows in flight per wave
+#ifndef MOE_COMBINE_CHUNKS
+#define MOE_COMBINE_CHUNKS 4
+#endif
+#ifndef MOE_COMBINE_BATCH
+#define MOE_COMBINE_BATCH 1
+#endif
+constexpr int kChunks = MOE_COMBINE_CHUNKS;     // 16-byte chunks per lane per column pass
+constexpr int kSlotBatch = MOE_COMBINE_BATCH;   // expert rows in flight per wave
 
 template <typename T>
 __global__ __launch_bounds__(256) void combine_vec_kernel(const T* __restrict__ Y,

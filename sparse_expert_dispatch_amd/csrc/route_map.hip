@@ -155,23 +155,38 @@ __global__ __launch_bounds__(256) void ec_slots_kernel(const int32_t* __restrict
   }
 }
 
-// One workgroup: each thread owns a contiguous run of tokens; their list
-// lengths are summed, scanned across the workgroup, and written back as
-// offsets.
+// One workgroup turns the mask into token offsets, kTokPer tokens per thread
+// per pass: each pass loads all its mask words at once, scans the counts
+// across the workgroup and carries the running total to the next pass.
+constexpr int kTokPer = 4;
+
 __global__ __launch_bounds__(kScanThreads) void ec_token_offsets_kernel(
     const uint32_t* __restrict__ mask, int n, int W, int32_t* __restrict__ token_offset) {
   __shared__ int scratch[kScanThreads / 64];
-  const int seg = (n + kScanThreads - 1) / kScanThreads;
-  const int t0 = min(n, (int)threadIdx.x * seg), t1 = min(n, t0 + seg);
-  int sum = 0;
-  for (int64_t i = (int64_t)t0 * W; i < (int64_t)t1 * W; ++i) sum += __popc(mask[i]);
-  int total = 0;
-  int run = block_exclusive_scan<kScanThreads>(sum, scratch, &total);
-  for (int t = t0; t < t1; ++t) {
-    token_offset[t] = run;
-    for (int w = 0; w < W; ++w) run += __popc(mask[(size_t)t * W + w]);
+  int carry = 0;
+  for (int base = 0; base < n; base += kScanThreads * kTokPer) {
+    const int t0 = base + threadIdx.x * kTokPer;
+    int cnt[kTokPer];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < kTokPer; ++i) {
+      const int t = t0 + i;
+      int c = 0;
+      if (t < n)
+        for (int w = 0; w < W; ++w) c += __popc(mask[(size_t)t * W + w]);
+      cnt[i] = c;
+      sum += c;
+    }
+    int total = 0;
+    int run = carry + block_exclusive_scan<kScanThreads>(sum, scratch, &total);
+#pragma unroll
+    for (int i = 0; i < kTokPer; ++i) {
+      if (t0 + i < n) token_offset[t0 + i] = run;
+      run += cnt[i];
+    }
+    carry += total;
   }
-  if (threadIdx.x == 0) token_offset[n] = total;
+  if (threadIdx.x == 0) token_offset[n] = carry;
 }
 
 __global__ __launch_bounds__(256) void ec_token_fill_kernel(const int32_t* __restrict__ I,

@@ -24,103 +24,113 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kRouterRows = 64;    // rows per workgroup (16 per wave)
-constexpr int kRouterBK = 64;      // K per LDS stage
-constexpr int kRouterCols = 256;   // expert columns per workgroup
-constexpr int kRouterLdsStride = kRouterBK + 8;   // bf16 elements per LDS row (padding skews banks)
-constexpr int kRouterMaxItems = kRouterBK * kRouterCols / 8 / 256;   // 16-byte W_g loads per thread
+constexpr int kRouterBK = 64;      // K per pipeline stage
+constexpr int kRouterCols = 256;   // expert columns per workgroup (4 waves x 64)
+constexpr int kRouterSplitsMax = 8;
 
-// Software pipeline: while the matrix cores work on K stage s (A fragments
-// in registers, the W_g stage in LDS buffer s % 2), the next stage's A
-// fragments and W_g rows are already loading into registers; they are
-// written (transposed) to the other LDS buffer after the MFMAs, so one
-// barrier per stage suffices.
+// W_g^T [E][d] from W_g [d][E]: each workgroup moves a 64 (K) x 64
+// (expert) tile through LDS with 16-byte global loads and stores (E is a
+// multiple of 16; a partial tile covers the last experts).
+__global__ __launch_bounds__(256) void router_wg_transpose_kernel(const bf16_t* __restrict__ Wg, int d,
+                                                                  int E, bf16_t* __restrict__ WgT) {
+  __shared__ bf16_t tile[64][64 + 2];
+  const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const int ecols = min(64, E - e0);                 // multiple of 16
+  // load: 64 rows x ecols columns, 8 columns per 16-byte load
+  const int cpr = ecols >> 3;
+  uint4 v[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int item = threadIdx.x + 256 * i;
+    if (item < 64 * cpr) {
+      const int kk = item / cpr, cc = (item % cpr) << 3;
+      v[i] = *reinterpret_cast<const uint4*>(Wg + (size_t)(k0 + kk) * E + e0 + cc);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int item = threadIdx.x + 256 * i;
+    if (item < 64 * cpr) {
+      const int kk = item / cpr, cc = (item % cpr) << 3;
+      const bf16_t* pv = reinterpret_cast<const bf16_t*>(&v[i]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) tile[kk][cc + q] = pv[q];
+    }
+  }
+  __syncthreads();
+  // store: ecols rows of W_g^T, 64 K values each (8 x 16 bytes)
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int item = threadIdx.x + 256 * i;
+    if (item < ecols * 8) {
+      const int ee = item >> 3, kc = (item & 7) << 3;
+      uint4 w;
+      bf16_t* pw = reinterpret_cast<bf16_t*>(&w);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) pw[q] = tile[kc + q][ee];
+      *reinterpret_cast<uint4*>(WgT + (size_t)(e0 + ee) * d + k0 + kc) = w;
+    }
+  }
+}
+
+// Z = X W_g on the matrix cores with no LDS: every wave owns 16 token rows
+// and up to 64 expert columns (4 tiles of v_mfma_f32_16x16x32_bf16) over one
+// K slice; A fragments come from X and B fragments from W_g^T, both as
+// 16-byte loads of 8 consecutive K values, and the next K stage is loading
+// while the current one is multiplied.  A workgroup is 4 waves: 64, 32 or
+// 16 rows by 64, 128 or 256 columns depending on E.
 __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
-    const bf16_t* __restrict__ X, const bf16_t* __restrict__ Wg, int n, int d, int E, int k_per_split,
-    float* __restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][kRouterCols * kRouterLdsStride];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int row0 = blockIdx.x * kRouterRows + wave * 16;
+    const bf16_t* __restrict__ X, const bf16_t* __restrict__ WgT, int n, int d, int E, int k_per_split,
+    int ncg, float* __restrict__ partial) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rg = wave / ncg, cg = wave % ncg;
+  const int rows_per_wg = 16 * (4 / ncg);
+  const int row0 = blockIdx.x * rows_per_wg + 16 * rg;
+  const int c0 = blockIdx.z * kRouterCols + 64 * cg;
   const int split = blockIdx.y;
-  const int c0 = blockIdx.z * kRouterCols;
-  const int ncols = min(kRouterCols, E - c0);     // multiple of 16
-  const int nt = ncols >> 4;                       // 16-column tiles
+  if (c0 >= E || row0 >= n) return;
+  const int nt = min(4, (E - c0) >> 4);                 // 16-column tiles of this wave
   const int kbeg = split * k_per_split;
   const int nk = k_per_split / kRouterBK;
-  const int per_row = ncols >> 3;                  // 8-column chunks per K row
-  const int items = kRouterBK * per_row;
-
-  f32x4_t acc[16];
+  const int kl = (lane >> 4) << 3;
+  const bf16_t* ap = X + (size_t)min(row0 + (lane & 15), n - 1) * d + kbeg + kl;
+  const bf16_t* bp[4];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 4; ++j) bp[j] = WgT + (size_t)(c0 + 16 * min(j, nt - 1) + (lane & 15)) * d + kbeg + kl;
 
-  // A fragment source: row (lane % 16), 8 K values at (lane / 16) * 8.
-  int arow = row0 + (lane & 15);
-  if (arow > n - 1) arow = n - 1;                  // tail rows are computed but never stored
-  const bf16_t* aptr = X + (size_t)arow * d + kbeg + ((lane >> 4) << 3);
-
-  u32x4_t wreg[kRouterMaxItems];
-  auto load_w = [&](int k0) {
+  f32x4_t acc[4];
 #pragma unroll
-    for (int i = 0; i < kRouterMaxItems; ++i) {
-      const int item = tid + 256 * i;
-      if (item < items) {
-        const int kk = item / per_row;
-        const int cc = (item - kk * per_row) << 3;
-        wreg[i] = *reinterpret_cast<const u32x4_t*>(Wg + (size_t)(k0 + kk) * E + c0 + cc);
-      }
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  bf16x8_t a[2][2], b[2][2][4];                          // [buffer][32-wide K step][tile]
+  auto load = [&](int st, int q) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      a[q][s] = *reinterpret_cast<const bf16x8_t*>(ap + st * kRouterBK + 32 * s);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j < nt) b[q][s][j] = *reinterpret_cast<const bf16x8_t*>(bp[j] + st * kRouterBK + 32 * s);
     }
   };
-  auto store_w = [&](int buf) {
+  auto mma = [&](int q) {
 #pragma unroll
-    for (int i = 0; i < kRouterMaxItems; ++i) {
-      const int item = tid + 256 * i;
-      if (item < items) {
-        const int kk = item / per_row;
-        const int cc = (item - kk * per_row) << 3;
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          sB[buf][(cc + 2 * h) * kRouterLdsStride + kk] = (bf16_t)(wreg[i][h] & 0xFFFFu);
-          sB[buf][(cc + 2 * h + 1) * kRouterLdsStride + kk] = (bf16_t)(wreg[i][h] >> 16);
-        }
-      }
-    }
+      for (int j = 0; j < 4; ++j)
+        if (j < nt) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q][s], b[q][s][j], acc[j], 0, 0, 0);
   };
-
-  load_w(kbeg);
-  bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(aptr);
-  bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(aptr + 32);
-  store_w(0);
-  for (int s = 0; s < nk; ++s) {
-    const int cur = s & 1;
-    const bool more = s + 1 < nk;
-    bf16x8_t na0 = a0, na1 = a1;
-    if (more) {
-      load_w(kbeg + (s + 1) * kRouterBK);
-      na0 = *reinterpret_cast<const bf16x8_t*>(aptr + (s + 1) * kRouterBK);
-      na1 = *reinterpret_cast<const bf16x8_t*>(aptr + (s + 1) * kRouterBK + 32);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (j < nt) {
-        const bf16_t* bp = sB[cur] + (j * 16 + (lane & 15)) * kRouterLdsStride + ((lane >> 4) << 3);
-        bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(bp);
-        bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(bp + 32);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[j], 0, 0, 0);
-      }
-    }
-    if (more) store_w(cur ^ 1);
-    a0 = na0;
-    a1 = na1;
+  load(0, 0);
+  for (int st = 0; st < nk; st += 2) {
+    if (st + 1 < nk) load(st + 1, 1);
+    mma(0);
+    if (st + 1 >= nk) break;
+    if (st + 2 < nk) load(st + 2, 0);
+    mma(1);
   }
   // C fragment: lane holds column (lane % 16), rows (lane / 16) * 4 + r.
   float* out = partial + (size_t)split * n * E;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < 4; ++j) {
     if (j < nt) {
       const int col = c0 + j * 16 + (lane & 15);
 #pragma unroll
@@ -233,18 +243,29 @@ hipError_t launch_router_finalize(const float* partial, int nsplit, int n, int E
                                   int score, float* logits, float* scores, float* scores_t,
                                   hipStream_t stream);
 
-static int router_splits(int n, int d) {
-  const int row_blocks = (n + kRouterRows - 1) / kRouterRows;
+static int router_ncg(int E) { return E >= 256 ? 4 : (E > 64 ? 2 : 1); }
+
+static int router_row_blocks(int n, int E) {
+  const int rows = 16 * (4 / router_ncg(E));
+  return (n + rows - 1) / rows;
+}
+
+// Split K until there are at least 512 workgroups (each slice a
+// multiple of the 64-wide stage).
+static int router_splits(int n, int d, int E) {
+  const int blocks = router_row_blocks(n, E) * ((E + kRouterCols - 1) / kRouterCols);
   const int kb = d / kRouterBK;
   int s = 1;
-  while (s < 4 && row_blocks * s < 256 && kb % (2 * s) == 0) s *= 2;
+  while (s < kRouterSplitsMax && blocks * s < 512 && kb % (2 * s) == 0) s *= 2;
   return s;
 }
 
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 size_t router_workspace_bytes(int n, int d, int E, int dtype) {
   if (!router_uses_mfma(dtype, d, E)) return 0;
-  const int s = router_splits(n, d);
-  return s > 1 ? (size_t)s * n * E * sizeof(float) : 0;
+  const int s = router_splits(n, d, E);
+  return align256((size_t)E * d * sizeof(bf16_t)) + (s > 1 ? (size_t)s * n * E * sizeof(float) : 0);
 }
 
 hipError_t launch_router(const void* X, const void* Wg, int dtype, const float* offset, int n, int d,
@@ -255,12 +276,15 @@ hipError_t launch_router(const void* X, const void* Wg, int dtype, const float* 
   const int64_t total = (int64_t)n * E;
   const dim3 sgrid((unsigned)((total + 255) / 256));
   if (router_uses_mfma(dtype, d, E)) {
-    nsplit = router_splits(n, d);
-    float* dst = nsplit > 1 ? static_cast<float*>(ws) : logits;
-    dim3 grid((n + kRouterRows - 1) / kRouterRows, nsplit, (E + kRouterCols - 1) / kRouterCols);
+    nsplit = router_splits(n, d, E);
+    char* w = static_cast<char*>(ws);
+    bf16_t* WgT = reinterpret_cast<bf16_t*>(w);
+    float* dst = nsplit > 1 ? reinterpret_cast<float*>(w + align256((size_t)E * d * sizeof(bf16_t))) : logits;
+    hipLaunchKernelGGL(router_wg_transpose_kernel, dim3(d / 64, (E + 63) / 64), dim3(256), 0, stream,
+                       static_cast<const bf16_t*>(Wg), d, E, WgT);
+    dim3 grid(router_row_blocks(n, E), nsplit, (E + kRouterCols - 1) / kRouterCols);
     hipLaunchKernelGGL(router_gemm_bf16_kernel, grid, dim3(256), 0, stream,
-                       static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(Wg), n, d, E,
-                       d / nsplit, dst);
+                       static_cast<const bf16_t*>(X), WgT, n, d, E, d / nsplit, router_ncg(E), dst);
     partial = dst;
   } else if (dtype == 1) {
     hipLaunchKernelGGL(router_gemm_scalar_kernel<bf16_t>, sgrid, dim3(256), 0, stream,

@@ -102,59 +102,60 @@ done:
 
 constexpr int kFinThreads = 1024;
 
-// Column sums of a [nb][cols] partial table, in a fixed order: thread group
-// g (of G = kFinThreads / cols rounded up to a power of two) sums rows g,
-// g + G, ...; the G group sums are then added in group order.  Result in
-// out_lds[0 .. cols).
-template <typename T>
-MOE_DEV void fixed_order_column_sums(const T* __restrict__ part, int nb, int cols, T* red,
-                                     T* out_lds) {
-#pragma clang fp contract(off)
-  int cp = 32;
-  while (cp < cols) cp <<= 1;
-  const int groups = kFinThreads / cp;
-  const int tid = threadIdx.x;
-  const int g = tid / cp, c = tid % cp;
-  T s = 0;
-  if (c < cols && g < groups) {
-#pragma unroll 8
-    for (int b = g; b < nb; b += groups) s = s + part[(size_t)b * cols + c];
-  }
-  red[tid] = s;
-  __syncthreads();
-  if (tid < cols) {
-    T v = 0;
-    for (int q = 0; q < groups; ++q) v = v + red[q * cp + tid];
-    out_lds[tid] = v;
-  }
-  __syncthreads();
+MOE_DEV int pow2_at_least(int x, int lo) {
+  int p = lo;
+  while (p < x) p <<= 1;
+  return p;
 }
 
+// One workgroup.  Every global value it needs is loaded in one phase (no
+// barrier in between, so the loads are all in flight together): thread group
+// g of the partial tables sums rows g, g + G, ... of its column; the group
+// sums are then added in group order, which fixes the summation order.
 __global__ __launch_bounds__(kFinThreads) void stats_final_kernel(
     const float* __restrict__ part_P, const float* __restrict__ part_Z,
     const int32_t* __restrict__ part_H, int nblocks, int n, int E, int k, int dir, float lb_coef,
     float z_coef, const int32_t* __restrict__ expert_count, const int32_t* __restrict__ expert_offset,
     float* __restrict__ stats, int32_t* __restrict__ hist) {
 #pragma clang fp contract(off)
-  __shared__ float red[kFinThreads];
-  __shared__ int ired[kFinThreads];
-  __shared__ float sPe[kMaxExperts];
-  __shared__ float sZ[1];
+  __shared__ float redP[kFinThreads];
+  __shared__ float redZ[kFinThreads];
+  __shared__ int redH[kFinThreads];
+  __shared__ float fp[kMaxExperts];
   __shared__ int sH[kMaxExperts + 1];
   __shared__ int wred[kFinThreads / 64][2];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
 
-  fixed_order_column_sums<float>(part_P, nblocks, E, red, sPe);
-  fixed_order_column_sums<float>(part_Z, nblocks, 1, red, sZ);
-  fixed_order_column_sums<int>(part_H, nblocks, E + 1, ired, sH);
-
-  // chosen total and largest kept load
-  int chosen = 0, maxload = 0;
-  for (int e = tid; e < E; e += kFinThreads) {
-    chosen += expert_count[e];
-    maxload = max(maxload, expert_offset[e + 1] - expert_offset[e]);
+  // ---- load phase
+  const int cpP = pow2_at_least(E, 32), gP = kFinThreads / cpP;
+  const int cpH = pow2_at_least(E + 1, 32), gH = kFinThreads / cpH;
+  float sp = 0.f, sz = 0.f;
+  int sh = 0;
+  {
+    const int g = tid / cpP, c = tid % cpP;
+    if (c < E) {
+#pragma unroll 16
+      for (int b = g; b < nblocks; b += gP) sp = sp + part_P[(size_t)b * E + c];
+    }
   }
+  {
+    const int g = tid / cpH, c = tid % cpH;
+    if (c <= E) {
+#pragma unroll 16
+      for (int b = g; b < nblocks; b += gH) sh += part_H[(size_t)b * (E + 1) + c];
+    }
+  }
+#pragma unroll 4
+  for (int b = tid; b < nblocks; b += kFinThreads) sz = sz + part_Z[b];
+  const int cnt = tid < E ? expert_count[tid] : 0;
+  const int load = tid < E ? expert_offset[tid + 1] - expert_offset[tid] : 0;
+  const int n_kept = expert_offset[E];
+  redP[tid] = sp;
+  redH[tid] = sh;
+  redZ[tid] = sz;
+  // ---- integer reductions: chosen total, largest kept load
+  int chosen = cnt, maxload = load;
   for (int o = 32; o >= 1; o >>= 1) {
     chosen += __shfl_xor(chosen, o, 64);
     maxload = max(maxload, __shfl_xor(maxload, o, 64));
@@ -169,16 +170,29 @@ __global__ __launch_bounds__(kFinThreads) void stats_final_kernel(
     ch += wred[w][0];
     ml = max(ml, wred[w][1]);
   }
-  if (hist)
-    for (int i = tid; i <= E; i += kFinThreads) hist[i] = sH[i];
+  if (tid <= E) {
+    int v = 0;
+    for (int q = 0; q < gH; ++q) v += redH[q * cpH + tid];
+    sH[tid] = v;
+    if (hist) hist[tid] = v;
+  }
+  if (tid < E) {
+    float v = 0.f;
+    for (int q = 0; q < gP; ++q) v = v + redP[q * cpP + tid];
+    fp[tid] = ((float)cnt / (float)ch) * (v / (float)n);
+  }
+  // z partials: a halving tree over the 1024 thread sums
+  for (int s = kFinThreads / 2; s >= 1; s >>= 1) {
+    __syncthreads();
+    if (tid < s) redZ[tid] = redZ[tid] + redZ[tid + s];
+  }
   // sum_e f_e P_e by a halving tree over experts
   const int P = next_pow2(E);
-  if (tid < P) red[tid] = tid < E ? ((float)expert_count[tid] / (float)ch) * (sPe[tid] / (float)n) : 0.f;
-  __syncthreads();
   for (int s = P >> 1; s >= 1; s >>= 1) {
-    if (tid < s) red[tid] = red[tid] + red[tid + s];
     __syncthreads();
+    if (tid < s) fp[tid] = fp[tid] + (tid + s < E ? fp[tid + s] : 0.f);
   }
+  __syncthreads();
   if (tid == 0) {
     int mt = 0;
     for (int i = E; i >= 0; --i)
@@ -186,11 +200,10 @@ __global__ __launch_bounds__(kFinThreads) void stats_final_kernel(
         mt = i;
         break;
       }
-    const int n_kept = expert_offset[E];
     const int total = dir == 0 ? n * k : E * k;
     const float mean_load = (float)n_kept / (float)E;
-    stats[0] = lb_coef * (float)E * red[0];
-    stats[1] = z_coef * (sZ[0] / (float)n);
+    stats[0] = lb_coef * (float)E * fp[0];
+    stats[1] = z_coef * (redZ[0] / (float)n);
     stats[2] = mean_load > 0.f ? ((float)ml - mean_load) / mean_load : 0.f;
     stats[3] = n_kept > 0 ? (float)ml / (float)n_kept : 0.f;
     stats[4] = (float)n_kept;

@@ -28,6 +28,8 @@
 // a contiguous eighth of the tile list, with the N tiles of one M tile
 // adjacent, so the workgroups that share an A panel (and a weight slice
 // across neighbouring M tiles) share that XCD's L2.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -46,13 +48,6 @@ constexpr int kLdsStride = kBK + 8;          // bf16 per LDS row
 constexpr int kTileElems = 128 * kLdsStride; // one 128-row operand tile
 constexpr int kGemmThreads = 256;
 constexpr int kXcds = 8;
-#ifndef MOE_GEMM_PREFETCH
-#define MOE_GEMM_PREFETCH 1
-#endif
-constexpr int kPrefetch = MOE_GEMM_PREFETCH;   // K stages in flight in registers
-#ifndef MOE_GEMM_V2
-#define MOE_GEMM_V2 0
-#endif
 #ifndef MOE_GEMM_ORDER
 #define MOE_GEMM_ORDER -1                        // tile order: -1 by shape, 0 N inner, 1 M inner
 #endif
@@ -246,7 +241,10 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
     }
 
     // Epilogue: activation, bf16 rounding, then the tile goes through LDS
-    // so that global stores are whole 16-byte chunks of output rows.
+    // so that global stores are whole 16-byte chunks of output rows.  The
+    // stores are non-temporal: the output is read by the next kernel, not by
+    // this one, and streaming it past the cache keeps the weight stream's
+    // reads and these writes from contending for L2.
     // 32x32 accumulator layout: lane holds column (lane % 32), element v ->
     // row (v / 4) * 8 + (lane / 32) * 4 + v % 4.
     bf16_t* sC = smem;
@@ -273,185 +271,12 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
     for (int q = tid; q < 128 * kOutChunksRow; q += kGemmThreads) {
       const int r = q / kOutChunksRow, c = (q % kOutChunksRow) * 8;
       if (r < c_m_valid && c_n0 + c < N)
-        *reinterpret_cast<u32x4_t*>(C + (size_t)(c_row_base + r) * N + c_n0 + c) =
-            *reinterpret_cast<const u32x4_t*>(sC + r * kCStride + c);
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(sC + r * kCStride + c),
+                                    reinterpret_cast<u32x4_t*>(C + (size_t)(c_row_base + r) * N + c_n0 + c));
     }
     __syncthreads();
     if (tn >= hi) break;
     t = tn;
-  }
-}
-
-// ---------------------------------------------------------------- weight-streaming kernel
-// Workgroup tile 128 rows x 256 weight rows (GELU / plain: 256 output
-// columns; SwiGLU: 128 outputs from 128 gate and 128 up rows).  Each wave
-// owns 64 weight rows and all 128 token rows: its B fragments (weights) go
-// straight from global memory into registers in the MFMA operand layout, so
-// weights never touch LDS; only the A panel (token rows, shared by the four
-// waves) is staged through a double-buffered LDS tile.  Per 16-wide K step
-// a wave issues 4 LDS reads and 8 v_mfma_f32_32x32x16_bf16 (4 x 2 tiles of
-// 32 x 32, 128 accumulators in AGPRs).  The next K stage's weights and A
-// rows are loading while the current one is multiplied.
-constexpr int kV2BN = 256;                 // weight rows per workgroup
-
-template <bool kDual, int kEpi>
-__global__ __launch_bounds__(kGemmThreads) void grouped_gemm_ws_kernel(
-    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
-    const int32_t* __restrict__ expert_offset, int E, int N, int K, int mt_inner,
-    bf16_t* __restrict__ C) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][128 * kLdsStride];
-  __shared__ int32_t tile_off[kMaxExperts + 1];
-  block_tile_plan(expert_offset, E, tile_off);
-  constexpr int kBNout = kDual ? kV2BN / 2 : kV2BN;   // output columns per workgroup
-  constexpr int kWaveCols = kBNout / 4;               // output columns per wave (64 or 32)
-  static_assert(kBK == 64, "the weight-streaming kernel stages K in steps of 64");
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int ntn = (N + kBNout - 1) / kBNout;
-  const int64_t n_tiles = (int64_t)tile_off[E] * ntn;
-  const int xcd = blockIdx.x % kXcds;
-  const int per_xcd_blocks = gridDim.x / kXcds;
-  const int64_t lo = n_tiles * xcd / kXcds, hi = n_tiles * (xcd + 1) / kXcds;
-  const int64_t nbrows = kDual ? 2 * (int64_t)N : (int64_t)N;
-  const int ld_row = tid >> 3;               // A staging: rows tid/8 + 32 i, chunk tid % 8
-  const int ld_chunk = (tid & 7) << 3;
-
-  for (int64_t t = lo + blockIdx.x / kXcds; t < hi; t += per_xcd_blocks) {
-    int e_lo = 0, e_hi = E - 1;
-    while (e_lo < e_hi) {
-      const int mid = (e_lo + e_hi + 1) >> 1;
-      if ((int64_t)tile_off[mid] * ntn <= t) e_lo = mid; else e_hi = mid - 1;
-    }
-    const int e = e_lo;
-    const int mtiles = tile_off[e + 1] - tile_off[e];
-    const int local = (int)(t - (int64_t)tile_off[e] * ntn);
-    const int mloc = mt_inner ? local % mtiles : local / ntn;
-    const int nt = mt_inner ? local / mtiles : local % ntn;
-    const int row_base = expert_offset[e] + mloc * kBM;
-    const int m_valid = min(kBM, expert_offset[e + 1] - row_base);
-    const int n0 = nt * kBNout;
-    const int wc0 = n0 + wave * kWaveCols;               // this wave's first output column
-    const bool wave_live = wc0 < N;
-    const bf16_t* Be = B + (size_t)e * nbrows * K;
-
-    const bf16_t* a_src[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = ld_row + 32 * i;
-      a_src[i] = A + (size_t)(row_base + min(r, m_valid - 1)) * K + ld_chunk;
-    }
-    // B fragment rows of this lane: column group j of the wave's 64 rows
-    const int kl = (lane >> 5) << 3;                      // K offset of the lane's 8 values
-    const bf16_t* b_src[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      int wrow;
-      if (kDual) wrow = (j == 0 ? 0 : N) + min(wc0, N - 32) + (lane & 31);
-      else wrow = min(wc0 + j * 32, N - 32) + (lane & 31);
-      b_src[j] = Be + (size_t)wrow * K + kl;
-    }
-
-    f32x16_t acc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    const int nk = K / kBK;
-    u32x4_t ra[4];
-    bf16x8_t bq[2][4][2];                                  // [buffer][k step][column group]
-    auto load_a = [&](int st) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + st * kBK);
-    };
-    auto store_a = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4_t*>(&sA[buf][(ld_row + 32 * i) * kLdsStride + ld_chunk]) = ra[i];
-    };
-    auto load_b = [&](int st, int q) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          bq[q][s][j] = *reinterpret_cast<const bf16x8_t*>(b_src[j] + st * kBK + s * 16);
-    };
-    auto mma_stage = [&](int buf, int q) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bf16x8_t af[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[i] = *reinterpret_cast<const bf16x8_t*>(&sA[buf][(i * 32 + (lane & 31)) * kLdsStride + s * 16 + kl]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bq[q][s][j], acc[i][j], 0, 0, 0);
-      }
-    };
-
-    load_a(0);
-    load_b(0, 0);
-    store_a(0);
-    if (nk > 1) {
-      load_a(1);
-      load_b(1, 1);
-    }
-    __syncthreads();
-    // two stages per trip so the register buffers have compile-time indices
-    for (int kt = 0; kt < nk; kt += 2) {
-      mma_stage(0, 0);
-      if (kt + 1 < nk) {
-        store_a(1);
-        if (kt + 2 < nk) {
-          load_a(kt + 2);
-          load_b(kt + 2, 0);
-        }
-      }
-      __syncthreads();
-      if (kt + 1 >= nk) break;
-      mma_stage(1, 1);
-      if (kt + 2 < nk) {
-        store_a(0);
-        if (kt + 3 < nk) {
-          load_a(kt + 3);
-          load_b(kt + 3, 1);
-        }
-      }
-      __syncthreads();
-    }
-
-    // Epilogue: accumulator element v of tile (i, j) is row
-    // i*32 + (v/4)*8 + (lane/32)*4 + v%4, column (lane % 32) of group j.
-    if (wave_live) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = i * 32 + (v >> 2) * 8 + ((lane >> 5) << 2) + (v & 3);
-          if (r >= m_valid) continue;
-          bf16_t* crow = C + (size_t)(row_base + r) * N;
-          if (kDual) {
-            const float g = acc[i][0][v], u = acc[i][1][v];
-            crow[wc0 + (lane & 31)] = f32_to_bf16(silu_f(g) * u);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const int col = wc0 + j * 32 + (lane & 31);
-              if (col >= N) continue;
-              float x = acc[i][j][v];
-              if (kEpi == kEpiGelu) x = gelu_f(x);
-              crow[col] = f32_to_bf16(x);
-            }
-          }
-        }
-      }
-    }
   }
 }
 
@@ -509,11 +334,6 @@ __global__ __launch_bounds__(256) void ffn_down_f32_kernel(const float* __restri
 
 // ---------------------------------------------------------------- host side
 
-#if MOE_GEMM_V2
-#define MOE_GEMM_KERNEL grouped_gemm_ws_kernel
-#else
-#define MOE_GEMM_KERNEL grouped_gemm_bf16_kernel
-#endif
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -545,7 +365,6 @@ hipError_t launch_expert_ffn(const void* X_perm, int dtype, const int32_t* exper
   char* w = static_cast<char*>(ws);
   void* H = w;
   if (dtype == 1) {
-    static const int blocks = persistent_blocks(MOE_GEMM_KERNEL<false, kEpiNone>);
     const bf16_t* x = static_cast<const bf16_t*>(X_perm);
     bf16_t* h = static_cast<bf16_t*>(H);
     // few rows per expert: the GEMMs stream weights, walk M tiles innermost
@@ -554,15 +373,22 @@ hipError_t launch_expert_ffn(const void* X_perm, int dtype, const int32_t* exper
 #else
     const int mt_inner = MOE_GEMM_ORDER;
 #endif
+    auto gemm = [&](auto dual, auto epi, const bf16_t* a, const bf16_t* b, int N, int K, bf16_t* c) {
+      constexpr bool kD = decltype(dual)::value;
+      constexpr int kE = decltype(epi)::value;
+      static const int blocks = persistent_blocks(grouped_gemm_bf16_kernel<kD, kE>);
+      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kD, kE>), dim3(blocks), dim3(kGemmThreads), 0, stream, a, b,
+                         expert_offset, E, N, K, mt_inner, c);
+    };
+    using std::integral_constant;
     if (act == 1)
-      hipLaunchKernelGGL((MOE_GEMM_KERNEL<true, kEpiSwiglu>), dim3(blocks), dim3(kGemmThreads), 0, stream,
-                         x, static_cast<const bf16_t*>(W1), expert_offset, E, f, d, mt_inner, h);
+      gemm(integral_constant<bool, true>{}, integral_constant<int, kEpiSwiglu>{}, x,
+           static_cast<const bf16_t*>(W1), f, d, h);
     else
-      hipLaunchKernelGGL((MOE_GEMM_KERNEL<false, kEpiGelu>), dim3(blocks), dim3(kGemmThreads), 0, stream,
-                         x, static_cast<const bf16_t*>(W1), expert_offset, E, f, d, mt_inner, h);
-    hipLaunchKernelGGL((MOE_GEMM_KERNEL<false, kEpiNone>), dim3(blocks), dim3(kGemmThreads), 0, stream, h,
-                       static_cast<const bf16_t*>(W2), expert_offset, E, d, f, mt_inner,
-                       static_cast<bf16_t*>(Y_perm));
+      gemm(integral_constant<bool, false>{}, integral_constant<int, kEpiGelu>{}, x,
+           static_cast<const bf16_t*>(W1), f, d, h);
+    gemm(integral_constant<bool, false>{}, integral_constant<int, kEpiNone>{}, h,
+         static_cast<const bf16_t*>(W2), d, f, static_cast<bf16_t*>(Y_perm));
   } else {
     const int64_t up = M_max * f, down = M_max * d;
     hipLaunchKernelGGL(ffn_up_f32_kernel, dim3((unsigned)((up + 255) / 256)), dim3(256), 0, stream,

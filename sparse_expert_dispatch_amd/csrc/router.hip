@@ -5,15 +5,15 @@
 // (S = softmax(X W_g), X: [n, d], W_g: [d, E]); page 5 "MoE routing
 // strategies explained", strategy 4 (sigmoid scores).
 //
-// bf16 path: one workgroup = 4 waves = 64 token rows x up to 256 experts,
-// over one K-slice of d (split-K when n alone gives too few workgroups to
-// fill 256 CUs).  A wave owns 16 rows; its A fragments come straight from
-// HBM (X is read exactly once), the W_g slice is staged through LDS
-// transposed to [E][K] so every lane reads its 8 consecutive K values of a
-// column with one 16-byte LDS read, and the products run on
-// v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  Per-slice partial logits
-// go to a workspace; the finalize kernel adds the slices in slice order (so
-// the result is deterministic), adds the offset and evaluates the scores.
+// bf16 path, three kernels: W_g [d, E] is first transposed to W_g^T [E, d]
+// in the workspace (K-contiguous rows, so a matrix-core B fragment is one
+// 16-byte load); the GEMM kernel then runs v_mfma_f32_16x16x32_bf16 with no
+// LDS, every wave owning 16 token rows and up to 64 experts, X read once from
+// HBM; K is split across workgroups (up to 8 slices) until the grid holds at
+// least 512 workgroups.  The per-slice partial logits go to the workspace;
+// the finalize kernel adds the slices in slice order (so the result is
+// deterministic), adds the offset and evaluates the scores.
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 

@@ -127,24 +127,70 @@ def sigmoid(z: np.ndarray) -> np.ndarray:
         return (f32(1.0) / (f32(1.0) + spec_exp(-z))).astype(np.float32)
 
 
+# Specified float32 log1p on [0, 1]: log1p(u) = 2 atanh(s), s = u / (2 + u),
+# and 2 atanh(s) = 2 s (1 + s^2/3 + s^4/5 + ... + s^14/15).  For u in [0, 1],
+# s <= 1/3, so the first omitted term is below (1/9)^8 / 17 < 2^-30 relative.
+# The series runs in Horner form over s^2 with float32 coefficients 1/(2j+1).
+LOG1P_COEF = [f32(1.0 / (2 * j + 1)) for j in range(8)]        # 1/1, 1/3, ..., 1/15
+
+
+def spec_log1p(u) -> np.ndarray:
+    """Specified float32 log(1 + u) for 0 <= u <= 1; one IEEE float32
+    operation per step."""
+    u = np.asarray(u, dtype=np.float32)
+    s = (u / (f32(2.0) + u)).astype(np.float32)
+    s2 = (s * s).astype(np.float32)
+    p = LOG1P_COEF[7]
+    for j in range(6, -1, -1):
+        p = (p * s2 + LOG1P_COEF[j]).astype(np.float32)
+    return ((s + s) * p).astype(np.float32)
+
+
+def spec_softplus(z) -> np.ndarray:
+    """Specified float32 softplus log(1 + e^z) = max(z, 0) + log1p(e^-|z|)."""
+    z = np.asarray(z, dtype=np.float32)
+    return (np.maximum(z, f32(0.0)) + spec_log1p(spec_exp(-np.abs(z)))).astype(np.float32)
+
+
+def sqrtsoftplus(z) -> np.ndarray:
+    """Specified sqrtsoftplus score sqrt(softplus(z)) with the correctly rounded
+    float32 square root (page 5 strategy 4: DeepSeek-V4 scores experts with
+    sqrtsoftplus and keeps the bias balancing of the sigmoid recipe)."""
+    return np.sqrt(spec_softplus(z)).astype(np.float32)
+
+
+def expert_score(z: np.ndarray, score: str) -> np.ndarray:
+    """Per-expert score of the bias-balanced recipes: sigmoid or sqrtsoftplus."""
+    if score == "sigmoid":
+        return sigmoid(z)
+    if score == "sqrtsoftplus":
+        return sqrtsoftplus(z)
+    raise ValueError(score)
+
+
 # ---------------------------------------------------------------------------
 # Router
 # ---------------------------------------------------------------------------
 
 
-def router_logits(x: np.ndarray, wg: np.ndarray, logit_offset: Optional[np.ndarray] = None):
+def router_logits(x: np.ndarray, wg: np.ndarray, logit_offset: Optional[np.ndarray] = None,
+                  noise: Optional[np.ndarray] = None, noise_std: float = 0.0):
     """Z = X W_g with W_g in the pages' [d, E] layout (page 2 "Token-choice
     ...": s = softmax(x W_g), W_g: [d, E]); the product is exact-ish in
     float64 and rounded once to float32; a per-expert offset is then added in
-    float32."""
+    float32.  Noisy top-k (page 4 "Pitfalls": Gaussian noise added to the
+    gating logits) adds noise_std * noise[t, e] last, with the standard
+    normals `noise` drawn by the caller: one float32 multiply, one add."""
     z = (widen(x) @ widen(wg)).astype(np.float32)
     if logit_offset is not None:
         z = (z + np.asarray(logit_offset, dtype=np.float32)[None, :]).astype(np.float32)
+    if noise is not None:
+        z = (z + (f32(noise_std) * np.asarray(noise, dtype=np.float32))).astype(np.float32)
     return z
 
 
 def router_scores(z: np.ndarray, score: str) -> np.ndarray:
-    return softmax_rows(z) if score == "softmax" else sigmoid(z)
+    return softmax_rows(z) if score == "softmax" else expert_score(z, score)
 
 
 # ---------------------------------------------------------------------------
@@ -209,9 +255,9 @@ def select_token_choice(z: np.ndarray, k: int, score: str = "softmax",
     """Token choice: every token keeps its k best experts.
 
     Keys: softmax scoring selects on the logits themselves (softmax is
-    monotone within a row, and page 3 selects on z_t directly); sigmoid
-    scoring selects on sigmoid(z) + b, the bias entering the choice only
-    (page 5 strategy 4).  Optional group-limited pre-selection.  Equal keys:
+    monotone within a row, and page 3 selects on z_t directly); sigmoid (or
+    sqrtsoftplus) scoring selects on score(z) + b, the bias entering the
+    choice only (page 5 strategy 4).  Optional group-limited pre-selection.  Equal keys:
     the lower expert index wins.
 
     Gates (mixing weights):
@@ -220,8 +266,9 @@ def select_token_choice(z: np.ndarray, k: int, score: str = "softmax",
         summed left to right in rank order;
       softmax, not norm_topk: the full-row softmax probability p_e (the
         top-1 Switch gate);
-      sigmoid: raw sigmoid scores (no bias), renormalised over the k when
-        norm_topk (page 5 strategy 4: mixing weights from the raw scores).
+      sigmoid / sqrtsoftplus: raw scores (no bias), renormalised over the k
+        when norm_topk (page 5 strategy 4: mixing weights from the raw
+        scores).
     Returns idx [n, k] int32 in rank order and gate [n, k] float32.
     """
     z = np.asarray(z, dtype=np.float32)
@@ -229,7 +276,7 @@ def select_token_choice(z: np.ndarray, k: int, score: str = "softmax",
     if score == "softmax":
         keys = z.copy()
     else:
-        sig = sigmoid(z)
+        sig = expert_score(z, score)
         keys = sig if sel_bias is None else (sig + np.asarray(sel_bias, np.float32)[None, :])
         keys = keys.astype(np.float32)
     if n_group > 1:
@@ -247,7 +294,7 @@ def select_token_choice(z: np.ndarray, k: int, score: str = "softmax",
         else:
             gate = np.take_along_axis(softmax_rows(z), idx, axis=1)
     else:
-        raw = np.take_along_axis(sigmoid(z), idx, axis=1)
+        raw = np.take_along_axis(expert_score(z, score), idx, axis=1)
         if norm_topk:
             s = raw[:, 0].copy()
             for j in range(1, k):
@@ -277,14 +324,23 @@ def select_expert_choice(z: np.ndarray, k: int):
 # ---------------------------------------------------------------------------
 
 
-def build_map_token_choice(idx: np.ndarray, gate: np.ndarray, E: int, capacity: Optional[int]):
+def build_map_token_choice(idx: np.ndarray, gate: np.ndarray, E: int, capacity: Optional[int],
+                           order: str = "token"):
     """Literal sequential arrival loop (page 1: tokens that arrive after an
-    expert's buffer fills skip it; page 5 strategy 2): assignments arrive in
-    token order, and within a token in rank order.  An assignment is kept iff
-    fewer than `capacity` earlier arrivals went to the same expert
-    (capacity None = dropless).  Kept assignments occupy compact expert-major
-    slots in arrival order."""
+    expert's buffer fills skip it; page 5 strategy 2).  order "token": the
+    assignments arrive in token order, and within a token in rank order;
+    order "rank": every token's first choice arrives before any second
+    choice (rank-major priority), tokens in order within a rank.  An
+    assignment is kept iff fewer than `capacity` earlier arrivals went to the
+    same expert (capacity None = dropless).  Kept assignments occupy compact
+    expert-major slots in arrival order."""
     n, k = idx.shape
+    if order == "token":
+        arrivals = [(t, r) for t in range(n) for r in range(k)]
+    elif order == "rank":
+        arrivals = [(t, r) for r in range(k) for t in range(n)]
+    else:
+        raise ValueError(order)
     C = n * k if capacity is None else int(capacity)
     count = np.bincount(idx.reshape(-1), minlength=E).astype(np.int64)
     kept = np.minimum(count, C)
@@ -298,17 +354,15 @@ def build_map_token_choice(idx: np.ndarray, gate: np.ndarray, E: int, capacity: 
     idx_l = idx.tolist()
     gate_l = gate.tolist()
     off_l = offset.tolist()
-    for t in range(n):
-        row = idx_l[t]
-        for r in range(k):
-            e = row[r]
-            pos = fill[e]
-            fill[e] = pos + 1
-            if pos < C:
-                s = off_l[e] + pos
-                slot_token[s] = t
-                slot_gate[s] = gate_l[t][r]
-                assign_slot[t, r] = s
+    for t, r in arrivals:
+        e = idx_l[t][r]
+        pos = fill[e]
+        fill[e] = pos + 1
+        if pos < C:
+            s = off_l[e] + pos
+            slot_token[s] = t
+            slot_gate[s] = gate_l[t][r]
+            assign_slot[t, r] = s
     # token-side lists: token t's k assignments in rank order, -1 where dropped
     token_offset = (np.arange(n + 1, dtype=np.int64) * k).astype(np.int32)
     token_slot = assign_slot.reshape(-1).copy()
@@ -427,7 +481,8 @@ def balance_stats(z: np.ndarray, rmap: dict, direction: str, k: int, score: str,
 
     lb_loss = coef * E * sum_e f_e P_e, f_e = chosen_e / sum(chosen) (before
               drops), P_e = mean over tokens of the normalised score
-              (softmax probability; for sigmoid scores sigma / row sum);
+              (softmax probability; for sigmoid or sqrtsoftplus scores the
+              score / its row sum);
               equals coef exactly at a balanced load.
     z_loss  = coef * mean_t (logsumexp_e z_te)^2.
     max_vio = (max_e load_e - mean_e load_e) / mean_e load_e, load = kept
@@ -444,8 +499,11 @@ def balance_stats(z: np.ndarray, rmap: dict, direction: str, k: int, score: str,
     if score == "softmax":
         zm = z64 - z64.max(axis=1, keepdims=True)
         p = np.exp(zm) / np.exp(zm).sum(axis=1, keepdims=True)
-    else:
+    elif score == "sigmoid":
         sg = 1.0 / (1.0 + np.exp(-z64))
+        p = sg / sg.sum(axis=1, keepdims=True)
+    else:
+        sg = np.sqrt(np.logaddexp(0.0, z64))                 # sqrt(softplus(z)) in float64
         p = sg / sg.sum(axis=1, keepdims=True)
     P = p.mean(axis=0)
     lb = lb_coef * E * float((f * P).sum())
@@ -466,6 +524,20 @@ def balance_stats(z: np.ndarray, rmap: dict, direction: str, k: int, score: str,
     return stats, hist
 
 
+def update_bias(bias: np.ndarray, expert_count: np.ndarray, n: int, k: int, gamma: float):
+    """Auxiliary-loss-free balancing step (page 5 strategy 4: after each step
+    the bias drops for overloaded experts and rises for idle ones).  Reading:
+    load_e = assignments chosen for expert e this step (before capacity
+    drops), mean = n k / E; b_e <- b_e - gamma * sign(load_e - mean), with the
+    sign taken exactly in integers (sign(load_e * E - n * k)), so an expert
+    exactly at the mean keeps its bias.  One float32 subtraction per expert."""
+    b = np.asarray(bias, dtype=np.float32)
+    E = b.shape[0]
+    diff = np.asarray(expert_count, dtype=np.int64) * E - int(n) * int(k)
+    step = (f32(gamma) * np.sign(diff).astype(np.float32)).astype(np.float32)
+    return (b - step).astype(np.float32)
+
+
 # ---------------------------------------------------------------------------
 # Whole layer
 # ---------------------------------------------------------------------------
@@ -482,7 +554,8 @@ def forward(cfg, inp: dict, inject_logits: Optional[np.ndarray] = None, experts=
     device whose logits differ in the last bits).  Returns a dict of every
     stage's result."""
     x = inp["x"]
-    z_ref = router_logits(x, inp["wg"], inp.get("logit_offset"))
+    z_ref = router_logits(x, inp["wg"], inp.get("logit_offset"), inp.get("noise"),
+                          getattr(cfg, "noise_std", 0.0))
     z = z_ref if inject_logits is None else np.asarray(inject_logits, dtype=np.float32)
     n, E = z.shape
     res = dict(logits=z_ref)
@@ -491,7 +564,8 @@ def forward(cfg, inp: dict, inject_logits: Optional[np.ndarray] = None, experts=
         idx, gate = select_token_choice(z, k, cfg.score, inp.get("sel_bias"), cfg.n_group,
                                         cfg.topk_group, cfg.group_topm, cfg.norm_topk)
         cap = tc_capacity(n, k, E, cfg.capacity_factor)
-        rmap = build_map_token_choice(idx, gate, E, None if cfg.capacity_factor is None else cap)
+        rmap = build_map_token_choice(idx, gate, E, None if cfg.capacity_factor is None else cap,
+                                      getattr(cfg, "capacity_order", "token"))
         res.update(sel_idx=idx, sel_gate=gate, capacity=cap)
     else:
         k = ec_k(n, cfg.c, E)
@@ -532,10 +606,14 @@ def forward_dense(cfg, inp: dict, z: np.ndarray, residual: bool = True) -> np.nd
         k = cfg.k
         idx, gate = select_token_choice(z, k, cfg.score, inp.get("sel_bias"), cfg.n_group,
                                         cfg.topk_group, cfg.group_topm, cfg.norm_topk)
+        # arrivals as rows of a one-hot matrix, in token-major or rank-major order
+        seq = idx if getattr(cfg, "capacity_order", "token") == "token" else idx.T
         onehot = np.zeros((n * k, E), dtype=np.int64)
-        onehot[np.arange(n * k), idx.reshape(-1)] = 1
+        onehot[np.arange(n * k), seq.reshape(-1)] = 1
         before = np.cumsum(onehot, axis=0) - onehot          # earlier arrivals per expert
-        pos = before[np.arange(n * k), idx.reshape(-1)].reshape(n, k)
+        pos = before[np.arange(n * k), seq.reshape(-1)].reshape(seq.shape)
+        if seq is not idx:
+            pos = pos.T
         C = n * k if cfg.capacity_factor is None else tc_capacity(n, k, E, cfg.capacity_factor)
         keep = pos < C
         for r in range(k):

@@ -30,7 +30,7 @@ from typing import Optional
 import numpy as np
 
 # tensor ids for the per-tensor seed streams
-_T_X, _T_WG, _T_W1, _T_W2, _T_OFFSET, _T_BIAS, _T_SW1, _T_SW2 = range(8)
+_T_X, _T_WG, _T_W1, _T_W2, _T_OFFSET, _T_BIAS, _T_SW1, _T_SW2, _T_NOISE = range(9)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -50,7 +50,7 @@ class MoEConfig:
     act: str                       # "gelu" | "swiglu"
     dtype: str                     # "f32" | "bf16"
     direction: str = "tc"          # "tc" | "ec"
-    score: str = "softmax"         # "softmax" | "sigmoid"
+    score: str = "softmax"         # "softmax" | "sigmoid" | "sqrtsoftplus"
     k: int = 1                     # token choice: experts per token
     c: float = 0.0                 # expert choice: capacity factor
     capacity_factor: Optional[float] = None   # token choice; None = dropless
@@ -62,6 +62,8 @@ class MoEConfig:
     zipf_offset_s: Optional[float] = None     # per-expert additive logit offset
     bias_halfwidth: Optional[float] = None    # selection bias ~ U(-h, h)
     shared_f: int = 0              # always-on shared expert hidden size (0 = none)
+    capacity_order: str = "token"  # capacity priority: "token" (token-major) | "rank" (rank-major)
+    noise_std: float = 0.0         # noisy top-k: logits += noise_std * N(0, 1) per (token, expert)
     lb_coef: float = 0.01
     z_coef: float = 0.001
     seed: int = 0
@@ -170,6 +172,14 @@ def gen_sel_bias(cfg: MoEConfig) -> Optional[np.ndarray]:
     return _rng(cfg, _T_BIAS).uniform(-h, h, size=cfg.E).astype(np.float32)
 
 
+def gen_noise(cfg: MoEConfig) -> Optional[np.ndarray]:
+    """Standard normals [n, E] for noisy top-k (scaled by noise_std inside
+    the router); the method's random numbers are inputs, drawn here."""
+    if not cfg.noise_std:
+        return None
+    return _rng(cfg, _T_NOISE).standard_normal((cfg.n, cfg.E), dtype=np.float32)
+
+
 def _threads() -> int:
     try:
         n = len(os.sched_getaffinity(0))
@@ -203,6 +213,7 @@ def gen_inputs(cfg: MoEConfig, with_experts: bool = True, threads: Optional[int]
         "wg": gen_wg(cfg),
         "logit_offset": gen_logit_offset(cfg),
         "sel_bias": gen_sel_bias(cfg),
+        "noise": gen_noise(cfg),
     }
     if with_experts:
         out["w1"], out["w2"] = gen_expert_weights(cfg, threads=threads)

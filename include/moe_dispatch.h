@@ -5,7 +5,7 @@
  * The layer (MoE-routing pages: page 2 "Expert choice routing", section "The
  * math"; page 5 "MoE routing strategies explained", strategies 1-6):
  *
- *   S = softmax(X W_g)  or  sigmoid(X W_g)              moe_router
+ *   S = softmax(X W_g), sigmoid or sqrtsoftplus         moe_router
  *   token choice: each token keeps its top-k experts;   moe_select
  *   expert choice: each expert keeps its top-k tokens
  *   capacity / routing map (P = onehot(I))              moe_build_map
@@ -13,6 +13,7 @@
  *   Y[e] = Expert_e(X_in[e])                            moe_expert_ffn
  *   out = residual + shared + scatter_add(G * Y, I)     moe_combine
  *   load-balance loss, z-loss, MaxVio                   moe_balance_stats
+ *   loss-free balancing: bias step from the loads       moe_update_bias
  *
  * Conventions common to every call:
  *  - Tensor arguments are DEVICE pointers owned by the caller.  The library
@@ -60,7 +61,8 @@ enum {
 };
 
 enum { MOE_F32 = 0, MOE_BF16 = 1 };               /* element type           */
-enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 };        /* router score function  */
+enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1, MOE_SQRTSOFTPLUS = 2 };   /* router score function */
+enum { MOE_TOKEN_MAJOR = 0, MOE_RANK_MAJOR = 1 }; /* capacity arrival order */
 enum { MOE_TOKEN_CHOICE = 0, MOE_EXPERT_CHOICE = 1 };
 enum { MOE_GELU = 0, MOE_SWIGLU = 1 };            /* expert activation      */
 
@@ -90,6 +92,10 @@ typedef struct {
   int32_t group_topm; /* group score = sum of the group's top-m keys, 1..4  */
   int32_t norm_topk;  /* 1: renormalise gates over the k selected experts  */
   int32_t capacity;   /* token choice: slots per expert; -1 = dropless     */
+  int32_t capacity_order; /* token choice: MOE_TOKEN_MAJOR (assignments arrive
+                         token by token, each token's in rank order) or
+                         MOE_RANK_MAJOR (every token's first choice arrives
+                         before any second choice); expert choice: 0       */
 } moe_route_cfg_t;
 
 /* Routing map (host struct of caller-owned device buffers; M_max =
@@ -144,32 +150,42 @@ moe_status_t moe_ffn_workspace_size(int64_t M_max, int32_t E, int32_t d, int32_t
 /* ---- the layer --------------------------------------------------------- */
 
 /* Router (page 2 "The math": S = softmax(X W_g), W_g: [d, E]; page 5
- * strategy 4: a sigmoid per expert instead).  Logits Z = X W_g accumulated
- * in fp32 (bf16 inputs on the matrix cores), plus logit_offset[e] when
- * given, written to logits [n,E] fp32.  Optional outputs: scores [n,E] and
+ * strategy 4: a sigmoid per expert instead, or sqrtsoftplus(z) =
+ * sqrt(log(1 + e^z)) for DeepSeek-V4).  Logits Z = X W_g accumulated in fp32
+ * (bf16 inputs on the matrix cores), plus logit_offset[e] when given, plus
+ * noise_std * noise[t,e] when `noise` is given (noisy top-k, page 4 "How MoE
+ * routing strategies make LLMs efficient", section "Pitfalls": Gaussian
+ * noise on the gating logits; `noise` [n,E] fp32 holds the caller's
+ * standard normals, one fp32 multiply and one add), written to logits [n,E]
+ * fp32; everything downstream sees these logits.  Optional outputs: scores
+ * [n,E] and
  * scores_t [E,n] (the transpose, the column-contiguous layout expert choice
  * selects from), both fp32, computed with the library's specified exp
  * (Cody-Waite reduction, degree-7 Taylor polynomial, single fp32 operations,
  * no fused multiply-add), a halving-stride tree sum over experts and IEEE
- * division, so equal logits give equal score bits on any conforming device.
+ * division, so equal logits give equal score bits on any conforming device
+ * (sqrtsoftplus: max(z,0) + log1p(spec_exp(-|z|)), log1p as a specified
+ * degree-15 odd series in u/(2+u), then the correctly rounded square root).
  * X [n,d] and W_g [d,E] in `dtype`; logit_offset [E] fp32 or NULL.
  * Any shape; bf16 with d % 64 == 0 and E % 16 == 0 runs on the matrix cores
  * (X and W_g 16-byte aligned), other shapes on a scalar fp32 kernel. */
 moe_status_t moe_router(const void *X, const void *Wg, int32_t dtype, const float *logit_offset,
-                        const moe_route_cfg_t *cfg, float *logits, float *scores, float *scores_t,
-                        void *ws, size_t ws_bytes, void *stream);
+                        const float *noise, float noise_std, const moe_route_cfg_t *cfg,
+                        float *logits, float *scores, float *scores_t, void *ws, size_t ws_bytes,
+                        void *stream);
 
 /* Selection.
  * Token choice (page 2 "Token-choice and its load-balance headache"; page 5
  * strategies 1, 2, 4, 5): every token keeps its k best experts, in rank
  * order, lower expert index first on equal keys.  Key = the logit (softmax
- * is monotone within a row) or sigmoid(z) + sel_bias[e] (sel_bias [E] fp32
- * or NULL; the bias enters the choice only).  With n_group > 1 the experts
+ * is monotone within a row) or score(z) + sel_bias[e] for the sigmoid and
+ * sqrtsoftplus scores (sel_bias [E] fp32 or NULL; the bias enters the
+ * choice only).  With n_group > 1 the experts
  * form n_group contiguous groups, each scored by the sum of its top
  * group_topm keys, and only the topk_group best groups (lower index on ties)
  * stay eligible.  Gates: softmax over the k selected logits when norm_topk,
- * else the full-row softmax probability; sigmoid: the raw sigmoid scores,
- * renormalised over the k when norm_topk.  Output sel_idx [n,k] int32,
+ * else the full-row softmax probability; sigmoid / sqrtsoftplus: the raw
+ * scores, renormalised over the k when norm_topk.  Output sel_idx [n,k] int32,
  * sel_gate [n,k] fp32.
  * Expert choice (page 2 "The transposed selection"): every expert keeps the
  * k tokens with the highest softmax score in its column, lower token index
@@ -181,10 +197,12 @@ moe_status_t moe_select(const float *logits, const float *scores_t, const float 
                         size_t ws_bytes, void *stream);
 
 /* Routing map.  Token choice: assignments arrive in token order and, within
- * a token, in rank order; an assignment is kept iff fewer than `capacity`
- * earlier arrivals went to its expert (page 1 "Dropped tokens flow in
- * opposite directions": tokens arriving after the buffer fills skip the
- * expert and ride the residual); capacity -1 keeps all (dropless).
+ * a token, in rank order (cfg->capacity_order MOE_TOKEN_MAJOR), or rank by
+ * rank, tokens in order within a rank (MOE_RANK_MAJOR: first choices have
+ * priority); an assignment is kept iff fewer than `capacity` earlier
+ * arrivals went to its expert (page 1 "Dropped tokens flow in opposite
+ * directions": tokens arriving after the buffer fills skip the expert and
+ * ride the residual); capacity -1 keeps all (dropless).
  * Expert choice: slot e*k + j holds I[e,j].  Fills every field of `map`;
  * kept slots are expert-major and in arrival order within an expert. */
 moe_status_t moe_build_map(const int32_t *sel_idx, const float *sel_gate, const moe_route_cfg_t *cfg,
@@ -230,6 +248,16 @@ moe_status_t moe_combine(const void *Y_perm, int32_t dtype, const moe_route_map_
 moe_status_t moe_balance_stats(const float *logits, const moe_route_map_t *map,
                                const moe_route_cfg_t *cfg, float lb_coef, float z_coef, float *stats,
                                int32_t *hist, void *ws, size_t ws_bytes, void *stream);
+
+/* Auxiliary-loss-free balancing (page 5 strategy 4: after each step the
+ * bias drops for overloaded experts and rises for idle ones).  Token
+ * choice: bias[e] -= gamma * sign(expert_count[e] - n*k/E), the sign taken
+ * exactly in integers (an expert exactly at the mean keeps its bias), one
+ * fp32 subtraction per expert, in place on the device.  expert_count [E]
+ * int32 is the map's pre-drop count (moe_build_map); bias [E] fp32 is the
+ * sel_bias of moe_select; gamma finite. */
+moe_status_t moe_update_bias(const int32_t *expert_count, const moe_route_cfg_t *cfg, float gamma,
+                             float *bias, void *stream);
 
 const char *moe_status_string(moe_status_t status);
 const char *moe_last_error(void);

@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_PKG, "lib", "libmoe_dispatch.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = range(5)
 MOE_F32, MOE_BF16 = 0, 1
-MOE_SOFTMAX, MOE_SIGMOID = 0, 1
+MOE_SOFTMAX, MOE_SIGMOID, MOE_SQRTSOFTPLUS = 0, 1, 2
+MOE_TOKEN_MAJOR, MOE_RANK_MAJOR = 0, 1
 MOE_TOKEN_CHOICE, MOE_EXPERT_CHOICE = 0, 1
 MOE_GELU, MOE_SWIGLU = 0, 1
 MOE_NSTATS = 8
@@ -30,7 +31,7 @@ EXPORTED = ("moe_ec_k", "moe_tc_capacity", "moe_max_slots", "moe_token_list_len"
             "moe_router_workspace_size",
             "moe_route_workspace_size", "moe_ffn_workspace_size", "moe_router", "moe_select",
             "moe_build_map", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_balance_stats",
-            "moe_status_string", "moe_last_error")
+            "moe_update_bias", "moe_status_string", "moe_last_error")
 
 
 class MoEError(RuntimeError):
@@ -42,7 +43,7 @@ class MoEError(RuntimeError):
 class RouteCfg(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in
                 ("n", "d", "E", "k", "dir", "score", "n_group", "topk_group", "group_topm",
-                 "norm_topk", "capacity")]
+                 "norm_topk", "capacity", "capacity_order")]
 
 
 class RouteMapC(ctypes.Structure):
@@ -76,13 +77,14 @@ def lib() -> ctypes.CDLL:
         "moe_router_workspace_size": (I32, [CFG, I32, SZP]),
         "moe_route_workspace_size": (I32, [CFG, SZP]),
         "moe_ffn_workspace_size": (I32, [I64, I32, I32, I32, I32, I32, SZP]),
-        "moe_router": (I32, [P, P, I32, P, CFG, P, P, P, P, SZ, P]),
+        "moe_router": (I32, [P, P, I32, P, P, F32, CFG, P, P, P, P, SZ, P]),
         "moe_select": (I32, [P, P, P, CFG, P, P, P, SZ, P]),
         "moe_build_map": (I32, [P, P, CFG, MAP, P, SZ, P]),
         "moe_dispatch": (I32, [P, I32, I32, I32, MAP, I64, P, P]),
         "moe_expert_ffn": (I32, [P, I32, P, I32, I32, I32, I32, P, P, I64, P, P, SZ, P]),
         "moe_combine": (I32, [P, I32, MAP, I32, I32, P, P, P, P]),
         "moe_balance_stats": (I32, [P, MAP, CFG, F32, F32, P, P, P, SZ, P]),
+        "moe_update_bias": (I32, [P, CFG, F32, P, P]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_last_error": (ctypes.c_char_p, []),
     }
@@ -143,9 +145,10 @@ def _check(status: int, where: str):
 
 
 def make_cfg(n, d, E, k, direction=MOE_TOKEN_CHOICE, score=MOE_SOFTMAX, n_group=1, topk_group=1,
-             group_topm=1, norm_topk=1, capacity=-1) -> RouteCfg:
+             group_topm=1, norm_topk=1, capacity=-1, capacity_order=MOE_TOKEN_MAJOR) -> RouteCfg:
     return RouteCfg(int(n), int(d), int(E), int(k), int(direction), int(score), int(n_group),
-                    int(topk_group), int(group_topm), int(norm_topk), int(capacity))
+                    int(topk_group), int(group_topm), int(norm_topk), int(capacity),
+                    int(capacity_order))
 
 
 class RouteMap:
@@ -224,11 +227,12 @@ def _ws(ws: Optional[torch.Tensor]):
 
 
 def moe_router(x, wg, logit_offset, cfg: RouteCfg, logits, scores=None, scores_t=None, ws=None,
-               stream=None):
+               stream=None, noise=None, noise_std=0.0):
     code = dtype_code(x)
     w, wb = _ws(ws)
     _check(lib().moe_router(_ptr(x, "x", _elem_dtypes(code)), _ptr(wg, "wg", _elem_dtypes(code)), code,
-                            _ptr(logit_offset, "logit_offset", _F32), ctypes.byref(cfg),
+                            _ptr(logit_offset, "logit_offset", _F32), _ptr(noise, "noise", _F32),
+                            float(noise_std), ctypes.byref(cfg),
                             _ptr(logits, "logits", _F32), _ptr(scores, "scores", _F32),
                             _ptr(scores_t, "scores_t", _F32), w, wb, _stream(stream)), "moe_router")
 
@@ -289,6 +293,12 @@ def moe_balance_stats(logits, rmap: RouteMap, cfg: RouteCfg, lb_coef, z_coef, st
                                    float(lb_coef), float(z_coef), _ptr(stats, "stats", _F32),
                                    _ptr(hist, "hist", _I32), w, wb, _stream(stream)),
            "moe_balance_stats")
+
+
+def moe_update_bias(expert_count, cfg: RouteCfg, gamma, bias, stream=None):
+    _check(lib().moe_update_bias(_ptr(expert_count, "expert_count", _I32), ctypes.byref(cfg),
+                                 float(gamma), _ptr(bias, "bias", _F32), _stream(stream)),
+           "moe_update_bias")
 
 
 def moe_status_string(status: int) -> str:

@@ -48,7 +48,10 @@ moe_status_t check_cfg(const moe_route_cfg_t* c) {
   REQUIRE(c->n > 0 && c->d > 0 && c->E > 0 && c->k > 0, "n, d, E, k must be positive (n=%d d=%d E=%d k=%d)",
           c->n, c->d, c->E, c->k);
   REQUIRE(c->dir == MOE_TOKEN_CHOICE || c->dir == MOE_EXPERT_CHOICE, "dir must be 0 or 1");
-  REQUIRE(c->score == MOE_SOFTMAX || c->score == MOE_SIGMOID, "score must be 0 or 1");
+  REQUIRE(c->score == MOE_SOFTMAX || c->score == MOE_SIGMOID || c->score == MOE_SQRTSOFTPLUS,
+          "score must be MOE_SOFTMAX, MOE_SIGMOID or MOE_SQRTSOFTPLUS");
+  REQUIRE(c->capacity_order == MOE_TOKEN_MAJOR || c->capacity_order == MOE_RANK_MAJOR,
+          "capacity_order must be MOE_TOKEN_MAJOR or MOE_RANK_MAJOR");
   REQUIRE(c->norm_topk == 0 || c->norm_topk == 1, "norm_topk must be 0 or 1");
   SUPPORTED(c->E <= moe::kMaxExperts, "E=%d exceeds the supported %d experts", c->E, moe::kMaxExperts);
   if (c->dir == MOE_TOKEN_CHOICE) {
@@ -68,6 +71,7 @@ moe_status_t check_cfg(const moe_route_cfg_t* c) {
   } else {
     REQUIRE(c->k <= c->n, "expert choice needs k <= n (k=%d n=%d)", c->k, c->n);
     SUPPORTED(c->score == MOE_SOFTMAX, "expert choice selects on softmax scores");
+    REQUIRE(c->capacity_order == MOE_TOKEN_MAJOR, "expert choice has no capacity order");
     SUPPORTED(c->n_group == 1, "expert choice has no group limit");
     SUPPORTED(c->n <= (1 << 24), "expert choice supports n <= 2^24");
     REQUIRE((int64_t)c->E * c->k <= INT32_MAX, "E*k overflows int32");
@@ -159,19 +163,21 @@ moe_status_t moe_ffn_workspace_size(int64_t M_max, int32_t E, int32_t d, int32_t
 }
 
 moe_status_t moe_router(const void* X, const void* Wg, int32_t dtype, const float* logit_offset,
-                        const moe_route_cfg_t* cfg, float* logits, float* scores, float* scores_t,
-                        void* ws, size_t ws_bytes, void* stream) {
+                        const float* noise, float noise_std, const moe_route_cfg_t* cfg, float* logits,
+                        float* scores, float* scores_t, void* ws, size_t ws_bytes, void* stream) {
   moe_status_t st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   REQUIRE(X && Wg && logits, "X, Wg and logits must be non-NULL");
   REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, "dtype must be MOE_F32 or MOE_BF16");
+  REQUIRE(!noise || std::isfinite(noise_std), "noise_std must be finite");
   if (dtype == MOE_BF16 && cfg->d % 64 == 0 && cfg->E % 16 == 0)   // the matrix-core path
     REQUIRE(aligned16(X) && aligned16(Wg), "X and Wg must be 16-byte aligned");
   const size_t need = moe::router_workspace_bytes(cfg->n, cfg->d, cfg->E, dtype);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(MOE_ERR_WORKSPACE, "router needs %zu workspace bytes, got %zu", need, ws_bytes);
-  return launched(moe::launch_router(X, Wg, dtype, logit_offset, cfg->n, cfg->d, cfg->E, cfg->score,
-                                     logits, scores, scores_t, ws, as_stream(stream)),
+  return launched(moe::launch_router(X, Wg, dtype, logit_offset, noise, noise ? noise_std : 0.f, cfg->n,
+                                     cfg->d, cfg->E, cfg->score, logits, scores, scores_t, ws,
+                                     as_stream(stream)),
                   "moe_router");
 }
 
@@ -211,8 +217,8 @@ moe_status_t moe_build_map(const int32_t* sel_idx, const float* sel_gate, const 
     return fail(MOE_ERR_WORKSPACE, "build_map needs %zu workspace bytes, got %zu", need, ws_bytes);
   const moe::MapPtrs m = map_ptrs(map);
   if (cfg->dir == MOE_TOKEN_CHOICE)
-    return launched(moe::launch_build_map_tc(sel_idx, sel_gate, cfg->n, cfg->E, cfg->k, cfg->capacity, m,
-                                             ws, as_stream(stream)),
+    return launched(moe::launch_build_map_tc(sel_idx, sel_gate, cfg->n, cfg->E, cfg->k, cfg->capacity,
+                                             cfg->capacity_order, m, ws, as_stream(stream)),
                     "moe_build_map");
   return launched(moe::launch_build_map_ec(sel_idx, sel_gate, cfg->n, cfg->E, cfg->k, m, ws,
                                            as_stream(stream)),
@@ -292,6 +298,18 @@ moe_status_t moe_balance_stats(const float* logits, const moe_route_map_t* map,
                                             cfg->score, lb_coef, z_coef, stats, hist, ws,
                                             as_stream(stream)),
                   "moe_balance_stats");
+}
+
+moe_status_t moe_update_bias(const int32_t* expert_count, const moe_route_cfg_t* cfg, float gamma,
+                             float* bias, void* stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  REQUIRE(cfg->dir == MOE_TOKEN_CHOICE, "the bias update balances token choice (expert choice loads are fixed)");
+  REQUIRE(expert_count && bias, "expert_count and bias must be non-NULL");
+  REQUIRE(std::isfinite(gamma), "gamma must be finite");
+  return launched(moe::launch_update_bias(expert_count, cfg->n, cfg->E, cfg->k, gamma, bias,
+                                          as_stream(stream)),
+                  "moe_update_bias");
 }
 
 const char* moe_status_string(moe_status_t status) {

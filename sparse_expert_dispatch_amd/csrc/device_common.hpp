@@ -74,6 +74,40 @@ MOE_DEV float spec_sigmoid(float z) {
   return 1.0f / (1.0f + spec_exp(-z));
 }
 
+// ---------------------------------------------------------------- specified sqrtsoftplus
+// log1p(u) for 0 <= u <= 1 as 2 atanh(s), s = u / (2 + u):
+// 2 s (1 + s^2/3 + ... + s^14/15) in Horner form over s^2 (s <= 1/3, so the
+// first omitted term is below 2^-30 relative); softplus(z) = max(z, 0) +
+// log1p(e^-|z|); the score is its correctly rounded square root.
+MOE_DEV float spec_log1p01(float u) {
+#pragma clang fp contract(off)
+  const float s = u / (2.0f + u);
+  const float s2 = s * s;
+  float p = (float)(1.0 / 15.0);
+  p = p * s2 + (float)(1.0 / 13.0);
+  p = p * s2 + (float)(1.0 / 11.0);
+  p = p * s2 + (float)(1.0 / 9.0);
+  p = p * s2 + (float)(1.0 / 7.0);
+  p = p * s2 + (float)(1.0 / 5.0);
+  p = p * s2 + (float)(1.0 / 3.0);
+  p = p * s2 + 1.0f;
+  return (s + s) * p;
+}
+
+MOE_DEV float spec_sqrtsoftplus(float z) {
+#pragma clang fp contract(off)
+  const float sp = fmaxf(z, 0.0f) + spec_log1p01(spec_exp(-fabsf(z)));
+  // __builtin_sqrtf lowers to the correctly rounded sequence (v_sqrt_f32,
+  // then a one-ulp neighbour test with exact residuals); __fsqrt_rn lowers
+  // to the bare v_sqrt_f32 on gfx950, which is not correctly rounded
+  return __builtin_sqrtf(sp);
+}
+
+// Per-expert score of the bias-balanced recipes: 1 = sigmoid, 2 = sqrtsoftplus.
+MOE_DEV float spec_expert_score(float z, int score) {
+  return score == 2 ? spec_sqrtsoftplus(z) : spec_sigmoid(z);
+}
+
 // ---------------------------------------------------------------- wave64 helpers
 
 MOE_DEV uint64_t wave_max_u64(uint64_t v) {

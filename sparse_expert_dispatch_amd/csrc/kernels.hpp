@@ -37,15 +37,15 @@ __device__ __forceinline__ float row_tree_sum(const float (&row)[R], int P) {
 
 // router.hip
 size_t router_workspace_bytes(int n, int d, int E, int dtype);
-hipError_t launch_router(const void* X, const void* Wg, int dtype, const float* offset, int n, int d,
-                         int E, int score, float* logits, float* scores, float* scores_t, void* ws,
-                         hipStream_t stream);
+hipError_t launch_router(const void* X, const void* Wg, int dtype, const float* offset,
+                         const float* noise, float noise_std, int n, int d, int E, int score,
+                         float* logits, float* scores, float* scores_t, void* ws, hipStream_t stream);
 
 // Scores (and/or their transpose) from finished logits: the router's
 // epilogue on its own; `logits` may be NULL.
 hipError_t launch_router_finalize(const float* partial, int nsplit, int n, int E, const float* offset,
-                                  int score, float* logits, float* scores, float* scores_t,
-                                  hipStream_t stream);
+                                  const float* noise, float noise_std, int score, float* logits,
+                                  float* scores, float* scores_t, hipStream_t stream);
 
 // select.hip
 struct SelectArgs {
@@ -70,7 +70,8 @@ struct MapPtrs {
 };
 size_t map_workspace_bytes(int dir, int n, int E, int k);
 hipError_t launch_build_map_tc(const int32_t* idx, const float* gate, int n, int E, int k,
-                               int capacity, const MapPtrs& m, void* ws, hipStream_t stream);
+                               int capacity, int rank_major, const MapPtrs& m, void* ws,
+                               hipStream_t stream);
 hipError_t launch_build_map_ec(const int32_t* I, const float* G, int n, int E, int k,
                                const MapPtrs& m, void* ws, hipStream_t stream);
 
@@ -92,5 +93,7 @@ size_t stats_workspace_bytes(int n, int E);
 hipError_t launch_balance_stats(const float* logits, const MapPtrs& m, int n, int E, int k, int dir,
                                 int score, float lb_coef, float z_coef, float* stats, int32_t* hist,
                                 void* ws, hipStream_t stream);
+hipError_t launch_update_bias(const int32_t* expert_count, int n, int E, int k, float gamma, float* bias,
+                              hipStream_t stream);
 
 }  // namespace moe

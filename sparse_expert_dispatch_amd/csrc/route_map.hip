@@ -10,7 +10,10 @@
 // the residual connection); page 2 "Expert choice routing", section "The
 // math" (P = onehot(I): slot e*k + j carries token I[e, j]).
 //
-// Token choice runs as a stable counting sort of the n*k arrivals by expert:
+// Token choice runs as a stable counting sort of the n*k arrivals by expert.
+// Arrival a is assignment (t, r) = (a / k, a % k) in token-major order, or
+// (a % n, a / n) in rank-major order (every first choice before any second
+// one):
 //  1. chunk histograms (LDS integer atomics; counts are order-free),
 //  2. one workgroup turns them into per-chunk starting positions per expert
 //     (a scan over chunks in chunk order) and expert offsets of the kept
@@ -28,8 +31,14 @@ namespace moe {
 constexpr int kMapChunk = 1024;      // arrivals per chunk
 constexpr int kScanThreads = 1024;
 
+// Element of idx [n, k] that arrives a-th.
+MOE_DEV int64_t arrival_elem(int64_t a, int n, int k, int rank_major) {
+  return rank_major ? (a % n) * k + a / n : a;
+}
+
 __global__ __launch_bounds__(256) void map_chunk_hist_kernel(const int32_t* __restrict__ idx,
-                                                             int64_t M, int E,
+                                                             int64_t M, int n, int k, int E,
+                                                             int rank_major,
                                                              int32_t* __restrict__ chunk_hist) {
   extern __shared__ int sh[];
   for (int e = threadIdx.x; e < E; e += 256) sh[e] = 0;
@@ -38,7 +47,7 @@ __global__ __launch_bounds__(256) void map_chunk_hist_kernel(const int32_t* __re
   for (int i = threadIdx.x; i < kMapChunk; i += 256) {
     const int64_t a = a0 + i;
     if (a < M) {
-      const int e = idx[a];
+      const int e = idx[arrival_elem(a, n, k, rank_major)];
       if ((unsigned)e < (unsigned)E) atomicAdd(&sh[e], 1);   // out-of-range ids are dropped
     }
   }
@@ -77,8 +86,8 @@ __global__ __launch_bounds__(kScanThreads) void map_scan_kernel(
 // Token choice also writes the token-side lists: token t's entries are its
 // k assignments in rank order (token_offset[t] = t*k), -1 for a dropped one.
 __global__ __launch_bounds__(64) void map_scatter_kernel(
-    const int32_t* __restrict__ idx, const float* __restrict__ gate, int64_t M, int k, int E,
-    int nbits, int capacity, const int32_t* __restrict__ chunk_base,
+    const int32_t* __restrict__ idx, const float* __restrict__ gate, int64_t M, int n, int k, int E,
+    int rank_major, int nbits, int capacity, const int32_t* __restrict__ chunk_base,
     const int32_t* __restrict__ expert_offset, MapPtrs m) {
   extern __shared__ int cnt[];
   const int lane = threadIdx.x;
@@ -91,7 +100,8 @@ __global__ __launch_bounds__(64) void map_scatter_kernel(
   for (int it = 0; it < kMapChunk; it += 64) {
     const int64_t a = a0 + it + lane;
     const bool inrange = a < M;
-    const int e_raw = inrange ? idx[a] : 0;
+    const int64_t q = arrival_elem(a, n, k, rank_major);    // (t, r) = (q / k, q % k)
+    const int e_raw = inrange ? idx[q] : 0;
     const bool valid = inrange && (unsigned)e_raw < (unsigned)E;
     const int e = valid ? e_raw : 0;
     uint64_t match = __ballot(valid);
@@ -111,12 +121,12 @@ __global__ __launch_bounds__(64) void map_scatter_kernel(
       int32_t s = -1;
       if (valid && (capacity < 0 || pos < capacity)) {
         s = expert_offset[e] + pos;
-        m.slot_token[s] = (int32_t)(a / k);
-        m.slot_gate[s] = gate[a];
+        m.slot_token[s] = (int32_t)(q / k);
+        m.slot_gate[s] = gate[q];
       }
-      m.assign_slot[a] = s;
-      m.token_slot[a] = s;
-      if (a % k == 0) m.token_offset[a / k] = (int32_t)a;
+      m.assign_slot[q] = s;
+      m.token_slot[q] = s;
+      if (q % k == 0) m.token_offset[q / k] = (int32_t)q;
     }
   }
 }
@@ -216,19 +226,20 @@ size_t map_workspace_bytes(int dir, int n, int E, int k) {
 }
 
 hipError_t launch_build_map_tc(const int32_t* idx, const float* gate, int n, int E, int k,
-                               int capacity, const MapPtrs& m, void* ws, hipStream_t stream) {
+                               int capacity, int rank_major, const MapPtrs& m, void* ws,
+                               hipStream_t stream) {
   const int64_t M = (int64_t)n * k;
   const int nch = chunks_of(M);
   int32_t* chunk_hist = static_cast<int32_t*>(ws);
   int32_t* chunk_base = chunk_hist + (size_t)nch * E;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  hipLaunchKernelGGL(map_chunk_hist_kernel, dim3(nch), dim3(256), E * sizeof(int), stream, idx, M, E,
-                     chunk_hist);
+  hipLaunchKernelGGL(map_chunk_hist_kernel, dim3(nch), dim3(256), E * sizeof(int), stream, idx, M, n, k,
+                     E, rank_major, chunk_hist);
   hipLaunchKernelGGL(map_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, chunk_hist, nch, E,
                      capacity, chunk_base, m.expert_count, m.expert_offset, m.n_kept);
   hipLaunchKernelGGL(map_scatter_kernel, dim3(nch), dim3(64), E * sizeof(int), stream, idx, gate, M,
-                     k, E, nbits, capacity, chunk_base, m.expert_offset, m);
+                     n, k, E, rank_major, nbits, capacity, chunk_base, m.expert_offset, m);
   return hipGetLastError();
 }
 

@@ -27,6 +27,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kRouterBK = 64;      // K per pipeline stage
 constexpr int kRouterCols = 256;   // expert columns per workgroup (4 waves x 64)
 constexpr int kRouterSplitsMax = 8;
+constexpr int kRouterDepth = 4;   // K stages in flight per wave
 
 // W_g^T [E][d] from W_g [d][E]: each workgroup moves a 64 (K) x 64
 // (expert) tile through LDS with 16-byte global loads and stores (E is a
@@ -76,8 +77,8 @@ __global__ __launch_bounds__(256) void router_wg_transpose_kernel(const bf16_t* 
 // Z = X W_g on the matrix cores with no LDS: every wave owns 16 token rows
 // and up to 64 expert columns (4 tiles of v_mfma_f32_16x16x32_bf16) over one
 // K slice; A fragments come from X and B fragments from W_g^T, both as
-// 16-byte loads of 8 consecutive K values, and the next K stage is loading
-// while the current one is multiplied.  A workgroup is 4 waves: 64, 32 or
+// 16-byte loads of 8 consecutive K values; kRouterDepth K stages are in
+// flight while the oldest is multiplied.  A workgroup is 4 waves: 64, 32 or
 // 16 rows by 64, 128 or 256 columns depending on E.
 __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ WgT, int n, int d, int E, int k_per_split,
@@ -102,7 +103,9 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
   f32x4_t acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  bf16x8_t a[2][2], b[2][2][4];                          // [buffer][32-wide K step][tile]
+  // register ring of kRouterDepth K stages: all of them are loading while
+  // the oldest is multiplied
+  bf16x8_t a[kRouterDepth][2], b[kRouterDepth][2][4];     // [slot][32-wide K step][tile]
   auto load = [&](int st, int q) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -119,13 +122,17 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
       for (int j = 0; j < 4; ++j)
         if (j < nt) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q][s], b[q][s][j], acc[j], 0, 0, 0);
   };
-  load(0, 0);
-  for (int st = 0; st < nk; st += 2) {
-    if (st + 1 < nk) load(st + 1, 1);
-    mma(0);
-    if (st + 1 >= nk) break;
-    if (st + 2 < nk) load(st + 2, 0);
-    mma(1);
+#pragma unroll
+  for (int q = 0; q < kRouterDepth; ++q)
+    if (q < nk) load(q, q);
+  for (int st = 0; st < nk; st += kRouterDepth) {
+#pragma unroll
+    for (int q = 0; q < kRouterDepth; ++q) {
+      if (st + q < nk) {
+        mma(q);
+        if (st + q + kRouterDepth < nk) load(st + q + kRouterDepth, q);
+      }
+    }
   }
   // C fragment: lane holds column (lane % 16), rows (lane / 16) * 4 + r.
   float* out = partial + (size_t)split * n * E;
@@ -164,7 +171,10 @@ static bool router_uses_mfma(int dtype, int d, int E) { return dtype == 1 && d %
 
 // Finalize: 16 rows per workgroup, one wave per row at a time; lane l holds
 // experts l + 64 j.  Sums the split partials in split order, adds the
-// offset, writes the logits and (on request) the specified scores,
+// offset, then the scaled noise of noisy top-k (page 4 "How MoE routing
+// strategies ...", section "Pitfalls": Gaussian noise on the gating
+// logits; the standard normals are an input), writes the logits and (on
+// request) the specified scores,
 // row-major and/or transposed.  The transpose goes through an LDS tile with
 // an odd row stride (E + 1 floats), so both the row-wise writes and the
 // column-wise reads are free of bank conflicts and the [E, n] stores are
@@ -172,8 +182,9 @@ static bool router_uses_mfma(int dtype, int d, int E) { return dtype == 1 && d %
 constexpr int kFinRows = 16;
 
 __global__ __launch_bounds__(1024) void router_finalize_kernel(
-    const float* partial, int nsplit, int n, int E, const float* __restrict__ offset, int score,
-    float* logits, float* __restrict__ scores, float* __restrict__ scores_t) {
+    const float* partial, int nsplit, int n, int E, const float* __restrict__ offset,
+    const float* __restrict__ noise, float noise_std, int score, float* logits,
+    float* __restrict__ scores, float* __restrict__ scores_t) {
   // `partial` and `logits` may be the same buffer (single K-slice): each
   // element is read and then written by the same thread.
 #pragma clang fp contract(off)
@@ -196,6 +207,7 @@ __global__ __launch_bounds__(1024) void router_finalize_kernel(
         float v = partial[(size_t)row * E + e];
         for (int s = 1; s < nsplit; ++s) v = v + partial[(size_t)s * n * E + (size_t)row * E + e];
         if (offset) v = v + offset[e];
+        if (noise) v = v + noise_std * noise[(size_t)row * E + e];
         z[j] = v;
         if (logits) logits[(size_t)row * E + e] = v;
       }
@@ -217,7 +229,7 @@ __global__ __launch_bounds__(1024) void router_finalize_kernel(
       for (int j = 0; j < kMaxExpertRegs; ++j) p[j] = t[j] / s;
     } else {
 #pragma unroll
-      for (int j = 0; j < kMaxExpertRegs; ++j) p[j] = spec_sigmoid(z[j]);
+      for (int j = 0; j < kMaxExpertRegs; ++j) p[j] = spec_expert_score(z[j], score);
     }
 #pragma unroll
     for (int j = 0; j < kMaxExpertRegs; ++j) {
@@ -240,8 +252,8 @@ __global__ __launch_bounds__(1024) void router_finalize_kernel(
 // ------------------------------------------------------------------ host side
 
 hipError_t launch_router_finalize(const float* partial, int nsplit, int n, int E, const float* offset,
-                                  int score, float* logits, float* scores, float* scores_t,
-                                  hipStream_t stream);
+                                  const float* noise, float noise_std, int score, float* logits,
+                                  float* scores, float* scores_t, hipStream_t stream);
 
 static int router_ncg(int E) { return E >= 256 ? 4 : (E > 64 ? 2 : 1); }
 
@@ -250,13 +262,16 @@ static int router_row_blocks(int n, int E) {
   return (n + rows - 1) / rows;
 }
 
-// Split K until there are at least 512 workgroups (each slice a
-// multiple of the 64-wide stage).
+// Split K until there are at least MOE_ROUTER_MIN_WGS workgroups (each
+// slice a multiple of the 64-wide stage).
+#ifndef MOE_ROUTER_MIN_WGS
+#define MOE_ROUTER_MIN_WGS 256
+#endif
 static int router_splits(int n, int d, int E) {
   const int blocks = router_row_blocks(n, E) * ((E + kRouterCols - 1) / kRouterCols);
   const int kb = d / kRouterBK;
   int s = 1;
-  while (s < kRouterSplitsMax && blocks * s < 512 && kb % (2 * s) == 0) s *= 2;
+  while (s < kRouterSplitsMax && blocks * s < MOE_ROUTER_MIN_WGS && kb % (2 * s) == 0) s *= 2;
   return s;
 }
 
@@ -268,9 +283,9 @@ size_t router_workspace_bytes(int n, int d, int E, int dtype) {
   return align256((size_t)E * d * sizeof(bf16_t)) + (s > 1 ? (size_t)s * n * E * sizeof(float) : 0);
 }
 
-hipError_t launch_router(const void* X, const void* Wg, int dtype, const float* offset, int n, int d,
-                         int E, int score, float* logits, float* scores, float* scores_t, void* ws,
-                         hipStream_t stream) {
+hipError_t launch_router(const void* X, const void* Wg, int dtype, const float* offset,
+                         const float* noise, float noise_std, int n, int d, int E, int score,
+                         float* logits, float* scores, float* scores_t, void* ws, hipStream_t stream) {
   const float* partial = logits;
   int nsplit = 1;
   const int64_t total = (int64_t)n * E;
@@ -295,13 +310,13 @@ hipError_t launch_router(const void* X, const void* Wg, int dtype, const float* 
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return launch_router_finalize(partial, nsplit, n, E, offset, score, logits, scores, scores_t,
-                                stream);
+  return launch_router_finalize(partial, nsplit, n, E, offset, noise, noise_std, score, logits, scores,
+                                scores_t, stream);
 }
 
 hipError_t launch_router_finalize(const float* partial, int nsplit, int n, int E, const float* offset,
-                                  int score, float* logits, float* scores, float* scores_t,
-                                  hipStream_t stream) {
+                                  const float* noise, float noise_std, int score, float* logits,
+                                  float* scores, float* scores_t, hipStream_t stream) {
   const size_t lds = scores_t ? (size_t)kFinRows * (E + 1) * sizeof(float) : 0;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&router_finalize_kernel),
@@ -309,7 +324,7 @@ hipError_t launch_router_finalize(const float* partial, int nsplit, int n, int E
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(router_finalize_kernel, dim3((n + kFinRows - 1) / kFinRows), dim3(1024), lds, stream, partial,
-                     nsplit, n, E, offset, score, logits, scores, scores_t);
+                     nsplit, n, E, offset, noise, noise_std, score, logits, scores, scores_t);
   return hipGetLastError();
 }
 

@@ -5,8 +5,9 @@
 // and its load-balance headache" (top-k along each row) and "The transposed
 // selection" / "The math" (G, I = TopK(S^T, k) along each column); page 5
 // "MoE routing strategies explained", strategies 1 (softmax over the k
-// selected scores as mixing weights), 2 (top-1), 4 (sigmoid scores, bias
-// used only when choosing, mixing weights from the raw scores) and 5
+// selected scores as mixing weights), 2 (top-1), 4 (sigmoid -- or, for
+// DeepSeek-V4, sqrtsoftplus -- scores, bias used only when choosing, mixing
+// weights from the raw scores) and 5
 // (group-limited routing: keep the best groups, then the top-k inside them).
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(256) void select_tc_kernel(const float* __restrict_
     if (a.score == 0) {
       key[j] = z[j];
     } else {
-      const float s = spec_sigmoid(z[j]);
+      const float s = spec_expert_score(z[j], a.score);
       key[j] = (bias && valid) ? s + bias[e] : s;
     }
     if (valid) {
@@ -135,10 +136,10 @@ __global__ __launch_bounds__(256) void select_tc_kernel(const float* __restrict_
       gate = spec_exp(sz[my_sel] - m) / s;
     }
   } else {
-    const float mine = spec_sigmoid(sz[my_sel]);
+    const float mine = spec_expert_score(sz[my_sel], a.score);
     if (a.norm_topk) {
       float s = 0.f;
-      for (int j = 0; j < a.k; ++j) s = s + spec_sigmoid(sz[__shfl(my_sel, j, 64)]);
+      for (int j = 0; j < a.k; ++j) s = s + spec_expert_score(sz[__shfl(my_sel, j, 64)], a.score);
       gate = mine / s;
     } else {
       gate = mine;
@@ -273,7 +274,8 @@ hipError_t launch_select_ec(const float* logits, const float* scores_t, int n, i
                             int32_t* I, float* G, void* ws, hipStream_t stream) {
   if (!scores_t) {
     float* st = static_cast<float*>(ws);
-    hipError_t err = launch_router_finalize(logits, 1, n, E, nullptr, 0, nullptr, nullptr, st, stream);
+    hipError_t err = launch_router_finalize(logits, 1, n, E, nullptr, nullptr, 0.f, 0, nullptr, nullptr, st,
+                                            stream);
     if (err != hipSuccess) return err;
     scores_t = st;
   }

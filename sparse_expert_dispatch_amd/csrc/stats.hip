@@ -10,7 +10,7 @@
 // computes
 //   lb_loss = lb_coef * E * sum_e f_e * P_e,  f_e = chosen_e / sum chosen,
 //             P_e = mean over tokens of the normalised score (softmax
-//             probability, or sigmoid / row sum of sigmoids),
+//             probability, or sigmoid / sqrtsoftplus score over its row sum),
 //   z_loss  = z_coef * mean_t (logsumexp_e z_te)^2,
 //   max_vio = (max_e load_e - mean load) / mean load,  load = kept rows,
 // plus kept / dropped counts and the experts-per-token histogram.
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(1024) void stats_rows_kernel(const float* __restric
     for (int j = 0; j < kMaxExpertRegs; ++j) {
       const bool valid = j < nj && lane + 64 * j < E;
       t[j] = valid ? spec_exp(z[j] - m) : 0.f;
-      u[j] = valid ? (score == 0 ? t[j] : spec_sigmoid(z[j])) : 0.f;
+      u[j] = valid ? (score == 0 ? t[j] : spec_expert_score(z[j], score)) : 0.f;
     }
     const float s_exp = row_tree_sum(t, P2);
     const float s_norm = score == 0 ? s_exp : row_tree_sum(u, P2);
@@ -234,6 +234,28 @@ hipError_t launch_balance_stats(const float* logits, const MapPtrs& m, int n, in
                      m.token_slot, n, E, score, part_P, part_Z, part_H);
   hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(kFinThreads), 0, stream, part_P, part_Z, part_H,
                      nb, n, E, k, dir, lb_coef, z_coef, m.expert_count, m.expert_offset, stats, hist);
+  return hipGetLastError();
+}
+
+// Loss-free balancing step (page 5 "MoE routing strategies explained",
+// strategy 4: after each step the bias drops for overloaded experts and
+// rises for idle ones): bias[e] -= gamma * sign(count[e] - n k / E), the sign
+// from the exact integer comparison count[e] * E vs n * k, so an expert
+// exactly at the mean keeps its bias.  One thread per expert.
+__global__ __launch_bounds__(256) void update_bias_kernel(const int32_t* __restrict__ count, int E,
+                                                          int64_t nk, float gamma, float* __restrict__ bias) {
+#pragma clang fp contract(off)
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  const int64_t diff = (int64_t)count[e] * E - nk;
+  const float sgn = diff > 0 ? 1.0f : (diff < 0 ? -1.0f : 0.0f);
+  bias[e] = bias[e] - gamma * sgn;
+}
+
+hipError_t launch_update_bias(const int32_t* expert_count, int n, int E, int k, float gamma, float* bias,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(update_bias_kernel, dim3((E + 255) / 256), dim3(256), 0, stream, expert_count, E,
+                     (int64_t)n * k, gamma, bias);
   return hipGetLastError();
 }
 

@@ -24,8 +24,9 @@ class MoELayer:
     `cfg` carries the layer's shape and routing options (the fields of
     sparse_expert_dispatch_amd.workloads.MoEConfig); `weights` holds device
     tensors wg [d,E], w1 [E, f|2f, d], w2 [E, d, f] and optionally
-    logit_offset [E], sel_bias [E], shared_w1, shared_w2.  bf16 tensors may be
-    torch.bfloat16 or raw uint16 bit patterns."""
+    logit_offset [E], sel_bias [E], noise [n,E] (standard normals of noisy
+    top-k, scaled by cfg.noise_std), shared_w1, shared_w2.  bf16 tensors may
+    be torch.bfloat16 or raw uint16 bit patterns."""
 
     def __init__(self, cfg, weights: dict, device="cuda"):
         self.cfg = cfg
@@ -38,10 +39,15 @@ class MoELayer:
         if tc and cfg.capacity_factor is not None:
             cap = N.moe_tc_capacity(n, self.k, E, cfg.capacity_factor)
         self.capacity = cap
+        score = {"softmax": N.MOE_SOFTMAX, "sigmoid": N.MOE_SIGMOID,
+                 "sqrtsoftplus": N.MOE_SQRTSOFTPLUS}[cfg.score]
+        order = {"token": N.MOE_TOKEN_MAJOR,
+                 "rank": N.MOE_RANK_MAJOR}[getattr(cfg, "capacity_order", "token")]
         self.rcfg = N.make_cfg(n, d, E, self.k,
-                               N.MOE_TOKEN_CHOICE if tc else N.MOE_EXPERT_CHOICE,
-                               N.MOE_SOFTMAX if cfg.score == "softmax" else N.MOE_SIGMOID,
-                               cfg.n_group, cfg.topk_group, cfg.group_topm, int(cfg.norm_topk), cap)
+                               N.MOE_TOKEN_CHOICE if tc else N.MOE_EXPERT_CHOICE, score,
+                               cfg.n_group, cfg.topk_group, cfg.group_topm, int(cfg.norm_topk), cap,
+                               order if tc else N.MOE_TOKEN_MAJOR)
+        self.noise_std = float(getattr(cfg, "noise_std", 0.0))
         self.dtype_code = N.MOE_BF16 if cfg.dtype == "bf16" else N.MOE_F32
         self.act = N.MOE_SWIGLU if cfg.act == "swiglu" else N.MOE_GELU
         edt = torch.bfloat16 if self.dtype_code == N.MOE_BF16 else torch.float32
@@ -75,8 +81,9 @@ class MoELayer:
     def route(self, x, stream=None):
         w = self.w
         tc = self.rcfg.dir == N.MOE_TOKEN_CHOICE
+        noise = w.get("noise") if self.noise_std else None
         N.moe_router(x, w["wg"], w.get("logit_offset"), self.rcfg, self.logits, None,
-                     None if tc else self.scores_t, self.ws_router, stream)
+                     None if tc else self.scores_t, self.ws_router, stream, noise, self.noise_std)
         N.moe_select(self.logits, None if tc else self.scores_t, w.get("sel_bias"), self.rcfg,
                      self.sel_idx, self.sel_gate, self.ws_route, stream)
         N.moe_build_map(self.sel_idx, self.sel_gate, self.rcfg, self.map, self.ws_route, stream)
@@ -97,6 +104,11 @@ class MoELayer:
     def balance_stats(self, stream=None):
         N.moe_balance_stats(self.logits, self.map, self.rcfg, self.cfg.lb_coef, self.cfg.z_coef,
                             self.stats, self.hist, self.ws_route, stream)
+
+    def update_bias(self, gamma: float, stream=None):
+        """Loss-free balancing step on weights["sel_bias"] from this step's
+        per-expert loads (after route())."""
+        N.moe_update_bias(self.map.expert_count, self.rcfg, gamma, self.w["sel_bias"], stream)
 
     def forward(self, x: torch.Tensor, residual: bool = True, stats: bool = True,
                 stream=None) -> torch.Tensor:

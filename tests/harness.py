@@ -43,7 +43,8 @@ def widen(a: np.ndarray) -> np.ndarray:
 
 def upload(cfg, inp: dict) -> dict:
     w = {"wg": to_device(inp["wg"]), "w1": to_device(inp["w1"]), "w2": to_device(inp["w2"]),
-         "logit_offset": to_device(inp.get("logit_offset")), "sel_bias": to_device(inp.get("sel_bias"))}
+         "logit_offset": to_device(inp.get("logit_offset")), "sel_bias": to_device(inp.get("sel_bias")),
+         "noise": to_device(inp.get("noise"))}
     if cfg.shared_f:
         w["shared_w1"] = to_device(inp["shared_w1"])
         w["shared_w2"] = to_device(inp["shared_w2"])
@@ -138,7 +139,8 @@ def check_map(g: dict, ref_map: dict):
 def compare_all(cfg, inp: dict, g: dict, full_ffn: bool = True, sample_tokens=None):
     """Stage-by-stage comparison of a GPU run `g` with the oracle."""
     t0 = time.time()
-    z_ref = O.router_logits(inp["x"], inp["wg"], inp.get("logit_offset"))
+    z_ref = O.router_logits(inp["x"], inp["wg"], inp.get("logit_offset"), inp.get("noise"),
+                            getattr(cfg, "noise_std", 0.0))
     check_logits(g["logits"], z_ref)
     z = g["logits"]
     bf16 = cfg.dtype == "bf16"
@@ -149,7 +151,8 @@ def compare_all(cfg, inp: dict, g: dict, full_ffn: bool = True, sample_tokens=No
                                           cfg.topk_group, cfg.group_topm, cfg.norm_topk)
         cap = O.tc_capacity(cfg.n, cfg.k, cfg.E, cfg.capacity_factor)
         assert g["capacity"] == (cap if cfg.capacity_factor is not None else -1)
-        rmap = O.build_map_token_choice(idx, gate, cfg.E, None if cfg.capacity_factor is None else cap)
+        rmap = O.build_map_token_choice(idx, gate, cfg.E, None if cfg.capacity_factor is None else cap,
+                                        getattr(cfg, "capacity_order", "token"))
         k = cfg.k
     else:
         k = O.ec_k(cfg.n, cfg.c, cfg.E)

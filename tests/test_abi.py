@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for name in names:
         assert hasattr(L, name), name
     assert sorted(N.EXPORTED) == names
@@ -65,8 +65,9 @@ def test_max_slots(L):
 FAKE = 0x10000   # a non-NULL, 16-byte aligned address that is never dereferenced
 
 
-def _router(L, cfg, dtype=N.MOE_BF16, x=FAKE, ws=None, wsb=0):
-    return L.moe_router(x, FAKE, dtype, None, ctypes.byref(cfg), FAKE, None, None, ws, wsb, None)
+def _router(L, cfg, dtype=N.MOE_BF16, x=FAKE, ws=None, wsb=0, noise=None, noise_std=0.0):
+    return L.moe_router(x, FAKE, dtype, None, noise, noise_std, ctypes.byref(cfg), FAKE, None, None, ws,
+                        wsb, None)
 
 
 @pytest.mark.parametrize("bad, status", [
@@ -79,6 +80,7 @@ def _router(L, cfg, dtype=N.MOE_BF16, x=FAKE, ws=None, wsb=0):
     (dict(capacity=-2), N.MOE_ERR_INVALID_ARG),
     (dict(score=7), N.MOE_ERR_INVALID_ARG),
     (dict(group_topm=0), N.MOE_ERR_INVALID_ARG),
+    (dict(capacity_order=2), N.MOE_ERR_INVALID_ARG),
 ])
 def test_config_validation(L, bad, status):
     kw = dict(n=256, d=64, E=8, k=2)
@@ -94,6 +96,25 @@ def test_expert_choice_validation(L):
     assert _router(L, cfg, N.MOE_F32) == N.MOE_ERR_INVALID_ARG
     cfg = N.make_cfg(100, 64, 8, 10, direction=N.MOE_EXPERT_CHOICE, score=N.MOE_SIGMOID)
     assert _router(L, cfg, N.MOE_F32) == N.MOE_ERR_UNSUPPORTED
+
+
+def test_routing_variant_validation(L):
+    # sqrtsoftplus scores and rank-major capacity are token-choice options
+    cfg = N.make_cfg(100, 64, 8, 10, direction=N.MOE_EXPERT_CHOICE, score=N.MOE_SQRTSOFTPLUS)
+    assert _router(L, cfg, N.MOE_F32) == N.MOE_ERR_UNSUPPORTED
+    cfg = N.make_cfg(100, 64, 8, 10, direction=N.MOE_EXPERT_CHOICE, capacity_order=N.MOE_RANK_MAJOR)
+    assert _router(L, cfg, N.MOE_F32) == N.MOE_ERR_INVALID_ARG
+    # noise needs a finite scale; without noise the scale is ignored
+    cfg = N.make_cfg(256, 64, 8, 2, score=N.MOE_SQRTSOFTPLUS, capacity_order=N.MOE_RANK_MAJOR)
+    assert _router(L, cfg, N.MOE_F32, noise=FAKE, noise_std=float("nan")) == N.MOE_ERR_INVALID_ARG
+    assert _router(L, cfg, N.MOE_F32, noise=FAKE, noise_std=float("inf")) == N.MOE_ERR_INVALID_ARG
+    # the bias update: token choice only, non-NULL buffers, finite gamma
+    assert L.moe_update_bias(FAKE, ctypes.byref(cfg), 0.001, None, None) == N.MOE_ERR_INVALID_ARG
+    assert L.moe_update_bias(FAKE, ctypes.byref(cfg), float("nan"), FAKE, None) == N.MOE_ERR_INVALID_ARG
+    ec = N.make_cfg(100, 64, 8, 10, direction=N.MOE_EXPERT_CHOICE)
+    assert L.moe_update_bias(FAKE, ctypes.byref(ec), 0.001, FAKE, None) == N.MOE_ERR_INVALID_ARG
+    bad = N.make_cfg(256, 64, 8, 9)
+    assert L.moe_update_bias(FAKE, ctypes.byref(bad), 0.001, FAKE, None) == N.MOE_ERR_INVALID_ARG
 
 
 def test_null_pointers_and_unsupported_shapes(L):

@@ -72,6 +72,12 @@ def test_expert_choice_sparse_capacity_leaves_tokens_unselected():
     assert g["stats"][6] > 0                                       # tokens no expert picked
 
 
+def test_expert_choice_many_tokens():
+    # 12000 tokens: the offset scan of the expert-choice map runs three
+    # passes of 4096 tokens, the column select holds 12000 keys in LDS
+    _run(W.SMALL_CONFIGS[2].scaled("ec_n12000", n=12000, d=128, E=64, f=64))
+
+
 def test_wide_expert_counts():
     # 256 sigmoid experts (score sums run partly in registers) and 128
     # expert-choice experts (softmax scores and their transpose over 128)

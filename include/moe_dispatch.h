@@ -201,8 +201,8 @@ moe_status_t moe_select(const float *logits, const float *scores_t, const float 
  * rank, tokens in order within a rank (MOE_RANK_MAJOR: first choices have
  * priority); an assignment is kept iff fewer than `capacity` earlier
  * arrivals went to its expert (page 1 "Dropped tokens flow in opposite
- * directions": tokens arriving after the buffer fills skip the expert and
- * ride the residual); capacity -1 keeps all (dropless).
+ * directions": an assignment that reaches a full buffer is not computed,
+ * its token keeps the residual); capacity -1 keeps all (dropless).
  * Expert choice: slot e*k + j holds I[e,j].  Fills every field of `map`;
  * kept slots are expert-major and in arrival order within an expert. */
 moe_status_t moe_build_map(const int32_t *sel_idx, const float *sel_gate, const moe_route_cfg_t *cfg,
@@ -249,8 +249,8 @@ moe_status_t moe_balance_stats(const float *logits, const moe_route_map_t *map,
                                const moe_route_cfg_t *cfg, float lb_coef, float z_coef, float *stats,
                                int32_t *hist, void *ws, size_t ws_bytes, void *stream);
 
-/* Auxiliary-loss-free balancing (page 5 strategy 4: after each step the
- * bias drops for overloaded experts and rises for idle ones).  Token
+/* Auxiliary-loss-free balancing (page 5 strategy 4: once per step, the bias
+ * of an over-used expert goes down and that of an under-used one up).  Token
  * choice: bias[e] -= gamma * sign(expert_count[e] - n*k/E), the sign taken
  * exactly in integers (an expert exactly at the mean keeps its bias), one
  * fp32 subtraction per expert, in place on the device.  expert_count [E]

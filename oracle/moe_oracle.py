@@ -10,9 +10,9 @@ It is the plain definition of what the layer computes, written out slowly:
 
 * router     S = softmax(X W_g) (or a sigmoid per expert)      -- page 2 "The math",
                                                                   page 5 strategy 4
-* selection  token choice: top-k along the expert axis of each row
+* selection  token choice: the k best experts of each token (a row)
              (page 2 "Token-choice and its load-balance headache"; page 5
-             strategies 1, 2, 4, 5); expert choice: top-k along the token axis
+             strategies 1, 2, 4, 5); expert choice: the k best tokens of each expert
              of each column, k = n c / E (page 1 "Who picks whom"; page 2
              "The transposed selection", "The math")
 * routing    capacity per expert, tokens arriving after the buffer is full skip
@@ -120,8 +120,8 @@ def softmax_rows(z: np.ndarray) -> np.ndarray:
 
 
 def sigmoid(z: np.ndarray) -> np.ndarray:
-    """Specified sigmoid 1 / (1 + spec_exp(-z)) (page 5 strategy 4 scores
-    experts with a sigmoid instead of a softmax)."""
+    """Specified sigmoid 1 / (1 + spec_exp(-z)) (page 5 strategy 4: DeepSeek-V3
+    gives every expert its own sigmoid score in place of a softmax row)."""
     z = np.asarray(z, dtype=np.float32)
     with np.errstate(over="ignore", divide="ignore"):
         return (f32(1.0) / (f32(1.0) + spec_exp(-z))).astype(np.float32)
@@ -525,8 +525,9 @@ def balance_stats(z: np.ndarray, rmap: dict, direction: str, k: int, score: str,
 
 
 def update_bias(bias: np.ndarray, expert_count: np.ndarray, n: int, k: int, gamma: float):
-    """Auxiliary-loss-free balancing step (page 5 strategy 4: after each step
-    the bias drops for overloaded experts and rises for idle ones).  Reading:
+    """Auxiliary-loss-free balancing step (page 5 strategy 4: once per step,
+    the bias of an over-used expert goes down and that of an under-used one
+    up).  Reading:
     load_e = assignments chosen for expert e this step (before capacity
     drops), mean = n k / E; b_e <- b_e - gamma * sign(load_e - mean), with the
     sign taken exactly in integers (sign(load_e * E - n * k)), so an expert

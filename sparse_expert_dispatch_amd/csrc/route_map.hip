@@ -4,10 +4,10 @@
 //
 // MoE-routing pages: page 1 "Token choice vs expert choice routing",
 // section "Dropped tokens flow in opposite directions" (a fixed per-expert
-// buffer; tokens arriving after it fills skip the expert and pass through
-// on the residual; dropless computes every assignment); page 5 "MoE routing
-// strategies explained", strategy 2 (overflow tokens skip the layer through
-// the residual connection); page 2 "Expert choice routing", section "The
+// buffer; an assignment reaching it when full is not computed and its token
+// keeps the residual; dropless computes every assignment); page 5 "MoE
+// routing strategies explained", strategy 2 (tokens beyond capacity bypass
+// the expert by way of the residual); page 2 "Expert choice routing", section "The
 // math" (P = onehot(I): slot e*k + j carries token I[e, j]).
 //
 // Token choice runs as a stable counting sort of the n*k arrivals by expert.

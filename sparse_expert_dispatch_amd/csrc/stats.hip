@@ -1,8 +1,9 @@
 // Routing-balance statistics.
 //
 // MoE-routing pages: page 1 "Token choice vs expert choice routing", section
-// "What each direction guarantees" (load-balancing loss at 0.01 and router
-// z-loss at 0.001; a balanced router gives every expert the same share);
+// "What each direction guarantees" (coefficients 0.01 for the load-balancing
+// loss and 0.001 for the z-loss; a balanced router gives every expert the
+// same share);
 // page 4 "How MoE routing strategies ...", section "Pitfalls" (watch
 // per-expert token counts; one expert with 80% of the traffic means the
 // router collapsed); page 5 "MoE routing strategies explained", TL;DR
@@ -238,8 +239,8 @@ hipError_t launch_balance_stats(const float* logits, const MapPtrs& m, int n, in
 }
 
 // Loss-free balancing step (page 5 "MoE routing strategies explained",
-// strategy 4: after each step the bias drops for overloaded experts and
-// rises for idle ones): bias[e] -= gamma * sign(count[e] - n k / E), the sign
+// strategy 4: once per step, the bias of an over-used expert goes down and
+// that of an under-used one up): bias[e] -= gamma * sign(count[e] - n k / E), the sign
 // from the exact integer comparison count[e] * E vs n * k, so an expert
 // exactly at the mean keeps its bias.  One thread per expert.
 __global__ __launch_bounds__(256) void update_bias_kernel(const int32_t* __restrict__ count, int E,

@@ -40,6 +40,9 @@
  *    [d, E] layout.
  *  - Inputs must be finite.  Results are deterministic: the same inputs give
  *    the same bits on every run (no floating-point atomics).
+ *  - A tensor argument of zero elements may be any non-NULL address (it is
+ *    never dereferenced); moe_dispatch and moe_expert_ffn with M_max = 0
+ *    return MOE_OK at once and ignore their tensor arguments.
  */
 #ifndef MOE_DISPATCH_H
 #define MOE_DISPATCH_H
@@ -122,7 +125,10 @@ typedef struct {
 
 /* Tokens per expert under expert choice, k = n c / E (page 1 "Who picks
  * whom"; page 2 "A worked example"), rounded half up.  Returns -1 on
- * invalid input (n, E <= 0, c <= 0). */
+ * invalid input (n, E <= 0, c <= 0).  A batch with n c / E < 1/2 gets
+ * k = 0, which every call accepts for expert choice: no expert takes a
+ * token, the map has no slots (M_max = 0; moe_dispatch and moe_expert_ffn
+ * do nothing), and the combine returns the residual plus the shared expert. */
 int32_t moe_ec_k(int32_t n, double c, int32_t E);
 
 /* Per-expert capacity under token choice: cf * k * n / E (the balanced load

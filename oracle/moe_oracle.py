@@ -495,7 +495,7 @@ def balance_stats(z: np.ndarray, rmap: dict, direction: str, k: int, score: str,
     n, E = z64.shape
     count = rmap["expert_count"].astype(np.float64)
     load = np.diff(rmap["expert_offset"].astype(np.int64)).astype(np.float64)
-    f = count / count.sum()
+    f = count / count.sum() if count.sum() > 0 else np.zeros_like(count)   # nothing chosen: f = 0
     if score == "softmax":
         zm = z64 - z64.max(axis=1, keepdims=True)
         p = np.exp(zm) / np.exp(zm).sum(axis=1, keepdims=True)

@@ -109,7 +109,17 @@ def _ptr(t: Optional[torch.Tensor], name: str, dtypes=None) -> Optional[int]:
         raise ValueError(f"{name} must be contiguous")
     if dtypes is not None and t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
-    return t.data_ptr()
+    return _addr(t)
+
+
+def _addr(t: torch.Tensor) -> int:
+    """Device address of t.  A zero-sized view (see alloc) reports address 0;
+    pass the address of its backing storage instead, so zero-length arrays
+    are never NULL at the C ABI."""
+    p = t.data_ptr()
+    if p == 0 and t.numel() == 0:
+        p = t.untyped_storage().data_ptr() + t.storage_offset() * t.element_size()
+    return p
 
 
 _BF16_STORAGE = (torch.bfloat16, torch.uint16, torch.int16)
@@ -151,6 +161,17 @@ def make_cfg(n, d, E, k, direction=MOE_TOKEN_CHOICE, score=MOE_SOFTMAX, n_group=
                     int(capacity_order))
 
 
+def alloc(shape, dtype, device="cuda") -> torch.Tensor:
+    """torch.empty(shape) backed by at least one element: zero-sized tensors
+    (expert choice with k = 0 has no slots) are views of a one-element
+    buffer, whose address the marshalling passes, so the C ABI's non-NULL
+    checks hold for them too."""
+    numel = 1
+    for s in shape:
+        numel *= int(s)
+    return torch.empty(max(numel, 1), dtype=dtype, device=device)[:numel].view(*shape)
+
+
 class RouteMap:
     """Device buffers of a routing map (allocated with torch)."""
 
@@ -164,15 +185,15 @@ class RouteMap:
         self.M_max = M
         self.expert_count = torch.empty(E, **i32)
         self.expert_offset = torch.empty(E + 1, **i32)
-        self.slot_token = torch.empty(M, **i32)
-        self.slot_gate = torch.empty(M, dtype=torch.float32, device=device)
-        self.assign_slot = torch.empty((n, k) if cfg.dir == MOE_TOKEN_CHOICE else (E, k), **i32)
+        self.slot_token = alloc((M,), torch.int32, device)
+        self.slot_gate = alloc((M,), torch.float32, device)
+        self.assign_slot = alloc((n, k) if cfg.dir == MOE_TOKEN_CHOICE else (E, k), torch.int32, device)
         self.token_offset = torch.empty(n + 1, **i32)
-        self.token_slot = torch.empty(moe_token_list_len(cfg), **i32)
+        self.token_slot = alloc((moe_token_list_len(cfg),), torch.int32, device)
         self.n_kept = torch.empty(1, **i32)
 
     def c(self) -> RouteMapC:
-        return RouteMapC(*[getattr(self, f).data_ptr() for f in self.FIELDS])
+        return RouteMapC(*[_addr(getattr(self, f)) for f in self.FIELDS])
 
 
 # ---------------------------------------------------------------- the C ABI, one to one

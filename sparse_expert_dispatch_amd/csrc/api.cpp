@@ -45,8 +45,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 moe_status_t check_cfg(const moe_route_cfg_t* c) {
   REQUIRE(c != nullptr, "cfg is NULL");
-  REQUIRE(c->n > 0 && c->d > 0 && c->E > 0 && c->k > 0, "n, d, E, k must be positive (n=%d d=%d E=%d k=%d)",
-          c->n, c->d, c->E, c->k);
+  // k = 0 is the degenerate expert choice of a batch too small for any
+  // expert to take a token (n c / E rounds to 0)
+  REQUIRE(c->n > 0 && c->d > 0 && c->E > 0 && (c->k > 0 || (c->k == 0 && c->dir == MOE_EXPERT_CHOICE)),
+          "n, d, E, k must be positive (n=%d d=%d E=%d k=%d; k = 0 only for expert choice)", c->n, c->d,
+          c->E, c->k);
   REQUIRE(c->dir == MOE_TOKEN_CHOICE || c->dir == MOE_EXPERT_CHOICE, "dir must be 0 or 1");
   REQUIRE(c->score == MOE_SOFTMAX || c->score == MOE_SIGMOID || c->score == MOE_SQRTSOFTPLUS,
           "score must be MOE_SOFTMAX, MOE_SIGMOID or MOE_SQRTSOFTPLUS");
@@ -155,7 +158,7 @@ moe_status_t moe_route_workspace_size(const moe_route_cfg_t* cfg, size_t* bytes)
 moe_status_t moe_ffn_workspace_size(int64_t M_max, int32_t E, int32_t d, int32_t f, int32_t act,
                                     int32_t dtype, size_t* bytes) {
   REQUIRE(bytes != nullptr, "bytes is NULL");
-  REQUIRE(M_max > 0 && E > 0 && d > 0 && f > 0, "M_max, E, d, f must be positive");
+  REQUIRE(M_max >= 0 && E > 0 && d > 0 && f > 0, "E, d, f must be positive, M_max non-negative");
   REQUIRE(act == MOE_GELU || act == MOE_SWIGLU, "act must be MOE_GELU or MOE_SWIGLU");
   REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, "dtype must be MOE_F32 or MOE_BF16");
   *bytes = moe::ffn_workspace_bytes(M_max, E, d, f, act, dtype);
@@ -186,6 +189,7 @@ moe_status_t moe_select(const float* logits, const float* scores_t, const float*
                         size_t ws_bytes, void* stream) {
   moe_status_t st = check_cfg(cfg);
   if (st != MOE_OK) return st;
+  if (cfg->k == 0) return MOE_OK;                 // expert choice with nothing to select
   REQUIRE(sel_idx && sel_gate, "sel_idx and sel_gate must be non-NULL");
   if (cfg->dir == MOE_TOKEN_CHOICE) {
     REQUIRE(logits, "logits must be non-NULL");
@@ -211,7 +215,7 @@ moe_status_t moe_build_map(const int32_t* sel_idx, const float* sel_gate, const 
   if (st != MOE_OK) return st;
   st = check_map(map);
   if (st != MOE_OK) return st;
-  REQUIRE(sel_idx && sel_gate, "sel_idx and sel_gate must be non-NULL");
+  REQUIRE((sel_idx && sel_gate) || cfg->k == 0, "sel_idx and sel_gate must be non-NULL");
   const size_t need = moe::map_workspace_bytes(cfg->dir, cfg->n, cfg->E, cfg->k);
   if (!ws || ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "build_map needs %zu workspace bytes, got %zu", need, ws_bytes);
@@ -227,11 +231,12 @@ moe_status_t moe_build_map(const int32_t* sel_idx, const float* sel_gate, const 
 
 moe_status_t moe_dispatch(const void* X, int32_t dtype, int32_t n, int32_t d, const moe_route_map_t* map,
                           int64_t M_max, void* X_perm, void* stream) {
+  REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, "dtype must be MOE_F32 or MOE_BF16");
+  REQUIRE(n > 0 && d > 0 && M_max >= 0, "n, d must be positive, M_max non-negative");
+  REQUIRE(M_max <= (int64_t)INT32_MAX * 4, "M_max too large");
+  if (M_max == 0) return MOE_OK;                  // no slots: nothing to move
   REQUIRE(X && X_perm, "X and X_perm must be non-NULL");
   REQUIRE(map && map->slot_token && map->n_kept, "map->slot_token and map->n_kept must be non-NULL");
-  REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, "dtype must be MOE_F32 or MOE_BF16");
-  REQUIRE(n > 0 && d > 0 && M_max > 0, "n, d, M_max must be positive");
-  REQUIRE(M_max <= (int64_t)INT32_MAX * 4, "M_max too large");
   const int eb = dtype == MOE_BF16 ? 2 : 4;
   if (((int64_t)d * eb) % 16 == 0)
     REQUIRE(aligned16(X) && aligned16(X_perm), "X and X_perm must be 16-byte aligned");
@@ -243,8 +248,9 @@ moe_status_t moe_dispatch(const void* X, int32_t dtype, int32_t n, int32_t d, co
 moe_status_t moe_expert_ffn(const void* X_perm, int32_t dtype, const int32_t* expert_offset, int32_t E,
                             int32_t d, int32_t f, int32_t act, const void* W1, const void* W2,
                             int64_t M_max, void* Y_perm, void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(E > 0 && d > 0 && f > 0 && M_max >= 0, "E, d, f must be positive, M_max non-negative");
+  if (M_max == 0) return MOE_OK;                  // no rows: nothing to compute
   REQUIRE(X_perm && expert_offset && W1 && W2 && Y_perm, "tensor arguments must be non-NULL");
-  REQUIRE(E > 0 && d > 0 && f > 0 && M_max > 0, "E, d, f, M_max must be positive");
   REQUIRE(act == MOE_GELU || act == MOE_SWIGLU, "act must be MOE_GELU or MOE_SWIGLU");
   REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, "dtype must be MOE_F32 or MOE_BF16");
   REQUIRE(M_max <= INT32_MAX, "M_max must fit in int32");

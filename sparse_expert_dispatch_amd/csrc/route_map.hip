@@ -216,6 +216,16 @@ __global__ __launch_bounds__(256) void ec_token_fill_kernel(const int32_t* __res
   token_slot[token_offset[t] + before] = (int32_t)s;
 }
 
+// Expert choice with k = 0 (a batch too small for any expert to take a
+// token): every count, offset and token list is empty.
+__global__ __launch_bounds__(256) void ec_empty_map_kernel(int n, int E, MapPtrs m) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < E) m.expert_count[i] = 0;
+  if (i <= E) m.expert_offset[i] = 0;
+  if (i <= n) m.token_offset[i] = 0;
+  if (i == 0) *m.n_kept = 0;
+}
+
 // ---------------------------------------------------------------- host side
 
 static int chunks_of(int64_t M) { return (int)((M + kMapChunk - 1) / kMapChunk); }
@@ -245,6 +255,11 @@ hipError_t launch_build_map_tc(const int32_t* idx, const float* gate, int n, int
 
 hipError_t launch_build_map_ec(const int32_t* I, const float* G, int n, int E, int k,
                                const MapPtrs& m, void* ws, hipStream_t stream) {
+  if (k == 0) {
+    hipLaunchKernelGGL(ec_empty_map_kernel, dim3((unsigned)((max(n, E) + 1 + 255) / 256)), dim3(256), 0,
+                       stream, n, E, m);
+    return hipGetLastError();
+  }
   const int W = (E + 31) / 32;
   uint32_t* mask = static_cast<uint32_t*>(ws);
   const int64_t words = (int64_t)n * W;

@@ -180,7 +180,8 @@ __global__ __launch_bounds__(kFinThreads) void stats_final_kernel(
   if (tid < E) {
     float v = 0.f;
     for (int q = 0; q < gP; ++q) v = v + redP[q * cpP + tid];
-    fp[tid] = ((float)cnt / (float)ch) * (v / (float)n);
+    // f_e = 0 when nothing was chosen (expert choice with k = 0)
+    fp[tid] = ch > 0 ? ((float)cnt / (float)ch) * (v / (float)n) : 0.f;
   }
   // z partials: a halving tree over the 1024 thread sums
   for (int s = kFinThreads / 2; s >= 1; s >>= 1) {

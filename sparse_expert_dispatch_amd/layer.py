@@ -58,11 +58,11 @@ class MoELayer:
         self.logits = torch.empty((n, E), **f32)
         self.scores_t = torch.empty((E, n), **f32) if not tc else None
         sel_shape = (n, self.k) if tc else (E, self.k)
-        self.sel_idx = torch.empty(sel_shape, **i32)
-        self.sel_gate = torch.empty(sel_shape, **f32)
+        self.sel_idx = N.alloc(sel_shape, torch.int32, dev)
+        self.sel_gate = N.alloc(sel_shape, torch.float32, dev)
         self.map = N.RouteMap(self.rcfg, dev)
-        self.x_perm = torch.empty((self.M_max, d), dtype=edt, device=dev)
-        self.y_perm = torch.empty((self.M_max, d), dtype=edt, device=dev)
+        self.x_perm = N.alloc((self.M_max, d), edt, dev)
+        self.y_perm = N.alloc((self.M_max, d), edt, dev)
         self.out = torch.empty((n, d), dtype=edt, device=dev)
         self.stats = torch.empty(N.MOE_NSTATS, **f32)
         self.hist = torch.empty(E + 1, **i32)

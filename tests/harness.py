@@ -217,7 +217,7 @@ def compare_all(cfg, inp: dict, g: dict, full_ffn: bool = True, sample_tokens=No
     # combine on its own: the device's expert outputs summed by the oracle;
     # the only difference left is one rounding of the fp32 sum to `dtype`
     gb = widen(g["branch"][tokens])
-    y_dev = widen(g["y_perm"])
+    y_dev = widen(g["y_perm"][:rmap["n_kept"]])          # rows past n_kept are never written
     sh_dev = widen(g["shared"]) if cfg.shared_f else None
     comb = np.zeros((len(tokens), cfg.d))
     for i, t in enumerate(tokens):

@@ -8,10 +8,21 @@ on one HIP stream, inputs and weights resident in HBM.
 Default workload: expert choice, bf16, n = 4096 tokens, d = 2048, 64 experts,
 capacity factor 2 (128 tokens per expert), GELU experts d -> 4096 -> d.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config 2|1..5|decode] [--no-cpu-baseline]
+
+--config decode times a decode step instead: 64 tokens, top-8 of 64 SwiGLU
+experts (d = 2048, f = 1024), where the grouped GEMM streams the weights of
+the experts the batch touches.
+
+A timed step is three parts (routing: router .. dispatch; the expert FFN;
+combine + statistics) with a HIP event between them on the layer's stream.
+By default the library calls are launched one by one; --graph replays each
+part as a captured HIP graph instead (on this stack that measured slower:
+the graph launches cost more than the direct launches they replace).
 
 Prints one JSON line: tokens/s over exactly K timed steps, the roofline of the
-dominant step (the expert FFN call), per-stage times, and the CPU oracle's
+dominant step (the expert FFN call, timed by the events around it), per-call
+times from eager steps run before the timed region, and the CPU oracle's
 throughput on the same workload for reference.
 """
 from __future__ import annotations
@@ -35,13 +46,15 @@ STAGES = ("router", "select", "build_map", "dispatch", "expert_ffn", "combine", 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expert_ffn_traffic.json")
 
 
-def algorithmic(cfg, k, M):
-    """Compulsory HBM bytes and FLOPs of each stage (each tensor touched once)."""
+def algorithmic(cfg, k, M, touched=None):
+    """Compulsory HBM bytes and FLOPs of each stage (each tensor touched once;
+    the FFN reads the weights of the `touched` experts, those with rows)."""
     b = 2 if cfg.dtype == "bf16" else 4
     n, d, E, f = cfg.n, cfg.d, cfg.E, cfg.f
+    touched = E if touched is None else touched
     w1r = 2 * f if cfg.act == "swiglu" else f
     flops_ffn = 2.0 * M * d * w1r + 2.0 * M * f * d
-    bytes_ffn = E * (w1r * d + d * f) * b + M * d * b + 2 * M * f * b + M * d * b
+    bytes_ffn = touched * (w1r * d + d * f) * b + M * d * b + 2 * M * f * b + M * d * b
     if cfg.shared_f:
         sr = 2 * cfg.shared_f if cfg.act == "swiglu" else cfg.shared_f
         flops_ffn += 2.0 * n * d * sr + 2.0 * n * cfg.shared_f * d
@@ -85,8 +98,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2, the headline one)")
+    ap.add_argument("--config", default="2",
+                    help="workload 1..5 (default 2, the headline one) or 'decode' (64 tokens, top-8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time HIP-graph replays of the three parts instead of direct launches")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -101,7 +117,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     N.lib()
-    cfg = W.FULL_CONFIGS[args.config]
+    cfg = W.FULL_CONFIGS[int(args.config)] if args.config.isdigit() else W.EXTRA_CONFIGS[args.config]
     print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     inp = W.gen_inputs(cfg)
     w1_host, w2_host = inp.pop("w1"), inp.pop("w2")
@@ -124,55 +140,80 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step(ev=None):
-        if ev is None:
-            layer.forward(x, residual=True)
-            return
-        ev[0].record(stream)
-        w = layer.w
-        tc = layer.rcfg.dir == N.MOE_TOKEN_CHOICE
-        N.moe_router(x, w["wg"], w.get("logit_offset"), layer.rcfg, layer.logits, None,
-                     None if tc else layer.scores_t, layer.ws_router)
-        ev[1].record(stream)
-        N.moe_select(layer.logits, None if tc else layer.scores_t, w.get("sel_bias"), layer.rcfg,
-                     layer.sel_idx, layer.sel_gate, layer.ws_route)
-        ev[2].record(stream)
-        N.moe_build_map(layer.sel_idx, layer.sel_gate, layer.rcfg, layer.map, layer.ws_route)
-        ev[3].record(stream)
-        N.moe_dispatch(x, layer.map, layer.x_perm)
-        ev[4].record(stream)
+    w = layer.w
+    tc = layer.rcfg.dir == N.MOE_TOKEN_CHOICE
+    # the step in three parts: routing (router .. dispatch), the expert FFN,
+    # and combine + statistics; each part is one or more library calls
+    calls_route = [
+        lambda: N.moe_router(x, w["wg"], w.get("logit_offset"), layer.rcfg, layer.logits, None,
+                             None if tc else layer.scores_t, layer.ws_router),
+        lambda: N.moe_select(layer.logits, None if tc else layer.scores_t, w.get("sel_bias"), layer.rcfg,
+                             layer.sel_idx, layer.sel_gate, layer.ws_route),
+        lambda: N.moe_build_map(layer.sel_idx, layer.sel_gate, layer.rcfg, layer.map, layer.ws_route),
+        lambda: N.moe_dispatch(x, layer.map, layer.x_perm),
+    ]
+
+    def ffn_part():
         N.moe_expert_ffn(layer.x_perm, layer.map.expert_offset, w["w1"], w["w2"], layer.act,
                          layer.y_perm, layer.ws_ffn)
         if layer.shared:
             N.moe_expert_ffn(x, layer.shared_offsets, w["shared_w1"], w["shared_w2"], layer.act,
                              layer.shared_out, layer.ws_shared)
-        ev[5].record(stream)
-        layer.combine(x, residual=True)
-        ev[6].record(stream)
-        layer.balance_stats()
-        ev[7].record(stream)
+
+    calls_post = [lambda: layer.combine(x, residual=True), lambda: layer.balance_stats()]
+    parts = [lambda: [c() for c in calls_route], ffn_part, lambda: [c() for c in calls_post]]
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        step()
+        for p in parts:
+            p()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    # per-stage breakdown: eager steps with an event after every call
+    # (before the timed region)
+    n_diag = min(args.steps, 20)
+    diag = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(n_diag)]
+    for ev in diag:
+        ev[0].record(stream)
+        for j, c in enumerate(calls_route + [ffn_part] + calls_post):
+            c()
+            ev[j + 1].record(stream)
+    torch.cuda.synchronize()
+    stage_ms = {s: [ev[j].elapsed_time(ev[j + 1]) for ev in diag] for j, s in enumerate(STAGES)}
+
+    if args.graph:
+        # each part captured once into a HIP graph; a timed step is three
+        # graph launches
+        graphs = []
+        for p in parts:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                p()
+            graphs.append(g)
+        parts = [g.replay for g in graphs]
+        for _ in range(args.warmup):
+            for p in parts:
+                p()
+        torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
+    for ev in events:
+        ev[0].record(stream)
+        for j, p in enumerate(parts):
+            p()
+            ev[j + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    print(f"[bench] timed {args.steps} steps in {elapsed:.4f}s", file=sys.stderr, flush=True)
+    print(f"[bench] timed {args.steps} steps in {elapsed:.4f}s "
+          f"({'HIP graphs' if args.graph else 'direct launches'})", file=sys.stderr, flush=True)
+    seg_ms = [float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events])) for j in range(3)]
 
-    stage_ms = {s: [] for s in STAGES}
-    for ev in events:
-        for j, s in enumerate(STAGES):
-            stage_ms[s].append(ev[j].elapsed_time(ev[j + 1]))
     k = layer.k
     M = int(layer.map.n_kept.item())
-    alg = algorithmic(cfg, k, M)
+    touched = int((layer.map.expert_offset.diff() > 0).sum().item())
+    alg = algorithmic(cfg, k, M, touched)
     stages = {}
     for s in STAGES:
         ms = float(np.mean(stage_ms[s]))
@@ -181,7 +222,7 @@ def main():
                      "hbm_frac": round(a["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         if a["flops"]:
             stages[s]["TFLOP/s"] = round(a["flops"] / (ms * 1e-3) / 1e12, 1)
-    ffn_ms = float(np.mean(stage_ms["expert_ffn"]))
+    ffn_ms = seg_ms[1]                     # the FFN part of the timed steps
     ffn = alg["expert_ffn"]
     intensity = ffn["flops"] / ffn["bytes"]
     ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -219,10 +260,14 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic (seeded normals; random-init weights of the stated shapes)",
         "config": {"workload": cfg.name, "n": cfg.n, "d": cfg.d, "E": cfg.E, "f": cfg.f, "act": cfg.act,
-                   "direction": cfg.direction, "k": k, "kept_assignments": M,
+                   "direction": cfg.direction, "k": k, "kept_assignments": M, "experts_touched": touched,
                    "parallelism": "single GPU"},
         "roofline": roofline,
+        "mode": "hip_graph" if args.graph else "eager",
+        "parts_us": {"route": round(seg_ms[0] * 1e3, 2), "expert_ffn": round(seg_ms[1] * 1e3, 2),
+                     "combine_stats": round(seg_ms[2] * 1e3, 2)},
         "stages": stages,
+        "stages_note": f"per-call breakdown from {n_diag} eager steps before the timed region",
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -122,6 +122,22 @@ class MoELayer:
         return self.out
 
 
+    def capture(self, x: torch.Tensor, residual: bool = True, stats: bool = True):
+        """Record one forward into a HIP graph (torch.cuda.CUDAGraph) and
+        return it; graph.replay() recomputes every buffer of this layer from
+        the current contents of `x` (a fixed device buffer) with one launch.
+        An eager forward runs first, so the library's one-time host queries
+        (occupancy, LDS attributes) stay outside the capture.  Every stage is
+        a kernel launch on the current stream: no memsets, no host
+        synchronisation, no allocation."""
+        self.forward(x, residual, stats)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.forward(x, residual, stats)
+        return graph
+
+
 def to_device(a, device="cuda") -> Optional[torch.Tensor]:
     """numpy array (float32, int32, or bf16 as uint16) -> device tensor
     (bf16 bit patterns become torch.bfloat16 without any conversion)."""

@@ -94,6 +94,14 @@ C5 = MoEConfig("sigmoid_bias_group_shared_bf16_n4096_d7168_e256", 5, n=4096, d=7
 
 FULL_CONFIGS = {c.cfg_id: c for c in (C1, C2, C3, C4, C5)}
 
+# A decode step of an OLMoE-shaped layer: 64 tokens, top-8 of 64 SwiGLU
+# experts, dropless.  Each expert sees about 8 rows, so the grouped GEMM is
+# weight streaming with almost no arithmetic per byte.
+DECODE = MoEConfig("decode_top8_swiglu_bf16_n64_d2048_e64", 6, n=64, d=2048, E=64, f=1024,
+                   act="swiglu", dtype="bf16", direction="tc", score="softmax", k=8,
+                   capacity_factor=None, norm_topk=True)
+EXTRA_CONFIGS = {"decode": DECODE}
+
 # Reduced shapes of the same five workloads: small enough for the oracle to
 # finish in seconds, large enough to span several GEMM tiles and leave ragged
 # per-expert tails.

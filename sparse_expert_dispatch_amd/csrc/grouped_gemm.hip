@@ -18,9 +18,10 @@
 // tile (SwiGLU: 128 x 64 outputs from 64 gate + 64 up weight rows, so the
 // gate and up accumulators of one output land in the same lane).  Each wave
 // computes 64 x 64 with 2 x 2 v_mfma_f32_32x32x16_bf16 tiles.  K advances
-// 64 at a time through double-buffered LDS tiles (rows padded by 16 bytes to
-// spread banks); the next K tile is fetched from HBM into registers while
-// the matrix cores work on the current one.
+// 64 at a time through LDS tiles (rows padded by 16 bytes to spread banks);
+// the next K tile is fetched from HBM into registers while the matrix cores
+// work on the current one.  Two builds of the kernel: double-buffered LDS
+// with two workgroups per CU, or one LDS copy with three (see the launcher).
 //
 // Scheduling: the per-expert tile counts are prefix-summed on the device
 // (no host synchronisation), and a persistent grid walks the resulting tile
@@ -46,6 +47,7 @@ constexpr int kBM = 128;
 constexpr int kBK = MOE_GEMM_BK;             // K per stage
 constexpr int kLdsStride = kBK + 8;          // bf16 per LDS row
 constexpr int kTileElems = 128 * kLdsStride; // one 128-row operand tile
+
 constexpr int kGemmThreads = 256;
 constexpr int kXcds = 8;
 #ifndef MOE_GEMM_ORDER
@@ -105,13 +107,17 @@ MOE_DEV int b_row_of(int r, int n0, int N) {
   return r < 64 ? n0 + r : N + n0 + (r - 64);
 }
 
-template <bool kDual, int kEpi>
-__global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
+// kLdsBufs = 2: double-buffered LDS stages (74 KB), two workgroups per CU.
+// kLdsBufs = 1: one LDS copy (37 KB) and a register budget for three
+// workgroups per CU; the stage in registers lands once every wave has left
+// the LDS copy (one extra barrier per stage).
+template <bool kDual, int kEpi, int kLdsBufs>
+__global__ __launch_bounds__(kGemmThreads, kLdsBufs == 1 ? 3 : 1) void grouped_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
     const int32_t* __restrict__ expert_offset, int E, int N, int K, int mt_inner,
     bf16_t* __restrict__ C) {
   // LDS: A and B K-stages, double buffered; reused for the output tile.
-  __shared__ __attribute__((aligned(16))) bf16_t smem[4 * kTileElems];
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * kLdsBufs * kTileElems];
   __shared__ int32_t tile_off[kMaxExperts + 1];
   block_tile_plan(expert_offset, E, tile_off);
   constexpr int kBNout = kDual ? 64 : 128;
@@ -119,7 +125,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
   constexpr int kChunksRow = kBK / 8;              // 16-byte chunks per operand row
   constexpr int kRowsPass = kGemmThreads / kChunksRow;
   constexpr int kCStride = kBNout + 8;             // bf16 per output-tile row in LDS
-  static_assert(128 * kCStride <= 4 * kTileElems, "output tile must fit the LDS stages");
+  static_assert(128 * kCStride <= 2 * kLdsBufs * kTileElems, "output tile must fit the LDS stages");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
   };
   auto store_stage = [&](int buf) {
     bf16_t* sA = smem + buf * kTileElems;
-    bf16_t* sB = smem + (2 + buf) * kTileElems;
+    bf16_t* sB = smem + (kLdsBufs + buf) * kTileElems;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       *reinterpret_cast<u32x4_t*>(&sA[(ld_row + kRowsPass * i) * kLdsStride + ld_chunk]) = ra[i];
@@ -203,9 +209,9 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
     for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
+      const int cur = kLdsBufs == 2 ? (kt & 1) : 0;
       const bf16_t* pa = smem + cur * kTileElems;
-      const bf16_t* pb = smem + (2 + cur) * kTileElems;
+      const bf16_t* pb = smem + (kLdsBufs + cur) * kTileElems;
 #pragma unroll
       for (int s = 0; s < kBK / 16; ++s) {
         const int kc = s * 16 + ((lane >> 5) << 3);
@@ -224,11 +230,21 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(
           for (int j = 0; j < 2; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
-      if (kt + 1 < nk) {
-        store_stage(cur ^ 1);
-        if (kt + 2 < nk) load_stage(kt + 2);
+      if (kLdsBufs == 2) {
+        if (kt + 1 < nk) {
+          store_stage(cur ^ 1);
+          if (kt + 2 < nk) load_stage(kt + 2);
+        }
+        __syncthreads();
+      } else {
+        // one LDS copy: every wave leaves it before the next stage lands
+        __syncthreads();
+        if (kt + 1 < nk) {
+          store_stage(0);
+          if (kt + 2 < nk) load_stage(kt + 2);
+          __syncthreads();
+        }
       }
-      __syncthreads();
     }
 
     // The next tile's first K stage starts loading before this tile's
@@ -373,12 +389,23 @@ hipError_t launch_expert_ffn(const void* X_perm, int dtype, const int32_t* exper
 #else
     const int mt_inner = MOE_GEMM_ORDER;
 #endif
+    // Weight-streaming shapes (few rows per expert, M tiles innermost)
+    // measured best with two double-buffered workgroups per CU; shapes with
+    // many rows per expert (matrix-core bound) with three single-buffered
+    // ones (2-3% faster there, 8-12% slower on weight streaming).
+    const bool two_bufs = mt_inner != 0;
     auto gemm = [&](auto dual, auto epi, const bf16_t* a, const bf16_t* b, int N, int K, bf16_t* c) {
       constexpr bool kD = decltype(dual)::value;
       constexpr int kE = decltype(epi)::value;
-      static const int blocks = persistent_blocks(grouped_gemm_bf16_kernel<kD, kE>);
-      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kD, kE>), dim3(blocks), dim3(kGemmThreads), 0, stream, a, b,
-                         expert_offset, E, N, K, mt_inner, c);
+      if (two_bufs) {
+        static const int blocks = persistent_blocks(grouped_gemm_bf16_kernel<kD, kE, 2>);
+        hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kD, kE, 2>), dim3(blocks), dim3(kGemmThreads), 0, stream,
+                           a, b, expert_offset, E, N, K, mt_inner, c);
+      } else {
+        static const int blocks = persistent_blocks(grouped_gemm_bf16_kernel<kD, kE, 1>);
+        hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kD, kE, 1>), dim3(blocks), dim3(kGemmThreads), 0, stream,
+                           a, b, expert_offset, E, N, K, mt_inner, c);
+      }
     };
     using std::integral_constant;
     if (act == 1)

@@ -234,6 +234,33 @@ moe_status_t moe_expert_ffn(const void *X_perm, int32_t dtype, const int32_t *ex
                             const void *W2, int64_t M_max, void *Y_perm, void *ws, size_t ws_bytes,
                             void *stream);
 
+/* Packed expert weights: the same bf16 values in the order the matrix cores
+ * consume them, so that the expert FFN reads every weight tile as whole
+ * contiguous blocks (the FFN of page 2 "The math" streams every expert's
+ * weights from memory once per call; this is a one-time layout change of
+ * the stored weights, done when they are loaded).  W [E, rows, K] (bf16,
+ * K-contiguous) -> W_packed, same size:
+ *   row block p of expert e = 32 rows: rows 32p .. 32p+31; with gate_up = 1
+ *   (a SwiGLU W1, rows = 2f, gate rows first) block 2q holds the gate rows
+ *   32q .. 32q+31 and block 2q+1 the up rows f+32q .. f+32q+31;
+ *   a 1 KB chunk holds, at 16-byte slot l (l = 0..63), 8 values of row
+ *   (l % 32) of its block, starting at K = 64 kt + 16 s + 8 (l / 32);
+ *   chunks are ordered by K stage kt (64 K), expert e, row block p, step s:
+ *   W_packed element ((((kt * E + e) * rows/32 + p) * 4 + s) * 64 + l) * 8 + j
+ *   = W[e][row(p, l % 32)][64 kt + 16 s + 8 (l / 32) + j].
+ * Pack W1 with gate_up = (act == MOE_SWIGLU), rows = f or 2f, K = d; W2 with
+ * gate_up = 0, rows = d, K = f.  Needs rows % 32 == 0 (gate_up: % 64) and
+ * K % 64 == 0; W and W_packed 16-byte aligned, not aliased. */
+moe_status_t moe_pack_expert_weights(const void *W, int32_t E, int32_t rows, int32_t K, int32_t gate_up,
+                                     void *W_packed, void *stream);
+
+/* moe_expert_ffn (bf16) on packed weights: same rows, same arithmetic and
+ * the same output bits as moe_expert_ffn on the unpacked weights; the same
+ * workspace size (moe_ffn_workspace_size with MOE_BF16) and shape rules. */
+moe_status_t moe_expert_ffn_packed(const void *X_perm, const int32_t *expert_offset, int32_t E, int32_t d,
+                                   int32_t f, int32_t act, const void *W1_packed, const void *W2_packed,
+                                   int64_t M_max, void *Y_perm, void *ws, size_t ws_bytes, void *stream);
+
 /* Combine out = scatter_add(G * Y, I) (page 2 "The math"), the gate applied
  * to the expert output: for every token, out = residual + shared_out + sum
  * of slot_gate[s] * Y_perm[s] over its token_slot list, in list order, fp32

@@ -31,7 +31,8 @@ EXPORTED = ("moe_ec_k", "moe_tc_capacity", "moe_max_slots", "moe_token_list_len"
             "moe_router_workspace_size",
             "moe_route_workspace_size", "moe_ffn_workspace_size", "moe_router", "moe_select",
             "moe_build_map", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_balance_stats",
-            "moe_update_bias", "moe_status_string", "moe_last_error")
+            "moe_update_bias", "moe_pack_expert_weights", "moe_expert_ffn_packed",
+            "moe_status_string", "moe_last_error")
 
 
 class MoEError(RuntimeError):
@@ -85,6 +86,8 @@ def lib() -> ctypes.CDLL:
         "moe_combine": (I32, [P, I32, MAP, I32, I32, P, P, P, P]),
         "moe_balance_stats": (I32, [P, MAP, CFG, F32, F32, P, P, P, SZ, P]),
         "moe_update_bias": (I32, [P, CFG, F32, P, P]),
+        "moe_pack_expert_weights": (I32, [P, I32, I32, I32, I32, P, P]),
+        "moe_expert_ffn_packed": (I32, [P, P, I32, I32, I32, I32, P, P, I64, P, P, SZ, P]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_last_error": (ctypes.c_char_p, []),
     }
@@ -295,6 +298,36 @@ def moe_expert_ffn(x_perm, expert_offset, w1, w2, act: int, y_perm, ws, stream=N
                                 _ptr(w2, "w2", _elem_dtypes(code)), int(x_perm.shape[0]),
                                 _ptr(y_perm, "y_perm", _elem_dtypes(code)), w, wb, _stream(stream)),
            "moe_expert_ffn")
+
+
+def moe_pack_expert_weights(w, gate_up: bool, w_packed, stream=None):
+    """w [E, rows, K] (or one expert's [rows, K]) bf16 -> w_packed (same shape
+    and size, the packed operand order)."""
+    E, rows, K = (1, *w.shape) if w.dim() == 2 else w.shape
+    _check(lib().moe_pack_expert_weights(_ptr(w, "w", _elem_dtypes(MOE_BF16)), int(E), int(rows), int(K),
+                                         int(bool(gate_up)), _ptr(w_packed, "w_packed", _elem_dtypes(MOE_BF16)),
+                                         _stream(stream)), "moe_pack_expert_weights")
+
+
+def pack_ffn_weights(w1, w2, act: int, stream=None):
+    """Packed copies of one FFN's W1 [E, f or 2f, d] and W2 [E, d, f]."""
+    w1p, w2p = torch.empty_like(w1), torch.empty_like(w2)
+    moe_pack_expert_weights(w1, act == MOE_SWIGLU, w1p, stream)
+    moe_pack_expert_weights(w2, False, w2p, stream)
+    return w1p, w2p
+
+
+def moe_expert_ffn_packed(x_perm, expert_offset, w1p, w2p, act: int, y_perm, ws, stream=None):
+    E = expert_offset.numel() - 1
+    d = x_perm.shape[1]
+    f = w2p.shape[-1]
+    w, wb = _ws(ws)
+    bf = _elem_dtypes(MOE_BF16)
+    _check(lib().moe_expert_ffn_packed(_ptr(x_perm, "x_perm", bf), _ptr(expert_offset, "expert_offset", _I32),
+                                       int(E), int(d), int(f), int(act), _ptr(w1p, "w1_packed", bf),
+                                       _ptr(w2p, "w2_packed", bf), int(x_perm.shape[0]),
+                                       _ptr(y_perm, "y_perm", bf), w, wb, _stream(stream)),
+           "moe_expert_ffn_packed")
 
 
 def moe_combine(y_perm, rmap: RouteMap, n: int, residual, shared_out, out, stream=None):

@@ -266,8 +266,43 @@ moe_status_t moe_expert_ffn(const void* X_perm, int32_t dtype, const int32_t* ex
     return fail(MOE_ERR_WORKSPACE, "expert_ffn needs %zu workspace bytes, got %zu", need, ws_bytes);
   REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
   return launched(moe::launch_expert_ffn(X_perm, dtype, expert_offset, E, d, f, act, W1, W2, M_max,
-                                         Y_perm, ws, as_stream(stream)),
+                                         Y_perm, ws, false, as_stream(stream)),
                   "moe_expert_ffn");
+}
+
+moe_status_t moe_pack_expert_weights(const void* W, int32_t E, int32_t rows, int32_t K, int32_t gate_up,
+                                     void* W_packed, void* stream) {
+  REQUIRE(W && W_packed, "W and W_packed must be non-NULL");
+  REQUIRE(W != W_packed, "W_packed must not alias W");
+  REQUIRE(E > 0 && rows > 0 && K > 0, "E, rows, K must be positive");
+  REQUIRE(gate_up == 0 || gate_up == 1, "gate_up must be 0 or 1");
+  SUPPORTED(rows % (gate_up ? 64 : 32) == 0 && K % 64 == 0,
+            "packing needs rows %% 32 == 0 (gate_up: rows %% 64 == 0) and K %% 64 == 0 (rows=%d K=%d)", rows, K);
+  REQUIRE(aligned16(W) && aligned16(W_packed), "W and W_packed must be 16-byte aligned");
+  return launched(moe::launch_pack_weights(W, E, rows, K, gate_up, W_packed, as_stream(stream)),
+                  "moe_pack_expert_weights");
+}
+
+moe_status_t moe_expert_ffn_packed(const void* X_perm, const int32_t* expert_offset, int32_t E, int32_t d,
+                                   int32_t f, int32_t act, const void* W1_packed, const void* W2_packed,
+                                   int64_t M_max, void* Y_perm, void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(E > 0 && d > 0 && f > 0 && M_max >= 0, "E, d, f must be positive, M_max non-negative");
+  if (M_max == 0) return MOE_OK;                  // no rows: nothing to compute
+  REQUIRE(X_perm && expert_offset && W1_packed && W2_packed && Y_perm, "tensor arguments must be non-NULL");
+  REQUIRE(act == MOE_GELU || act == MOE_SWIGLU, "act must be MOE_GELU or MOE_SWIGLU");
+  REQUIRE(M_max <= INT32_MAX, "M_max must fit in int32");
+  SUPPORTED(E <= moe::kMaxExperts, "bf16 expert FFN supports E <= %d (E=%d)", moe::kMaxExperts, E);
+  SUPPORTED(d % 64 == 0 && f % 64 == 0, "bf16 expert FFN needs d %% 64 == 0 and f %% 64 == 0 (d=%d f=%d)",
+            d, f);
+  REQUIRE(aligned16(X_perm) && aligned16(W1_packed) && aligned16(W2_packed) && aligned16(Y_perm),
+          "bf16 tensors must be 16-byte aligned");
+  const size_t need = moe::ffn_workspace_bytes(M_max, E, d, f, act, MOE_BF16);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "expert_ffn needs %zu workspace bytes, got %zu", need, ws_bytes);
+  REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
+  return launched(moe::launch_expert_ffn(X_perm, MOE_BF16, expert_offset, E, d, f, act, W1_packed, W2_packed,
+                                         M_max, Y_perm, ws, true, as_stream(stream)),
+                  "moe_expert_ffn_packed");
 }
 
 moe_status_t moe_combine(const void* Y_perm, int32_t dtype, const moe_route_map_t* map, int32_t n,

@@ -14,14 +14,21 @@
 // the MFMA operand layout wants: every lane feeds 8 consecutive K values of
 // one row (A) or one column (B).
 //
-// bf16 kernel: a workgroup (4 waves) owns a 128-row x 128-column output
-// tile (SwiGLU: 128 x 64 outputs from 64 gate + 64 up weight rows, so the
-// gate and up accumulators of one output land in the same lane).  Each wave
-// computes 64 x 64 with 2 x 2 v_mfma_f32_32x32x16_bf16 tiles.  K advances
-// 64 at a time through LDS tiles (rows padded by 16 bytes to spread banks);
-// the next K tile is fetched from HBM into registers while the matrix cores
-// work on the current one.  Two builds of the kernel: double-buffered LDS
-// with two workgroups per CU, or one LDS copy with three (see the launcher).
+// Two bf16 kernels, both on v_mfma_f32_32x32x16_bf16:
+//  - grouped_gemm_bf16_kernel (LDS kernel): a workgroup (4 waves) owns a
+//    128-row output tile, 128 or 256 columns wide (SwiGLU: half as many
+//    outputs from as many gate + up weight rows, so the gate and up
+//    accumulators of one output land in the same lane); each wave computes
+//    64 x 64 or 64 x 128.  K advances 64 at a time through LDS tiles; the
+//    next K tile is fetched from HBM into registers while the matrix cores
+//    work on the current one.  Weights in the natural layout or packed.
+//  - stream_gemm_bf16_kernel (weight streaming, packed weights only): the
+//    weights bypass LDS and stream into registers several K stages ahead
+//    (see the kernel).
+// The launcher picks the streaming kernel for packed weights when every
+// expert has few rows (the GEMMs are bound by the weight stream), the LDS
+// kernel with 128 x 256 tiles when experts have many rows (matrix-core
+// bound), and the LDS kernel for the natural layout.
 //
 // Scheduling: the per-expert tile counts are prefix-summed on the device
 // (no host synchronisation), and a persistent grid walks the resulting tile
@@ -30,6 +37,7 @@
 // adjacent, so the workgroups that share an A panel (and a weight slice
 // across neighbouring M tiles) share that XCD's L2.
 #include <type_traits>
+#include <utility>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -46,7 +54,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kBM = 128;
 constexpr int kBK = MOE_GEMM_BK;             // K per stage
 constexpr int kLdsStride = kBK + 8;          // bf16 per LDS row
-constexpr int kTileElems = 128 * kLdsStride; // one 128-row operand tile
 
 constexpr int kGemmThreads = 256;
 constexpr int kXcds = 8;
@@ -59,17 +66,20 @@ enum { kEpiNone = 0, kEpiGelu = 1, kEpiSwiglu = 2 };
 // GELU x * Phi(x) with erf from Abramowitz & Stegun formula 7.1.26
 // (|error| <= 1.5e-7 over the real line, far below the bf16 rounding of the
 // result): erf(z) = 1 - (a1 t + ... + a5 t^5) exp(-z^2), t = 1 / (1 + p z),
-// z >= 0, odd extension for z < 0.
+// z >= 0, odd extension for z < 0.  The reciprocals here and in SiLU are
+// the hardware's v_rcp_f32 (1 ulp): a correctly rounded division costs
+// several times more, and the activation runs on every hidden element in
+// the GEMM epilogue, where it stalls the matrix cores.
 MOE_DEV float gelu_f(float x) {
   const float z = fabsf(x) * 0.70710678118654752f;
-  const float t = __frcp_rn(1.0f + 0.3275911f * z);
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * z);
   const float poly =
       t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
   const float erf_z = 1.0f - poly * __expf(-z * z);
   const float erf_x = x < 0.f ? -erf_z : erf_z;
   return 0.5f * x * (1.0f + erf_x);
 }
-MOE_DEV float silu_f(float x) { return x * __frcp_rn(1.0f + __expf(-x)); }
+MOE_DEV float silu_f(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // Tile list, built by every workgroup in LDS at kernel start (no separate
 // launch, no host synchronisation): tile_off[e] = sum over e' < e of
@@ -98,34 +108,50 @@ MOE_DEV void block_tile_plan(const int32_t* __restrict__ expert_offset, int E, i
   __syncthreads();
 }
 
-template <bool kDual>
+// Weight row of B-tile row r for a tile of kBRows weight rows at output
+// column n0.  Dual (SwiGLU): rows [0, G) gate, [G, 2G) up, G = kBRows / 2.
+// Rows past N re-read the last row; their output columns are never stored.
+template <bool kDual, int kBRows>
 MOE_DEV int b_row_of(int r, int n0, int N) {
-  // LDS B row r -> weight row.  Dual: rows 0..63 gate, 64..127 up (N is a
-  // multiple of 64, so a dual tile is always full).  Single: a half tile at
-  // the end of N re-reads the last row; those columns are never stored.
   if (!kDual) return min(n0 + r, N - 1);
-  return r < 64 ? n0 + r : N + n0 + (r - 64);
+  constexpr int G = kBRows / 2;
+  return r < G ? min(n0 + r, N - 1) : N + min(n0 + r - G, N - 1);
 }
 
-// kLdsBufs = 2: double-buffered LDS stages (74 KB), two workgroups per CU.
-// kLdsBufs = 1: one LDS copy (37 KB) and a register budget for three
-// workgroups per CU; the stage in registers lands once every wave has left
-// the LDS copy (one extra barrier per stage).
-template <bool kDual, int kEpi, int kLdsBufs>
-__global__ __launch_bounds__(kGemmThreads, kLdsBufs == 1 ? 3 : 1) void grouped_gemm_bf16_kernel(
-    const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
-    const int32_t* __restrict__ expert_offset, int E, int N, int K, int mt_inner,
-    bf16_t* __restrict__ C) {
-  // LDS: A and B K-stages, double buffered; reused for the output tile.
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * kLdsBufs * kTileElems];
-  __shared__ int32_t tile_off[kMaxExperts + 1];
-  block_tile_plan(expert_offset, E, tile_off);
-  constexpr int kBNout = kDual ? 64 : 128;
-  constexpr int kLoads = kBK / 16;                 // 16-byte loads per thread per operand and stage
+// kNB: 32-column MFMA blocks per wave in N (2: 64 x 64 per wave, 128 x 128
+// tile; 4: 64 x 128 per wave, 128 x 256 tile, which reads 25% fewer LDS bytes
+// per MFMA and each A panel once per 256 weight rows).
+// kLdsBufs = 2: double-buffered LDS stages; 1: one LDS copy, the stage in
+// registers lands once every wave has left it (one extra barrier per stage),
+// which halves the LDS footprint (kNB = 2: three workgroups per CU instead
+// of two; kNB = 4: two instead of one).
+// kPacked: B is in the packed operand order written by pack_weights_kernel
+// (each K stage of 32 weight rows is one contiguous 4 KB block; LDS holds
+// the blocks unpadded and every fragment read is 64 consecutive 16-byte
+// chunks); otherwise B is the natural [rows, K] layout.
+template <bool kDual, int kEpi, int kLdsBufs, int kNB, bool kPacked>
+__global__ __launch_bounds__(kGemmThreads, kNB == 4 ? 2 : (kLdsBufs == 1 ? 3 : 1)) void
+grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
+                         const int32_t* __restrict__ expert_offset, int E, int N, int K, int mt_inner,
+                         bf16_t* __restrict__ C) {
+  constexpr int kBRows = 2 * kNB * 32;             // weight rows per tile
+  constexpr int kBNout = kDual ? kBRows / 2 : kBRows;
+  constexpr int kTileA = 128 * kLdsStride;
+  constexpr int kTileB = kPacked ? kBRows * kBK : kBRows * kLdsStride;
+  static_assert(!kPacked || kBK == 64, "a packed K stage is 4 row-block chunks of 16 K");
+  constexpr int kStageElems = kTileA + kTileB;
   constexpr int kChunksRow = kBK / 8;              // 16-byte chunks per operand row
   constexpr int kRowsPass = kGemmThreads / kChunksRow;
-  constexpr int kCStride = kBNout + 8;             // bf16 per output-tile row in LDS
-  static_assert(128 * kCStride <= 2 * kLdsBufs * kTileElems, "output tile must fit the LDS stages");
+  constexpr int kLoadsA = 128 / kRowsPass;         // 16-byte loads per thread per stage
+  constexpr int kLoadsB = kBRows / kRowsPass;
+  constexpr int kPassCols = kBNout < 128 ? kBNout : 128;   // output columns per epilogue pass
+  constexpr int kPasses = kBNout / kPassCols;
+  constexpr int kCStride = kPassCols + 8;          // bf16 per output row in LDS
+  static_assert(128 * kCStride <= kLdsBufs * kStageElems, "an epilogue pass must fit the LDS stages");
+  // LDS: the K stage(s); reused for the output tile.
+  __shared__ __attribute__((aligned(16))) bf16_t smem[kLdsBufs * kStageElems];
+  __shared__ int32_t tile_off[kMaxExperts + 1];
+  block_tile_plan(expert_offset, E, tile_off);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -141,11 +167,29 @@ __global__ __launch_bounds__(kGemmThreads, kLdsBufs == 1 ? 3 : 1) void grouped_g
   const int ld_chunk = (tid % kChunksRow) * 8;
   const int nk = K / kBK;
 
+  // LDS row of this wave's B block j (32 weight rows from lane row 0)
+  auto b_block_row = [&](int j) {
+    if (!kDual) return wn * kNB * 32 + j * 32;
+    constexpr int G = kBRows / 2, half = kNB / 2;
+    return j < half ? wn * (G / 2) + j * 32 : G + wn * (G / 2) + (j - half) * 32;
+  };
+  // packed: tile-local row block of this wave's B block j (SwiGLU blocks
+  // alternate gate, up for consecutive 32-column output blocks)
+  auto b_block_packed = [&](int j) {
+    if (!kDual) return wn * kNB + j;
+    constexpr int half = kNB / 2;
+    return j < half ? 2 * (wn * half + j) : 2 * (wn * half + j - half) + 1;
+  };
+
   // Per-tile state: output placement and the global sources of this
   // thread's 16-byte staging loads.
+  // Per-tile state (wave-uniform: kept in scalar registers) and, for the
+  // natural B layout, the global sources of this thread's B loads.  A and
+  // packed B addresses are formed per load from the uniform tile base.
   int row_base = 0, m_valid = 0, n0 = 0;
-  const bf16_t* a_src[kLoads];
-  const bf16_t* b_src[kLoads];
+  const bf16_t* a_tile = A;
+  const bf16_t* b_tile = B;
+  const bf16_t* b_src[kPacked ? 1 : kLoadsB];
   auto setup = [&](int64_t t) {
     // expert owning tile t: expert e holds tiles [tile_off[e] * ntn, tile_off[e+1] * ntn)
     int e_lo = 0, e_hi = E - 1;
@@ -153,7 +197,7 @@ __global__ __launch_bounds__(kGemmThreads, kLdsBufs == 1 ? 3 : 1) void grouped_g
       const int mid = (e_lo + e_hi + 1) >> 1;
       if ((int64_t)tile_off[mid] * ntn <= t) e_lo = mid; else e_hi = mid - 1;
     }
-    const int e = e_lo;
+    const int e = __builtin_amdgcn_readfirstlane(e_lo);
     const int mtiles = tile_off[e + 1] - tile_off[e];
     const int local = (int)(t - (int64_t)tile_off[e] * ntn);
     // weight-streaming shapes walk an expert's M tiles innermost (its weight
@@ -161,33 +205,53 @@ __global__ __launch_bounds__(kGemmThreads, kLdsBufs == 1 ? 3 : 1) void grouped_g
     // rows per expert walk N innermost (the A panel stays in L2)
     const int mloc = mt_inner ? local % mtiles : local / ntn;
     const int nt = mt_inner ? local / mtiles : local % ntn;
-    row_base = expert_offset[e] + mloc * kBM;
-    m_valid = min(kBM, expert_offset[e + 1] - row_base);
-    n0 = nt * kBNout;
-    const bf16_t* Be = B + (size_t)e * nbrows * K;
+    row_base = __builtin_amdgcn_readfirstlane(expert_offset[e] + mloc * kBM);
+    m_valid = __builtin_amdgcn_readfirstlane(min(kBM, expert_offset[e + 1] - row_base));
+    n0 = __builtin_amdgcn_readfirstlane(nt * kBNout);
+    a_tile = A + (size_t)row_base * K;
+    // packed: expert e's row blocks in the first K stage's slab; natural: its matrix
+    b_tile = kPacked ? B + (size_t)e * (nbrows / 32) * 2048 : B + (size_t)e * nbrows * K;
+    if (!kPacked) {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int r = ld_row + kRowsPass * i;
-      a_src[i] = A + (size_t)(row_base + min(r, m_valid - 1)) * K + ld_chunk;   // tail rows re-read
-      b_src[i] = Be + (size_t)b_row_of<kDual>(r, n0, N) * K + ld_chunk;
+      for (int i = 0; i < kLoadsB; ++i) {
+        const int r = ld_row + kRowsPass * i;
+        b_src[i] = b_tile + (size_t)b_row_of<kDual, kBRows>(r, n0, N) * K + ld_chunk;
+      }
     }
   };
-  u32x4_t ra[kLoads], rb[kLoads];
+  u32x4_t ra[kLoadsA], rb[kLoadsB];
   auto load_stage = [&](int st) {
     const int koff = st * kBK;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + koff);
-      rb[i] = *reinterpret_cast<const u32x4_t*>(b_src[i] + koff);
+    for (int i = 0; i < kLoadsA; ++i) {
+      const int r = min(ld_row + kRowsPass * i, m_valid - 1);     // tail rows re-read the last row
+      ra[i] = *reinterpret_cast<const u32x4_t*>(a_tile + r * K + ld_chunk + koff);
+    }
+#pragma unroll
+    for (int i = 0; i < kLoadsB; ++i) {
+      if (kPacked) {
+        // load i fetches tile-local row block i (columns past N re-read the last block)
+        const int last = N / 32 - 1;
+        const int pb = kDual ? 2 * min(n0 / 32 + (i >> 1), last) + (i & 1) : min(n0 / 32 + i, last);
+        rb[i] = *reinterpret_cast<const u32x4_t*>(b_tile + ((size_t)st * E * (nbrows / 32) + pb) * 2048 +
+                                                  tid * 8);
+      } else {
+        rb[i] = *reinterpret_cast<const u32x4_t*>(b_src[i] + koff);
+      }
     }
   };
   auto store_stage = [&](int buf) {
-    bf16_t* sA = smem + buf * kTileElems;
-    bf16_t* sB = smem + (kLdsBufs + buf) * kTileElems;
+    bf16_t* sA = smem + buf * kStageElems;
+    bf16_t* sB = sA + kTileA;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
+    for (int i = 0; i < kLoadsA; ++i)
       *reinterpret_cast<u32x4_t*>(&sA[(ld_row + kRowsPass * i) * kLdsStride + ld_chunk]) = ra[i];
-      *reinterpret_cast<u32x4_t*>(&sB[(ld_row + kRowsPass * i) * kLdsStride + ld_chunk]) = rb[i];
+#pragma unroll
+    for (int i = 0; i < kLoadsB; ++i) {
+      if (kPacked)
+        *reinterpret_cast<u32x4_t*>(&sB[i * kBK * 32 + tid * 8]) = rb[i];
+      else
+        *reinterpret_cast<u32x4_t*>(&sB[(ld_row + kRowsPass * i) * kLdsStride + ld_chunk]) = rb[i];
     }
   };
 
@@ -196,38 +260,38 @@ __global__ __launch_bounds__(kGemmThreads, kLdsBufs == 1 ? 3 : 1) void grouped_g
   setup(t);
   load_stage(0);
   while (true) {
-    // K pipeline: LDS double buffer; the next stage's global loads are in
-    // flight while the matrix cores work on the current one.
+    // K pipeline: the next stage's global loads are in flight while the
+    // matrix cores work on the current one.
     store_stage(0);
     if (nk > 1) load_stage(1);
     __syncthreads();
-    f32x16_t acc[2][2];
+    f32x16_t acc[2][kNB];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < kNB; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kLdsBufs == 2 ? (kt & 1) : 0;
-      const bf16_t* pa = smem + cur * kTileElems;
-      const bf16_t* pb = smem + (kLdsBufs + cur) * kTileElems;
+      const bf16_t* pa = smem + cur * kStageElems;
+      const bf16_t* pb = pa + kTileA;
 #pragma unroll
       for (int s = 0; s < kBK / 16; ++s) {
         const int kc = s * 16 + ((lane >> 5) << 3);
-        bf16x8_t af[2], bfr[2];
+        bf16x8_t af[2], bfr[kNB];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
           af[i] = *reinterpret_cast<const bf16x8_t*>(pa + (wm * 64 + i * 32 + (lane & 31)) * kLdsStride + kc);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int brow = kDual ? (j * 64 + wn * 32 + (lane & 31)) : (wn * 64 + j * 32 + (lane & 31));
-          bfr[j] = *reinterpret_cast<const bf16x8_t*>(pb + brow * kLdsStride + kc);
-        }
+        for (int j = 0; j < kNB; ++j)
+          bfr[j] = kPacked
+                       ? *reinterpret_cast<const bf16x8_t*>(pb + (b_block_packed(j) * (kBK / 16) + s) * 512 + lane * 8)
+                       : *reinterpret_cast<const bf16x8_t*>(pb + (b_block_row(j) + (lane & 31)) * kLdsStride + kc);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < kNB; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
       if (kLdsBufs == 2) {
@@ -257,43 +321,301 @@ __global__ __launch_bounds__(kGemmThreads, kLdsBufs == 1 ? 3 : 1) void grouped_g
     }
 
     // Epilogue: activation, bf16 rounding, then the tile goes through LDS
-    // so that global stores are whole 16-byte chunks of output rows.  The
-    // stores are non-temporal: the output is read by the next kernel, not by
-    // this one, and streaming it past the cache keeps the weight stream's
-    // reads and these writes from contending for L2.
+    // (kPassCols output columns per pass) so that global stores are whole
+    // 16-byte chunks of output rows.  The stores are non-temporal: the
+    // output is read by the next kernel, not by this one, and streaming it
+    // past the cache keeps the weight stream's reads and these writes from
+    // contending for L2.
     // 32x32 accumulator layout: lane holds column (lane % 32), element v ->
     // row (v / 4) * 8 + (lane / 32) * 4 + v % 4.
     bf16_t* sC = smem;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int p = 0; p < kPasses; ++p) {
+      if (p > 0) __syncthreads();                  // the previous pass has been read out
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = wm * 64 + i * 32 + (v >> 2) * 8 + ((lane >> 5) << 2) + (v & 3);
-        if (kDual) {
-          const float g = acc[i][0][v], u = acc[i][1][v];
-          sC[r * kCStride + wn * 32 + (lane & 31)] = f32_to_bf16(silu_f(g) * u);
-        } else {
+      for (int i = 0; i < 2; ++i) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            float x = acc[i][j][v];
-            if (kEpi == kEpiGelu) x = gelu_f(x);
-            sC[r * kCStride + wn * 64 + j * 32 + (lane & 31)] = f32_to_bf16(x);
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * 64 + i * 32 + (v >> 2) * 8 + ((lane >> 5) << 2) + (v & 3);
+          if (kDual) {
+#pragma unroll
+            for (int j = 0; j < kNB / 2; ++j) {
+              const int col = wn * (kBNout / 2) + j * 32 + (lane & 31);
+              const float g = acc[i][j][v], u = acc[i][j + kNB / 2][v];
+              sC[r * kCStride + col] = f32_to_bf16(silu_f(g) * u);
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < kNB; ++j) {
+              const int col = wn * kNB * 32 + j * 32 + (lane & 31);
+              if (col / kPassCols != p) continue;
+              float x = acc[i][j][v];
+              if (kEpi == kEpiGelu) x = gelu_f(x);
+              sC[r * kCStride + col - p * kPassCols] = f32_to_bf16(x);
+            }
           }
         }
       }
-    }
-    __syncthreads();
-    constexpr int kOutChunksRow = kBNout / 8;
-    for (int q = tid; q < 128 * kOutChunksRow; q += kGemmThreads) {
-      const int r = q / kOutChunksRow, c = (q % kOutChunksRow) * 8;
-      if (r < c_m_valid && c_n0 + c < N)
-        __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(sC + r * kCStride + c),
-                                    reinterpret_cast<u32x4_t*>(C + (size_t)(c_row_base + r) * N + c_n0 + c));
+      __syncthreads();
+      constexpr int kOutChunksRow = kPassCols / 8;
+      const int pc0 = c_n0 + p * kPassCols;
+      for (int q = tid; q < 128 * kOutChunksRow; q += kGemmThreads) {
+        const int r = q / kOutChunksRow, c = (q % kOutChunksRow) * 8;
+        if (r < c_m_valid && pc0 + c < N)
+          __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(sC + r * kCStride + c),
+                                      reinterpret_cast<u32x4_t*>(C + (size_t)(c_row_base + r) * N + pc0 + c));
+      }
     }
     __syncthreads();
     if (tn >= hi) break;
     t = tn;
   }
+}
+
+
+// ---------------------------------------------------------------- weight-streaming kernel
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+MOE_DEV void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Shapes with few rows per expert do little arithmetic per weight byte and
+// are bound by the weight stream.  The LDS kernel above stages both
+// operands through LDS, and at one to two waves per SIMD its compute phase
+// alone (LDS writes, fragment reads, barriers) takes about as long as the
+// weight stream, so the two barely overlap.  This kernel keeps the packed
+// weights out of LDS: each wave owns all 128 rows of the tile and its own
+// two 32-row weight blocks, and loads those blocks from HBM straight into
+// registers in MFMA operand order (one contiguous 1 KB chunk per load
+// instruction), kDepth K stages ahead, continuing across tile boundaries so
+// the stream never drains.  Only A (the activations, L2-resident) goes
+// through LDS, double-buffered, with one barrier per stage.
+//
+// Tile: 128 rows x 256 output columns (wave w: columns 64w .. 64w+63), or
+// SwiGLU 128 x 128 (wave w: the gate and up blocks of columns 32w ..).  M
+// tiles of an expert are innermost, as in the LDS kernel's weight-streaming
+// order.  K / 64 must be a multiple of kDepth (the register ring is indexed
+// at compile time); the launcher checks.
+template <bool kDual, int kEpi, int kDepth>
+__global__ __launch_bounds__(kGemmThreads, 1) void
+stream_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bp,
+                        const int32_t* __restrict__ expert_offset, int E, int N, int K,
+                        bf16_t* __restrict__ C) {
+  static_assert(kBK == 64, "a stage is four 16-K operand chunks");
+  constexpr int kNW = kDual ? 128 : 256;           // output columns per tile
+  constexpr int kCStride = kNW + 8;                // bf16 per output row in LDS
+  constexpr int kATile = 128 * kLdsStride;
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2 * kATile];
+  __shared__ __attribute__((aligned(16))) bf16_t sC[128 * kCStride];
+  __shared__ int32_t tile_off[kMaxExperts + 1];
+  block_tile_plan(expert_offset, E, tile_off);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ntn = (N + kNW - 1) / kNW;
+  const int64_t n_tiles = (int64_t)tile_off[E] * ntn;
+  const int xcd = blockIdx.x % kXcds;
+  const int per_xcd_blocks = gridDim.x / kXcds;
+  const int64_t lo = n_tiles * xcd / kXcds, hi = n_tiles * (xcd + 1) / kXcds;
+  const int64_t t0 = lo + blockIdx.x / kXcds;
+  if (t0 >= hi) return;
+  const int ntiles = (int)((hi - t0 + per_xcd_blocks - 1) / per_xcd_blocks);
+  const int nk = K / kBK;
+  const int P = kDual ? 2 * N / 32 : N / 32;       // weight row blocks per expert
+  const int last_pb = N / 32 - 1;
+  const size_t stage_stride = (size_t)E * P * 2048;  // packed elements per K stage, all experts
+  const int ld_row = tid >> 3, ld_chunk = (tid & 7) * 8;
+
+  // Placement of this workgroup's j-th tile (M tiles of an expert innermost).
+  struct Place {
+    int row_base, m_valid, n0, e;
+  };
+  auto locate = [&](int j) {
+    const int64_t t = t0 + (int64_t)j * per_xcd_blocks;
+    int e_lo = 0, e_hi = E - 1;
+    while (e_lo < e_hi) {
+      const int mid = (e_lo + e_hi + 1) >> 1;
+      if ((int64_t)tile_off[mid] * ntn <= t) e_lo = mid; else e_hi = mid - 1;
+    }
+    Place p;
+    p.e = __builtin_amdgcn_readfirstlane(e_lo);
+    const int mtiles = tile_off[p.e + 1] - tile_off[p.e];
+    const int local = (int)(t - (int64_t)tile_off[p.e] * ntn);
+    p.row_base = __builtin_amdgcn_readfirstlane(expert_offset[p.e] + (local % mtiles) * kBM);
+    p.m_valid = __builtin_amdgcn_readfirstlane(min(kBM, expert_offset[p.e + 1] - p.row_base));
+    p.n0 = __builtin_amdgcn_readfirstlane((local / mtiles) * kNW);
+    return p;
+  };
+
+  // Load cursor: the stage the next issue() fetches.  Past the last tile it
+  // re-reads the last stage (in bounds, never used), so every iteration
+  // issues the same loads and the compiler's memory-counter waits stay exact.
+  int l_j = 0, l_kt = 0, l_mv = 1;
+  const bf16_t* l_a = A;
+  const bf16_t* l_b0 = Bp;
+  const bf16_t* l_b1 = Bp;
+  auto load_tile = [&](int j) {
+    const Place p = locate(min(j, ntiles - 1));
+    l_a = A + (size_t)p.row_base * K;
+    l_mv = p.m_valid;
+    int pb0, pb1;
+    if (kDual) {
+      const int ob = min(p.n0 / 32 + wave, last_pb);
+      pb0 = 2 * ob;
+      pb1 = 2 * ob + 1;
+    } else {
+      pb0 = min(p.n0 / 32 + 2 * wave, last_pb);
+      pb1 = min(p.n0 / 32 + 2 * wave + 1, last_pb);
+    }
+    l_b0 = Bp + ((size_t)p.e * P + pb0) * 2048 + lane * 8;
+    l_b1 = Bp + ((size_t)p.e * P + pb1) * 2048 + lane * 8;
+  };
+  u32x4_t ra[kDepth][4], rb[kDepth][2][4];
+  auto issue = [&](auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
+    const int kt = l_j < ntiles ? l_kt : nk - 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = min(ld_row + 32 * i, l_mv - 1);             // tail rows re-read the last row
+      ra[slot][i] = *reinterpret_cast<const u32x4_t*>(l_a + r * K + ld_chunk + kt * kBK);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      rb[slot][0][s] = *reinterpret_cast<const u32x4_t*>(l_b0 + kt * stage_stride + s * 512);
+      rb[slot][1][s] = *reinterpret_cast<const u32x4_t*>(l_b1 + kt * stage_stride + s * 512);
+    }
+    if (++l_kt == nk) {
+      l_kt = 0;
+      ++l_j;
+      load_tile(l_j);
+    }
+  };
+  int buf = 0;
+  auto store_a = [&](auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4_t*>(&sA[buf * kATile + (ld_row + 32 * i) * kLdsStride + ld_chunk]) = ra[slot][i];
+  };
+
+  using std::integral_constant;
+  load_tile(0);
+  static_for<0, kDepth>([&](auto u) { issue(u); });
+  store_a(integral_constant<int, 0>{});
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][b][v] = 0.f;
+    for (int kt0 = 0; kt0 < nk; kt0 += kDepth) {
+      static_for<0, kDepth>([&](auto uc) {
+        // one K stage: MFMAs on this stage's A (LDS) and B (ring slot U),
+        // the next stage's A into the other LDS buffer, the slot refilled
+        // kDepth stages ahead
+        constexpr int U = decltype(uc)::value;
+        const bf16_t* pa = sA + buf * kATile;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int kc = s * 16 + ((lane >> 5) << 3);
+          bf16x8_t af[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            af[i] = *reinterpret_cast<const bf16x8_t*>(pa + (i * 32 + (lane & 31)) * kLdsStride + kc);
+          const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, rb[U][0][s]);
+          const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, rb[U][1][s]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], b0, acc[i][0], 0, 0, 0);
+            acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], b1, acc[i][1], 0, 0, 0);
+          }
+        }
+        buf ^= 1;
+        store_a(integral_constant<int, (U + 1) % kDepth>{});
+        issue(integral_constant<int, U>{});
+        __syncthreads();
+      });
+    }
+
+    // Epilogue: activation, bf16 rounding, the tile through LDS, whole
+    // 16-byte chunks of output rows with non-temporal stores.  The loads of
+    // the next tile's first stages are already in flight.  32x32
+    // accumulator layout: lane holds column (lane % 32), element v -> row
+    // (v / 4) * 8 + (lane / 32) * 4 + v % 4.
+    const Place p = locate(j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = i * 32 + (v >> 2) * 8 + ((lane >> 5) << 2) + (v & 3);
+        if (kDual) {
+          sC[r * kCStride + wave * 32 + (lane & 31)] = f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
+        } else {
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            float x = acc[i][b][v];
+            if (kEpi == kEpiGelu) x = gelu_f(x);
+            sC[r * kCStride + wave * 64 + b * 32 + (lane & 31)] = f32_to_bf16(x);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int kOutChunksRow = kNW / 8;
+    for (int q = tid; q < 128 * kOutChunksRow; q += kGemmThreads) {
+      const int r = q / kOutChunksRow, c = (q % kOutChunksRow) * 8;
+      if (r < p.m_valid && p.n0 + c < N)
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(sC + r * kCStride + c),
+                                    reinterpret_cast<u32x4_t*>(C + (size_t)(p.row_base + r) * N + p.n0 + c));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- weight packing
+// Packed operand order of the expert weights W [E, R, K] (bf16,
+// K-contiguous; R % 32 == 0, K % 64 == 0).  Row block p of an expert holds
+// 32 weight rows: rows 32p .. 32p+31, or for a SwiGLU W1 (R = 2F, gate rows
+// first) the gate rows 32q .. of output block q at p = 2q and the matching
+// up rows F + 32q .. at p = 2q + 1.  A 1 KB chunk holds, at 16-byte slot
+// l = 0..63, the 8 values W[e][row(p, l % 32)][k0 + 8 (l / 32) + 0..7]:
+// exactly the B operand of one v_mfma_f32_32x32x16_bf16 (32 output
+// columns, 16 K).  Chunks are ordered K stage (64 K) first, then expert,
+// row block, and the stage's four 16-K steps:
+//   element ((((kt * E + e) * R/32 + p) * 4 + s) * 64 + l) * 8 + j
+//   holds W[e][row(p, l % 32)][64 kt + 16 s + 8 (l / 32) + j].
+// So one K stage of a GEMM tile (consecutive row blocks of one expert) is
+// one contiguous run, and the tiles in flight at the same time (the same
+// stage of neighbouring tiles) sit next to each other in memory, which
+// keeps HBM row-buffer locality across the chip.
+//
+// One thread per 16-byte chunk: the writes are fully coalesced, each read
+// is one 16-byte piece of a row.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const bf16_t* __restrict__ W, int64_t chunks,
+                                                           int E, int R, int K, int gate_up,
+                                                           bf16_t* __restrict__ P) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= chunks) return;
+  const int lane = (int)(c & 63);
+  const int s = (int)((c >> 6) & 3);
+  const int64_t blk = c >> 8;                      // (kt * E + e) * R/32 + p
+  const int nb = R / 32;
+  const int p = (int)(blk % nb);
+  const int64_t ke = blk / nb;
+  const int e = (int)(ke % E);
+  const int kt = (int)(ke / E);
+  const int row = gate_up ? ((p & 1) ? R / 2 : 0) + (p >> 1) * 32 + (lane & 31) : p * 32 + (lane & 31);
+  const int k0 = kt * 64 + s * 16 + (lane >> 5) * 8;
+  *reinterpret_cast<u32x4_t*>(P + c * 8) =
+      *reinterpret_cast<const u32x4_t*>(W + ((int64_t)e * R + row) * (int64_t)K + k0);
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -351,6 +673,17 @@ __global__ __launch_bounds__(256) void ffn_down_f32_kernel(const float* __restri
 // ---------------------------------------------------------------- host side
 
 
+#ifndef MOE_GEMM_NB_STREAM
+#define MOE_GEMM_NB_STREAM 2     // N blocks per wave, weight-streaming shapes
+#endif
+#ifndef MOE_GEMM_NB_MFMA
+#define MOE_GEMM_NB_MFMA 4       // N blocks per wave, shapes with many rows per expert
+#endif
+
+#ifndef MOE_STREAM_DEPTH
+#define MOE_STREAM_DEPTH 2       // K stages of packed weights in flight per wave, weight streaming
+#endif
+
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t ffn_workspace_bytes(int64_t M_max, int E, int d, int f, int act, int dtype) {
@@ -375,9 +708,25 @@ static int persistent_blocks(Kern kernel) {
   return ((per_cu * cus) / kXcds) * kXcds;
 }
 
+// One launch of a persistent kernel; the grid size is computed once per
+// kernel (its occupancy does not change).
+template <auto kKernel, typename... Args>
+static void launch_persistent(hipStream_t stream, Args... args) {
+  static const int blocks = persistent_blocks(kKernel);
+  hipLaunchKernelGGL(kKernel, dim3(blocks), dim3(kGemmThreads), 0, stream, args...);
+}
+
+hipError_t launch_pack_weights(const void* W, int E, int R, int K, int gate_up, void* P,
+                               hipStream_t stream) {
+  const int64_t chunks = (int64_t)E * R * K / 8;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const bf16_t*>(W), chunks, E, R, K, gate_up, static_cast<bf16_t*>(P));
+  return hipGetLastError();
+}
+
 hipError_t launch_expert_ffn(const void* X_perm, int dtype, const int32_t* expert_offset, int E,
                              int d, int f, int act, const void* W1, const void* W2, int64_t M_max,
-                             void* Y_perm, void* ws, hipStream_t stream) {
+                             void* Y_perm, void* ws, bool packed, hipStream_t stream) {
   char* w = static_cast<char*>(ws);
   void* H = w;
   if (dtype == 1) {
@@ -390,21 +739,32 @@ hipError_t launch_expert_ffn(const void* X_perm, int dtype, const int32_t* exper
     const int mt_inner = MOE_GEMM_ORDER;
 #endif
     // Weight-streaming shapes (few rows per expert, M tiles innermost)
-    // measured best with two double-buffered workgroups per CU; shapes with
-    // many rows per expert (matrix-core bound) with three single-buffered
-    // ones (2-3% faster there, 8-12% slower on weight streaming).
+    // measured best with 128 x 128 tiles and two double-buffered workgroups
+    // per CU; shapes with many rows per expert (matrix-core bound) with
+    // 128 x 256 tiles (a quarter fewer LDS bytes per MFMA) and one LDS copy,
+    // two workgroups per CU (8-10% faster there, slower on weight streaming).
     const bool two_bufs = mt_inner != 0;
     auto gemm = [&](auto dual, auto epi, const bf16_t* a, const bf16_t* b, int N, int K, bf16_t* c) {
       constexpr bool kD = decltype(dual)::value;
       constexpr int kE = decltype(epi)::value;
-      if (two_bufs) {
-        static const int blocks = persistent_blocks(grouped_gemm_bf16_kernel<kD, kE, 2>);
-        hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kD, kE, 2>), dim3(blocks), dim3(kGemmThreads), 0, stream,
-                           a, b, expert_offset, E, N, K, mt_inner, c);
+      const int nk = K / kBK;
+      if (packed && mt_inner && nk % MOE_STREAM_DEPTH == 0) {
+        launch_persistent<stream_gemm_bf16_kernel<kD, kE, MOE_STREAM_DEPTH>>(stream, a, b, expert_offset, E, N,
+                                                                              K, c);
+      } else if (two_bufs) {
+        if (packed)
+          launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 2, MOE_GEMM_NB_STREAM, true>>(
+              stream, a, b, expert_offset, E, N, K, mt_inner, c);
+        else
+          launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 2, MOE_GEMM_NB_STREAM, false>>(
+              stream, a, b, expert_offset, E, N, K, mt_inner, c);
       } else {
-        static const int blocks = persistent_blocks(grouped_gemm_bf16_kernel<kD, kE, 1>);
-        hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kD, kE, 1>), dim3(blocks), dim3(kGemmThreads), 0, stream,
-                           a, b, expert_offset, E, N, K, mt_inner, c);
+        if (packed)
+          launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 1, MOE_GEMM_NB_MFMA, true>>(
+              stream, a, b, expert_offset, E, N, K, mt_inner, c);
+        else
+          launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 1, MOE_GEMM_NB_MFMA, false>>(
+              stream, a, b, expert_offset, E, N, K, mt_inner, c);
       }
     };
     using std::integral_constant;

@@ -86,7 +86,8 @@ hipError_t launch_combine(const void* Y, int dtype, const int32_t* token_offset,
 size_t ffn_workspace_bytes(int64_t M_max, int E, int d, int f, int act, int dtype);
 hipError_t launch_expert_ffn(const void* X_perm, int dtype, const int32_t* expert_offset, int E,
                              int d, int f, int act, const void* W1, const void* W2, int64_t M_max,
-                             void* Y_perm, void* ws, hipStream_t stream);
+                             void* Y_perm, void* ws, bool packed, hipStream_t stream);
+hipError_t launch_pack_weights(const void* W, int E, int R, int K, int gate_up, void* P, hipStream_t stream);
 
 // stats.hip
 size_t stats_workspace_bytes(int n, int E);

@@ -26,9 +26,14 @@ class MoELayer:
     tensors wg [d,E], w1 [E, f|2f, d], w2 [E, d, f] and optionally
     logit_offset [E], sel_bias [E], noise [n,E] (standard normals of noisy
     top-k, scaled by cfg.noise_std), shared_w1, shared_w2.  bf16 tensors may
-    be torch.bfloat16 or raw uint16 bit patterns."""
+    be torch.bfloat16 or raw uint16 bit patterns.
 
-    def __init__(self, cfg, weights: dict, device="cuda"):
+    packed (bf16 only; default on): the expert weights are copied once, at
+    construction, into the packed operand order of moe_pack_expert_weights
+    and the FFNs run moe_expert_ffn_packed (same results, contiguous weight
+    reads).  Later changes to weights["w1"] etc. are not seen."""
+
+    def __init__(self, cfg, weights: dict, device="cuda", packed: Optional[bool] = None):
         self.cfg = cfg
         self.device = torch.device(device)
         self.w = weights
@@ -71,6 +76,15 @@ class MoELayer:
         self.ws_ffn = _bytes(N.moe_ffn_workspace_size(self.M_max, E, d, cfg.f, self.act,
                                                       self.dtype_code), dev)
         self.shared = bool(getattr(cfg, "shared_f", 0))
+        bf16 = self.dtype_code == N.MOE_BF16
+        self.packed = bf16 if packed is None else bool(packed)
+        if self.packed:
+            if not bf16:
+                raise ValueError("packed expert weights are bf16 only")
+            self.w1p, self.w2p = N.pack_ffn_weights(weights["w1"], weights["w2"], self.act)
+            if self.shared:
+                self.shared_w1p, self.shared_w2p = N.pack_ffn_weights(weights["shared_w1"],
+                                                                      weights["shared_w2"], self.act)
         if self.shared:
             self.shared_out = torch.empty((n, d), dtype=edt, device=dev)
             self.shared_offsets = torch.tensor([0, n], **i32)
@@ -89,8 +103,19 @@ class MoELayer:
         N.moe_build_map(self.sel_idx, self.sel_gate, self.rcfg, self.map, self.ws_route, stream)
 
     def experts(self, x, stream=None):
-        w = self.w
         N.moe_dispatch(x, self.map, self.x_perm, stream)
+        self.expert_ffn(x, stream)
+
+    def expert_ffn(self, x, stream=None):
+        """The routed experts on the dispatched rows (and the shared expert on x)."""
+        w = self.w
+        if self.packed:
+            N.moe_expert_ffn_packed(self.x_perm, self.map.expert_offset, self.w1p, self.w2p, self.act,
+                                    self.y_perm, self.ws_ffn, stream)
+            if self.shared:
+                N.moe_expert_ffn_packed(x, self.shared_offsets, self.shared_w1p, self.shared_w2p, self.act,
+                                        self.shared_out, self.ws_shared, stream)
+            return
         N.moe_expert_ffn(self.x_perm, self.map.expert_offset, w["w1"], w["w2"], self.act,
                          self.y_perm, self.ws_ffn, stream)
         if self.shared:

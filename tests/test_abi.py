@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     for name in names:
         assert hasattr(L, name), name
     assert sorted(N.EXPORTED) == names
@@ -132,6 +132,27 @@ def test_null_pointers_and_unsupported_shapes(L):
     st = L.moe_expert_ffn(FAKE, N.MOE_BF16, None, 8, 128, 128, N.MOE_GELU, FAKE, FAKE, 64, FAKE,
                           FAKE, 1 << 30, None)
     assert st == N.MOE_ERR_INVALID_ARG
+
+
+def test_packed_weight_validation(L):
+    pack = L.moe_pack_expert_weights
+    assert pack(None, 8, 128, 64, 0, FAKE, None) == N.MOE_ERR_INVALID_ARG
+    assert pack(FAKE, 8, 128, 64, 0, FAKE, None) == N.MOE_ERR_INVALID_ARG          # aliased
+    assert pack(FAKE, 8, 100, 64, 0, FAKE + 4096, None) == N.MOE_ERR_UNSUPPORTED   # rows % 32
+    assert pack(FAKE, 8, 96, 64, 1, FAKE + 4096, None) == N.MOE_ERR_UNSUPPORTED    # gate/up: rows % 64
+    assert pack(FAKE, 8, 128, 48, 0, FAKE + 4096, None) == N.MOE_ERR_UNSUPPORTED   # K % 64
+    assert pack(FAKE, 8, 128, 64, 2, FAKE + 4096, None) == N.MOE_ERR_INVALID_ARG
+    assert pack(FAKE + 8, 8, 128, 64, 0, FAKE + 4096, None) == N.MOE_ERR_INVALID_ARG   # misaligned
+    ffn = L.moe_expert_ffn_packed
+    assert ffn(None, None, 8, 128, 128, N.MOE_GELU, None, None, 0, None, None, 0, None) == N.MOE_OK
+    assert ffn(FAKE, FAKE, 8, 100, 128, N.MOE_GELU, FAKE, FAKE, 64, FAKE, FAKE, 1 << 30, None) == \
+        N.MOE_ERR_UNSUPPORTED
+    assert ffn(FAKE, FAKE, 8, 128, 128, N.MOE_GELU, FAKE, FAKE, 64, FAKE, FAKE, 16, None) == \
+        N.MOE_ERR_WORKSPACE
+    assert ffn(FAKE, None, 8, 128, 128, N.MOE_SWIGLU, FAKE, FAKE, 64, FAKE, FAKE, 1 << 30, None) == \
+        N.MOE_ERR_INVALID_ARG
+    assert ffn(FAKE, FAKE, 8, 128, 128, 7, FAKE, FAKE, 64, FAKE, FAKE, 1 << 30, None) == \
+        N.MOE_ERR_INVALID_ARG
 
 
 def test_workspace_checks(L):

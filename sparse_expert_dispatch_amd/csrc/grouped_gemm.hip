@@ -66,20 +66,42 @@ enum { kEpiNone = 0, kEpiGelu = 1, kEpiSwiglu = 2 };
 // GELU x * Phi(x) with erf from Abramowitz & Stegun formula 7.1.26
 // (|error| <= 1.5e-7 over the real line, far below the bf16 rounding of the
 // result): erf(z) = 1 - (a1 t + ... + a5 t^5) exp(-z^2), t = 1 / (1 + p z),
-// z >= 0, odd extension for z < 0.  The reciprocals here and in SiLU are
-// the hardware's v_rcp_f32 (1 ulp): a correctly rounded division costs
-// several times more, and the activation runs on every hidden element in
-// the GEMM epilogue, where it stalls the matrix cores.
+// z >= 0, odd extension for z < 0.  The activation runs on every hidden
+// element in the GEMM epilogue, where its VALU work stalls the matrix
+// cores, so it is written for instruction count: the polynomial and the
+// final scaling as fused multiply-adds, exp(-z^2) as the hardware's
+// v_exp_f32 on -z^2 log2(e), and the reciprocals here and in SiLU as
+// v_rcp_f32 (1 ulp).  About 15 VALU instructions per element.
 MOE_DEV float gelu_f(float x) {
   const float z = fabsf(x) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * z);
-  const float poly =
-      t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
-  const float erf_z = 1.0f - poly * __expf(-z * z);
-  const float erf_x = x < 0.f ? -erf_z : erf_z;
-  return 0.5f * x * (1.0f + erf_x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  const float q = fmaf(fmaf(fmaf(fmaf(1.061405429f, t, -1.453152027f), t, 1.421413741f), t, -0.284496736f), t,
+                       0.254829592f);
+  const float e = __builtin_amdgcn_exp2f((z * z) * -1.44269504088896341f);
+  const float erf_z = fmaf(-(q * t), e, 1.0f);
+  const float hx = 0.5f * x;
+  return fmaf(hx, copysignf(erf_z, x), hx);
 }
-MOE_DEV float silu_f(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+MOE_DEV float silu_f(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.44269504088896341f));
+}
+
+// Two bf16 roundings in one v_cvt_pk_bf16_f32 (round to nearest even, the
+// same bits as f32_to_bf16 for finite inputs); lo in bits 0..15.
+MOE_DEV uint32_t bf16x2_rne(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+// The epilogue value of one accumulator element: SwiGLU silu(gate) * up,
+// GELU, or the plain product.
+template <int kEpi>
+MOE_DEV float epi_value(float g, float u) {
+  if (kEpi == kEpiSwiglu) return silu_f(g) * u;
+  if (kEpi == kEpiGelu) return gelu_f(g);
+  return g;
+}
 
 // Tile list, built by every workgroup in LDS at kernel start (no separate
 // launch, no host synchronisation): tile_off[e] = sum over e' < e of
@@ -335,23 +357,25 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict_
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+        for (int v = 0; v < 16; v += 2) {         // elements v, v + 1: rows r, r + 1 of one column
           const int r = wm * 64 + i * 32 + (v >> 2) * 8 + ((lane >> 5) << 2) + (v & 3);
           if (kDual) {
 #pragma unroll
             for (int j = 0; j < kNB / 2; ++j) {
               const int col = wn * (kBNout / 2) + j * 32 + (lane & 31);
-              const float g = acc[i][j][v], u = acc[i][j + kNB / 2][v];
-              sC[r * kCStride + col] = f32_to_bf16(silu_f(g) * u);
+              const uint32_t h = bf16x2_rne(epi_value<kEpi>(acc[i][j][v], acc[i][j + kNB / 2][v]),
+                                            epi_value<kEpi>(acc[i][j][v + 1], acc[i][j + kNB / 2][v + 1]));
+              sC[r * kCStride + col] = (bf16_t)h;
+              sC[(r + 1) * kCStride + col] = (bf16_t)(h >> 16);
             }
           } else {
 #pragma unroll
             for (int j = 0; j < kNB; ++j) {
               const int col = wn * kNB * 32 + j * 32 + (lane & 31);
               if (col / kPassCols != p) continue;
-              float x = acc[i][j][v];
-              if (kEpi == kEpiGelu) x = gelu_f(x);
-              sC[r * kCStride + col - p * kPassCols] = f32_to_bf16(x);
+              const uint32_t h = bf16x2_rne(epi_value<kEpi>(acc[i][j][v], 0.f), epi_value<kEpi>(acc[i][j][v + 1], 0.f));
+              sC[r * kCStride + col - p * kPassCols] = (bf16_t)h;
+              sC[(r + 1) * kCStride + col - p * kPassCols] = (bf16_t)(h >> 16);
             }
           }
         }
@@ -555,16 +579,21 @@ stream_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
+      for (int v = 0; v < 16; v += 2) {           // elements v, v + 1: rows r, r + 1 of one column
         const int r = i * 32 + (v >> 2) * 8 + ((lane >> 5) << 2) + (v & 3);
         if (kDual) {
-          sC[r * kCStride + wave * 32 + (lane & 31)] = f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
+          const int col = wave * 32 + (lane & 31);
+          const uint32_t h = bf16x2_rne(epi_value<kEpi>(acc[i][0][v], acc[i][1][v]),
+                                        epi_value<kEpi>(acc[i][0][v + 1], acc[i][1][v + 1]));
+          sC[r * kCStride + col] = (bf16_t)h;
+          sC[(r + 1) * kCStride + col] = (bf16_t)(h >> 16);
         } else {
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
-            float x = acc[i][b][v];
-            if (kEpi == kEpiGelu) x = gelu_f(x);
-            sC[r * kCStride + wave * 64 + b * 32 + (lane & 31)] = f32_to_bf16(x);
+            const int col = wave * 64 + b * 32 + (lane & 31);
+            const uint32_t h = bf16x2_rne(epi_value<kEpi>(acc[i][b][v], 0.f), epi_value<kEpi>(acc[i][b][v + 1], 0.f));
+            sC[r * kCStride + col] = (bf16_t)h;
+            sC[(r + 1) * kCStride + col] = (bf16_t)(h >> 16);
           }
         }
       }

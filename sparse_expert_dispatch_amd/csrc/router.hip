@@ -7,11 +7,11 @@
 //
 // bf16 path, three kernels: W_g [d, E] is first transposed to W_g^T [E, d]
 // in the workspace (K-contiguous rows, so a matrix-core B fragment is one
-// 16-byte load); the GEMM kernel then runs v_mfma_f32_16x16x32_bf16 with no
-// LDS, every wave owning 16 token rows and up to 64 experts, X read once from
-// HBM; K is split across workgroups (up to 8 slices) until the grid holds at
-// least 512 workgroups.  The per-slice partial logits go to the workspace;
-// the finalize kernel adds the slices in slice order (so the result is
+// 16-byte load); the GEMM kernel then runs v_mfma_f32_16x16x32_bf16 on
+// 128-row x 64-expert workgroup tiles, X read once from HBM, W_g^T shared
+// through LDS; K is split across workgroups (up to 8 slices) until the grid
+// fills the GPU.  The per-slice partial logits go to the workspace; the
+// finalize kernel adds the slices in slice order (so the result is
 // deterministic), adds the offset and evaluates the scores.
 
 #include "device_common.hpp"
@@ -25,9 +25,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRouterBK = 64;      // K per pipeline stage
-constexpr int kRouterCols = 256;   // expert columns per workgroup (4 waves x 64)
 constexpr int kRouterSplitsMax = 8;
-constexpr int kRouterDepth = 4;   // K stages in flight per wave
 
 // W_g^T [E][d] from W_g [d][E]: each workgroup moves a 64 (K) x 64
 // (expert) tile through LDS with 16-byte global loads and stores (E is a
@@ -74,79 +72,109 @@ __global__ __launch_bounds__(256) void router_wg_transpose_kernel(const bf16_t* 
   }
 }
 
-// Z = X W_g on the matrix cores with no LDS: every wave owns 16 token rows
-// and up to 64 expert columns (4 tiles of v_mfma_f32_16x16x32_bf16) over one
-// K slice; A fragments come from X and B fragments from W_g^T, both as
-// 16-byte loads of 8 consecutive K values; kRouterDepth K stages are in
-// flight while the oldest is multiplied.  A workgroup is 4 waves: 64, 32 or
-// 16 rows by 64, 128 or 256 columns depending on E.
+// Z = X W_g on the matrix cores.  A workgroup (4 waves) owns 128 token rows
+// and 64 expert columns over one K slice: each wave 32 rows (2 x 4 tiles of
+// v_mfma_f32_16x16x32_bf16), its X fragments loaded straight from HBM as
+// 16-byte chunks of 8 consecutive K values; the 64 x 64 W_g^T block of each
+// K stage is loaded once per workgroup into LDS (rows padded by 16 bytes:
+// the fragment reads are conflict-free) and shared by the four waves.  With
+// 16 rows per wave and W_g^T fragments read from L2 by every wave, W_g
+// traffic was four times X's; here it is half.  The next stage's X and W_g^T
+// loads are in flight in registers while the current stage is multiplied.
+constexpr int kRouterRows = 128;   // token rows per workgroup (4 waves x 32)
+constexpr int kRouterAhead = 4;    // K stages in flight
+constexpr int kRouterECols = 64;   // expert columns per workgroup
+constexpr int kRouterWStride = kRouterBK + 8;
+
 __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ WgT, int n, int d, int E, int k_per_split,
-    int ncg, float* __restrict__ partial) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int rg = wave / ncg, cg = wave % ncg;
-  const int rows_per_wg = 16 * (4 / ncg);
-  const int row0 = blockIdx.x * rows_per_wg + 16 * rg;
-  const int c0 = blockIdx.z * kRouterCols + 64 * cg;
+    float* __restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) bf16_t sW[2][kRouterECols * kRouterWStride];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row0 = blockIdx.x * kRouterRows + 32 * wave;
+  const int c0 = blockIdx.z * kRouterECols;
   const int split = blockIdx.y;
-  if (c0 >= E || row0 >= n) return;
-  const int nt = min(4, (E - c0) >> 4);                 // 16-column tiles of this wave
+  const int nt = min(4, (E - c0) >> 4);                 // 16-column tiles of this workgroup
   const int kbeg = split * k_per_split;
   const int nk = k_per_split / kRouterBK;
   const int kl = (lane >> 4) << 3;
-  const bf16_t* ap = X + (size_t)min(row0 + (lane & 15), n - 1) * d + kbeg + kl;
-  const bf16_t* bp[4];
+  // X fragment sources: row tile i, lane -> row (lane % 16), K offset kl
+  const bf16_t* xp[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) bp[j] = WgT + (size_t)(c0 + 16 * min(j, nt - 1) + (lane & 15)) * d + kbeg + kl;
+  for (int i = 0; i < 2; ++i) xp[i] = X + (size_t)min(row0 + 16 * i + (lane & 15), n - 1) * d + kbeg + kl;
+  // W_g^T stage loads: 64 rows x 8 chunks of 16 bytes, two per thread (rows
+  // past E re-read the last expert; their columns are never stored)
+  const int wr = tid >> 3, wc = (tid & 7) << 3;
+  const bf16_t* wp[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) wp[h] = WgT + (size_t)min(c0 + wr + 32 * h, E - 1) * d + kbeg + wc;
 
-  f32x4_t acc[4];
+  f32x4_t acc[2][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // register ring of kRouterDepth K stages: all of them are loading while
-  // the oldest is multiplied
-  bf16x8_t a[kRouterDepth][2], b[kRouterDepth][2][4];     // [slot][32-wide K step][tile]
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // Stage ring: kRouterAhead stages of X (registers) and W_g^T (registers,
+  // then LDS) are in flight while the oldest is multiplied; ring slots are
+  // compile-time (a partial last round is skipped stage by stage, uniformly
+  // across the workgroup).
+  bf16x8_t xr[kRouterAhead][2][2];                      // [slot][32-wide K step][row tile]
+  u32x4_t wr_[kRouterAhead][2];
   auto load = [&](int st, int q) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      a[q][s] = *reinterpret_cast<const bf16x8_t*>(ap + st * kRouterBK + 32 * s);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (j < nt) b[q][s][j] = *reinterpret_cast<const bf16x8_t*>(bp[j] + st * kRouterBK + 32 * s);
-    }
-  };
-  auto mma = [&](int q) {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (j < nt) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q][s], b[q][s][j], acc[j], 0, 0, 0);
+      for (int i = 0; i < 2; ++i) xr[q][s][i] = *reinterpret_cast<const bf16x8_t*>(xp[i] + st * kRouterBK + 32 * s);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) wr_[q][h] = *reinterpret_cast<const u32x4_t*>(wp[h] + st * kRouterBK);
+  };
+  auto store_w = [&](int q, int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<u32x4_t*>(&sW[buf][(wr + 32 * h) * kRouterWStride + wc]) = wr_[q][h];
   };
 #pragma unroll
-  for (int q = 0; q < kRouterDepth; ++q)
+  for (int q = 0; q < kRouterAhead; ++q)
     if (q < nk) load(q, q);
-  for (int st = 0; st < nk; st += kRouterDepth) {
+  for (int st0 = 0; st0 < nk; st0 += kRouterAhead) {
 #pragma unroll
-    for (int q = 0; q < kRouterDepth; ++q) {
-      if (st + q < nk) {
-        mma(q);
-        if (st + q + kRouterDepth < nk) load(st + q + kRouterDepth, q);
+    for (int q = 0; q < kRouterAhead; ++q) {
+      const int st = st0 + q;
+      if (st >= nk) break;
+      const int buf = st & 1;
+      store_w(q, buf);
+      __syncthreads();                               // W stage visible; the other buffer is free
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (j < nt) {
+            const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(
+                &sW[buf][(16 * j + (lane & 15)) * kRouterWStride + 32 * s + kl]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xr[q][s][i], b, acc[i][j], 0, 0, 0);
+          }
+        }
       }
+      if (st + kRouterAhead < nk) load(st + kRouterAhead, q);
     }
   }
   // C fragment: lane holds column (lane % 16), rows (lane / 16) * 4 + r.
   float* out = partial + (size_t)split * n * E;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (j < nt) {
-      const int col = c0 + j * 16 + (lane & 15);
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = row0 + ((lane >> 4) << 2) + r;
-        if (row < n) out[(size_t)row * E + col] = acc[j][r];
+    for (int j = 0; j < 4; ++j) {
+      if (j < nt) {
+        const int col = c0 + j * 16 + (lane & 15);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = row0 + 16 * i + ((lane >> 4) << 2) + r;
+          if (row < n) out[(size_t)row * E + col] = acc[i][j][r];
+        }
       }
     }
-  }
 }
 
 // Scalar router for fp32 inputs and for shapes the MFMA tiling does not
@@ -204,8 +232,15 @@ __global__ __launch_bounds__(1024) void router_finalize_kernel(
       const int e = lane + 64 * j;
       z[j] = 0.f;
       if (j < nj && e < E) {
-        float v = partial[(size_t)row * E + e];
-        for (int s = 1; s < nsplit; ++s) v = v + partial[(size_t)s * n * E + (size_t)row * E + e];
+        // all slices' loads in flight at once, then added in slice order
+        float ps[kRouterSplitsMax];
+#pragma unroll
+        for (int s = 0; s < kRouterSplitsMax; ++s)
+          ps[s] = s < nsplit ? partial[(size_t)s * n * E + (size_t)row * E + e] : 0.f;
+        float v = ps[0];
+#pragma unroll
+        for (int s = 1; s < kRouterSplitsMax; ++s)
+          if (s < nsplit) v = v + ps[s];
         if (offset) v = v + offset[e];
         if (noise) v = v + noise_std * noise[(size_t)row * E + e];
         z[j] = v;
@@ -255,12 +290,7 @@ hipError_t launch_router_finalize(const float* partial, int nsplit, int n, int E
                                   const float* noise, float noise_std, int score, float* logits,
                                   float* scores, float* scores_t, hipStream_t stream);
 
-static int router_ncg(int E) { return E >= 256 ? 4 : (E > 64 ? 2 : 1); }
-
-static int router_row_blocks(int n, int E) {
-  const int rows = 16 * (4 / router_ncg(E));
-  return (n + rows - 1) / rows;
-}
+static int router_row_blocks(int n) { return (n + kRouterRows - 1) / kRouterRows; }
 
 // Split K until there are at least MOE_ROUTER_MIN_WGS workgroups (each
 // slice a multiple of the 64-wide stage).
@@ -268,7 +298,7 @@ static int router_row_blocks(int n, int E) {
 #define MOE_ROUTER_MIN_WGS 256
 #endif
 static int router_splits(int n, int d, int E) {
-  const int blocks = router_row_blocks(n, E) * ((E + kRouterCols - 1) / kRouterCols);
+  const int blocks = router_row_blocks(n) * ((E + kRouterECols - 1) / kRouterECols);
   const int kb = d / kRouterBK;
   int s = 1;
   while (s < kRouterSplitsMax && blocks * s < MOE_ROUTER_MIN_WGS && kb % (2 * s) == 0) s *= 2;
@@ -297,9 +327,9 @@ hipError_t launch_router(const void* X, const void* Wg, int dtype, const float* 
     float* dst = nsplit > 1 ? reinterpret_cast<float*>(w + align256((size_t)E * d * sizeof(bf16_t))) : logits;
     hipLaunchKernelGGL(router_wg_transpose_kernel, dim3(d / 64, (E + 63) / 64), dim3(256), 0, stream,
                        static_cast<const bf16_t*>(Wg), d, E, WgT);
-    dim3 grid(router_row_blocks(n, E), nsplit, (E + kRouterCols - 1) / kRouterCols);
+    dim3 grid(router_row_blocks(n), nsplit, (E + kRouterECols - 1) / kRouterECols);
     hipLaunchKernelGGL(router_gemm_bf16_kernel, grid, dim3(256), 0, stream,
-                       static_cast<const bf16_t*>(X), WgT, n, d, E, d / nsplit, router_ncg(E), dst);
+                       static_cast<const bf16_t*>(X), WgT, n, d, E, d / nsplit, dst);
     partial = dst;
   } else if (dtype == 1) {
     hipLaunchKernelGGL(router_gemm_scalar_kernel<bf16_t>, sgrid, dim3(256), 0, stream,

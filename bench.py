@@ -157,7 +157,8 @@ def main():
         lambda: N.moe_select(layer.logits, None if tc else layer.scores_t, w.get("sel_bias"), layer.rcfg,
                              layer.sel_idx, layer.sel_gate, layer.ws_route),
         lambda: N.moe_build_map(layer.sel_idx, layer.sel_gate, layer.rcfg, layer.map, layer.ws_route),
-        lambda: N.moe_dispatch(x, layer.map, layer.x_perm),
+        # packed weights: the up GEMM gathers the rows itself (no call here)
+        lambda: None if layer.packed else layer.dispatch(x),
     ]
 
     def ffn_part():
@@ -219,6 +220,9 @@ def main():
     alg = algorithmic(cfg, k, M, touched)
     stages = {}
     for s in STAGES:
+        if s == "dispatch" and layer.packed:
+            stages[s] = {"fused": "into expert_ffn: the up GEMM gathers X rows through slot_token"}
+            continue
         ms = float(np.mean(stage_ms[s]))
         a = alg[s]
         stages[s] = {"us": round(ms * 1e3, 2), "GB/s": round(a["bytes"] / (ms * 1e-3) / 1e9, 1),

@@ -254,12 +254,23 @@ moe_status_t moe_expert_ffn(const void *X_perm, int32_t dtype, const int32_t *ex
 moe_status_t moe_pack_expert_weights(const void *W, int32_t E, int32_t rows, int32_t K, int32_t gate_up,
                                      void *W_packed, void *stream);
 
-/* moe_expert_ffn (bf16) on packed weights: same rows, same arithmetic and
- * the same output bits as moe_expert_ffn on the unpacked weights; the same
- * workspace size (moe_ffn_workspace_size with MOE_BF16) and shape rules. */
-moe_status_t moe_expert_ffn_packed(const void *X_perm, const int32_t *expert_offset, int32_t E, int32_t d,
-                                   int32_t f, int32_t act, const void *W1_packed, const void *W2_packed,
-                                   int64_t M_max, void *Y_perm, void *ws, size_t ws_bytes, void *stream);
+/* moe_expert_ffn (bf16) on packed weights, optionally with the dispatch
+ * fused in: the same arithmetic and the same output bits as moe_dispatch +
+ * moe_expert_ffn on the unpacked weights; the same workspace size
+ * (moe_ffn_workspace_size with MOE_BF16) and shape rules.
+ *   row_index NULL: X is X_perm (the dispatched rows, slot s = row s; n_x is
+ *     ignored).
+ *   row_index non-NULL: X is the token matrix [n_x, d] and slot s of expert
+ *     e reads X[row_index[s]] (page 2 "The math": X_in = P X, taken by the
+ *     GEMM's own row loads instead of a separate gather); pass the routing
+ *     map's slot_token.  Entries outside [0, n_x) are clamped into it (the
+ *     map never produces them).
+ * Y_perm rows are the slots either way; rows >= expert_offset[E] are left
+ * untouched. */
+moe_status_t moe_expert_ffn_packed(const void *X, int32_t n_x, const int32_t *row_index,
+                                   const int32_t *expert_offset, int32_t E, int32_t d, int32_t f, int32_t act,
+                                   const void *W1_packed, const void *W2_packed, int64_t M_max, void *Y_perm,
+                                   void *ws, size_t ws_bytes, void *stream);
 
 /* Combine out = scatter_add(G * Y, I) (page 2 "The math"), the gate applied
  * to the expert output: for every token, out = residual + shared_out + sum

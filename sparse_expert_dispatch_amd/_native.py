@@ -87,7 +87,7 @@ def lib() -> ctypes.CDLL:
         "moe_balance_stats": (I32, [P, MAP, CFG, F32, F32, P, P, P, SZ, P]),
         "moe_update_bias": (I32, [P, CFG, F32, P, P]),
         "moe_pack_expert_weights": (I32, [P, I32, I32, I32, I32, P, P]),
-        "moe_expert_ffn_packed": (I32, [P, P, I32, I32, I32, I32, P, P, I64, P, P, SZ, P]),
+        "moe_expert_ffn_packed": (I32, [P, I32, P, P, I32, I32, I32, I32, P, P, I64, P, P, SZ, P]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_last_error": (ctypes.c_char_p, []),
     }
@@ -317,15 +317,23 @@ def pack_ffn_weights(w1, w2, act: int, stream=None):
     return w1p, w2p
 
 
-def moe_expert_ffn_packed(x_perm, expert_offset, w1p, w2p, act: int, y_perm, ws, stream=None):
+def moe_expert_ffn_packed(x, expert_offset, w1p, w2p, act: int, y_perm, ws, stream=None, row_index=None,
+                          m_max=None):
+    """Packed-weight FFN.  row_index=None: x is x_perm (rows = slots).
+    row_index = the map's slot_token: x is the token matrix [n, d] and the
+    up GEMM gathers its rows (the dispatch fused in); m_max then gives the
+    slot count (default: y_perm's rows)."""
     E = expert_offset.numel() - 1
-    d = x_perm.shape[1]
+    d = x.shape[1]
     f = w2p.shape[-1]
+    M_max = int(m_max if m_max is not None else (y_perm.shape[0] if row_index is not None else x.shape[0]))
     w, wb = _ws(ws)
     bf = _elem_dtypes(MOE_BF16)
-    _check(lib().moe_expert_ffn_packed(_ptr(x_perm, "x_perm", bf), _ptr(expert_offset, "expert_offset", _I32),
+    _check(lib().moe_expert_ffn_packed(_ptr(x, "x", bf), int(x.shape[0]),
+                                       _ptr(row_index, "row_index", _I32) if row_index is not None else None,
+                                       _ptr(expert_offset, "expert_offset", _I32),
                                        int(E), int(d), int(f), int(act), _ptr(w1p, "w1_packed", bf),
-                                       _ptr(w2p, "w2_packed", bf), int(x_perm.shape[0]),
+                                       _ptr(w2p, "w2_packed", bf), M_max,
                                        _ptr(y_perm, "y_perm", bf), w, wb, _stream(stream)),
            "moe_expert_ffn_packed")
 

@@ -265,8 +265,8 @@ moe_status_t moe_expert_ffn(const void* X_perm, int32_t dtype, const int32_t* ex
   if (!ws || ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "expert_ffn needs %zu workspace bytes, got %zu", need, ws_bytes);
   REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
-  return launched(moe::launch_expert_ffn(X_perm, dtype, expert_offset, E, d, f, act, W1, W2, M_max,
-                                         Y_perm, ws, false, as_stream(stream)),
+  return launched(moe::launch_expert_ffn(X_perm, nullptr, 0, dtype, expert_offset, E, d, f, act, W1, W2,
+                                         M_max, Y_perm, ws, false, as_stream(stream)),
                   "moe_expert_ffn");
 }
 
@@ -283,25 +283,27 @@ moe_status_t moe_pack_expert_weights(const void* W, int32_t E, int32_t rows, int
                   "moe_pack_expert_weights");
 }
 
-moe_status_t moe_expert_ffn_packed(const void* X_perm, const int32_t* expert_offset, int32_t E, int32_t d,
-                                   int32_t f, int32_t act, const void* W1_packed, const void* W2_packed,
-                                   int64_t M_max, void* Y_perm, void* ws, size_t ws_bytes, void* stream) {
+moe_status_t moe_expert_ffn_packed(const void* X, int32_t n_x, const int32_t* row_index,
+                                   const int32_t* expert_offset, int32_t E, int32_t d, int32_t f, int32_t act,
+                                   const void* W1_packed, const void* W2_packed, int64_t M_max, void* Y_perm,
+                                   void* ws, size_t ws_bytes, void* stream) {
   REQUIRE(E > 0 && d > 0 && f > 0 && M_max >= 0, "E, d, f must be positive, M_max non-negative");
   if (M_max == 0) return MOE_OK;                  // no rows: nothing to compute
-  REQUIRE(X_perm && expert_offset && W1_packed && W2_packed && Y_perm, "tensor arguments must be non-NULL");
+  REQUIRE(X && expert_offset && W1_packed && W2_packed && Y_perm, "tensor arguments must be non-NULL");
+  REQUIRE(!row_index || n_x > 0, "n_x must be positive when row_index is given");
   REQUIRE(act == MOE_GELU || act == MOE_SWIGLU, "act must be MOE_GELU or MOE_SWIGLU");
   REQUIRE(M_max <= INT32_MAX, "M_max must fit in int32");
   SUPPORTED(E <= moe::kMaxExperts, "bf16 expert FFN supports E <= %d (E=%d)", moe::kMaxExperts, E);
   SUPPORTED(d % 64 == 0 && f % 64 == 0, "bf16 expert FFN needs d %% 64 == 0 and f %% 64 == 0 (d=%d f=%d)",
             d, f);
-  REQUIRE(aligned16(X_perm) && aligned16(W1_packed) && aligned16(W2_packed) && aligned16(Y_perm),
+  REQUIRE(aligned16(X) && aligned16(W1_packed) && aligned16(W2_packed) && aligned16(Y_perm),
           "bf16 tensors must be 16-byte aligned");
   const size_t need = moe::ffn_workspace_bytes(M_max, E, d, f, act, MOE_BF16);
   if (!ws || ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "expert_ffn needs %zu workspace bytes, got %zu", need, ws_bytes);
   REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
-  return launched(moe::launch_expert_ffn(X_perm, MOE_BF16, expert_offset, E, d, f, act, W1_packed, W2_packed,
-                                         M_max, Y_perm, ws, true, as_stream(stream)),
+  return launched(moe::launch_expert_ffn(X, row_index, n_x, MOE_BF16, expert_offset, E, d, f, act, W1_packed,
+                                         W2_packed, M_max, Y_perm, ws, true, as_stream(stream)),
                   "moe_expert_ffn_packed");
 }
 

@@ -153,9 +153,9 @@ MOE_DEV int b_row_of(int r, int n0, int N) {
 // chunks); otherwise B is the natural [rows, K] layout.
 template <bool kDual, int kEpi, int kLdsBufs, int kNB, bool kPacked>
 __global__ __launch_bounds__(kGemmThreads, kNB == 4 ? 2 : (kLdsBufs == 1 ? 3 : 1)) void
-grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B,
-                         const int32_t* __restrict__ expert_offset, int E, int N, int K, int mt_inner,
-                         bf16_t* __restrict__ C) {
+grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ row_index, int n_a,
+                         const bf16_t* __restrict__ B, const int32_t* __restrict__ expert_offset, int E,
+                         int N, int K, int mt_inner, bf16_t* __restrict__ C) {
   constexpr int kBRows = 2 * kNB * 32;             // weight rows per tile
   constexpr int kBNout = kDual ? kBRows / 2 : kBRows;
   constexpr int kTileA = 128 * kLdsStride;
@@ -203,34 +203,62 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict_
     return j < half ? 2 * (wn * half + j) : 2 * (wn * half + j - half) + 1;
   };
 
-  // Per-tile state: output placement and the global sources of this
-  // thread's 16-byte staging loads.
-  // Per-tile state (wave-uniform: kept in scalar registers) and, for the
-  // natural B layout, the global sources of this thread's B loads.  A and
-  // packed B addresses are formed per load from the uniform tile base.
-  int row_base = 0, m_valid = 0, n0 = 0;
-  const bf16_t* a_tile = A;
-  const bf16_t* b_tile = B;
-  const bf16_t* b_src[kPacked ? 1 : kLoadsB];
-  auto setup = [&](int64_t t) {
-    // expert owning tile t: expert e holds tiles [tile_off[e] * ntn, tile_off[e+1] * ntn)
+  // Placement of tile t: expert e holds tiles [tile_off[e] * ntn,
+  // tile_off[e+1] * ntn).  Weight-streaming shapes walk an expert's M tiles
+  // innermost (its weight slice is fetched once and the other M tiles hit
+  // L2); shapes with many rows per expert walk N innermost (the A panel
+  // stays in L2).
+  struct Place {
+    int row_base, m_valid, n0, e;
+  };
+  auto place = [&](int64_t t) {
     int e_lo = 0, e_hi = E - 1;
     while (e_lo < e_hi) {
       const int mid = (e_lo + e_hi + 1) >> 1;
       if ((int64_t)tile_off[mid] * ntn <= t) e_lo = mid; else e_hi = mid - 1;
     }
-    const int e = __builtin_amdgcn_readfirstlane(e_lo);
-    const int mtiles = tile_off[e + 1] - tile_off[e];
-    const int local = (int)(t - (int64_t)tile_off[e] * ntn);
-    // weight-streaming shapes walk an expert's M tiles innermost (its weight
-    // slice is fetched once and the other M tiles hit L2); shapes with many
-    // rows per expert walk N innermost (the A panel stays in L2)
+    Place p;
+    p.e = __builtin_amdgcn_readfirstlane(e_lo);
+    const int mtiles = tile_off[p.e + 1] - tile_off[p.e];
+    const int local = (int)(t - (int64_t)tile_off[p.e] * ntn);
     const int mloc = mt_inner ? local % mtiles : local / ntn;
     const int nt = mt_inner ? local / mtiles : local % ntn;
-    row_base = __builtin_amdgcn_readfirstlane(expert_offset[e] + mloc * kBM);
-    m_valid = __builtin_amdgcn_readfirstlane(min(kBM, expert_offset[e + 1] - row_base));
-    n0 = __builtin_amdgcn_readfirstlane(nt * kBNout);
-    a_tile = A + (size_t)row_base * K;
+    p.row_base = __builtin_amdgcn_readfirstlane(expert_offset[p.e] + mloc * kBM);
+    p.m_valid = __builtin_amdgcn_readfirstlane(min(kBM, expert_offset[p.e + 1] - p.row_base));
+    p.n0 = __builtin_amdgcn_readfirstlane(nt * kBNout);
+    return p;
+  };
+  // A rows of this thread's staging loads for tile t: the tile's slots, or
+  // with row_index the rows of A those slots gather (the dispatch fused into
+  // the GEMM); tail rows repeat the last valid one.  The rows of the next
+  // tile are fetched one tile ahead (parked in LDS, which is cheaper than
+  // registers here), so a gathered index is never waited on.
+  __shared__ int nx_row[kLoadsA][kGemmThreads];
+  auto rows_of = [&](int64_t t) {
+    const Place p = place(min(t, hi - 1));
+#pragma unroll
+    for (int i = 0; i < kLoadsA; ++i) {
+      const int s = p.row_base + min(ld_row + kRowsPass * i, p.m_valid - 1);
+      nx_row[i][tid] = row_index ? min(max(row_index[s], 0), n_a - 1) : s;
+    }
+  };
+
+  // Per-tile state (wave-uniform: kept in scalar registers) and, for the
+  // natural B layout, the global sources of this thread's B loads.  Packed B
+  // addresses are formed per load from the uniform tile base.
+  int row_base = 0, m_valid = 0, n0 = 0;
+  int a_row[kLoadsA];
+  const bf16_t* b_tile = B;
+  const bf16_t* b_src[kPacked ? 1 : kLoadsB];
+  auto setup = [&](int64_t t) {
+    const Place p = place(t);
+    const int e = p.e;
+    row_base = p.row_base;
+    m_valid = p.m_valid;
+    n0 = p.n0;
+#pragma unroll
+    for (int i = 0; i < kLoadsA; ++i) a_row[i] = nx_row[i][tid];
+    rows_of(t + per_xcd_blocks);
     // packed: expert e's row blocks in the first K stage's slab; natural: its matrix
     b_tile = kPacked ? B + (size_t)e * (nbrows / 32) * 2048 : B + (size_t)e * nbrows * K;
     if (!kPacked) {
@@ -245,10 +273,8 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict_
   auto load_stage = [&](int st) {
     const int koff = st * kBK;
 #pragma unroll
-    for (int i = 0; i < kLoadsA; ++i) {
-      const int r = min(ld_row + kRowsPass * i, m_valid - 1);     // tail rows re-read the last row
-      ra[i] = *reinterpret_cast<const u32x4_t*>(a_tile + r * K + ld_chunk + koff);
-    }
+    for (int i = 0; i < kLoadsA; ++i)
+      ra[i] = *reinterpret_cast<const u32x4_t*>(A + (size_t)a_row[i] * K + ld_chunk + koff);
 #pragma unroll
     for (int i = 0; i < kLoadsB; ++i) {
       if (kPacked) {
@@ -279,6 +305,7 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict_
 
   int64_t t = lo + blockIdx.x / kXcds;
   if (t >= hi) return;
+  rows_of(t);
   setup(t);
   load_stage(0);
   while (true) {
@@ -426,9 +453,9 @@ MOE_DEV void static_for(F&& f) {
 // at compile time); the launcher checks.
 template <bool kDual, int kEpi, int kDepth>
 __global__ __launch_bounds__(kGemmThreads, 1) void
-stream_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bp,
-                        const int32_t* __restrict__ expert_offset, int E, int N, int K,
-                        bf16_t* __restrict__ C) {
+stream_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ row_index, int n_a,
+                        const bf16_t* __restrict__ Bp, const int32_t* __restrict__ expert_offset, int E,
+                        int N, int K, bf16_t* __restrict__ C) {
   static_assert(kBK == 64, "a stage is four 16-K operand chunks");
   constexpr int kNW = kDual ? 128 : 256;           // output columns per tile
   constexpr int kCStride = kNW + 8;                // bf16 per output row in LDS
@@ -476,17 +503,31 @@ stream_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__
     return p;
   };
 
+  // A rows of this thread's staging loads for tile j: the tile's slots, or
+  // with row_index the rows of A those slots gather (the dispatch fused into
+  // the GEMM); tail rows repeat the last valid one.
+  auto rows_of = [&](int j, int (&rows)[4]) {
+    const Place p = locate(min(j, ntiles - 1));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = p.row_base + min(ld_row + 32 * i, p.m_valid - 1);
+      rows[i] = row_index ? min(max(row_index[s], 0), n_a - 1) : s;
+    }
+  };
+
   // Load cursor: the stage the next issue() fetches.  Past the last tile it
   // re-reads the last stage (in bounds, never used), so every iteration
   // issues the same loads and the compiler's memory-counter waits stay exact.
-  int l_j = 0, l_kt = 0, l_mv = 1;
-  const bf16_t* l_a = A;
+  // The A rows of the next tile are fetched one tile ahead.
+  int l_j = 0, l_kt = 0;
+  int l_row[4], nx_row[4];
   const bf16_t* l_b0 = Bp;
   const bf16_t* l_b1 = Bp;
   auto load_tile = [&](int j) {
     const Place p = locate(min(j, ntiles - 1));
-    l_a = A + (size_t)p.row_base * K;
-    l_mv = p.m_valid;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l_row[i] = nx_row[i];
+    rows_of(j + 1, nx_row);
     int pb0, pb1;
     if (kDual) {
       const int ob = min(p.n0 / 32 + wave, last_pb);
@@ -504,10 +545,8 @@ stream_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__
     constexpr int slot = decltype(slot_c)::value;
     const int kt = l_j < ntiles ? l_kt : nk - 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = min(ld_row + 32 * i, l_mv - 1);             // tail rows re-read the last row
-      ra[slot][i] = *reinterpret_cast<const u32x4_t*>(l_a + r * K + ld_chunk + kt * kBK);
-    }
+    for (int i = 0; i < 4; ++i)
+      ra[slot][i] = *reinterpret_cast<const u32x4_t*>(A + (size_t)l_row[i] * K + ld_chunk + kt * kBK);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       rb[slot][0][s] = *reinterpret_cast<const u32x4_t*>(l_b0 + kt * stage_stride + s * 512);
@@ -528,6 +567,7 @@ stream_gemm_bf16_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__
   };
 
   using std::integral_constant;
+  rows_of(0, nx_row);
   load_tile(0);
   static_for<0, kDepth>([&](auto u) { issue(u); });
   store_a(integral_constant<int, 0>{});
@@ -753,9 +793,10 @@ hipError_t launch_pack_weights(const void* W, int E, int R, int K, int gate_up, 
   return hipGetLastError();
 }
 
-hipError_t launch_expert_ffn(const void* X_perm, int dtype, const int32_t* expert_offset, int E,
-                             int d, int f, int act, const void* W1, const void* W2, int64_t M_max,
-                             void* Y_perm, void* ws, bool packed, hipStream_t stream) {
+hipError_t launch_expert_ffn(const void* X_perm, const int32_t* row_index, int n_x, int dtype,
+                             const int32_t* expert_offset, int E, int d, int f, int act, const void* W1,
+                             const void* W2, int64_t M_max, void* Y_perm, void* ws, bool packed,
+                             hipStream_t stream) {
   char* w = static_cast<char*>(ws);
   void* H = w;
   if (dtype == 1) {
@@ -773,37 +814,41 @@ hipError_t launch_expert_ffn(const void* X_perm, int dtype, const int32_t* exper
     // 128 x 256 tiles (a quarter fewer LDS bytes per MFMA) and one LDS copy,
     // two workgroups per CU (8-10% faster there, slower on weight streaming).
     const bool two_bufs = mt_inner != 0;
-    auto gemm = [&](auto dual, auto epi, const bf16_t* a, const bf16_t* b, int N, int K, bf16_t* c) {
+    // a_index / n_a: rows of A gathered through an index (the up GEMM with a
+    // fused dispatch) or nullptr (A's rows are the slots)
+    auto gemm = [&](auto dual, auto epi, const bf16_t* a, const int32_t* a_index, int n_a, const bf16_t* b,
+                    int N, int K, bf16_t* c) {
       constexpr bool kD = decltype(dual)::value;
       constexpr int kE = decltype(epi)::value;
       const int nk = K / kBK;
       if (packed && mt_inner && nk % MOE_STREAM_DEPTH == 0) {
-        launch_persistent<stream_gemm_bf16_kernel<kD, kE, MOE_STREAM_DEPTH>>(stream, a, b, expert_offset, E, N,
-                                                                              K, c);
+        launch_persistent<stream_gemm_bf16_kernel<kD, kE, MOE_STREAM_DEPTH>>(stream, a, a_index, n_a, b,
+                                                                              expert_offset, E, N, K, c);
       } else if (two_bufs) {
         if (packed)
           launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 2, MOE_GEMM_NB_STREAM, true>>(
-              stream, a, b, expert_offset, E, N, K, mt_inner, c);
+              stream, a, a_index, n_a, b, expert_offset, E, N, K, mt_inner, c);
         else
           launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 2, MOE_GEMM_NB_STREAM, false>>(
-              stream, a, b, expert_offset, E, N, K, mt_inner, c);
+              stream, a, a_index, n_a, b, expert_offset, E, N, K, mt_inner, c);
       } else {
         if (packed)
           launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 1, MOE_GEMM_NB_MFMA, true>>(
-              stream, a, b, expert_offset, E, N, K, mt_inner, c);
+              stream, a, a_index, n_a, b, expert_offset, E, N, K, mt_inner, c);
         else
           launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 1, MOE_GEMM_NB_MFMA, false>>(
-              stream, a, b, expert_offset, E, N, K, mt_inner, c);
+              stream, a, a_index, n_a, b, expert_offset, E, N, K, mt_inner, c);
       }
     };
     using std::integral_constant;
+    const int n_h = (int)M_max;
     if (act == 1)
-      gemm(integral_constant<bool, true>{}, integral_constant<int, kEpiSwiglu>{}, x,
+      gemm(integral_constant<bool, true>{}, integral_constant<int, kEpiSwiglu>{}, x, row_index, n_x,
            static_cast<const bf16_t*>(W1), f, d, h);
     else
-      gemm(integral_constant<bool, false>{}, integral_constant<int, kEpiGelu>{}, x,
+      gemm(integral_constant<bool, false>{}, integral_constant<int, kEpiGelu>{}, x, row_index, n_x,
            static_cast<const bf16_t*>(W1), f, d, h);
-    gemm(integral_constant<bool, false>{}, integral_constant<int, kEpiNone>{}, h,
+    gemm(integral_constant<bool, false>{}, integral_constant<int, kEpiNone>{}, h, nullptr, n_h,
          static_cast<const bf16_t*>(W2), d, f, static_cast<bf16_t*>(Y_perm));
   } else {
     const int64_t up = M_max * f, down = M_max * d;

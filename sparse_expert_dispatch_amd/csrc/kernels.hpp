@@ -84,9 +84,12 @@ hipError_t launch_combine(const void* Y, int dtype, const int32_t* token_offset,
 
 // grouped_gemm.hip
 size_t ffn_workspace_bytes(int64_t M_max, int E, int d, int f, int act, int dtype);
-hipError_t launch_expert_ffn(const void* X_perm, int dtype, const int32_t* expert_offset, int E,
-                             int d, int f, int act, const void* W1, const void* W2, int64_t M_max,
-                             void* Y_perm, void* ws, bool packed, hipStream_t stream);
+// row_index (bf16 only): the up GEMM's A row of slot s is X_perm[row_index[s]]
+// (X_perm then has n_x rows); nullptr: row s.
+hipError_t launch_expert_ffn(const void* X_perm, const int32_t* row_index, int n_x, int dtype,
+                             const int32_t* expert_offset, int E, int d, int f, int act, const void* W1,
+                             const void* W2, int64_t M_max, void* Y_perm, void* ws, bool packed,
+                             hipStream_t stream);
 hipError_t launch_pack_weights(const void* W, int E, int R, int K, int gate_up, void* P, hipStream_t stream);
 
 // stats.hip

@@ -102,16 +102,23 @@ class MoELayer:
                      self.sel_idx, self.sel_gate, self.ws_route, stream)
         N.moe_build_map(self.sel_idx, self.sel_gate, self.rcfg, self.map, self.ws_route, stream)
 
-    def experts(self, x, stream=None):
+    def dispatch(self, x, stream=None):
+        """X_perm = P X as its own gather (the packed FFN fuses it instead)."""
         N.moe_dispatch(x, self.map, self.x_perm, stream)
+
+    def experts(self, x, stream=None):
+        if not self.packed:
+            self.dispatch(x, stream)
         self.expert_ffn(x, stream)
 
     def expert_ffn(self, x, stream=None):
-        """The routed experts on the dispatched rows (and the shared expert on x)."""
+        """The routed experts (and the shared expert on x).  Packed weights:
+        the up GEMM gathers its rows from x through the map's slot_token
+        (dispatch fused in); otherwise it reads the dispatched X_perm."""
         w = self.w
         if self.packed:
-            N.moe_expert_ffn_packed(self.x_perm, self.map.expert_offset, self.w1p, self.w2p, self.act,
-                                    self.y_perm, self.ws_ffn, stream)
+            N.moe_expert_ffn_packed(x, self.map.expert_offset, self.w1p, self.w2p, self.act, self.y_perm,
+                                    self.ws_ffn, stream, row_index=self.map.slot_token, m_max=self.M_max)
             if self.shared:
                 N.moe_expert_ffn_packed(x, self.shared_offsets, self.shared_w1p, self.shared_w2p, self.act,
                                         self.shared_out, self.ws_shared, stream)

@@ -58,6 +58,7 @@ def run_gpu(cfg, inp: dict, weights=None) -> dict:
     layer = MoELayer(cfg, w)
     layer.route(x)
     layer.experts(x)
+    layer.dispatch(x)            # the standalone gather too (the packed FFN fuses it)
     layer.combine(x, residual=False)
     branch = layer.out.clone()
     layer.combine(x, residual=True)

@@ -144,14 +144,17 @@ def test_packed_weight_validation(L):
     assert pack(FAKE, 8, 128, 64, 2, FAKE + 4096, None) == N.MOE_ERR_INVALID_ARG
     assert pack(FAKE + 8, 8, 128, 64, 0, FAKE + 4096, None) == N.MOE_ERR_INVALID_ARG   # misaligned
     ffn = L.moe_expert_ffn_packed
-    assert ffn(None, None, 8, 128, 128, N.MOE_GELU, None, None, 0, None, None, 0, None) == N.MOE_OK
-    assert ffn(FAKE, FAKE, 8, 100, 128, N.MOE_GELU, FAKE, FAKE, 64, FAKE, FAKE, 1 << 30, None) == \
+    assert ffn(None, 0, None, None, 8, 128, 128, N.MOE_GELU, None, None, 0, None, None, 0, None) == N.MOE_OK
+    assert ffn(FAKE, 0, None, FAKE, 8, 100, 128, N.MOE_GELU, FAKE, FAKE, 64, FAKE, FAKE, 1 << 30, None) == \
         N.MOE_ERR_UNSUPPORTED
-    assert ffn(FAKE, FAKE, 8, 128, 128, N.MOE_GELU, FAKE, FAKE, 64, FAKE, FAKE, 16, None) == \
+    assert ffn(FAKE, 0, None, FAKE, 8, 128, 128, N.MOE_GELU, FAKE, FAKE, 64, FAKE, FAKE, 16, None) == \
         N.MOE_ERR_WORKSPACE
-    assert ffn(FAKE, None, 8, 128, 128, N.MOE_SWIGLU, FAKE, FAKE, 64, FAKE, FAKE, 1 << 30, None) == \
+    assert ffn(FAKE, 0, None, None, 8, 128, 128, N.MOE_SWIGLU, FAKE, FAKE, 64, FAKE, FAKE, 1 << 30, None) == \
         N.MOE_ERR_INVALID_ARG
-    assert ffn(FAKE, FAKE, 8, 128, 128, 7, FAKE, FAKE, 64, FAKE, FAKE, 1 << 30, None) == \
+    assert ffn(FAKE, 0, None, FAKE, 8, 128, 128, 7, FAKE, FAKE, 64, FAKE, FAKE, 1 << 30, None) == \
+        N.MOE_ERR_INVALID_ARG
+    # the fused gather needs the row count of X
+    assert ffn(FAKE, 0, FAKE, FAKE, 8, 128, 128, N.MOE_GELU, FAKE, FAKE, 64, FAKE, FAKE, 1 << 30, None) == \
         N.MOE_ERR_INVALID_ARG
 
 

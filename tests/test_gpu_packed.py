@@ -107,3 +107,32 @@ def test_packed_ffn_equals_natural_several_tiles_per_workgroup(act):
     a, b, M = _ffn_pair(rows, 1280, 2560 if act == N.MOE_GELU else 1280, act, 14)
     assert np.array_equal(a, b)
     assert (b[M:] == np.int16(0x40E0)).all()
+
+
+@pytest.mark.parametrize("rows,d,f", [([0, 3, 128, 129, 300, 64, 5, 200], 256, 512),     # weight streaming
+                                      ([1500, 0, 700], 192, 384)])                    # matrix-core order
+@pytest.mark.parametrize("act", [N.MOE_GELU, N.MOE_SWIGLU])
+def test_fused_gather_equals_dispatch_then_ffn(rows, d, f, act):
+    # row_index = a routing map's slot_token: the up GEMM reads X[row_index[s]]
+    # itself; the result must equal the FFN on the explicitly gathered rows
+    g = torch.Generator(device="cuda").manual_seed(15)
+    n, E, M = 700, len(rows), int(sum(rows))
+    w1r = 2 * f if act == N.MOE_SWIGLU else f
+    x = torch.randn(n, d, device="cuda", generator=g).to(torch.bfloat16)
+    idx = torch.randint(0, n, (M + 5,), device="cuda", generator=g, dtype=torch.int32)
+    w1 = (torch.randn(E, w1r, d, device="cuda", generator=g) * d ** -0.5).to(torch.bfloat16)
+    w2 = (torch.randn(E, d, f, device="cuda", generator=g) * f ** -0.5).to(torch.bfloat16)
+    w1p, w2p = N.pack_ffn_weights(w1, w2, act)
+    off = torch.tensor(np.r_[0, np.cumsum(rows)], dtype=torch.int32, device="cuda")
+    ws = torch.empty((N.moe_ffn_workspace_size(M + 5, E, d, f, act, N.MOE_BF16) + 7) // 8,
+                     dtype=torch.float64, device="cuda")
+    y_fused = torch.full((M + 5, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    y_ref = y_fused.clone()
+    N.moe_expert_ffn_packed(x, off, w1p, w2p, act, y_fused, ws, row_index=idx, m_max=M + 5)
+    x_perm = x[idx.long()].contiguous()
+    N.moe_expert_ffn_packed(x_perm, off, w1p, w2p, act, y_ref, ws)
+    torch.cuda.synchronize()
+    a = y_fused.view(torch.int16).cpu().numpy()
+    b = y_ref.view(torch.int16).cpu().numpy()
+    assert np.array_equal(a, b)
+    assert (a[M:] == np.int16(0x40E0)).all()

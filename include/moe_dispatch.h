@@ -11,6 +11,8 @@
  *   capacity / routing map (P = onehot(I))              moe_build_map
  *   X_in[e] = P[e] X                                    moe_dispatch
  *   Y[e] = Expert_e(X_in[e])                            moe_expert_ffn
+ *     (bf16, packed weights, dispatch fused in)         moe_pack_expert_weights,
+ *                                                       moe_expert_ffn_packed
  *   out = residual + shared + scatter_add(G * Y, I)     moe_combine
  *   load-balance loss, z-loss, MaxVio                   moe_balance_stats
  *   loss-free balancing: bias step from the loads       moe_update_bias

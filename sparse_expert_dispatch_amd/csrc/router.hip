@@ -5,12 +5,12 @@
 // (S = softmax(X W_g), X: [n, d], W_g: [d, E]); page 5 "MoE routing
 // strategies explained", strategy 4 (sigmoid scores).
 //
-// bf16 path, three kernels: W_g [d, E] is first transposed to W_g^T [E, d]
-// in the workspace (K-contiguous rows, so a matrix-core B fragment is one
-// 16-byte load); the GEMM kernel then runs v_mfma_f32_16x16x32_bf16 on
-// 128-row x 64-expert workgroup tiles, X read once from HBM, W_g^T shared
-// through LDS; K is split across workgroups (up to 8 slices) until the grid
-// fills the GPU.  The per-slice partial logits go to the workspace; the
+// bf16 path, two kernels: the GEMM kernel runs v_mfma_f32_16x16x32_bf16 on
+// 128-row x 64-expert workgroup tiles, X read once from HBM; each K stage of
+// W_g [d, E] is loaded once per workgroup and transposed on its way into
+// LDS ([expert][K] rows, so a matrix-core B fragment is one 16-byte read);
+// K is split across workgroups (up to 8 slices) until the grid fills the
+// GPU.  The per-slice partial logits go to the workspace; the
 // finalize kernel adds the slices in slice order (so the result is
 // deterministic), adds the offset and evaluates the scores.
 
@@ -27,51 +27,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kRouterBK = 64;      // K per pipeline stage
 constexpr int kRouterSplitsMax = 8;
 
-// W_g^T [E][d] from W_g [d][E]: each workgroup moves a 64 (K) x 64
-// (expert) tile through LDS with 16-byte global loads and stores (E is a
-// multiple of 16; a partial tile covers the last experts).
-__global__ __launch_bounds__(256) void router_wg_transpose_kernel(const bf16_t* __restrict__ Wg, int d,
-                                                                  int E, bf16_t* __restrict__ WgT) {
-  __shared__ bf16_t tile[64][64 + 2];
-  const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  const int ecols = min(64, E - e0);                 // multiple of 16
-  // load: 64 rows x ecols columns, 8 columns per 16-byte load
-  const int cpr = ecols >> 3;
-  uint4 v[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int item = threadIdx.x + 256 * i;
-    if (item < 64 * cpr) {
-      const int kk = item / cpr, cc = (item % cpr) << 3;
-      v[i] = *reinterpret_cast<const uint4*>(Wg + (size_t)(k0 + kk) * E + e0 + cc);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int item = threadIdx.x + 256 * i;
-    if (item < 64 * cpr) {
-      const int kk = item / cpr, cc = (item % cpr) << 3;
-      const bf16_t* pv = reinterpret_cast<const bf16_t*>(&v[i]);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) tile[kk][cc + q] = pv[q];
-    }
-  }
-  __syncthreads();
-  // store: ecols rows of W_g^T, 64 K values each (8 x 16 bytes)
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int item = threadIdx.x + 256 * i;
-    if (item < ecols * 8) {
-      const int ee = item >> 3, kc = (item & 7) << 3;
-      uint4 w;
-      bf16_t* pw = reinterpret_cast<bf16_t*>(&w);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) pw[q] = tile[kc + q][ee];
-      *reinterpret_cast<uint4*>(WgT + (size_t)(e0 + ee) * d + k0 + kc) = w;
-    }
-  }
-}
-
 // Z = X W_g on the matrix cores.  A workgroup (4 waves) owns 128 token rows
 // and 64 expert columns over one K slice: each wave 32 rows (2 x 4 tiles of
 // v_mfma_f32_16x16x32_bf16), its X fragments loaded straight from HBM as
@@ -87,7 +42,7 @@ constexpr int kRouterECols = 64;   // expert columns per workgroup
 constexpr int kRouterWStride = kRouterBK + 8;
 
 __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
-    const bf16_t* __restrict__ X, const bf16_t* __restrict__ WgT, int n, int d, int E, int k_per_split,
+    const bf16_t* __restrict__ X, const bf16_t* __restrict__ Wg, int n, int d, int E, int k_per_split,
     float* __restrict__ partial) {
   __shared__ __attribute__((aligned(16))) bf16_t sW[2][kRouterECols * kRouterWStride];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -102,12 +57,14 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
   const bf16_t* xp[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) xp[i] = X + (size_t)min(row0 + 16 * i + (lane & 15), n - 1) * d + kbeg + kl;
-  // W_g^T stage loads: 64 rows x 8 chunks of 16 bytes, two per thread (rows
-  // past E re-read the last expert; their columns are never stored)
-  const int wr = tid >> 3, wc = (tid & 7) << 3;
+  // W_g stage loads straight from the [d, E] layout: 64 K rows x 8 chunks of
+  // 8 experts, two chunks per thread (experts past E re-read the last
+  // chunk; their columns are never stored); the LDS store transposes them
+  // into [expert][K] rows
+  const int wk = tid >> 3, we = (tid & 7) << 3;
   const bf16_t* wp[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) wp[h] = WgT + (size_t)min(c0 + wr + 32 * h, E - 1) * d + kbeg + wc;
+  for (int h = 0; h < 2; ++h) wp[h] = Wg + (size_t)(kbeg + wk + 32 * h) * E + min(c0 + we, E - 8);
 
   f32x4_t acc[2][4];
 #pragma unroll
@@ -126,12 +83,15 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < 2; ++i) xr[q][s][i] = *reinterpret_cast<const bf16x8_t*>(xp[i] + st * kRouterBK + 32 * s);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) wr_[q][h] = *reinterpret_cast<const u32x4_t*>(wp[h] + st * kRouterBK);
+    for (int h = 0; h < 2; ++h) wr_[q][h] = *reinterpret_cast<const u32x4_t*>(wp[h] + (size_t)st * kRouterBK * E);
   };
   auto store_w = [&](int q, int buf) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      *reinterpret_cast<u32x4_t*>(&sW[buf][(wr + 32 * h) * kRouterWStride + wc]) = wr_[q][h];
+    for (int h = 0; h < 2; ++h) {
+      const bf16_t* v = reinterpret_cast<const bf16_t*>(&wr_[q][h]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sW[buf][(we + j) * kRouterWStride + wk + 32 * h] = v[j];
+    }
   };
 #pragma unroll
   for (int q = 0; q < kRouterAhead; ++q)
@@ -305,12 +265,10 @@ static int router_splits(int n, int d, int E) {
   return s;
 }
 
-static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
 size_t router_workspace_bytes(int n, int d, int E, int dtype) {
   if (!router_uses_mfma(dtype, d, E)) return 0;
   const int s = router_splits(n, d, E);
-  return align256((size_t)E * d * sizeof(bf16_t)) + (s > 1 ? (size_t)s * n * E * sizeof(float) : 0);
+  return s > 1 ? (size_t)s * n * E * sizeof(float) : 0;
 }
 
 hipError_t launch_router(const void* X, const void* Wg, int dtype, const float* offset,
@@ -322,14 +280,10 @@ hipError_t launch_router(const void* X, const void* Wg, int dtype, const float* 
   const dim3 sgrid((unsigned)((total + 255) / 256));
   if (router_uses_mfma(dtype, d, E)) {
     nsplit = router_splits(n, d, E);
-    char* w = static_cast<char*>(ws);
-    bf16_t* WgT = reinterpret_cast<bf16_t*>(w);
-    float* dst = nsplit > 1 ? reinterpret_cast<float*>(w + align256((size_t)E * d * sizeof(bf16_t))) : logits;
-    hipLaunchKernelGGL(router_wg_transpose_kernel, dim3(d / 64, (E + 63) / 64), dim3(256), 0, stream,
-                       static_cast<const bf16_t*>(Wg), d, E, WgT);
+    float* dst = nsplit > 1 ? static_cast<float*>(ws) : logits;
     dim3 grid(router_row_blocks(n), nsplit, (E + kRouterECols - 1) / kRouterECols);
     hipLaunchKernelGGL(router_gemm_bf16_kernel, grid, dim3(256), 0, stream,
-                       static_cast<const bf16_t*>(X), WgT, n, d, E, d / nsplit, dst);
+                       static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(Wg), n, d, E, d / nsplit, dst);
     partial = dst;
   } else if (dtype == 1) {
     hipLaunchKernelGGL(router_gemm_scalar_kernel<bf16_t>, sgrid, dim3(256), 0, stream,

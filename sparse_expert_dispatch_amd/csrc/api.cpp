@@ -220,6 +220,7 @@ moe_status_t moe_build_map(const int32_t* sel_idx, const float* sel_gate, const 
   if (!ws || ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "build_map needs %zu workspace bytes, got %zu", need, ws_bytes);
   const moe::MapPtrs m = map_ptrs(map);
+  SUPPORTED((int64_t)cfg->n * cfg->k <= INT32_MAX, "routing maps need n k < 2^31 (n=%d k=%d)", cfg->n, cfg->k);
   if (cfg->dir == MOE_TOKEN_CHOICE)
     return launched(moe::launch_build_map_tc(sel_idx, sel_gate, cfg->n, cfg->E, cfg->k, cfg->capacity,
                                              cfg->capacity_order, m, ws, as_stream(stream)),

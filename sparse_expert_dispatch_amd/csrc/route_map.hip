@@ -85,23 +85,45 @@ __global__ __launch_bounds__(kScanThreads) void map_scan_kernel(
 
 // Token choice also writes the token-side lists: token t's entries are its
 // k assignments in rank order (token_offset[t] = t*k), -1 for a dropped one.
+// The chunk's expert ids and gates are loaded into registers up front (all
+// kMapChunk / 64 loads per lane in flight at once) and the expert offsets
+// into LDS, so the in-order walk below waits on no global load.
+constexpr int kScatterIters = kMapChunk / 64;
+
 __global__ __launch_bounds__(64) void map_scatter_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ gate, int64_t M, int n, int k, int E,
     int rank_major, int nbits, int capacity, const int32_t* __restrict__ chunk_base,
     const int32_t* __restrict__ expert_offset, MapPtrs m) {
-  extern __shared__ int cnt[];
+  extern __shared__ int cnt[];                      // [E] running positions, then [E] offsets
+  int* eoff = cnt + E;
   const int lane = threadIdx.x;
   const int c = blockIdx.x;
-  for (int e = lane; e < E; e += 64) cnt[e] = chunk_base[(size_t)c * E + e];
+  for (int e = lane; e < E; e += 64) {
+    cnt[e] = chunk_base[(size_t)c * E + e];
+    eoff[e] = expert_offset[e];
+  }
+  // 32-bit indices (the host checks n k < 2^31): a 64-bit division per
+  // element would cost more than the walk itself
+  const int Mi = (int)M;
+  const int a0 = c * kMapChunk;
+  int q_all[kScatterIters], e_all[kScatterIters];
+  float g_all[kScatterIters];
+#pragma unroll
+  for (int i = 0; i < kScatterIters; ++i) {
+    const int a = a0 + 64 * i + lane;
+    const int q = a < Mi ? (rank_major ? (a % n) * k + a / n : a) : 0;   // element of idx arriving a-th
+    q_all[i] = q;
+    e_all[i] = a < Mi ? idx[q] : 0;
+    g_all[i] = a < Mi ? gate[q] : 0.f;
+  }
   __syncthreads();
   const uint64_t lt_mask = (1ull << lane) - 1ull;
-  const int64_t a0 = (int64_t)c * kMapChunk;
-  if (c == 0 && lane == 0) m.token_offset[M / k] = (int32_t)M;
-  for (int it = 0; it < kMapChunk; it += 64) {
-    const int64_t a = a0 + it + lane;
-    const bool inrange = a < M;
-    const int64_t q = arrival_elem(a, n, k, rank_major);    // (t, r) = (q / k, q % k)
-    const int e_raw = inrange ? idx[q] : 0;
+  if (c == 0 && lane == 0) m.token_offset[Mi / k] = Mi;
+#pragma unroll
+  for (int i = 0; i < kScatterIters; ++i) {
+    const bool inrange = a0 + 64 * i + lane < Mi;
+    const int q = q_all[i];                                   // (t, r) = (q / k, q % k)
+    const int e_raw = e_all[i];
     const bool valid = inrange && (unsigned)e_raw < (unsigned)E;
     const int e = valid ? e_raw : 0;
     uint64_t match = __ballot(valid);
@@ -120,9 +142,9 @@ __global__ __launch_bounds__(64) void map_scatter_kernel(
     if (inrange) {
       int32_t s = -1;
       if (valid && (capacity < 0 || pos < capacity)) {
-        s = expert_offset[e] + pos;
-        m.slot_token[s] = (int32_t)(q / k);
-        m.slot_gate[s] = gate[q];
+        s = eoff[e] + pos;
+        m.slot_token[s] = q / k;
+        m.slot_gate[s] = g_all[i];
       }
       m.assign_slot[q] = s;
       m.token_slot[q] = s;
@@ -248,7 +270,7 @@ hipError_t launch_build_map_tc(const int32_t* idx, const float* gate, int n, int
                      E, rank_major, chunk_hist);
   hipLaunchKernelGGL(map_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, chunk_hist, nch, E,
                      capacity, chunk_base, m.expert_count, m.expert_offset, m.n_kept);
-  hipLaunchKernelGGL(map_scatter_kernel, dim3(nch), dim3(64), E * sizeof(int), stream, idx, gate, M,
+  hipLaunchKernelGGL(map_scatter_kernel, dim3(nch), dim3(64), 2 * E * sizeof(int), stream, idx, gate, M,
                      n, k, E, rank_major, nbits, capacity, chunk_base, m.expert_offset, m);
   return hipGetLastError();
 }

@@ -238,6 +238,98 @@ __global__ __launch_bounds__(256) void ec_token_fill_kernel(const int32_t* __res
   token_slot[token_offset[t] + before] = (int32_t)s;
 }
 
+// The whole map in one workgroup, for batches whose token mask and token
+// offsets fit in LDS: every thread loads its slots' tokens and gates at
+// once (slot u * 1024 + tid, u < kEcSmallSlots), builds the mask with LDS
+// atomics, scans the popcounts in LDS and takes each slot's list position
+// from the LDS mask, so only the loads of I, G and the result stores touch
+// global memory, and nothing needs clearing between calls.  Same results
+// as the four-kernel path.
+constexpr int kEcSmallSlots = 16;
+constexpr int kEcSmallLdsWords = 16384;   // 64 KB of mask and offsets
+
+__global__ __launch_bounds__(kScanThreads) void ec_map_small_kernel(const int32_t* __restrict__ I,
+                                                                    const float* __restrict__ G, int n,
+                                                                    int E, int k, int W, MapPtrs m) {
+  extern __shared__ uint32_t ec_lds[];
+  uint32_t* smask = ec_lds;                                   // [n][W]
+  int* soff = reinterpret_cast<int*>(ec_lds + (size_t)n * W);  // [n]
+  __shared__ int scratch[kScanThreads / 64];
+  const int tid = threadIdx.x;
+  const int M = E * k;
+  int tok[kEcSmallSlots];
+  float gt[kEcSmallSlots];
+#pragma unroll
+  for (int u = 0; u < kEcSmallSlots; ++u) {
+    const int s = u * kScanThreads + tid;
+    tok[u] = s < M ? I[s] : -1;
+    gt[u] = s < M ? G[s] : 0.f;
+  }
+  for (int i = tid; i < n * W; i += kScanThreads) smask[i] = 0u;
+  if (tid < E) {
+    m.expert_count[tid] = k;
+    m.expert_offset[tid] = tid * k;
+  }
+  if (tid == 0) {
+    m.expert_offset[E] = M;
+    *m.n_kept = M;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kEcSmallSlots; ++u) {
+    const int s = u * kScanThreads + tid;
+    if (s < M) {
+      const int t = tok[u];
+      const int e = s / k;
+      m.slot_token[s] = t;
+      m.slot_gate[s] = gt[u];
+      m.assign_slot[s] = s;
+      if ((unsigned)t < (unsigned)n) atomicOr(&smask[t * W + (e >> 5)], 1u << (e & 31));
+    }
+  }
+  __syncthreads();
+  int carry = 0;
+  for (int base = 0; base < n; base += kScanThreads * kTokPer) {
+    const int t0 = base + tid * kTokPer;
+    int cnt[kTokPer];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < kTokPer; ++i) {
+      int c = 0;
+      if (t0 + i < n)
+        for (int w = 0; w < W; ++w) c += __popc(smask[(t0 + i) * W + w]);
+      cnt[i] = c;
+      sum += c;
+    }
+    int total = 0;
+    int run = carry + block_exclusive_scan<kScanThreads>(sum, scratch, &total);
+#pragma unroll
+    for (int i = 0; i < kTokPer; ++i) {
+      if (t0 + i < n) {
+        soff[t0 + i] = run;
+        m.token_offset[t0 + i] = run;
+      }
+      run += cnt[i];
+    }
+    carry += total;
+  }
+  if (tid == 0) m.token_offset[n] = carry;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kEcSmallSlots; ++u) {
+    const int s = u * kScanThreads + tid;
+    const int t = tok[u];
+    if (s < M && (unsigned)t < (unsigned)n) {
+      const int e = s / k;
+      const uint32_t* row = smask + t * W;
+      int before = 0;
+      for (int w = 0; w < (e >> 5); ++w) before += __popc(row[w]);
+      before += __popc(row[e >> 5] & ((1u << (e & 31)) - 1u));
+      m.token_slot[soff[t] + before] = s;
+    }
+  }
+}
+
 // Expert choice with k = 0 (a batch too small for any expert to take a
 // token): every count, offset and token list is empty.
 __global__ __launch_bounds__(256) void ec_empty_map_kernel(int n, int E, MapPtrs m) {
@@ -283,6 +375,12 @@ hipError_t launch_build_map_ec(const int32_t* I, const float* G, int n, int E, i
     return hipGetLastError();
   }
   const int W = (E + 31) / 32;
+  if ((int64_t)E * k <= (int64_t)kScanThreads * kEcSmallSlots &&
+      (int64_t)n * (W + 1) <= kEcSmallLdsWords) {
+    hipLaunchKernelGGL(ec_map_small_kernel, dim3(1), dim3(kScanThreads),
+                       (size_t)n * (W + 1) * sizeof(uint32_t), stream, I, G, n, E, k, W, m);
+    return hipGetLastError();
+  }
   uint32_t* mask = static_cast<uint32_t*>(ws);
   const int64_t words = (int64_t)n * W;
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,

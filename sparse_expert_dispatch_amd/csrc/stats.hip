@@ -16,17 +16,20 @@
 //   max_vio = (max_e load_e - mean load) / mean load,  load = kept rows,
 // plus kept / dropped counts and the experts-per-token histogram.
 //
-// Two kernels.  The row kernel (16 tokens per workgroup, one per wave) adds up
-// each block's normalised scores, squared log-sum-exps and experts-per-token
-// histogram; the final kernel (one workgroup) reduces the block partials in
-// a fixed order, so the floats are reproducible bit for bit.
+// Two kernels.  The row kernel (16 tokens per workgroup, one per wave) adds
+// up each block's normalised scores, squared log-sum-exps and experts-per-
+// token histogram; the final kernel (one workgroup) reduces the block
+// partials in a fixed order, so the floats are reproducible bit for bit.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 
-constexpr int kStatRows = 16;   // rows per block, one per wave
+constexpr int kStatRowsPerWave = 1;
+constexpr int kStatRows = 16 * kStatRowsPerWave;   // rows per block
 
+// NJ = expert registers per lane (experts e = lane + 64 j, j < NJ).
+template <int NJ>
 __global__ __launch_bounds__(1024) void stats_rows_kernel(const float* __restrict__ logits,
                                                          const int32_t* __restrict__ token_offset,
                                                          const int32_t* __restrict__ token_slot,
@@ -35,73 +38,88 @@ __global__ __launch_bounds__(1024) void stats_rows_kernel(const float* __restric
                                                          float* __restrict__ part_Z,
                                                          int32_t* __restrict__ part_H) {
 #pragma clang fp contract(off)
-  __shared__ float sP[kStatRows][kMaxExperts];
-  __shared__ float sZ[kStatRows];
+  constexpr int R = kStatRowsPerWave;
+  __shared__ float sP[16][64 * NJ];
+  __shared__ float sZ[16];
   __shared__ int sH[kMaxExperts + 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int nj = (E + 63) >> 6;
   const int P2 = next_pow2(E);
   for (int i = threadIdx.x; i <= E; i += 1024) sH[i] = 0;
-  __syncthreads();
-  float accP[kMaxExpertRegs];
+  const int row0 = blockIdx.x * kStatRows + wave * R;
+  // every row's list bounds and logits, loaded before the first wait
+  int q0[R], q1[R];
+  float z[R][NJ];
 #pragma unroll
-  for (int j = 0; j < kMaxExpertRegs; ++j) accP[j] = 0.f;
-  float accZ = 0.f;
-  {
-    const int row = blockIdx.x * kStatRows + wave;
-    if (row >= n) goto done;
-    float z[kMaxExpertRegs];
-    float m = -__builtin_huge_valf();
+  for (int r = 0; r < R; ++r) {
+    const int row = row0 + r;
+    const bool in = row < n;
+    q0[r] = in ? token_offset[row] : 0;
+    q1[r] = in ? token_offset[row + 1] : 0;
 #pragma unroll
-    for (int j = 0; j < kMaxExpertRegs; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int e = lane + 64 * j;
-      z[j] = (j < nj && e < E) ? logits[(size_t)row * E + e] : 0.f;
-      if (j < nj && e < E) m = fmaxf(m, z[j]);
+      z[r][j] = in && e < E ? logits[(size_t)row * E + e] : -__builtin_huge_valf();
     }
-    // kept experts of this token: its list entries that are not drops
-    const int q0 = token_offset[row], q1 = token_offset[row + 1];
-    int kept = 0;
-    for (int q = q0; q < q1; q += 64)
-      kept += __popcll(__ballot(q + lane < q1 && token_slot[q + lane] >= 0));
-    if (lane == 0) atomicAdd(&sH[min(kept, E)], 1);
-    m = wave_max_f32(m);
-    float t[kMaxExpertRegs], u[kMaxExpertRegs];
+  }
+  // kept experts of each token: its list entries that are not drops
+  int kept[R];
 #pragma unroll
-    for (int j = 0; j < kMaxExpertRegs; ++j) {
-      const bool valid = j < nj && lane + 64 * j < E;
-      t[j] = valid ? spec_exp(z[j] - m) : 0.f;
-      u[j] = valid ? (score == 0 ? t[j] : spec_expert_score(z[j], score)) : 0.f;
+  for (int r = 0; r < R; ++r) {
+    kept[r] = 0;
+    for (int q = q0[r]; q < q1[r]; q += 64)
+      kept[r] += __popcll(__ballot(q + lane < q1[r] && token_slot[q + lane] >= 0));
+  }
+  float accP[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) accP[j] = 0.f;
+  float accZ = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (row0 + r >= n) break;
+    float m = z[r][0];
+#pragma unroll
+    for (int j = 1; j < NJ; ++j) m = fmaxf(m, z[r][j]);
+    m = wave_max_f32(m);
+    float t[NJ], u[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const bool valid = lane + 64 * j < E;
+      t[j] = valid ? spec_exp(z[r][j] - m) : 0.f;
+      u[j] = valid ? (score == 0 ? t[j] : spec_expert_score(z[r][j], score)) : 0.f;
     }
     const float s_exp = row_tree_sum(t, P2);
     const float s_norm = score == 0 ? s_exp : row_tree_sum(u, P2);
 #pragma unroll
-    for (int j = 0; j < kMaxExpertRegs; ++j) accP[j] = accP[j] + u[j] / s_norm;
+    for (int j = 0; j < NJ; ++j) accP[j] = accP[j] + u[j] / s_norm;
     const float lse = m + logf(s_exp);
     accZ = accZ + lse * lse;
   }
-done:
 #pragma unroll
-  for (int j = 0; j < kMaxExpertRegs; ++j) {
-    const int e = lane + 64 * j;
-    if (j < nj && e < E) sP[wave][e] = accP[j];
-  }
+  for (int j = 0; j < NJ; ++j) sP[wave][lane + 64 * j] = accP[j];
   if (lane == 0) sZ[wave] = accZ;
-  __syncthreads();
+  __syncthreads();   // sH cleared, rows' sums staged
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (row0 + r < n) atomicAdd(&sH[min(kept[r], E)], 1);
+  }
   for (int e = threadIdx.x; e < E; e += 1024) {
     float v = sP[0][e];
-    for (int w = 1; w < kStatRows; ++w) v = v + sP[w][e];
+    for (int w = 1; w < 16; ++w) v = v + sP[w][e];
     part_P[(size_t)blockIdx.x * E + e] = v;
   }
-  for (int i = threadIdx.x; i <= E; i += 1024) part_H[(size_t)blockIdx.x * (E + 1) + i] = sH[i];
   if (threadIdx.x == 0) {
     float v = sZ[0];
-    for (int w = 1; w < kStatRows; ++w) v = v + sZ[w];
+    for (int w = 1; w < 16; ++w) v = v + sZ[w];
     part_Z[blockIdx.x] = v;
   }
+  __syncthreads();   // histogram complete
+  for (int i = threadIdx.x; i <= E; i += 1024) part_H[(size_t)blockIdx.x * (E + 1) + i] = sH[i];
 }
 
 constexpr int kFinThreads = 1024;
+constexpr int kFinRows = 16;   // partial rows per thread and load round
 
 MOE_DEV int pow2_at_least(int x, int lo) {
   int p = lo;
@@ -109,54 +127,64 @@ MOE_DEV int pow2_at_least(int x, int lo) {
   return p;
 }
 
-// One workgroup.  Every global value it needs is loaded in one phase (no
-// barrier in between, so the loads are all in flight together): thread group
-// g of the partial tables sums rows g, g + G, ... of its column; the group
-// sums are then added in group order, which fixes the summation order.
+// One workgroup.  Column c of the partial tables (c < E: score sums and
+// histogram bins; c = E: the last bin; c = E + 1: squared log-sum-exps) is
+// summed by the G = 1024 / cp thread groups (cp = power of two >= E + 2):
+// group g takes rows g, g + G, ..., kFinRows of them per round with every
+// load of a round issued before the first add; the group sums are then added
+// in group order, which fixes the summation order.  After two barriers one
+// wave finishes: sum_e f_e P_e by the halving tree over experts (lanes and
+// registers), the top non-empty histogram bin from per-wave ballots.
 __global__ __launch_bounds__(kFinThreads) void stats_final_kernel(
     const float* __restrict__ part_P, const float* __restrict__ part_Z,
     const int32_t* __restrict__ part_H, int nblocks, int n, int E, int k, int dir, float lb_coef,
     float z_coef, const int32_t* __restrict__ expert_count, const int32_t* __restrict__ expert_offset,
     float* __restrict__ stats, int32_t* __restrict__ hist) {
 #pragma clang fp contract(off)
-  __shared__ float redP[kFinThreads];
-  __shared__ float redZ[kFinThreads];
+  __shared__ float redF[kFinThreads];
   __shared__ int redH[kFinThreads];
   __shared__ float fp[kMaxExperts];
-  __shared__ int sH[kMaxExperts + 1];
-  __shared__ int wred[kFinThreads / 64][2];
+  __shared__ int wred[kFinThreads / 64][3];
+  __shared__ float sZ;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
 
-  // ---- load phase
-  const int cpP = pow2_at_least(E, 32), gP = kFinThreads / cpP;
-  const int cpH = pow2_at_least(E + 1, 32), gH = kFinThreads / cpH;
-  float sp = 0.f, sz = 0.f;
-  int sh = 0;
-  {
-    const int g = tid / cpP, c = tid % cpP;
-    if (c < E) {
-#pragma unroll 16
-      for (int b = g; b < nblocks; b += gP) sp = sp + part_P[(size_t)b * E + c];
-    }
-  }
-  {
-    const int g = tid / cpH, c = tid % cpH;
-    if (c <= E) {
-#pragma unroll 16
-      for (int b = g; b < nblocks; b += gH) sh += part_H[(size_t)b * (E + 1) + c];
-    }
-  }
-#pragma unroll 4
-  for (int b = tid; b < nblocks; b += kFinThreads) sz = sz + part_Z[b];
-  const int cnt = tid < E ? expert_count[tid] : 0;
-  const int load = tid < E ? expert_offset[tid + 1] - expert_offset[tid] : 0;
+  // ---- load phase.  Every load is unconditional from a clamped, in-bounds
+  // address into a register of its own (the masking comes after), so a
+  // round's loads issue back to back with no wait between them.
+  const int cnt_raw = expert_count[min(tid, E - 1)];
+  const int off_lo = expert_offset[min(tid, E)];
+  const int off_hi = expert_offset[min(tid + 1, E)];
   const int n_kept = expert_offset[E];
-  redP[tid] = sp;
+  const int cp = pow2_at_least(E + 2, 32), G = kFinThreads / cp;
+  const int g = tid / cp, c = tid % cp;
+  const int cP = min(c, E - 1), cH = min(c, E);
+  float sf = 0.f;
+  int sh = 0;
+  for (int b0 = g; b0 < nblocks; b0 += G * kFinRows) {
+    float vp[kFinRows], vz[kFinRows];
+    int vh[kFinRows];
+#pragma unroll
+    for (int u = 0; u < kFinRows; ++u) {
+      const int b = min(b0 + u * G, nblocks - 1);
+      vp[u] = part_P[(size_t)b * E + cP];
+      vz[u] = part_Z[b];
+      vh[u] = part_H[(size_t)b * (E + 1) + cH];
+    }
+    // bit masks rather than selects: every load has an unconditional use,
+    // so none is sunk into a branch behind a wait
+#pragma unroll
+    for (int u = 0; u < kFinRows; ++u) {
+      const bool in = b0 + u * G < nblocks;
+      const int mp = -(int)(in && c < E), mz = -(int)(in && c == E + 1), mh = -(int)(in && c <= E);
+      sf = sf + __int_as_float((__float_as_int(vp[u]) & mp) | (__float_as_int(vz[u]) & mz));
+      sh += vh[u] & mh;
+    }
+  }
+  redF[tid] = sf;
   redH[tid] = sh;
-  redZ[tid] = sz;
   // ---- integer reductions: chosen total, largest kept load
-  int chosen = cnt, maxload = load;
+  int chosen = tid < E ? cnt_raw : 0, maxload = tid < E ? off_hi - off_lo : 0;
   for (int o = 32; o >= 1; o >>= 1) {
     chosen += __shfl_xor(chosen, o, 64);
     maxload = max(maxload, __shfl_xor(maxload, o, 64));
@@ -167,50 +195,51 @@ __global__ __launch_bounds__(kFinThreads) void stats_final_kernel(
   }
   __syncthreads();
   int ch = 0, ml = 0;
+#pragma unroll
   for (int w = 0; w < kFinThreads / 64; ++w) {
     ch += wred[w][0];
     ml = max(ml, wred[w][1]);
   }
+  // ---- column totals in group order (the G reads of a column are independent)
+  int hv = 0;
   if (tid <= E) {
-    int v = 0;
-    for (int q = 0; q < gH; ++q) v += redH[q * cpH + tid];
-    sH[tid] = v;
-    if (hist) hist[tid] = v;
+#pragma unroll 8
+    for (int q = 0; q < G; ++q) hv += redH[q * cp + tid];
+    if (hist) hist[tid] = hv;
   }
   if (tid < E) {
     float v = 0.f;
-    for (int q = 0; q < gP; ++q) v = v + redP[q * cpP + tid];
+#pragma unroll 8
+    for (int q = 0; q < G; ++q) v = v + redF[q * cp + tid];
     // f_e = 0 when nothing was chosen (expert choice with k = 0)
-    fp[tid] = ch > 0 ? ((float)cnt / (float)ch) * (v / (float)n) : 0.f;
+    fp[tid] = ch > 0 ? ((float)cnt_raw / (float)ch) * (v / (float)n) : 0.f;
   }
-  // z partials: a halving tree over the 1024 thread sums
-  for (int s = kFinThreads / 2; s >= 1; s >>= 1) {
-    __syncthreads();
-    if (tid < s) redZ[tid] = redZ[tid] + redZ[tid + s];
+  if (tid == E + 1) {
+    float v = 0.f;
+#pragma unroll 8
+    for (int q = 0; q < G; ++q) v = v + redF[q * cp + tid];
+    sZ = v;
   }
-  // sum_e f_e P_e by a halving tree over experts
-  const int P = next_pow2(E);
-  for (int s = P >> 1; s >= 1; s >>= 1) {
-    __syncthreads();
-    if (tid < s) fp[tid] = fp[tid] + (tid + s < E ? fp[tid + s] : 0.f);
-  }
+  const uint64_t nz = __ballot(tid <= E && hv > 0);
+  if (lane == 0) wred[wave][2] = nz ? wave * 64 + 63 - __clzll(nz) : 0;
   __syncthreads();
-  if (tid == 0) {
-    int mt = 0;
-    for (int i = E; i >= 0; --i)
-      if (sH[i] > 0) {
-        mt = i;
-        break;
-      }
+  if (wave != 0) return;
+  float fr[kMaxExpertRegs];
+#pragma unroll
+  for (int j = 0; j < kMaxExpertRegs; ++j) fr[j] = lane + 64 * j < E ? fp[lane + 64 * j] : 0.f;
+  const float fsum = row_tree_sum(fr, next_pow2(E));
+  int mt = lane < kFinThreads / 64 ? wred[lane][2] : 0;
+  for (int o = 32; o >= 1; o >>= 1) mt = max(mt, __shfl_xor(mt, o, 64));
+  if (lane == 0) {
     const int total = dir == 0 ? n * k : E * k;
     const float mean_load = (float)n_kept / (float)E;
-    stats[0] = lb_coef * (float)E * fp[0];
-    stats[1] = z_coef * (redZ[0] / (float)n);
+    stats[0] = lb_coef * (float)E * fsum;
+    stats[1] = z_coef * (sZ / (float)n);
     stats[2] = mean_load > 0.f ? ((float)ml - mean_load) / mean_load : 0.f;
     stats[3] = n_kept > 0 ? (float)ml / (float)n_kept : 0.f;
     stats[4] = (float)n_kept;
     stats[5] = (float)(total - n_kept);
-    stats[6] = (float)sH[0];
+    stats[6] = (float)hv;
     stats[7] = (float)mt;
   }
 }
@@ -232,8 +261,12 @@ hipError_t launch_balance_stats(const float* logits, const MapPtrs& m, int n, in
   float* part_Z = reinterpret_cast<float*>(w + align256((size_t)nb * E * sizeof(float)));
   int32_t* part_H = reinterpret_cast<int32_t*>(w + align256((size_t)nb * E * sizeof(float)) +
                                                align256((size_t)nb * sizeof(float)));
-  hipLaunchKernelGGL(stats_rows_kernel, dim3(nb), dim3(1024), 0, stream, logits, m.token_offset,
-                     m.token_slot, n, E, score, part_P, part_Z, part_H);
+  const auto rows = E <= 64 ? stats_rows_kernel<1>
+                    : E <= 128 ? stats_rows_kernel<2>
+                    : E <= 256 ? stats_rows_kernel<4>
+                               : stats_rows_kernel<8>;
+  hipLaunchKernelGGL(rows, dim3(nb), dim3(1024), 0, stream, logits, m.token_offset, m.token_slot, n, E,
+                     score, part_P, part_Z, part_H);
   hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(kFinThreads), 0, stream, part_P, part_Z, part_H,
                      nb, n, E, k, dir, lb_coef, z_coef, m.expert_count, m.expert_offset, stats, hist);
   return hipGetLastError();

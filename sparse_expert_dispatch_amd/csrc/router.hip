@@ -5,14 +5,17 @@
 // (S = softmax(X W_g), X: [n, d], W_g: [d, E]); page 5 "MoE routing
 // strategies explained", strategy 4 (sigmoid scores).
 //
-// bf16 path, two kernels: the GEMM kernel runs v_mfma_f32_16x16x32_bf16 on
-// 128-row x 64-expert workgroup tiles, X read once from HBM; each K stage of
-// W_g [d, E] is loaded once per workgroup and transposed on its way into
-// LDS ([expert][K] rows, so a matrix-core B fragment is one 16-byte read);
-// K is split across workgroups (up to 8 slices) until the grid fills the
-// GPU.  The per-slice partial logits go to the workspace; the
-// finalize kernel adds the slices in slice order (so the result is
-// deterministic), adds the offset and evaluates the scores.
+// bf16 with at most 64 experts: one fused kernel (GEMM on the matrix cores
+// with W_g read in its [d, E] layout through LDS transpose reads, K split
+// over the waves of a workgroup and summed in wave order, then offset,
+// noise, scores and their transpose), no intermediate in memory.  bf16 with
+// more experts: a split-K GEMM kernel (128-row x 64-expert tiles, each K
+// stage of W_g transposed on its way into LDS; K split across workgroups,
+// up to 8 slices, until the grid fills the GPU) writes per-slice partial
+// logits to the workspace, and a finalize kernel adds the slices in slice
+// order (deterministic), adds the offset and evaluates the scores.  fp32,
+// or shapes the matrix-core tiling does not cover: a scalar GEMM, then the
+// finalize kernel.
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -157,6 +160,194 @@ __global__ __launch_bounds__(256) void router_gemm_scalar_kernel(const T* __rest
 
 static bool router_uses_mfma(int dtype, int d, int E) { return dtype == 1 && d % 64 == 0 && E % 16 == 0; }
 
+// Scores of one row held as lane l, register j -> expert l + 64 j (entries
+// with j >= nj or l + 64 j >= E are ignored): the softmax over the row
+// (score 0: max, exp of the differences, halving-tree sum, quotient) or
+// the per-expert sigmoid / sqrtsoftplus.  Both router paths call it, so
+// they produce the same bits from the same logits.
+template <int R>
+MOE_DEV void row_scores(const float (&z)[R], int nj, int E, int score, float (&p)[R]) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  if (score == 0) {
+    float m = -__builtin_huge_valf();
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if (j < nj && lane + 64 * j < E) m = fmaxf(m, z[j]);
+    m = wave_max_f32(m);
+    float t[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) t[j] = (j < nj && lane + 64 * j < E) ? spec_exp(z[j] - m) : 0.f;
+    const float s = row_tree_sum(t, next_pow2(E));
+#pragma unroll
+    for (int j = 0; j < R; ++j) p[j] = t[j] / s;
+  } else {
+#pragma unroll
+    for (int j = 0; j < R; ++j) p[j] = spec_expert_score(z[j], score);
+  }
+}
+
+// Fused router for up to 64 experts: the GEMM, the offset and noise, the
+// scores and their transpose in one kernel, with no K-split partials in
+// memory.  A workgroup owns 16 RT token rows and all E experts; its KW
+// waves split K (wave w takes the w-th d / KW slice) and each keeps 16 RT x
+// E accumulators (v_mfma_f32_16x16x32_bf16).  Per 32-wide K step a wave
+// copies the 32 x 64 block of W_g [d, E] as loaded (row-major, no
+// transpose) into its own LDS rows, and reads the matrix-core B fragments
+// back with ds_read_b64_tr_b16: within each 16-lane group, lane 4q + e
+// receives element e of the 4-element runs addressed by lanes q, q + 4,
+// q + 8, q + 12.  Pointing lane i of a group at row (i / 4) and experts
+// 4 (i % 4) .. +3 of the block therefore hands lane r four consecutive K
+// values of expert r; two such reads make the 8-value fragment.  The waves'
+// LDS regions are private, so the K loop has no barrier.  The partial
+// accumulators are then added through LDS in wave order (deterministic),
+// and the rows finish as in the finalize kernel.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+constexpr int kFusedLdw = 72;     // bf16 per LDS row of a W_g step (64 experts + 16 bytes)
+constexpr int kFusedRedLd = 68;   // floats per LDS row of the cross-wave sums
+#ifndef MOE_ROUTER_AHEAD
+#define MOE_ROUTER_AHEAD 4
+#endif
+#ifndef MOE_ROUTER_KW_BIG
+#define MOE_ROUTER_KW_BIG 8
+#endif
+#ifndef MOE_ROUTER_KW_SMALL
+#define MOE_ROUTER_KW_SMALL 16
+#endif
+constexpr int kFusedAhead = MOE_ROUTER_AHEAD;   // K steps in flight per wave
+
+template <int KW, int RT>
+constexpr size_t router_fused_lds() {
+  constexpr size_t w = (size_t)KW * 32 * kFusedLdw * 2;
+  constexpr size_t r = (size_t)KW * 16 * RT * kFusedRedLd * 4;
+  return (w > r ? w : r) + (size_t)16 * RT * 65 * 4;
+}
+
+template <int KW, int RT, int AHEAD>
+__global__ __launch_bounds__(64 * KW) void router_fused_bf16_kernel(
+    const bf16_t* __restrict__ X, const bf16_t* __restrict__ Wg, int n, int d, int E,
+    const float* __restrict__ offset, const float* __restrict__ noise, float noise_std, int score,
+    float* __restrict__ logits, float* __restrict__ scores, float* __restrict__ scores_t) {
+#pragma clang fp contract(off)
+  extern __shared__ __attribute__((aligned(16))) char router_lds[];
+  constexpr int kRows = 16 * RT;
+  constexpr size_t kMain = router_fused_lds<KW, RT>() - (size_t)kRows * 65 * 4;
+  bf16_t* sW = reinterpret_cast<bf16_t*>(router_lds);   // [KW][32][kFusedLdw], during the K loop
+  float* red = reinterpret_cast<float*>(router_lds);    // [KW][kRows][kFusedRedLd], after it
+  float* sT = reinterpret_cast<float*>(router_lds + kMain);   // [kRows][E + 1]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r0 = blockIdx.x * kRows;
+  const int ksl = d / KW;
+  const int kbeg = wave * ksl;
+  const int ns = ksl / 32;
+  const int kl = (lane >> 4) << 3;
+  // Buffer loads: the uniform part of every address (workgroup rows, wave
+  // K slice, step) is in the resource base or the scalar offset, the lane
+  // part in one 32-bit register.  X rows past n lie outside the resource
+  // and read as zero.
+  const __amdgpu_buffer_rsrc_t xr_src = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(X + (size_t)r0 * d + kbeg), (short)0, min(kRows, n - r0) * d * 2, 0x00020000);
+  int xoff[RT];
+#pragma unroll
+  for (int i = 0; i < RT; ++i) xoff[i] = ((16 * i + (lane & 15)) * d + kl) * 2;
+  // W_g step loads: rows 8 h + lane / 8, experts 8 (lane % 8) .. +7 (clamped
+  // to the last whole chunk when E < 64; those LDS columns are never read)
+  const int wr = lane >> 3, wc = (lane & 7) << 3;
+  const __amdgpu_buffer_rsrc_t wr_src = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(Wg + (size_t)kbeg * E), (short)0, ksl * E * 2, 0x00020000);
+  const int woff = (wr * E + min(wc, E - 8)) * 2;
+  bf16_t* sw = sW + wave * 32 * kFusedLdw;
+  const int tr_off = (8 * (lane >> 4) + ((lane >> 2) & 3)) * kFusedLdw + 4 * (lane & 3);
+
+  // Always four 16-expert tiles: with E < 64 the extra tiles multiply LDS
+  // columns past E (clamped copies) and their sums are never read.
+  constexpr int NT = 4;
+  f32x4_t acc[RT][NT];
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  bf16x8_t xr[AHEAD][RT];
+  u32x4_t wv[AHEAD][4];
+  auto load = [&](int st, int q) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+      xr[q][i] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(xr_src, xoff[i], st * 64, 0));
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      wv[q][h] = __builtin_amdgcn_raw_buffer_load_b128(wr_src, woff, (st * 32 + 8 * h) * E * 2, 0);
+  };
+  // AHEAD divides ns, so every round of the ring runs whole; loads are
+  // issued unconditionally (the last round re-reads step ns - 1), which
+  // keeps the loop free of branches.
+#pragma unroll
+  for (int q = 0; q < AHEAD; ++q) load(min(q, ns - 1), q);
+  for (int st0 = 0; st0 < ns; st0 += AHEAD) {
+#pragma unroll
+    for (int q = 0; q < AHEAD; ++q) {
+      // one wave's LDS operations execute in order: these stores land after
+      // the previous step's transpose reads
+#pragma unroll
+      for (int h = 0; h < 4; ++h) *reinterpret_cast<u32x4_t*>(sw + (8 * h + wr) * kFusedLdw + wc) = wv[q][h];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(sw + tr_off + 16 * j));
+        const v4i16 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(sw + tr_off + 4 * kFusedLdw + 16 * j));
+        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int i = 0; i < RT; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xr[q][i], b, acc[i][j], 0, 0, 0);
+      }
+      load(min(st0 + q + AHEAD, ns - 1), q);
+    }
+  }
+  __syncthreads();   // every wave is done with its W_g rows; the sums reuse the space
+  // C fragment: lane holds column (lane % 16), rows 4 (lane / 16) + r
+  float* rw = red + wave * kRows * kFusedRedLd;
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        rw[(16 * i + 4 * (lane >> 4) + r) * kFusedRedLd + 16 * j + (lane & 15)] = acc[i][j][r];
+  __syncthreads();
+  const int ld = E + 1;
+  for (int rr = wave; rr < kRows; rr += KW) {
+    const int row = r0 + rr;
+    if (row >= n) break;
+    const int e = lane;
+    float z[1] = {0.f};
+    if (e < E) {
+      float v = red[rr * kFusedRedLd + e];
+#pragma unroll
+      for (int w = 1; w < KW; ++w) v = v + red[(w * kRows + rr) * kFusedRedLd + e];
+      if (offset) v = v + offset[e];
+      if (noise) v = v + noise_std * noise[(size_t)row * E + e];
+      z[0] = v;
+      if (logits) logits[(size_t)row * E + e] = v;
+    }
+    if (!scores && !scores_t) continue;
+    float p[1];
+    row_scores(z, 1, E, score, p);
+    if (e < E) {
+      if (scores) scores[(size_t)row * E + e] = p[0];
+      if (scores_t) sT[rr * ld + e] = p[0];
+    }
+  }
+  if (!scores_t) return;
+  __syncthreads();
+  const int rows = min(kRows, n - r0);
+  for (int item = tid; item < E * kRows; item += 64 * KW) {
+    const int e = item / kRows, rr = item % kRows;
+    if (rr < rows) scores_t[(size_t)e * n + r0 + rr] = sT[rr * ld + e];
+  }
+}
+
 // Finalize: 16 rows per workgroup, one wave per row at a time; lane l holds
 // experts l + 64 j.  Sums the split partials in split order, adds the
 // offset, then the scaled noise of noisy top-k (page 4 "How MoE routing
@@ -209,23 +400,7 @@ __global__ __launch_bounds__(1024) void router_finalize_kernel(
     }
     if (!scores && !scores_t) continue;
     float p[kMaxExpertRegs];
-    if (score == 0) {   // softmax
-      float m = -__builtin_huge_valf();
-#pragma unroll
-      for (int j = 0; j < kMaxExpertRegs; ++j)
-        if (j < nj && lane + 64 * j < E) m = fmaxf(m, z[j]);
-      m = wave_max_f32(m);
-      float t[kMaxExpertRegs];
-#pragma unroll
-      for (int j = 0; j < kMaxExpertRegs; ++j)
-        t[j] = (j < nj && lane + 64 * j < E) ? spec_exp(z[j] - m) : 0.f;
-      const float s = row_tree_sum(t, P);
-#pragma unroll
-      for (int j = 0; j < kMaxExpertRegs; ++j) p[j] = t[j] / s;
-    } else {
-#pragma unroll
-      for (int j = 0; j < kMaxExpertRegs; ++j) p[j] = spec_expert_score(z[j], score);
-    }
+    row_scores(z, nj, E, score, p);
 #pragma unroll
     for (int j = 0; j < kMaxExpertRegs; ++j) {
       const int e = lane + 64 * j;
@@ -265,7 +440,39 @@ static int router_splits(int n, int d, int E) {
   return s;
 }
 
+// Fused path: up to 64 experts (the workgroup holds all of them), K in
+// 32-wide steps per wave.  Shapes: RT = 2 when there are at least 512
+// 16-row tiles, else 1; MOE_ROUTER_KW_SMALL waves per workgroup when there
+// are fewer than 64 workgroups (short batches: more K slices in flight),
+// else MOE_ROUTER_KW_BIG.
+struct FusedShape {
+  bool ok;
+  int kw, rt;
+};
+static FusedShape router_fused_shape(int n, int d, int E, int dtype) {
+  FusedShape f{false, MOE_ROUTER_KW_BIG, 1};
+  if (dtype != 1 || E % 16 != 0 || E > 64 || n < 1) return f;
+  const int tiles = (n + 15) / 16;
+  f.rt = tiles >= 512 ? 2 : 1;
+  const int blocks = (n + 16 * f.rt - 1) / (16 * f.rt);
+  f.kw = blocks < 64 && d % (32 * MOE_ROUTER_KW_SMALL) == 0 ? MOE_ROUTER_KW_SMALL : MOE_ROUTER_KW_BIG;
+  f.ok = d % (32 * f.kw) == 0;
+  return f;
+}
+
+// Workgroups with more than 64 KB of LDS need the kernel's limit raised;
+// once per kernel, not per launch (the call costs host time).
+template <auto kKernel, size_t kLds>
+static hipError_t lds_limit_once() {
+  if (kLds <= 65536) return hipSuccess;
+  static const hipError_t status = hipFuncSetAttribute(reinterpret_cast<const void*>(kKernel),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       (int)kLds);
+  return status;
+}
+
 size_t router_workspace_bytes(int n, int d, int E, int dtype) {
+  if (router_fused_shape(n, d, E, dtype).ok) return 0;
   if (!router_uses_mfma(dtype, d, E)) return 0;
   const int s = router_splits(n, d, E);
   return s > 1 ? (size_t)s * n * E * sizeof(float) : 0;
@@ -274,6 +481,32 @@ size_t router_workspace_bytes(int n, int d, int E, int dtype) {
 hipError_t launch_router(const void* X, const void* Wg, int dtype, const float* offset,
                          const float* noise, float noise_std, int n, int d, int E, int score,
                          float* logits, float* scores, float* scores_t, void* ws, hipStream_t stream) {
+  const FusedShape fs = router_fused_shape(n, d, E, dtype);
+  if (fs.ok) {
+    const bf16_t* x = static_cast<const bf16_t*>(X);
+    const bf16_t* w = static_cast<const bf16_t*>(Wg);
+    auto go = [&](auto kern, hipError_t limit, size_t lds, int rows, int threads) -> hipError_t {
+      if (limit != hipSuccess) return limit;
+      hipLaunchKernelGGL(kern, dim3((unsigned)((n + rows - 1) / rows)), dim3(threads), lds, stream, x, w, n, d,
+                         E, offset, noise, noise_std, score, logits, scores, scores_t);
+      return hipGetLastError();
+    };
+#define MOE_FUSED(KW, RT, A)                                                                             \
+  go(router_fused_bf16_kernel<KW, RT, A>,                                                                \
+     lds_limit_once<router_fused_bf16_kernel<KW, RT, A>, router_fused_lds<KW, RT>()>(),                   \
+     router_fused_lds<KW, RT>(), 16 * RT, 64 * KW)
+#define MOE_FUSED_RING(KW, RT)                                                                      \
+  (ns % kFusedAhead == 0 ? MOE_FUSED(KW, RT, kFusedAhead) : ns % 2 == 0 ? MOE_FUSED(KW, RT, 2) \
+                                                                         : MOE_FUSED(KW, RT, 1))
+    const int ns = d / fs.kw / 32;   // K steps per wave
+    hipError_t err;
+    if (fs.kw == MOE_ROUTER_KW_SMALL && MOE_ROUTER_KW_SMALL != MOE_ROUTER_KW_BIG) err = MOE_FUSED_RING(MOE_ROUTER_KW_SMALL, 1);
+    else if (fs.rt == 2) err = MOE_FUSED_RING(MOE_ROUTER_KW_BIG, 2);
+    else err = MOE_FUSED_RING(MOE_ROUTER_KW_BIG, 1);
+#undef MOE_FUSED_RING
+#undef MOE_FUSED
+    return err;
+  }
   const float* partial = logits;
   int nsplit = 1;
   const int64_t total = (int64_t)n * E;

@@ -121,19 +121,24 @@ template <> struct Elem<bf16_t> {
 
 // One wave per token.  acc = residual; acc += shared; then acc += g * y for
 // the token's slots in list order (negative entries are dropped
-// assignments); one rounding at the store.  The token's slot list and gates
-// are loaded once (lane q holds entry q) and read back with readlane; the
-// rows of kSlotBatch slots are loaded together before they are added.
+// assignments); one rounding at the store.  The token index is uniform
+// across the wave, so its list bounds, slot ids and gates are scalar loads:
+// they run beside the vector loads of the residual row instead of queueing
+// behind them (vector loads complete in issue order).  Per column pass: the
+// residual and shared rows are requested, then the first kSlotBatch list
+// entries and their gates, then those slots' rows; only then is the
+// residual unpacked, so its fetch, the list lookups and the first rows'
+// fetch overlap.  Later batches follow one at a time.
 #ifndef MOE_COMBINE_CHUNKS
 #define MOE_COMBINE_CHUNKS 4
 #endif
 #ifndef MOE_COMBINE_BATCH
-#define MOE_COMBINE_BATCH 1
+#define MOE_COMBINE_BATCH 2
 #endif
 constexpr int kChunks = MOE_COMBINE_CHUNKS;     // 16-byte chunks per lane per column pass
 constexpr int kSlotBatch = MOE_COMBINE_BATCH;   // expert rows in flight per wave
 
-template <typename T>
+template <typename T, bool kRes, bool kShared>
 __global__ __launch_bounds__(256) void combine_vec_kernel(const T* __restrict__ Y,
                                                           const int32_t* __restrict__ token_offset,
                                                           const int32_t* __restrict__ token_slot,
@@ -145,75 +150,74 @@ __global__ __launch_bounds__(256) void combine_vec_kernel(const T* __restrict__ 
   const int lane = threadIdx.x & 63;
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= n) return;
-  const int q0 = token_offset[t], q1 = token_offset[t + 1];
   const size_t rowoff = (size_t)t * d;
-  // the first 64 list entries live in registers for every column pass;
-  // longer lists (a token picked by more than 64 experts) reload the rest
-  const int cnt0 = min(64, q1 - q0);
-  const int s0 = lane < cnt0 ? token_slot[q0 + lane] : -1;
-  const float g0 = s0 >= 0 ? slot_gate[s0] : 0.f;
+  const int q0 = token_offset[t], q1 = token_offset[t + 1];
   for (int col0 = 0; col0 < d; col0 += 64 * V * kChunks) {
-    float acc[kChunks][V];
+    // Columns past d (a ragged last pass) load the row's last chunk instead
+    // and are not stored: no load sits behind a per-lane branch, which would
+    // make the compiler wait for every earlier load first.
     bool ok[kChunks];
+    int cl[kChunks];
     u32x4_t rres[kChunks], rsh[kChunks];
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       const int col = col0 + (c * 64 + lane) * V;
       ok[c] = col < d;
-      if (ok[c] && residual) rres[c] = *reinterpret_cast<const u32x4_t*>(residual + rowoff + col);
-      if (ok[c] && shared) rsh[c] = *reinterpret_cast<const u32x4_t*>(shared + rowoff + col);
+      cl[c] = min(col, d - V);
+      if (kRes) rres[c] = *reinterpret_cast<const u32x4_t*>(residual + rowoff + cl[c]);
+      if (kShared) rsh[c] = *reinterpret_cast<const u32x4_t*>(shared + rowoff + cl[c]);
     }
+    int sl[kSlotBatch];
+    float gl[kSlotBatch];
+    u32x4_t ry[kSlotBatch][kChunks];
+    auto fetch = [&](int qb) {
+#pragma unroll
+      for (int b = 0; b < kSlotBatch; ++b) sl[b] = qb + b < q1 ? token_slot[qb + b] : -1;
+#pragma unroll
+      for (int b = 0; b < kSlotBatch; ++b) gl[b] = sl[b] >= 0 ? slot_gate[sl[b]] : 0.f;
+      // entries past the list (or dropped) load row 0, which always exists,
+      // and are skipped when adding
+#pragma unroll
+      for (int b = 0; b < kSlotBatch; ++b) {
+        const T* yrow = Y + (size_t)(sl[b] < 0 ? 0 : sl[b]) * d;
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) ry[b][c] = *reinterpret_cast<const u32x4_t*>(yrow + cl[c]);
+      }
+    };
+    float acc[kChunks][V];
+    auto add = [&]() {
+#pragma unroll
+      for (int b = 0; b < kSlotBatch; ++b) {
+        if (sl[b] < 0) continue;
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+          float y[V];
+          Elem<T>::unpack(ry[b][c], y);
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[c][i] = fmaf(gl[b], y[i], acc[c][i]);
+        }
+      }
+    };
+    fetch(q0);
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-      if (ok[c] && residual) {
+      if (kRes) {
         Elem<T>::unpack(rres[c], acc[c]);
       } else {
 #pragma unroll
         for (int i = 0; i < V; ++i) acc[c][i] = 0.f;
       }
-      if (ok[c] && shared) {
+      if (kShared) {
         float sh[V];
         Elem<T>::unpack(rsh[c], sh);
 #pragma unroll
         for (int i = 0; i < V; ++i) acc[c][i] += sh[i];
       }
     }
-    for (int w0 = q0; w0 < q1; w0 += 64) {
-      const int cnt = min(64, q1 - w0);
-      int my_s = s0;
-      float my_g = g0;
-      if (w0 != q0) {
-        my_s = lane < cnt ? token_slot[w0 + lane] : -1;
-        my_g = my_s >= 0 ? slot_gate[my_s] : 0.f;
-      }
-      for (int qb = 0; qb < cnt; qb += kSlotBatch) {
-        u32x4_t ry[kSlotBatch][kChunks];
-        int sb[kSlotBatch];
-        float gb[kSlotBatch];
-#pragma unroll
-        for (int b = 0; b < kSlotBatch; ++b) {
-          const int q = qb + b;
-          sb[b] = q < cnt ? __builtin_amdgcn_readlane(my_s, q) : -1;
-          gb[b] = q < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_g), q)) : 0.f;
-          const T* yrow = Y + (size_t)(sb[b] < 0 ? 0 : sb[b]) * d;
-#pragma unroll
-          for (int c = 0; c < kChunks; ++c)
-            if (ok[c] && sb[b] >= 0)
-              ry[b][c] = *reinterpret_cast<const u32x4_t*>(yrow + col0 + (c * 64 + lane) * V);
-        }
-#pragma unroll
-        for (int b = 0; b < kSlotBatch; ++b) {
-          if (sb[b] < 0) continue;
-#pragma unroll
-          for (int c = 0; c < kChunks; ++c) {
-            if (!ok[c]) continue;
-            float y[V];
-            Elem<T>::unpack(ry[b][c], y);
-#pragma unroll
-            for (int i = 0; i < V; ++i) acc[c][i] = fmaf(gb[b], y[i], acc[c][i]);
-          }
-        }
-      }
+    add();
+    for (int qb = q0 + kSlotBatch; qb < q1; qb += kSlotBatch) {
+      fetch(qb);
+      add();
     }
 #pragma unroll
     for (int c = 0; c < kChunks; ++c)
@@ -248,24 +252,34 @@ __global__ __launch_bounds__(256) void combine_scalar_kernel(const T* __restrict
   }
 }
 
+template <typename T>
+static hipError_t launch_combine_t(const T* Y, const int32_t* token_offset, const int32_t* token_slot,
+                                   const float* slot_gate, int n, int d, const T* residual, const T* shared,
+                                   T* out, hipStream_t stream) {
+  const dim3 grid((n + 3) / 4), block(256);
+  constexpr int V = Elem<T>::kVec;
+  if (d % V != 0) {
+    hipLaunchKernelGGL(combine_scalar_kernel<T>, grid, block, 0, stream, Y, token_offset, token_slot, slot_gate,
+                       n, d, residual, shared, out);
+  } else {
+    auto k = residual ? (shared ? combine_vec_kernel<T, true, true> : combine_vec_kernel<T, true, false>)
+                      : (shared ? combine_vec_kernel<T, false, true> : combine_vec_kernel<T, false, false>);
+    hipLaunchKernelGGL(k, grid, block, 0, stream, Y, token_offset, token_slot, slot_gate, n, d, residual, shared,
+                       out);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const void* Y, int dtype, const int32_t* token_offset,
                           const int32_t* token_slot, const float* slot_gate, int n, int d,
                           const void* residual, const void* shared, void* out, hipStream_t stream) {
-  const dim3 grid((n + 3) / 4), block(256);
-  if (dtype == 1) {
-    typedef bf16_t T;
-    auto k = d % 8 == 0 ? combine_vec_kernel<T> : combine_scalar_kernel<T>;
-    hipLaunchKernelGGL(k, grid, block, 0, stream, static_cast<const T*>(Y), token_offset, token_slot,
-                       slot_gate, n, d, static_cast<const T*>(residual),
-                       static_cast<const T*>(shared), static_cast<T*>(out));
-  } else {
-    typedef float T;
-    auto k = d % 4 == 0 ? combine_vec_kernel<T> : combine_scalar_kernel<T>;
-    hipLaunchKernelGGL(k, grid, block, 0, stream, static_cast<const T*>(Y), token_offset, token_slot,
-                       slot_gate, n, d, static_cast<const T*>(residual),
-                       static_cast<const T*>(shared), static_cast<T*>(out));
-  }
-  return hipGetLastError();
+  if (dtype == 1)
+    return launch_combine_t(static_cast<const bf16_t*>(Y), token_offset, token_slot, slot_gate, n, d,
+                            static_cast<const bf16_t*>(residual), static_cast<const bf16_t*>(shared),
+                            static_cast<bf16_t*>(out), stream);
+  return launch_combine_t(static_cast<const float*>(Y), token_offset, token_slot, slot_gate, n, d,
+                          static_cast<const float*>(residual), static_cast<const float*>(shared),
+                          static_cast<float*>(out), stream);
 }
 
 }  // namespace moe

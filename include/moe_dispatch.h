@@ -1,6 +1,6 @@
 /*
- * moe_dispatch.h -- C ABI of a Mixture-of-Experts layer forward on one
- * AMD Instinct MI355X (gfx950).
+ * moe_dispatch.h -- C ABI of a Mixture-of-Experts layer forward, and its
+ * backward, on one AMD Instinct MI355X (gfx950).
  *
  * The layer (MoE-routing pages: page 2 "Expert choice routing", section "The
  * math"; page 5 "MoE routing strategies explained", strategies 1-6):
@@ -16,6 +16,14 @@
  *   out = residual + shared + scatter_add(G * Y, I)     moe_combine
  *   load-balance loss, z-loss, MaxVio                   moe_balance_stats
  *   loss-free balancing: bias step from the loads       moe_update_bias
+ *
+ * The backward (gradients of <dOut, out> + the auxiliary losses, routing
+ * fixed), each step reversed:
+ *   dY = G * dOut[I], dG = <dOut[I], Y>                 moe_combine_backward
+ *   dX_in, dW1, dW2 of the expert FFNs                  moe_expert_ffn_backward
+ *   dZ from dG and the auxiliary losses                 moe_gate_backward
+ *   dX += dZ W_g^T, dW_g = X^T dZ                       moe_router_backward
+ *   dX += P^T dX_in                                     moe_dispatch_backward
  *
  * Conventions common to every call:
  *  - Tensor arguments are DEVICE pointers owned by the caller.  The library
@@ -304,6 +312,94 @@ moe_status_t moe_balance_stats(const float *logits, const moe_route_map_t *map,
  * sel_bias of moe_select; gamma finite. */
 moe_status_t moe_update_bias(const int32_t *expert_count, const moe_route_cfg_t *cfg, float gamma,
                              float *bias, void *stream);
+
+/* ---- the backward pass ---------------------------------------------------
+ * Gradients of L = <dOut, out> + lb_loss + z_loss for one forward, the
+ * routing held fixed: the top-k choice, the capacity drops and the counts
+ * are piecewise constant in the logits, so they pass no gradient.  The two
+ * auxiliary losses are moe_balance_stats' lb_loss and z_loss with the same
+ * coefficients (page 1 "What each direction guarantees" gives them as
+ * training losses added to the task loss).  One layer's calls, in order:
+ *   moe_combine_backward   dY_perm, d_gate            from dOut
+ *   moe_expert_ffn_backward dX_perm, dW1, dW2          from dY_perm
+ *   (shared expert: moe_expert_ffn_backward with E = 1, offsets {0, n}, on X
+ *    and dOut)
+ *   moe_gate_backward      dZ                          from d_gate
+ *   moe_router_backward    dX_r = dOut + dZ W_g^T, dW_g, d offset
+ *   moe_dispatch_backward  dX = dX_r (+ shared dX) + sum over slots of dX_perm
+ * bf16 activations are rounded once per stored tensor, products accumulate
+ * in fp32, weight gradients are fp32. */
+
+/* Backward of the combine (page 2 "The math": out = scatter_add(G * Y, I)).
+ * For every kept slot s < n_kept with t = slot_token[s]:
+ *   dY_perm[s] = slot_gate[s] * dOut[t]        (fp32 product, one rounding)
+ *   d_gate[s]  = sum_j dOut[t, j] * Y_perm[s, j]  (fp32, a fixed order)
+ * dOut [n,d], Y_perm and dY_perm [M_max,d] in dtype; d_gate [M_max] fp32;
+ * rows >= n_kept untouched.  The residual's and the shared expert's
+ * gradients are dOut itself.  dY_perm must not alias an input. */
+moe_status_t moe_combine_backward(const void *dOut, const void *Y_perm, int32_t dtype, int32_t n, int32_t d,
+                                  const moe_route_map_t *map, int64_t M_max, void *dY_perm, float *d_gate,
+                                  void *stream);
+
+/* Workspace for moe_expert_ffn_backward: the recomputed pre-activation
+ * [M_max, f_rows] in fp32, the activation H [M_max, f] and the gradient of
+ * the pre-activation [M_max, f_rows] in dtype (f_rows = f, or 2f for
+ * SwiGLU). */
+moe_status_t moe_ffn_backward_workspace_size(int64_t M_max, int32_t E, int32_t d, int32_t f, int32_t act,
+                                             int32_t dtype, size_t *bytes);
+
+/* Backward of the expert FFN (page 2 "The math": Y[e] = Expert_e(X_in[e])),
+ * per expert e over rows expert_offset[e] .. expert_offset[e+1]-1:
+ *   A = X W1^T (recomputed, kept in fp32), H = act(A), dH = dY W2,
+ *   dA = dH * act'(A)  (GELU: exact, x Phi(x); SwiGLU: d gate = dH * up *
+ *   silu'(gate), d up = dH * silu(gate), gate columns first),
+ *   dX_perm = dA W1, dW1[e] = dA^T X_perm, dW2[e] = dY^T H.
+ * X_perm, dY_perm, dX_perm [M_max,d] and W1 [E,f_rows,d], W2 [E,d,f] (the
+ * natural layout, not packed) in dtype; dW1 [E,f_rows,d] and dW2 [E,d,f]
+ * fp32, zero for experts without rows.  bf16 runs on the matrix cores
+ * (16-byte aligned tensors); fp32 on a plain kernel.  Errors: invalid
+ * shapes, M_max x f_rows or a weight matrix of 2^31 elements or more,
+ * MOE_ERR_WORKSPACE when ws is short. */
+moe_status_t moe_expert_ffn_backward(const void *X_perm, int32_t dtype, const int32_t *expert_offset, int32_t E,
+                                     int32_t d, int32_t f, int32_t act, const void *W1, const void *W2,
+                                     const void *dY_perm, int64_t M_max, void *dX_perm, float *dW1, float *dW2,
+                                     void *ws, size_t ws_bytes, void *stream);
+
+/* Backward of the gates and the auxiliary losses to the logits: dZ [n,E]
+ * fp32 at `logits` (the router's fp32 output), from d_gate [M_max] (per
+ * slot, moe_combine_backward).  Gate formulas as moe_select computes them:
+ * token choice softmax over the k selected logits (norm_topk) or the
+ * full-row probability; sigmoid / sqrtsoftplus scores renormalised over the
+ * k (norm_topk) or raw; expert choice S[t, e] of the row softmax.  A
+ * dropped assignment (assign_slot -1) contributes no gate gradient.  Plus
+ * lb_coef E f_e / n on every normalised score p_te (f_e = the share of
+ * chosen assignments, a constant) and z_coef (2 / n) lse_t softmax(z_t) for
+ * the z-loss.  sel_idx [n,k] (token choice; ignored for expert choice) and
+ * the map from the forward; every derivative in fp32. */
+moe_status_t moe_gate_backward(const float *logits, const int32_t *sel_idx, const float *d_gate,
+                               const moe_route_cfg_t *cfg, const moe_route_map_t *map, float lb_coef,
+                               float z_coef, float *dZ, void *stream);
+
+/* Workspace for moe_router_backward. */
+moe_status_t moe_router_backward_workspace_size(const moe_route_cfg_t *cfg, int32_t dtype, size_t *bytes);
+
+/* Backward of the router Z = X W_g (+ offset) (page 2 "The math"):
+ *   dX [n,d] = base + dZ W_g^T (dtype; base [n,d] in dtype or NULL = 0;
+ *     dX NULL: skipped),
+ *   dWg [d,E] = X^T dZ (fp32; NULL: skipped),
+ *   d_offset [E] = column sums of dZ (fp32; NULL: skipped).
+ * dZ is rounded to dtype for the products (bf16 on the matrix cores, fp32
+ * accumulation).  dX must not alias X or base. */
+moe_status_t moe_router_backward(const void *X, const void *Wg, int32_t dtype, const float *dZ,
+                                 const moe_route_cfg_t *cfg, const void *base, void *dX, float *dWg,
+                                 float *d_offset, void *ws, size_t ws_bytes, void *stream);
+
+/* Backward of the dispatch (page 2 "The math": X_in = P X, so dX = P^T
+ * dX_in): dX[t] = base[t] + base2[t] + sum of dX_perm[s] over token t's
+ * kept slots in list order, fp32 accumulation, one rounding to dtype.
+ * base, base2 [n,d] optional (NULL = 0); dX [n,d] must not alias an input. */
+moe_status_t moe_dispatch_backward(const void *dX_perm, int32_t dtype, const moe_route_map_t *map, int32_t n,
+                                   int32_t d, const void *base, const void *base2, void *dX, void *stream);
 
 const char *moe_status_string(moe_status_t status);
 const char *moe_last_error(void);

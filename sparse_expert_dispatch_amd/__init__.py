@@ -1,4 +1,4 @@
-"""MI355X-native Mixture-of-Experts layer forward.
+"""MI355X-native Mixture-of-Experts layer forward and backward.
 
 The compute lives in libmoe_dispatch.so (hand-written HIP kernels for
 gfx950, C ABI in include/moe_dispatch.h); this package is its thin Python
@@ -11,4 +11,6 @@ from ._native import (  # noqa: F401
     MOE_SOFTMAX, MOE_SWIGLU, MOE_TOKEN_CHOICE, STAT_NAMES, MoEError, RouteCfg, RouteMap, lib,
     make_cfg, moe_balance_stats, moe_build_map, moe_combine, moe_dispatch, moe_ec_k, moe_expert_ffn,
     moe_ffn_workspace_size, moe_last_error, moe_max_slots, moe_route_workspace_size, moe_router,
-    moe_router_workspace_size, moe_select, moe_status_string, moe_tc_capacity, moe_token_list_len)
+    moe_router_workspace_size, moe_select, moe_status_string, moe_tc_capacity, moe_token_list_len,
+    moe_combine_backward, moe_dispatch_backward, moe_expert_ffn_backward, moe_ffn_backward_workspace_size,
+    moe_gate_backward, moe_router_backward, moe_router_backward_workspace_size)

@@ -32,7 +32,9 @@ EXPORTED = ("moe_ec_k", "moe_tc_capacity", "moe_max_slots", "moe_token_list_len"
             "moe_route_workspace_size", "moe_ffn_workspace_size", "moe_router", "moe_select",
             "moe_build_map", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_balance_stats",
             "moe_update_bias", "moe_pack_expert_weights", "moe_expert_ffn_packed",
-            "moe_status_string", "moe_last_error")
+            "moe_combine_backward", "moe_ffn_backward_workspace_size", "moe_expert_ffn_backward",
+            "moe_gate_backward", "moe_router_backward_workspace_size", "moe_router_backward",
+            "moe_dispatch_backward", "moe_status_string", "moe_last_error")
 
 
 class MoEError(RuntimeError):
@@ -88,6 +90,13 @@ def lib() -> ctypes.CDLL:
         "moe_update_bias": (I32, [P, CFG, F32, P, P]),
         "moe_pack_expert_weights": (I32, [P, I32, I32, I32, I32, P, P]),
         "moe_expert_ffn_packed": (I32, [P, I32, P, P, I32, I32, I32, I32, P, P, I64, P, P, SZ, P]),
+        "moe_combine_backward": (I32, [P, P, I32, I32, I32, MAP, I64, P, P, P]),
+        "moe_ffn_backward_workspace_size": (I32, [I64, I32, I32, I32, I32, I32, SZP]),
+        "moe_expert_ffn_backward": (I32, [P, I32, P, I32, I32, I32, I32, P, P, P, I64, P, P, P, P, SZ, P]),
+        "moe_gate_backward": (I32, [P, P, P, CFG, MAP, F32, F32, P, P]),
+        "moe_router_backward_workspace_size": (I32, [CFG, I32, SZP]),
+        "moe_router_backward": (I32, [P, P, I32, P, CFG, P, P, P, P, P, SZ, P]),
+        "moe_dispatch_backward": (I32, [P, I32, MAP, I32, I32, P, P, P, P]),
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_last_error": (ctypes.c_char_p, []),
     }
@@ -361,6 +370,75 @@ def moe_update_bias(expert_count, cfg: RouteCfg, gamma, bias, stream=None):
     _check(lib().moe_update_bias(_ptr(expert_count, "expert_count", _I32), ctypes.byref(cfg),
                                  float(gamma), _ptr(bias, "bias", _F32), _stream(stream)),
            "moe_update_bias")
+
+
+# ---------------------------------------------------------------- backward
+
+def moe_combine_backward(dout, y_perm, rmap: RouteMap, dy_perm, d_gate, stream=None):
+    code = dtype_code(dout)
+    cm = rmap.c()
+    el = _elem_dtypes(code)
+    _check(lib().moe_combine_backward(_ptr(dout, "dout", el), _ptr(y_perm, "y_perm", el), code,
+                                      int(dout.shape[0]), int(dout.shape[1]), ctypes.byref(cm),
+                                      int(y_perm.shape[0]), _ptr(dy_perm, "dy_perm", el),
+                                      _ptr(d_gate, "d_gate", _F32), _stream(stream)), "moe_combine_backward")
+
+
+def moe_ffn_backward_workspace_size(M_max: int, E: int, d: int, f: int, act: int, dtype: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().moe_ffn_backward_workspace_size(int(M_max), int(E), int(d), int(f), int(act), int(dtype),
+                                                 ctypes.byref(out)), "moe_ffn_backward_workspace_size")
+    return out.value
+
+
+def moe_expert_ffn_backward(x_perm, expert_offset, w1, w2, act: int, dy_perm, dx_perm, dw1, dw2, ws,
+                            stream=None):
+    """W1 [E, f_rows, d] and W2 [E, d, f] in the natural layout; dW1 and dW2
+    fp32 of the same shapes."""
+    code = dtype_code(x_perm)
+    el = _elem_dtypes(code)
+    E = expert_offset.numel() - 1
+    d, f = w2.shape[-2], w2.shape[-1]
+    w, wb = _ws(ws)
+    _check(lib().moe_expert_ffn_backward(_ptr(x_perm, "x_perm", el), code, _ptr(expert_offset, "expert_offset", _I32),
+                                         E, d, f, int(act), _ptr(w1, "w1", el), _ptr(w2, "w2", el),
+                                         _ptr(dy_perm, "dy_perm", el), int(x_perm.shape[0]),
+                                         _ptr(dx_perm, "dx_perm", el), _ptr(dw1, "dw1", _F32),
+                                         _ptr(dw2, "dw2", _F32), w, wb, _stream(stream)), "moe_expert_ffn_backward")
+
+
+def moe_gate_backward(logits, sel_idx, d_gate, cfg: RouteCfg, rmap: RouteMap, lb_coef, z_coef, dz, stream=None):
+    cm = rmap.c()
+    _check(lib().moe_gate_backward(_ptr(logits, "logits", _F32), _ptr(sel_idx, "sel_idx", _I32),
+                                   _ptr(d_gate, "d_gate", _F32), ctypes.byref(cfg), ctypes.byref(cm),
+                                   float(lb_coef), float(z_coef), _ptr(dz, "dz", _F32), _stream(stream)),
+           "moe_gate_backward")
+
+
+def moe_router_backward_workspace_size(cfg: RouteCfg, dtype: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().moe_router_backward_workspace_size(ctypes.byref(cfg), int(dtype), ctypes.byref(out)),
+           "moe_router_backward_workspace_size")
+    return out.value
+
+
+def moe_router_backward(x, wg, dz, cfg: RouteCfg, base, dx, dwg, d_offset, ws, stream=None):
+    code = dtype_code(x)
+    el = _elem_dtypes(code)
+    w, wb = _ws(ws)
+    _check(lib().moe_router_backward(_ptr(x, "x", el), _ptr(wg, "wg", el), code, _ptr(dz, "dz", _F32),
+                                     ctypes.byref(cfg), _ptr(base, "base", el), _ptr(dx, "dx", el),
+                                     _ptr(dwg, "dwg", _F32), _ptr(d_offset, "d_offset", _F32), w, wb,
+                                     _stream(stream)), "moe_router_backward")
+
+
+def moe_dispatch_backward(dx_perm, rmap: RouteMap, n: int, base, base2, dx, stream=None):
+    code = dtype_code(dx)
+    el = _elem_dtypes(code)
+    cm = rmap.c()
+    _check(lib().moe_dispatch_backward(_ptr(dx_perm, "dx_perm", el), code, ctypes.byref(cm), int(n),
+                                       int(dx.shape[1]), _ptr(base, "base", el), _ptr(base2, "base2", el),
+                                       _ptr(dx, "dx", el), _stream(stream)), "moe_dispatch_backward")
 
 
 def moe_status_string(status: int) -> str:

@@ -356,6 +356,127 @@ moe_status_t moe_update_bias(const int32_t* expert_count, const moe_route_cfg_t*
                   "moe_update_bias");
 }
 
+// ---- backward -----------------------------------------------------------
+
+moe_status_t moe_combine_backward(const void* dOut, const void* Y_perm, int32_t dtype, int32_t n, int32_t d,
+                                  const moe_route_map_t* map, int64_t M_max, void* dY_perm, float* d_gate,
+                                  void* stream) {
+  REQUIRE(n > 0 && d > 0 && M_max >= 0, "n, d must be positive, M_max non-negative");
+  REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, "dtype must be MOE_F32 or MOE_BF16");
+  if (M_max == 0) return MOE_OK;
+  REQUIRE(M_max <= INT32_MAX, "M_max must fit in int32");
+  REQUIRE(dOut && Y_perm && dY_perm && d_gate, "tensor arguments must be non-NULL");
+  REQUIRE(map && map->slot_token && map->slot_gate && map->n_kept,
+          "map->slot_token, slot_gate and n_kept must be non-NULL");
+  REQUIRE(dY_perm != Y_perm && dY_perm != dOut, "dY_perm must not alias an input");
+  if (dtype == MOE_BF16 && d % 8 == 0)
+    REQUIRE(aligned16(dOut) && aligned16(Y_perm) && aligned16(dY_perm), "tensors must be 16-byte aligned");
+  return launched(moe::launch_combine_backward(dOut, Y_perm, dtype, d, map->slot_token, map->slot_gate,
+                                               map->n_kept, M_max, dY_perm, d_gate, as_stream(stream)),
+                  "moe_combine_backward");
+}
+
+moe_status_t moe_ffn_backward_workspace_size(int64_t M_max, int32_t E, int32_t d, int32_t f, int32_t act,
+                                             int32_t dtype, size_t* bytes) {
+  REQUIRE(bytes != nullptr, "bytes is NULL");
+  REQUIRE(M_max >= 0 && E > 0 && d > 0 && f > 0, "E, d, f must be positive, M_max non-negative");
+  REQUIRE(act == MOE_GELU || act == MOE_SWIGLU, "act must be MOE_GELU or MOE_SWIGLU");
+  REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, "dtype must be MOE_F32 or MOE_BF16");
+  *bytes = moe::ffn_backward_workspace_bytes(M_max, E, d, f, act, dtype);
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_ffn_backward(const void* X_perm, int32_t dtype, const int32_t* expert_offset, int32_t E,
+                                     int32_t d, int32_t f, int32_t act, const void* W1, const void* W2,
+                                     const void* dY_perm, int64_t M_max, void* dX_perm, float* dW1, float* dW2,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(E > 0 && d > 0 && f > 0 && M_max >= 0, "E, d, f must be positive, M_max non-negative");
+  REQUIRE(act == MOE_GELU || act == MOE_SWIGLU, "act must be MOE_GELU or MOE_SWIGLU");
+  REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, "dtype must be MOE_F32 or MOE_BF16");
+  REQUIRE(expert_offset && W1 && W2 && dW1 && dW2, "expert_offset, W1, W2, dW1 and dW2 must be non-NULL");
+  REQUIRE(M_max == 0 || (X_perm && dY_perm && dX_perm), "X_perm, dY_perm and dX_perm must be non-NULL");
+  REQUIRE(M_max <= INT32_MAX, "M_max must fit in int32");
+  SUPPORTED(E <= moe::kMaxExperts, "expert FFN backward supports E <= %d (E=%d)", moe::kMaxExperts, E);
+  const int64_t fr = act == MOE_SWIGLU ? 2 * (int64_t)f : f;
+  REQUIRE(M_max * fr <= INT32_MAX && M_max * (int64_t)d <= INT32_MAX && fr * d <= INT32_MAX,
+          "M_max x width and the weight matrices must have fewer than 2^31 elements");
+  if (dtype == MOE_BF16)
+    REQUIRE(aligned16(W1) && aligned16(W2) && (M_max == 0 || (aligned16(X_perm) && aligned16(dY_perm) &&
+                                                              aligned16(dX_perm))),
+            "bf16 tensors must be 16-byte aligned");
+  const size_t need = moe::ffn_backward_workspace_bytes(M_max, E, d, f, act, dtype);
+  if (need && (!ws || ws_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "expert_ffn_backward needs %zu workspace bytes, got %zu", need, ws_bytes);
+  REQUIRE(!need || aligned16(ws), "workspace must be 16-byte aligned");
+  return launched(moe::launch_expert_ffn_backward(X_perm, dtype, expert_offset, E, d, f, act, W1, W2, dY_perm,
+                                                  M_max, dX_perm, dW1, dW2, ws, as_stream(stream)),
+                  "moe_expert_ffn_backward");
+}
+
+moe_status_t moe_gate_backward(const float* logits, const int32_t* sel_idx, const float* d_gate,
+                               const moe_route_cfg_t* cfg, const moe_route_map_t* map, float lb_coef,
+                               float z_coef, float* dZ, void* stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  st = check_map(map);
+  if (st != MOE_OK) return st;
+  REQUIRE(logits && dZ, "logits and dZ must be non-NULL");
+  REQUIRE(cfg->k == 0 || d_gate, "d_gate must be non-NULL");
+  REQUIRE(cfg->dir == MOE_EXPERT_CHOICE || sel_idx, "token choice needs sel_idx");
+  REQUIRE(std::isfinite(lb_coef) && std::isfinite(z_coef), "coefficients must be finite");
+  return launched(moe::launch_gate_backward(logits, sel_idx, d_gate, map_ptrs(map), cfg->n, cfg->E, cfg->k,
+                                            cfg->dir, cfg->score, cfg->norm_topk, lb_coef, z_coef, dZ,
+                                            as_stream(stream)),
+                  "moe_gate_backward");
+}
+
+moe_status_t moe_router_backward_workspace_size(const moe_route_cfg_t* cfg, int32_t dtype, size_t* bytes) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  REQUIRE(bytes != nullptr, "bytes is NULL");
+  REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, "dtype must be MOE_F32 or MOE_BF16");
+  *bytes = moe::router_backward_workspace_bytes(cfg->n, cfg->d, cfg->E, dtype);
+  return MOE_OK;
+}
+
+moe_status_t moe_router_backward(const void* X, const void* Wg, int32_t dtype, const float* dZ,
+                                 const moe_route_cfg_t* cfg, const void* base, void* dX, float* dWg,
+                                 float* d_offset, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, "dtype must be MOE_F32 or MOE_BF16");
+  REQUIRE(X && Wg && dZ, "X, Wg and dZ must be non-NULL");
+  REQUIRE(!dX || (dX != X && dX != base), "dX must not alias X or base");
+  REQUIRE((int64_t)cfg->n * cfg->d <= INT32_MAX && (int64_t)cfg->d * cfg->E <= INT32_MAX,
+          "n x d and d x E must have fewer than 2^31 elements");
+  if (dtype == MOE_BF16)
+    REQUIRE(aligned16(X) && aligned16(Wg) && (!dX || aligned16(dX)) && (!base || aligned16(base)),
+            "bf16 tensors must be 16-byte aligned");
+  const size_t need = moe::router_backward_workspace_bytes(cfg->n, cfg->d, cfg->E, dtype);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "router_backward needs %zu workspace bytes, got %zu", need, ws_bytes);
+  REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
+  return launched(moe::launch_router_backward(X, Wg, dtype, dZ, cfg->n, cfg->d, cfg->E, base, dX, dWg,
+                                              d_offset, ws, as_stream(stream)),
+                  "moe_router_backward");
+}
+
+moe_status_t moe_dispatch_backward(const void* dX_perm, int32_t dtype, const moe_route_map_t* map, int32_t n,
+                                   int32_t d, const void* base, const void* base2, void* dX, void* stream) {
+  REQUIRE(dX_perm && dX, "dX_perm and dX must be non-NULL");
+  REQUIRE(map && map->token_offset && map->token_slot, "map->token_offset and token_slot must be non-NULL");
+  REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, "dtype must be MOE_F32 or MOE_BF16");
+  REQUIRE(n > 0 && d > 0, "n, d must be positive");
+  REQUIRE(dX != dX_perm && dX != base && dX != base2, "dX must not alias an input");
+  const int vec = dtype == MOE_BF16 ? 8 : 4;
+  if (d % vec == 0)
+    REQUIRE(aligned16(dX_perm) && aligned16(dX) && (!base || aligned16(base)) && (!base2 || aligned16(base2)),
+            "tensors must be 16-byte aligned");
+  return launched(moe::launch_combine(dX_perm, dtype, map->token_offset, map->token_slot, nullptr, n, d, base,
+                                      base2, dX, as_stream(stream)),
+                  "moe_dispatch_backward");
+}
+
 const char* moe_status_string(moe_status_t status) {
   switch (status) {
     case MOE_OK: return "ok";

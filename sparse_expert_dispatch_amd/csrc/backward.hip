@@ -1,0 +1,915 @@
+// Backward pass of the MoE layer: gradients of L = <dOut, out> + lb_loss +
+// z_loss with the routing (choice, drops, counts) held fixed.
+//
+// MoE-routing pages: page 2 "Expert choice routing", section "The math"
+// (X_in = P X, Y = Expert(X_in), out = scatter_add(G * Y, I): the backward
+// runs these maps in reverse); page 1 "Token choice vs expert choice
+// routing", section "What each direction guarantees" (the auxiliary loss
+// coefficients); page 5 "MoE routing strategies explained", strategies 1
+// and 4 (softmax and sigmoid gates).
+//
+// Kernels:
+// * combine backward: one wave per kept slot: dY = gate * dOut[token] and
+//   d_gate = <dOut[token], Y> (fixed-order fp32 dot product);
+// * gate backward: one wave per token: the gate formula's derivative plus
+//   the load-balance and z-loss terms, written to dZ [n, E];
+// * a grouped bf16 GEMM on v_mfma_f32_16x16x32_bf16 for every product of
+//   the expert FFN and router backward.  Groups split either the rows (the
+//   expert-major buffer: pre-activation recompute, dH, dX, router dX) or K
+//   (weight gradients: a sum over an expert's rows).  Each operand is staged
+//   into LDS per 32-wide K step as it is stored: a K-contiguous operand as
+//   [row][K] and read with 16-byte loads, a K-strided one (K is its row
+//   index: W2 and W1 in dH = dY W2 and dX = dA W1, and both operands of a
+//   weight gradient) as [K][row] and read with ds_read_b64_tr_b16, whose
+//   16-lane transpose hands each lane four consecutive K values of its own
+//   column, so no copy is ever transposed in memory.  The activation
+//   derivative is fused into the dH epilogue;
+// * a plain fp32 grouped GEMM (one thread per output) for fp32 data and for
+//   shapes the bf16 tiling does not cover.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+typedef __bf16 bwbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float bwf32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t bwu32x4_t __attribute__((ext_vector_type(4)));
+typedef short bwv4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bwv4i16 bw_lds_v4i16;
+
+// ------------------------------------------------------------------ helpers
+
+MOE_DEV float load_f(const float* p) { return *p; }
+MOE_DEV float load_f(const bf16_t* p) { return bf16_to_f32(*p); }
+MOE_DEV void store_f(float* p, float v) { *p = v; }
+MOE_DEV void store_f(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+
+// GELU x Phi(x) with Phi from erff, and its derivative Phi(x) + x phi(x).
+MOE_DEV float gelu_exact(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+MOE_DEV float gelu_exact_grad(float x) {
+  return 0.5f * (1.0f + erff(x * 0.70710678118654752f)) + x * 0.39894228040143268f * expf(-0.5f * x * x);
+}
+MOE_DEV float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// ------------------------------------------------------------ combine backward
+
+// One wave per slot s < n_kept: t = slot_token[s], g = slot_gate[s];
+// dY[s] = g * dOut[t] (fp32 product, one rounding), d_gate[s] = sum over
+// columns of dOut[t] * Y[s]: each lane accumulates its columns in order with
+// fmaf, then a halving tree over the lanes.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const T* __restrict__ dout, const T* __restrict__ Y,
+                                                          const int32_t* __restrict__ slot_token,
+                                                          const float* __restrict__ slot_gate,
+                                                          const int32_t* __restrict__ n_kept, int64_t M_max,
+                                                          int d, T* __restrict__ dY, float* __restrict__ d_gate) {
+  const int lane = threadIdx.x & 63;
+  const int64_t s = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t rows = min((int64_t)*n_kept, M_max);
+  if (s >= rows) return;
+  const int t = slot_token[s];
+  const float g = slot_gate[s];
+  const T* o = dout + (size_t)t * d;
+  const T* y = Y + (size_t)s * d;
+  T* dy = dY + (size_t)s * d;
+  float dot = 0.f;
+  for (int c = lane; c < d; c += 64) {
+    const float ov = load_f(o + c);
+    store_f(dy + c, g * ov);
+    dot = fmaf(ov, load_f(y + c), dot);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) dot = dot + __shfl_down(dot, off, 64);
+  if (lane == 0) d_gate[s] = dot;
+}
+
+// bf16 rows of whole 16-byte chunks: 8 columns per lane and chunk.
+__global__ __launch_bounds__(256) void combine_bwd_vec_kernel(const bf16_t* __restrict__ dout,
+                                                              const bf16_t* __restrict__ Y,
+                                                              const int32_t* __restrict__ slot_token,
+                                                              const float* __restrict__ slot_gate,
+                                                              const int32_t* __restrict__ n_kept, int64_t M_max,
+                                                              int d, bf16_t* __restrict__ dY,
+                                                              float* __restrict__ d_gate) {
+  const int lane = threadIdx.x & 63;
+  const int64_t s = __builtin_amdgcn_readfirstlane((int)((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)));
+  const int64_t rows = min((int64_t)*n_kept, M_max);
+  if (s >= rows) return;
+  const int t = slot_token[s];
+  const float g = slot_gate[s];
+  const bwu32x4_t* o = reinterpret_cast<const bwu32x4_t*>(dout + (size_t)t * d);
+  const bwu32x4_t* y = reinterpret_cast<const bwu32x4_t*>(Y + (size_t)s * d);
+  bwu32x4_t* dy = reinterpret_cast<bwu32x4_t*>(dY + (size_t)s * d);
+  const int nv = d / 8;
+  float dot = 0.f;
+  for (int c = lane; c < nv; c += 64) {
+    const bwu32x4_t ov = o[c], yv = y[c];
+    bwu32x4_t out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float o0 = __uint_as_float(ov[i] << 16), o1 = __uint_as_float(ov[i] & 0xFFFF0000u);
+      const float y0 = __uint_as_float(yv[i] << 16), y1 = __uint_as_float(yv[i] & 0xFFFF0000u);
+      out[i] = pack_bf16x2(g * o0, g * o1);
+      dot = fmaf(o0, y0, dot);
+      dot = fmaf(o1, y1, dot);
+    }
+    dy[c] = out;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) dot = dot + __shfl_down(dot, off, 64);
+  if (lane == 0) d_gate[s] = dot;
+}
+
+hipError_t launch_combine_backward(const void* dout, const void* Y, int dtype, int d, const int32_t* slot_token,
+                                   const float* slot_gate, const int32_t* n_kept, int64_t M_max, void* dY,
+                                   float* d_gate, hipStream_t stream) {
+  if (M_max <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((M_max + 3) / 4)), block(256);
+  if (dtype == 1 && d % 8 == 0)
+    hipLaunchKernelGGL(combine_bwd_vec_kernel, grid, block, 0, stream, static_cast<const bf16_t*>(dout),
+                       static_cast<const bf16_t*>(Y), slot_token, slot_gate, n_kept, M_max, d,
+                       static_cast<bf16_t*>(dY), d_gate);
+  else if (dtype == 1)
+    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, grid, block, 0, stream, static_cast<const bf16_t*>(dout),
+                       static_cast<const bf16_t*>(Y), slot_token, slot_gate, n_kept, M_max, d,
+                       static_cast<bf16_t*>(dY), d_gate);
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<float>, grid, block, 0, stream, static_cast<const float*>(dout),
+                       static_cast<const float*>(Y), slot_token, slot_gate, n_kept, M_max, d,
+                       static_cast<float*>(dY), d_gate);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------- gate backward
+
+// One wave per token, lane l holds experts l + 64 j (j < NJ).  dz starts
+// from the gate formula's derivative (selected experts only, through a
+// per-wave LDS row so that lane q's contribution reaches the lane owning
+// expert idx[q]; the k experts of a token are distinct), then adds
+// p (c - <p, c>) for the load-balance loss (c_e = lb_coef E f_e / n;
+// scores: through r / sum r) and z_coef (2 / n) lse p for the z-loss.
+constexpr int kGateRows = 16;
+
+template <int NJ>
+__global__ __launch_bounds__(1024) void gate_bwd_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ sel_idx, const float* __restrict__ d_gate,
+    const int32_t* __restrict__ assign_slot, const int32_t* __restrict__ token_offset,
+    const int32_t* __restrict__ token_slot, const int32_t* __restrict__ expert_count, int n, int E, int k,
+    int dir, int score, int norm_topk, float lb_coef, float z_coef, float* __restrict__ dZ) {
+  __shared__ float s_c[kMaxExperts];
+  __shared__ float s_row[kGateRows][64 * NJ];
+  __shared__ float s_tot;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // load-balance weights c_e = lb_coef * E * f_e / n, f_e = count_e / sum(count)
+  if (wave == 0) {
+    float tot = 0.f;
+    for (int e = lane; e < E; e += 64) tot += (float)expert_count[e];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o, 64);
+    if (lane == 0) s_tot = tot;
+  }
+  for (int j = lane; j < 64 * NJ; j += 64) s_row[wave][j] = 0.f;
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 1024)
+    s_c[e] = s_tot > 0.f ? lb_coef * (float)E * ((float)expert_count[e] / s_tot) / (float)n : 0.f;
+  __syncthreads();
+  const int t = blockIdx.x * kGateRows + wave;
+  if (t >= n) return;
+  float z[NJ], p[NJ];
+  float m = -__builtin_huge_valf();
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + 64 * j;
+    z[j] = e < E ? logits[(size_t)t * E + e] : -__builtin_huge_valf();
+    m = fmaxf(m, z[j]);
+  }
+  m = wave_max_f32(m);
+  float ssum = 0.f;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    p[j] = lane + 64 * j < E ? expf(z[j] - m) : 0.f;
+    ssum += p[j];
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ssum += __shfl_xor(ssum, o, 64);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) p[j] = p[j] / ssum;
+  const float lse = m + logf(ssum);
+  float* row = s_row[wave];
+
+  if (dir == 0) {
+    // lane q < k: the token's q-th choice
+    const bool on = lane < k;
+    const int e_q = on ? sel_idx[(size_t)t * k + lane] : 0;
+    const int a_q = on ? assign_slot[(size_t)t * k + lane] : -1;
+    const float dg = a_q >= 0 ? d_gate[a_q] : 0.f;
+    const float zq = on ? logits[(size_t)t * E + e_q] : 0.f;
+    if (score == 0 && !norm_topk) {
+      // full-row softmax probability: dp at the chosen experts
+      if (on) row[e_q] = dg;
+    } else {
+      float dzq;
+      if (score == 0) {
+        float mq = on ? zq : -__builtin_huge_valf();
+        mq = wave_max_f32(mq);
+        const float eq = on ? expf(zq - mq) : 0.f;
+        float sq = eq;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, 64);
+        const float gq = eq / sq;
+        float sgd = gq * dg;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) sgd += __shfl_xor(sgd, o, 64);
+        dzq = gq * (dg - sgd);
+      } else {
+        const float sg = sigm(zq);
+        const float r = score == 1 ? sg : sqrtf(fmaxf(zq, 0.f) + log1pf(expf(-fabsf(zq))));
+        const float rp = score == 1 ? sg * (1.f - sg) : sg / (2.f * r);
+        float dr = dg;
+        if (norm_topk) {
+          float R = on ? r : 0.f;
+#pragma unroll
+          for (int o = 32; o >= 1; o >>= 1) R += __shfl_xor(R, o, 64);
+          const float gq = r / R;
+          float sgd = on ? gq * dg : 0.f;
+#pragma unroll
+          for (int o = 32; o >= 1; o >>= 1) sgd += __shfl_xor(sgd, o, 64);
+          dr = (dg - sgd) / R;
+        }
+        dzq = dr * rp;
+      }
+      if (on) row[e_q] = dzq;
+    }
+  } else {
+    // expert choice: dS at the experts whose slots are in the token's list
+    const int q0 = token_offset[t], q1 = token_offset[t + 1];
+    for (int q = q0 + lane; q < q1; q += 64) {
+      const int s = token_slot[q];
+      if (s >= 0) row[s / k] = d_gate[s];
+    }
+  }
+  // one wave's LDS writes are visible to its later reads
+  float dz[NJ], g_in[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) g_in[j] = row[lane + 64 * j];
+  const bool through_softmax = dir == 1 || (score == 0 && !norm_topk);
+  float pd = 0.f;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) pd += p[j] * g_in[j];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) pd += __shfl_xor(pd, o, 64);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) dz[j] = through_softmax ? p[j] * (g_in[j] - pd) : g_in[j];
+  // load-balance loss
+  if (lb_coef != 0.f && s_tot > 0.f) {
+    float c[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) c[j] = lane + 64 * j < E ? s_c[lane + 64 * j] : 0.f;
+    if (score == 0) {
+      float pc = 0.f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) pc += p[j] * c[j];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) pc += __shfl_xor(pc, o, 64);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) dz[j] += p[j] * (c[j] - pc);
+    } else {
+      float r[NJ], rp[NJ];
+      float R = 0.f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const bool v = lane + 64 * j < E;
+        const float sg = sigm(z[j]);
+        r[j] = !v ? 0.f : score == 1 ? sg : sqrtf(fmaxf(z[j], 0.f) + log1pf(expf(-fabsf(z[j]))));
+        rp[j] = !v ? 0.f : score == 1 ? sg * (1.f - sg) : sg / (2.f * r[j]);
+        R += r[j];
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) R += __shfl_xor(R, o, 64);
+      float pc = 0.f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) pc += (r[j] / R) * c[j];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) pc += __shfl_xor(pc, o, 64);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) dz[j] += rp[j] * (c[j] - pc) / R;
+    }
+  }
+  if (z_coef != 0.f) {
+    const float zc = z_coef * (2.f / (float)n) * lse;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) dz[j] += zc * p[j];
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + 64 * j;
+    if (e < E) dZ[(size_t)t * E + e] = dz[j];
+  }
+}
+
+hipError_t launch_gate_backward(const float* logits, const int32_t* sel_idx, const float* d_gate,
+                                const MapPtrs& m, int n, int E, int k, int dir, int score, int norm_topk,
+                                float lb_coef, float z_coef, float* dZ, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const dim3 grid((n + kGateRows - 1) / kGateRows), block(1024);
+  const auto kern = E <= 64 ? gate_bwd_kernel<1> : E <= 128 ? gate_bwd_kernel<2>
+                    : E <= 256 ? gate_bwd_kernel<4> : gate_bwd_kernel<8>;
+  hipLaunchKernelGGL(kern, grid, block, 0, stream, logits, sel_idx, d_gate, m.assign_slot, m.token_offset,
+                     m.token_slot, m.expert_count, n, E, k, dir, score, norm_topk, lb_coef, z_coef, dZ);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- grouped GEMM
+
+// C(i, j) = sum_k A(i, k) B(k, j).  A(i, k) = A[i * lda + k] when kAK (K
+// contiguous) else A[k * lda + i]; B(k, j) = B[j * ldb + k] when kBK else
+// B[k * ldb + j].
+//   Row-grouped (kMode 0): group g owns rows offsets[g] .. offsets[g+1]-1 of
+//   A and C (absolute row indices); B of group g starts at B + g *
+//   b_stride; K = args.K; J columns.
+//   K-grouped (kMode 1): group g sums over k = offsets[g] .. offsets[g+1]-1
+//   (rows of A and B), C of group g starts at C + g * c_stride and has
+//   I x J entries.
+struct GemmArgs {
+  const bf16_t* A;
+  int64_t lda;
+  const bf16_t* B;
+  int64_t ldb;
+  int64_t b_stride;
+  void* C;
+  int64_t ldc;
+  int64_t c_stride;
+  const int32_t* offsets;
+  int groups, I, J, K;
+  const bf16_t* base;  // EPI_BF16_ADD: C = base + A B (ld = ldc)
+  const float* pre;    // activation backward: fp32 pre-activations [rows, ld_pre]
+  int64_t ld_pre;
+  bf16_t* h_out;       // activation backward: act(pre) [rows, ld_h]
+  int64_t ld_h;
+  int f;               // activation backward: hidden size (SwiGLU up columns start at f)
+};
+
+enum { EPI_BF16 = 0, EPI_BF16_ADD = 1, EPI_F32 = 2, EPI_GELU_BWD = 3, EPI_SWIGLU_BWD = 4 };
+
+// Epilogue of one output element (row `r`, column `c`, value v); row-grouped
+// rows are absolute, K-grouped outputs start at the group's C.
+template <int kEpi>
+MOE_DEV void epi_store(const GemmArgs& a, void* Cg, int64_t r, int c, float v) {
+#pragma clang fp contract(off)
+  if (kEpi == EPI_F32) {
+    static_cast<float*>(Cg)[r * a.ldc + c] = v;
+  } else if (kEpi == EPI_BF16) {
+    static_cast<bf16_t*>(Cg)[r * a.ldc + c] = f32_to_bf16(v);
+  } else if (kEpi == EPI_BF16_ADD) {
+    const float b = a.base ? bf16_to_f32(a.base[r * a.ldc + c]) : 0.f;
+    static_cast<bf16_t*>(Cg)[r * a.ldc + c] = f32_to_bf16(b + v);
+  } else if (kEpi == EPI_GELU_BWD) {
+    const float x = a.pre[r * a.ld_pre + c];
+    static_cast<bf16_t*>(Cg)[r * a.ldc + c] = f32_to_bf16(v * gelu_exact_grad(x));
+    a.h_out[r * a.ld_h + c] = f32_to_bf16(gelu_exact(x));
+  } else {
+    const float gp = a.pre[r * a.ld_pre + c];
+    const float up = a.pre[r * a.ld_pre + a.f + c];
+    const float sg = sigm(gp);
+    const float si = gp * sg;
+    static_cast<bf16_t*>(Cg)[r * a.ldc + c] = f32_to_bf16(v * up * (sg * (1.f + gp * (1.f - sg))));
+    static_cast<bf16_t*>(Cg)[r * a.ldc + a.f + c] = f32_to_bf16(v * si);
+    a.h_out[r * a.ld_h + c] = f32_to_bf16(si * up);
+  }
+}
+
+// Locate row-grouped tile `bx`: group g and its 128-row tile index, or g = -1
+// past the last tile.  Lane l of wave 0 counts the tiles of a contiguous run
+// of groups; a wave scan gives every run its first tile.
+MOE_DEV void locate_row_tile(const int32_t* __restrict__ offsets, int G, int bx, int* s_g, int* s_tile) {
+  const int lane = threadIdx.x & 63;
+  const int per = (G + 63) / 64;
+  const int g0 = min(G, lane * per), g1 = min(G, g0 + per);
+  int cnt = 0;
+  for (int g = g0; g < g1; ++g) cnt += (offsets[g + 1] - offsets[g] + 127) >> 7;
+  const int incl = wave_inclusive_scan_i32(cnt);
+  int base = incl - cnt;
+  if (lane == 0) *s_g = -1;
+  __builtin_amdgcn_wave_barrier();
+  if (bx >= base && bx < incl) {
+    for (int g = g0; g < g1; ++g) {
+      const int tiles = (offsets[g + 1] - offsets[g] + 127) >> 7;
+      if (bx < base + tiles) {
+        *s_g = g;
+        *s_tile = bx - base;
+        break;
+      }
+      base += tiles;
+    }
+  }
+}
+
+constexpr int kGT = 128;             // tile rows and columns
+constexpr int kGK = 32;              // K per step
+constexpr int kLdKc = kGK + 8;       // LDS stride (bf16) of a K-contiguous stage [128][40]
+constexpr int kLdKs = kGT + 8;       // LDS stride of a K-strided stage [32][136]
+constexpr int kStageElems = kGT * kLdKc;   // 5120 >= 32 * 136 = 4352
+
+template <bool kAK, bool kBK, int kMode, int kEpi>
+__global__ __launch_bounds__(256) void bw_gemm_bf16_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2][kStageElems];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[2][kStageElems];
+  __shared__ int s_g, s_tile;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;   // 2 x 2 waves of 64 x 64
+
+  int g, i0, j0 = blockIdx.y * kGT;
+  int64_t row0 = 0;       // row-grouped: first absolute row of the tile
+  int rows = kGT;         // row-grouped: valid rows of the tile
+  int kbeg = 0, klen = a.K;
+  if (kMode == 0) {
+    if (wave == 0) locate_row_tile(a.offsets, a.groups, blockIdx.x, &s_g, &s_tile);
+    __syncthreads();
+    g = s_g;
+    if (g < 0) return;
+    row0 = (int64_t)a.offsets[g] + (int64_t)s_tile * kGT;
+    rows = min((int64_t)kGT, (int64_t)a.offsets[g + 1] - row0);
+    i0 = 0;
+  } else {
+    g = blockIdx.z;
+    i0 = blockIdx.x * kGT;
+    kbeg = a.offsets[g];
+    klen = a.offsets[g + 1] - kbeg;
+  }
+  void* Cg = kMode == 0 ? a.C
+                        : (void*)((char*)a.C + (size_t)g * a.c_stride * (kEpi == EPI_F32 ? 4 : 2));
+  const int ns = (klen + kGK - 1) / kGK;
+  if (kMode == 1 && ns == 0) {
+    // an expert without rows: zero gradient
+    for (int e = tid; e < kGT * kGT; e += 256) {
+      const int r = i0 + e / kGT, c = j0 + e % kGT;
+      if (r < a.I && c < a.J) epi_store<kEpi>(a, Cg, r, c, 0.f);
+    }
+    return;
+  }
+  // buffer resources (bounds: rows past the group read as zero)
+  const bf16_t* abase;
+  int64_t abytes;
+  if (kMode == 0) {
+    abase = a.A + row0 * a.lda;
+    abytes = (int64_t)rows * a.lda * 2;
+  } else {
+    abase = a.A + (int64_t)kbeg * a.lda;
+    abytes = (int64_t)klen * a.lda * 2;
+  }
+  const bf16_t* bbase;
+  int64_t bbytes;
+  if (kMode == 0) {
+    bbase = a.B + (int64_t)g * a.b_stride;
+    bbytes = kBK ? (int64_t)a.J * a.ldb * 2 : (int64_t)a.K * a.ldb * 2;
+  } else {
+    bbase = a.B + (int64_t)kbeg * a.ldb;
+    bbytes = (int64_t)klen * a.ldb * 2;
+  }
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(abase), (short)0, (int)min(abytes, (int64_t)0x7FFFFFFF), 0x00020000);
+  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(bbase), (short)0, (int)min(bbytes, (int64_t)0x7FFFFFFF), 0x00020000);
+
+  // Per step each thread moves two 16-byte chunks of each operand.
+  //   K-contiguous: chunk c -> row c / 4 of the tile, K offset 8 (c % 4);
+  //   K-strided:    chunk c -> K row c / 16, column offset 8 (c % 16).
+  int a_off[2], b_off[2], a_lds[2], b_lds[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = tid + 256 * h;
+    if (kAK) {
+      const int r = c >> 2, kq = (c & 3) * 8;
+      a_off[h] = (int)(((int64_t)(i0 + r) * a.lda + kq) * 2);
+      a_lds[h] = r * kLdKc + kq;
+    } else {
+      const int kr = c >> 4, ic = (c & 15) * 8;
+      a_off[h] = (int)(((int64_t)kr * a.lda + i0 + ic) * 2);
+      a_lds[h] = kr * kLdKs + ic;
+    }
+    if (kBK) {
+      const int r = c >> 2, kq = (c & 3) * 8;
+      b_off[h] = (int)(((int64_t)(j0 + r) * a.ldb + kq) * 2);
+      b_lds[h] = r * kLdKc + kq;
+    } else {
+      const int kr = c >> 4, jc = (c & 15) * 8;
+      b_off[h] = (int)(((int64_t)kr * a.ldb + j0 + jc) * 2);
+      b_lds[h] = kr * kLdKs + jc;
+    }
+  }
+  // scalar step offsets (bytes): K-contiguous operands advance along the
+  // row, K-strided ones by 32 rows
+  const int a_step = kAK ? kGK * 2 : (int)(kGK * a.lda * 2);
+  const int b_step = kBK ? kGK * 2 : (int)(kGK * a.ldb * 2);
+  bwu32x4_t ra[2], rb[2];
+  auto load = [&](int st) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ra[h] = __builtin_amdgcn_raw_buffer_load_b128(ar, a_off[h], st * a_step, 0);
+      rb[h] = __builtin_amdgcn_raw_buffer_load_b128(br, b_off[h], st * b_step, 0);
+    }
+    // K-contiguous operands: K columns past K (a tail step) must be zero
+    if (kAK || kBK) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kq = ((tid + 256 * h) & 3) * 8;
+        const bool in = st * kGK + kq < klen;
+        if (kAK && !in) ra[h] = bwu32x4_t{0u, 0u, 0u, 0u};
+        if (kBK && !in) rb[h] = bwu32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      *reinterpret_cast<bwu32x4_t*>(&sA[buf][a_lds[h]]) = ra[h];
+      *reinterpret_cast<bwu32x4_t*>(&sB[buf][b_lds[h]]) = rb[h];
+    }
+  };
+  bwf32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = bwf32x4_t{0.f, 0.f, 0.f, 0.f};
+  // fragment offsets: K-contiguous stage -> row (lane % 16), K 8 (lane / 16);
+  // K-strided stage -> transpose read, K row 8 (lane / 16) + (lane % 16) / 4,
+  // column 4 (lane % 4)
+  const int kc_off = (lane & 15) * kLdKc + 8 * (lane >> 4);
+  const int ks_off = (8 * (lane >> 4) + ((lane >> 2) & 3)) * kLdKs + 4 * (lane & 3);
+  auto frag = [&](const bf16_t* s, bool kcontig, int rowbase) -> bwbf16x8_t {
+    if (kcontig) return *reinterpret_cast<const bwbf16x8_t*>(s + kc_off + rowbase * kLdKc);
+    const bwv4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bw_lds_v4i16*)(s + ks_off + rowbase));
+    const bwv4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bw_lds_v4i16*)(s + ks_off + 4 * kLdKs + rowbase));
+    return __builtin_bit_cast(bwbf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int st = 0; st < ns; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < ns) load(st + 1);
+    bwbf16x8_t fa[4], fb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = frag(sA[buf], kAK, 64 * wr + 16 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = frag(sB[buf], kBK, 64 * wc + 16 * j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    if (st + 1 < ns) store(buf ^ 1);
+    __syncthreads();
+  }
+  // C fragment: lane holds column (lane % 16), rows 4 (lane / 16) + r
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ti = 64 * wr + 16 * i + 4 * (lane >> 4) + r;
+        const int tj = 64 * wc + 16 * j + (lane & 15);
+        const int c = j0 + tj;
+        if (kMode == 0) {
+          if (ti < rows && c < a.J) epi_store<kEpi>(a, Cg, row0 + ti, c, acc[i][j][r]);
+        } else {
+          if (i0 + ti < a.I && c < a.J) epi_store<kEpi>(a, Cg, i0 + ti, c, acc[i][j][r]);
+        }
+      }
+}
+
+// Plain grouped GEMM, one thread per output element, fp32 accumulation in
+// K order; T = float or bf16.  Same argument meaning as the bf16 kernel.
+template <typename T, bool kAK, bool kBK, int kMode, int kEpi>
+__global__ __launch_bounds__(256) void bw_gemm_plain_kernel(GemmArgs a, int64_t rows_total) {
+  const T* A = reinterpret_cast<const T*>(a.A);
+  const T* Bm = reinterpret_cast<const T*>(a.B);
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int g;
+  int64_t r;
+  int c;
+  int kbeg = 0, klen = a.K;
+  if (kMode == 0) {
+    if (idx >= rows_total * a.J) return;
+    r = idx / a.J;
+    c = (int)(idx % a.J);
+    if (r >= a.offsets[a.groups]) return;
+    int lo = 0, hi = a.groups - 1;   // last group with offsets[g] <= r
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.offsets[mid] <= r) lo = mid;
+      else hi = mid - 1;
+    }
+    g = lo;
+  } else {
+    g = blockIdx.y;
+    if (idx >= (int64_t)a.I * a.J) return;
+    r = idx / a.J;
+    c = (int)(idx % a.J);
+    kbeg = a.offsets[g];
+    klen = a.offsets[g + 1] - kbeg;
+  }
+  const T* Bg = kMode == 0 ? Bm + (int64_t)g * a.b_stride : Bm;
+  float acc = 0.f;
+  for (int kk = 0; kk < klen; ++kk) {
+    const int64_t k = kbeg + kk;
+    const float av = kAK ? load_f(A + r * a.lda + k) : load_f(A + k * a.lda + r);
+    const float bv = kBK ? load_f(Bg + (int64_t)c * a.ldb + (kMode == 0 ? kk : k))
+                         : load_f(Bg + (kMode == 0 ? (int64_t)kk : k) * a.ldb + c);
+    acc = fmaf(av, bv, acc);
+  }
+  void* Cg = kMode == 0 ? a.C : (void*)((char*)a.C + (size_t)g * a.c_stride * (kEpi == EPI_F32 ? 4 : sizeof(T)));
+  if (kEpi == EPI_F32) {
+    static_cast<float*>(Cg)[r * a.ldc + c] = acc;
+  } else if (kEpi == EPI_BF16 || kEpi == EPI_BF16_ADD) {
+    const T* base = reinterpret_cast<const T*>(a.base);
+    const float b = (kEpi == EPI_BF16_ADD && base) ? load_f(base + r * a.ldc + c) : 0.f;
+    store_f(static_cast<T*>(Cg) + r * a.ldc + c, b + acc);
+  } else {
+    const float* pre = a.pre;
+    T* h = reinterpret_cast<T*>(a.h_out);
+    T* C = static_cast<T*>(Cg);
+    if (kEpi == EPI_GELU_BWD) {
+      const float x = load_f(pre + r * a.ld_pre + c);
+      store_f(C + r * a.ldc + c, acc * gelu_exact_grad(x));
+      store_f(h + r * a.ld_h + c, gelu_exact(x));
+    } else {
+      const float gp = load_f(pre + r * a.ld_pre + c), up = load_f(pre + r * a.ld_pre + a.f + c);
+      const float sg = sigm(gp), si = gp * sg;
+      store_f(C + r * a.ldc + c, acc * up * (sg * (1.f + gp * (1.f - sg))));
+      store_f(C + r * a.ldc + a.f + c, acc * si);
+      store_f(h + r * a.ld_h + c, si * up);
+    }
+  }
+}
+
+// Host side: grid and kernel choice.  bf16 on the matrix cores needs the
+// K-contiguous operands' leading dimensions to be multiples of 8 (16-byte
+// rows), K % 8 == 0, and every leading dimension a multiple of 8; anything
+// else, and fp32, runs the plain kernel.
+template <bool kAK, bool kBK, int kMode, int kEpi>
+static hipError_t run_gemm(const GemmArgs& a, int dtype, int64_t rows_bound, hipStream_t stream) {
+  const bool mfma = dtype == 1 && a.lda % 8 == 0 && a.ldb % 8 == 0 && (kMode == 1 || a.K % 8 == 0);
+  if (mfma) {
+    dim3 grid;
+    if (kMode == 0)
+      grid = dim3((unsigned)((rows_bound + kGT - 1) / kGT + a.groups), (unsigned)((a.J + kGT - 1) / kGT), 1);
+    else
+      grid = dim3((unsigned)((a.I + kGT - 1) / kGT), (unsigned)((a.J + kGT - 1) / kGT), (unsigned)a.groups);
+    hipLaunchKernelGGL((bw_gemm_bf16_kernel<kAK, kBK, kMode, kEpi>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (kMode == 0) {
+      const int64_t total = rows_bound * a.J;
+      if (total == 0) return hipSuccess;
+      const dim3 grid((unsigned)((total + 255) / 256));
+      if (dtype == 1)
+        hipLaunchKernelGGL((bw_gemm_plain_kernel<bf16_t, kAK, kBK, kMode, kEpi>), grid, dim3(256), 0, stream, a,
+                           rows_bound);
+      else
+        hipLaunchKernelGGL((bw_gemm_plain_kernel<float, kAK, kBK, kMode, kEpi>), grid, dim3(256), 0, stream, a,
+                           rows_bound);
+    } else {
+      const dim3 grid((unsigned)(((int64_t)a.I * a.J + 255) / 256), (unsigned)a.groups);
+      if (dtype == 1)
+        hipLaunchKernelGGL((bw_gemm_plain_kernel<bf16_t, kAK, kBK, kMode, kEpi>), grid, dim3(256), 0, stream, a,
+                           (int64_t)0);
+      else
+        hipLaunchKernelGGL((bw_gemm_plain_kernel<float, kAK, kBK, kMode, kEpi>), grid, dim3(256), 0, stream, a,
+                           (int64_t)0);
+    }
+  }
+  return hipGetLastError();
+}
+
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace: the pre-activation in fp32 (it feeds act' and act, so it is
+// not rounded to bf16), H and dA in the activation type.
+size_t ffn_backward_workspace_bytes(int64_t M_max, int E, int d, int f, int act, int dtype) {
+  (void)E;
+  (void)d;
+  const size_t eb = dtype == 1 ? 2 : 4;
+  const int64_t fr = act == 1 ? 2 * (int64_t)f : f;
+  const int64_t M = M_max > 0 ? M_max : 0;
+  return al256((size_t)M * fr * 4) + al256((size_t)M * f * eb) + al256((size_t)M * fr * eb);
+}
+
+hipError_t launch_expert_ffn_backward(const void* X_perm, int dtype, const int32_t* expert_offset, int E, int d,
+                                      int f, int act, const void* W1, const void* W2, const void* dY_perm,
+                                      int64_t M_max, void* dX_perm, float* dW1, float* dW2, void* ws,
+                                      hipStream_t stream) {
+  const size_t eb = dtype == 1 ? 2 : 4;
+  const int fr = act == 1 ? 2 * f : f;
+  const int64_t M = M_max > 0 ? M_max : 0;
+  char* w = static_cast<char*>(ws);
+  float* pre = reinterpret_cast<float*>(w);
+  void* h = w + al256((size_t)M * fr * 4);
+  void* da = w + al256((size_t)M * fr * 4) + al256((size_t)M * f * eb);
+  hipError_t err;
+  // 1. pre-activation A = X W1^T  (row-grouped; W1[e] is [fr][d]: K-contiguous)
+  {
+    GemmArgs a{};
+    a.A = static_cast<const bf16_t*>(X_perm);
+    a.lda = d;
+    a.B = static_cast<const bf16_t*>(W1);
+    a.ldb = d;
+    a.b_stride = (int64_t)fr * d;
+    a.C = pre;
+    a.ldc = fr;
+    a.offsets = expert_offset;
+    a.groups = E;
+    a.J = fr;
+    a.K = d;
+    err = run_gemm<true, true, 0, EPI_F32>(a, dtype, M, stream);
+    if (err != hipSuccess) return err;
+  }
+  // 2. dH = dY W2 with the activation backward in the epilogue: dA, H
+  //    (W2[e] is [d][f]: K = d is its row index)
+  {
+    GemmArgs a{};
+    a.A = static_cast<const bf16_t*>(dY_perm);
+    a.lda = d;
+    a.B = static_cast<const bf16_t*>(W2);
+    a.ldb = f;
+    a.b_stride = (int64_t)d * f;
+    a.C = da;
+    a.ldc = fr;
+    a.offsets = expert_offset;
+    a.groups = E;
+    a.J = f;
+    a.K = d;
+    a.pre = pre;
+    a.ld_pre = fr;
+    a.h_out = static_cast<bf16_t*>(h);
+    a.ld_h = f;
+    a.f = f;
+    err = act == 1 ? run_gemm<true, false, 0, EPI_SWIGLU_BWD>(a, dtype, M, stream)
+                   : run_gemm<true, false, 0, EPI_GELU_BWD>(a, dtype, M, stream);
+    if (err != hipSuccess) return err;
+  }
+  // 3. dX = dA W1 (W1[e] is [fr][d]: K = fr is its row index)
+  {
+    GemmArgs a{};
+    a.A = static_cast<const bf16_t*>(da);
+    a.lda = fr;
+    a.B = static_cast<const bf16_t*>(W1);
+    a.ldb = d;
+    a.b_stride = (int64_t)fr * d;
+    a.C = dX_perm;
+    a.ldc = d;
+    a.offsets = expert_offset;
+    a.groups = E;
+    a.J = d;
+    a.K = fr;
+    err = run_gemm<true, false, 0, EPI_BF16>(a, dtype, M, stream);
+    if (err != hipSuccess) return err;
+  }
+  // 4. dW2[e] = dY^T H  (K-grouped over the expert's rows)
+  {
+    GemmArgs a{};
+    a.A = static_cast<const bf16_t*>(dY_perm);
+    a.lda = d;
+    a.B = static_cast<const bf16_t*>(h);
+    a.ldb = f;
+    a.C = dW2;
+    a.ldc = f;
+    a.c_stride = (int64_t)d * f;
+    a.offsets = expert_offset;
+    a.groups = E;
+    a.I = d;
+    a.J = f;
+    err = run_gemm<false, false, 1, EPI_F32>(a, dtype, 0, stream);
+    if (err != hipSuccess) return err;
+  }
+  // 5. dW1[e] = dA^T X
+  {
+    GemmArgs a{};
+    a.A = static_cast<const bf16_t*>(da);
+    a.lda = fr;
+    a.B = static_cast<const bf16_t*>(X_perm);
+    a.ldb = d;
+    a.C = dW1;
+    a.ldc = d;
+    a.c_stride = (int64_t)fr * d;
+    a.offsets = expert_offset;
+    a.groups = E;
+    a.I = fr;
+    a.J = d;
+    err = run_gemm<false, false, 1, EPI_F32>(a, dtype, 0, stream);
+  }
+  return err;
+}
+
+// Router backward: dX = base + dZ W_g^T, dW_g = X^T dZ (K split into
+// kRouterBwSplits slices of rows summed in slice order), d_offset = column
+// sums of dZ.  dZ is first rounded to the activation type (the matrix-core
+// operand); the workspace holds it, the slice partials and two offset
+// tables ({0, n} and the slice bounds).
+constexpr int kRouterBwSplits = 16;
+
+size_t router_backward_workspace_bytes(int n, int d, int E, int dtype) {
+  const size_t eb = dtype == 1 ? 2 : 4;
+  return al256((size_t)n * E * eb) + al256((size_t)kRouterBwSplits * d * E * 4) +
+         al256((size_t)(kRouterBwSplits + 3) * sizeof(int32_t));
+}
+
+__global__ __launch_bounds__(256) void to_dtype_kernel(const float* __restrict__ src, int64_t count, int dtype,
+                                                       void* __restrict__ dst, int32_t* __restrict__ offs,
+                                                       int n, int splits) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < count) {
+    if (dtype == 1) static_cast<bf16_t*>(dst)[i] = f32_to_bf16(src[i]);
+    else static_cast<float*>(dst)[i] = src[i];
+  }
+  // offs[0..1] = {0, n}; offs[2 .. 2 + splits] = slice bounds
+  if (i < 2) offs[i] = i == 0 ? 0 : n;
+  if (i <= splits) offs[2 + i] = (int32_t)(((int64_t)n * i) / splits);
+}
+
+__global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ part, int64_t count, int splits,
+                                                        float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  float v = part[i];
+  for (int s = 1; s < splits; ++s) v = v + part[(int64_t)s * count + i];
+  out[i] = v;
+}
+
+// One workgroup per expert: thread i adds rows i, i + 256, ... in order,
+// then a halving tree over the 256 partial sums.
+__global__ __launch_bounds__(256) void col_sum_kernel(const float* __restrict__ dz, int n, int E,
+                                                      float* __restrict__ out) {
+  __shared__ float red[256];
+  const int e = blockIdx.x;
+  float v = 0.f;
+  for (int t = threadIdx.x; t < n; t += 256) v = v + dz[(size_t)t * E + e];
+  red[threadIdx.x] = v;
+  for (int s = 128; s >= 1; s >>= 1) {
+    __syncthreads();
+    if ((int)threadIdx.x < s) red[threadIdx.x] = red[threadIdx.x] + red[threadIdx.x + s];
+  }
+  if (threadIdx.x == 0) out[e] = red[0];
+}
+
+hipError_t launch_router_backward(const void* X, const void* Wg, int dtype, const float* dZ, int n, int d, int E,
+                                  const void* base, void* dX, float* dWg, float* d_offset, void* ws,
+                                  hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const size_t eb = dtype == 1 ? 2 : 4;
+  char* w = static_cast<char*>(ws);
+  void* dz_t = w;
+  float* part = reinterpret_cast<float*>(w + al256((size_t)n * E * eb));
+  int32_t* offs =
+      reinterpret_cast<int32_t*>(w + al256((size_t)n * E * eb) + al256((size_t)kRouterBwSplits * d * E * 4));
+  const int64_t cnt = (int64_t)n * E;
+  hipLaunchKernelGGL(to_dtype_kernel, dim3((unsigned)((max(cnt, (int64_t)kRouterBwSplits + 1) + 255) / 256)),
+                     dim3(256), 0, stream, dZ, cnt, dtype, dz_t, offs, n, kRouterBwSplits);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (dX) {
+    // one group of n rows; W_g [d][E] is K-contiguous along E
+    GemmArgs a{};
+    a.A = static_cast<const bf16_t*>(dz_t);
+    a.lda = E;
+    a.B = static_cast<const bf16_t*>(Wg);
+    a.ldb = E;
+    a.C = dX;
+    a.ldc = d;
+    a.offsets = offs;
+    a.groups = 1;
+    a.J = d;
+    a.K = E;
+    a.base = static_cast<const bf16_t*>(base);
+    err = run_gemm<true, true, 0, EPI_BF16_ADD>(a, dtype, n, stream);
+    if (err != hipSuccess) return err;
+  }
+  if (dWg) {
+    GemmArgs a{};
+    a.A = static_cast<const bf16_t*>(X);
+    a.lda = d;
+    a.B = static_cast<const bf16_t*>(dz_t);
+    a.ldb = E;
+    a.C = part;
+    a.ldc = E;
+    a.c_stride = (int64_t)d * E;
+    a.offsets = offs + 2;
+    a.groups = kRouterBwSplits;
+    a.I = d;
+    a.J = E;
+    err = run_gemm<false, false, 1, EPI_F32>(a, dtype, 0, stream);
+    if (err != hipSuccess) return err;
+    const int64_t c2 = (int64_t)d * E;
+    hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((c2 + 255) / 256)), dim3(256), 0, stream, part, c2,
+                       kRouterBwSplits, dWg);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (d_offset) {
+    hipLaunchKernelGGL(col_sum_kernel, dim3((unsigned)E), dim3(256), 0, stream, dZ, n, E, d_offset);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
+}  // namespace moe

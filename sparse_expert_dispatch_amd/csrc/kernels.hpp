@@ -92,6 +92,23 @@ hipError_t launch_expert_ffn(const void* X_perm, const int32_t* row_index, int n
                              hipStream_t stream);
 hipError_t launch_pack_weights(const void* W, int E, int R, int K, int gate_up, void* P, hipStream_t stream);
 
+// backward.hip
+hipError_t launch_combine_backward(const void* dout, const void* Y, int dtype, int d, const int32_t* slot_token,
+                                   const float* slot_gate, const int32_t* n_kept, int64_t M_max, void* dY,
+                                   float* d_gate, hipStream_t stream);
+hipError_t launch_gate_backward(const float* logits, const int32_t* sel_idx, const float* d_gate,
+                                const MapPtrs& m, int n, int E, int k, int dir, int score, int norm_topk,
+                                float lb_coef, float z_coef, float* dZ, hipStream_t stream);
+size_t ffn_backward_workspace_bytes(int64_t M_max, int E, int d, int f, int act, int dtype);
+hipError_t launch_expert_ffn_backward(const void* X_perm, int dtype, const int32_t* expert_offset, int E, int d,
+                                      int f, int act, const void* W1, const void* W2, const void* dY_perm,
+                                      int64_t M_max, void* dX_perm, float* dW1, float* dW2, void* ws,
+                                      hipStream_t stream);
+size_t router_backward_workspace_bytes(int n, int d, int E, int dtype);
+hipError_t launch_router_backward(const void* X, const void* Wg, int dtype, const float* dZ, int n, int d, int E,
+                                  const void* base, void* dX, float* dWg, float* d_offset, void* ws,
+                                  hipStream_t stream);
+
 // stats.hip
 size_t stats_workspace_bytes(int n, int E);
 hipError_t launch_balance_stats(const float* logits, const MapPtrs& m, int n, int E, int k, int dir,

@@ -121,7 +121,8 @@ template <> struct Elem<bf16_t> {
 
 // One wave per token.  acc = residual; acc += shared; then acc += g * y for
 // the token's slots in list order (negative entries are dropped
-// assignments); one rounding at the store.  The token index is uniform
+// assignments; slot_gate NULL: every g = 1, the dispatch's backward); one
+// rounding at the store.  The token index is uniform
 // across the wave, so its list bounds, slot ids and gates are scalar loads:
 // they run beside the vector loads of the residual row instead of queueing
 // behind them (vector loads complete in issue order).  Per column pass: the
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(256) void combine_vec_kernel(const T* __restrict__ 
 #pragma unroll
       for (int b = 0; b < kSlotBatch; ++b) sl[b] = qb + b < q1 ? token_slot[qb + b] : -1;
 #pragma unroll
-      for (int b = 0; b < kSlotBatch; ++b) gl[b] = sl[b] >= 0 ? slot_gate[sl[b]] : 0.f;
+      for (int b = 0; b < kSlotBatch; ++b) gl[b] = sl[b] < 0 ? 0.f : slot_gate ? slot_gate[sl[b]] : 1.f;
       // entries past the list (or dropped) load row 0, which always exists,
       // and are skipped when adding
 #pragma unroll
@@ -246,7 +247,7 @@ __global__ __launch_bounds__(256) void combine_scalar_kernel(const T* __restrict
     for (int q = q0; q < q1; ++q) {
       const int s = token_slot[q];
       if (s < 0) continue;
-      a = fmaf(slot_gate[s], Elem<T>::one(Y + (size_t)s * d + c), a);
+      a = fmaf(slot_gate ? slot_gate[s] : 1.f, Elem<T>::one(Y + (size_t)s * d + c), a);
     }
     Elem<T>::put(out + rowoff + c, a);
   }

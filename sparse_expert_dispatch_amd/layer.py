@@ -154,6 +154,53 @@ class MoELayer:
         return self.out
 
 
+    def backward(self, x: torch.Tensor, dout: torch.Tensor, residual: bool = True, stream=None) -> dict:
+        """Gradients of <dout, out> + lb_loss + z_loss for the last forward(x)
+        (routing fixed; the coefficients are the config's lb_coef, z_coef).
+        Returns device tensors: dx [n, d] (dtype), dwg [d, E], d_offset [E],
+        dw1 / dw2 (fp32, the natural weight shapes) and, with a shared expert,
+        shared_dw1 / shared_dw2; plus the intermediates dz, d_gate, dx_perm.
+        On packed weights the forward never materialised X_perm; this runs
+        the standalone dispatch for it first."""
+        cfg, w = self.cfg, self.w
+        n, d, E = cfg.n, cfg.d, cfg.E
+        if not hasattr(self, "bw"):
+            dev = self.device
+            edt = self.out.dtype
+            f32 = dict(dtype=torch.float32, device=dev)
+            bw = dict(dy_perm=N.alloc((self.M_max, d), edt, dev), d_gate=N.alloc((self.M_max,), torch.float32, dev),
+                      dx_perm=N.alloc((self.M_max, d), edt, dev), dw1=torch.empty(w["w1"].shape, **f32),
+                      dw2=torch.empty(w["w2"].shape, **f32), dz=torch.empty((n, E), **f32),
+                      dx_r=torch.empty((n, d), dtype=edt, device=dev), dx=torch.empty((n, d), dtype=edt, device=dev),
+                      dwg=torch.empty((d, E), **f32), d_offset=torch.empty(E, **f32))
+            sizes = [N.moe_ffn_backward_workspace_size(self.M_max, E, d, cfg.f, self.act, self.dtype_code),
+                     N.moe_router_backward_workspace_size(self.rcfg, self.dtype_code)]
+            if self.shared:
+                bw["dx_shared"] = torch.empty((n, d), dtype=edt, device=dev)
+                bw["shared_dw1"] = torch.empty(w["shared_w1"].shape, **f32)
+                bw["shared_dw2"] = torch.empty(w["shared_w2"].shape, **f32)
+                sizes.append(N.moe_ffn_backward_workspace_size(n, 1, d, cfg.shared_f, self.act, self.dtype_code))
+            bw["ws"] = _bytes(max(sizes), dev)
+            self.bw = bw
+        b = self.bw
+        if self.packed:
+            self.dispatch(x, stream)
+        N.moe_combine_backward(dout, self.y_perm, self.map, b["dy_perm"], b["d_gate"], stream)
+        N.moe_expert_ffn_backward(self.x_perm, self.map.expert_offset, w["w1"], w["w2"], self.act, b["dy_perm"],
+                                  b["dx_perm"], b["dw1"], b["dw2"], b["ws"], stream)
+        if self.shared:
+            N.moe_expert_ffn_backward(x, self.shared_offsets, w["shared_w1"], w["shared_w2"], self.act, dout,
+                                      b["dx_shared"], b["shared_dw1"], b["shared_dw2"], b["ws"], stream)
+        N.moe_gate_backward(self.logits, self.sel_idx, b["d_gate"], self.rcfg, self.map, cfg.lb_coef, cfg.z_coef,
+                            b["dz"], stream)
+        N.moe_router_backward(x, w["wg"], b["dz"], self.rcfg, dout if residual else None, b["dx_r"], b["dwg"],
+                              b["d_offset"], b["ws"], stream)
+        N.moe_dispatch_backward(b["dx_perm"], self.map, n, b["dx_r"], b.get("dx_shared"), b["dx"], stream)
+        out = {key: b[key] for key in ("dx", "dwg", "d_offset", "dw1", "dw2", "dz", "d_gate", "dx_perm", "dy_perm")}
+        if self.shared:
+            out["shared_dw1"], out["shared_dw2"] = b["shared_dw1"], b["shared_dw2"]
+        return out
+
     def capture(self, x: torch.Tensor, residual: bool = True, stats: bool = True):
         """Record one forward into a HIP graph (torch.cuda.CUDAGraph) and
         return it; graph.replay() recomputes every buffer of this layer from

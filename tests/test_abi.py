@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 26
     for name in names:
         assert hasattr(L, name), name
     assert sorted(N.EXPORTED) == names
@@ -190,3 +190,48 @@ def test_python_binding_refuses_cpu_tensors(L):
     x = torch.zeros(16, 64)
     with pytest.raises(ValueError):
         M.moe_router(x, torch.zeros(64, 8), None, cfg, torch.zeros(16, 8))
+
+
+def test_backward_validation(L):
+    """The backward entry points reject bad arguments on the host."""
+    cfg = N.make_cfg(256, 128, 8, 2)
+    cm = N.RouteMapC(*([FAKE] * 8))
+    cmb = ctypes.byref(cm)
+    # combine backward: aliasing, dtype, M_max = 0 is a no-op
+    assert L.moe_combine_backward(FAKE, FAKE + 4096, N.MOE_BF16, 256, 128, cmb, 512, FAKE, FAKE, None) == \
+        N.MOE_ERR_INVALID_ARG
+    assert L.moe_combine_backward(FAKE, FAKE + 4096, 5, 256, 128, cmb, 512, FAKE + 8192, FAKE, None) == \
+        N.MOE_ERR_INVALID_ARG
+    assert L.moe_combine_backward(None, None, N.MOE_BF16, 256, 128, cmb, 0, None, None, None) == N.MOE_OK
+    assert L.moe_combine_backward(FAKE + 2, FAKE + 4096, N.MOE_BF16, 256, 128, cmb, 512, FAKE + 8192, FAKE,
+                                  None) == N.MOE_ERR_INVALID_ARG                        # misaligned bf16
+    # expert FFN backward: workspace, activation, null weights
+    need = M.moe_ffn_backward_workspace_size(512, 8, 128, 64, N.MOE_SWIGLU, N.MOE_BF16)
+    assert need >= 512 * (128 + 64 + 128) * 2
+    ffn = L.moe_expert_ffn_backward
+    assert ffn(FAKE, N.MOE_BF16, FAKE, 8, 128, 64, N.MOE_SWIGLU, FAKE, FAKE, FAKE, 512, FAKE, FAKE, FAKE,
+               FAKE, 16, None) == N.MOE_ERR_WORKSPACE
+    assert ffn(FAKE, N.MOE_BF16, FAKE, 8, 128, 64, 3, FAKE, FAKE, FAKE, 512, FAKE, FAKE, FAKE, FAKE, need,
+               None) == N.MOE_ERR_INVALID_ARG
+    assert ffn(FAKE, N.MOE_BF16, FAKE, 8, 128, 64, N.MOE_GELU, None, FAKE, FAKE, 512, FAKE, FAKE, FAKE, FAKE,
+               need, None) == N.MOE_ERR_INVALID_ARG
+    assert ffn(FAKE, N.MOE_BF16, FAKE, 1024, 128, 64, N.MOE_GELU, FAKE, FAKE, FAKE, 512, FAKE, FAKE, FAKE,
+               FAKE, need, None) == N.MOE_ERR_UNSUPPORTED                               # E > 512
+    # gate backward: token choice needs sel_idx; the map must be complete
+    assert L.moe_gate_backward(FAKE, None, FAKE, ctypes.byref(cfg), cmb, 0.01, 0.001, FAKE, None) == \
+        N.MOE_ERR_INVALID_ARG
+    cm_bad = N.RouteMapC(*([FAKE] * 7 + [0]))
+    assert L.moe_gate_backward(FAKE, FAKE, FAKE, ctypes.byref(cfg), ctypes.byref(cm_bad), 0.01, 0.001, FAKE,
+                               None) == N.MOE_ERR_INVALID_ARG
+    assert L.moe_gate_backward(FAKE, FAKE, FAKE, ctypes.byref(cfg), cmb, float("nan"), 0.001, FAKE, None) == \
+        N.MOE_ERR_INVALID_ARG
+    # router backward: workspace and aliasing
+    rneed = M.moe_router_backward_workspace_size(cfg, N.MOE_BF16)
+    assert rneed >= 256 * 8 * 2
+    assert L.moe_router_backward(FAKE, FAKE, N.MOE_BF16, FAKE, ctypes.byref(cfg), None, FAKE + 4096, FAKE, FAKE,
+                                 FAKE, 8, None) == N.MOE_ERR_WORKSPACE
+    assert L.moe_router_backward(FAKE, FAKE, N.MOE_BF16, FAKE, ctypes.byref(cfg), None, FAKE, FAKE, FAKE, FAKE,
+                                 rneed, None) == N.MOE_ERR_INVALID_ARG                  # dX aliases X
+    # dispatch backward: output must not alias an input
+    assert L.moe_dispatch_backward(FAKE, N.MOE_BF16, cmb, 256, 128, FAKE + 4096, None, FAKE + 4096, None) == \
+        N.MOE_ERR_INVALID_ARG

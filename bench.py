@@ -8,11 +8,16 @@ on one HIP stream, inputs and weights resident in HBM.
 Default workload: expert choice, bf16, n = 4096 tokens, d = 2048, 64 experts,
 capacity factor 2 (128 tokens per expert), GELU experts d -> 4096 -> d.
 
-    python bench.py [--steps K] [--warmup W] [--config 2|1..5|decode] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config 2|1..5|decode] [--no-cpu-baseline] [--backward]
 
 --config decode times a decode step instead: 64 tokens, top-8 of 64 SwiGLU
 experts (d = 2048, f = 1024), where the grouped GEMM streams the weights of
 the experts the batch touches.
+
+--backward times the layer's backward on the same workload instead (one
+step = the gradients of <dOut, out> + the auxiliary losses for one forward:
+combine, expert FFN, shared expert, gate, router and dispatch backward), with
+the expert FFN backward as the roofline kernel; it prints its own JSON line.
 
 A timed step is three parts (routing: router .. dispatch; the expert FFN;
 combine + statistics) with a HIP event between them on the layer's stream.
@@ -105,6 +110,9 @@ def main():
                     help="time HIP-graph replays of the three parts instead of direct launches")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the layer's backward (gradients of <dOut, out> + the auxiliary losses) "
+                         "instead of the forward")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -146,6 +154,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.backward:
+        run_backward(args, cfg, inp, w1_host, w2_host, layer, x, stream)
+        return
 
     w = layer.w
     tc = layer.rcfg.dir == N.MOE_TOKEN_CHOICE
@@ -283,6 +295,157 @@ def main():
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(cfg, inp, w1_host, w2_host)
     print(json.dumps(line), flush=True)
+
+
+def ffn_backward_bytes(cfg, M, touched):
+    """Compulsory bytes of moe_expert_ffn_backward, GEMM by GEMM: every
+    operand read once and every result written once per GEMM (the
+    recomputed pre-activation is fp32; dA, H and dX in the activation type;
+    dW1, dW2 fp32 for the experts with rows; experts without rows get their
+    zero gradients written too)."""
+    b = 2 if cfg.dtype == "bf16" else 4
+    d, f, E = cfg.d, cfg.f, cfg.E
+    fr = 2 * f if cfg.act == "swiglu" else f
+    w1, w2 = touched * fr * d * b, touched * d * f * b
+    recompute = M * d * b + w1 + M * fr * 4
+    dh = M * d * b + w2 + M * fr * 4 + M * fr * b + M * f * b
+    dx = M * fr * b + w1 + M * d * b
+    dw2 = M * d * b + M * f * b + E * d * f * 4
+    dw1 = M * fr * b + M * d * b + E * fr * d * 4
+    flops = 2.0 * M * d * fr * 3 + 2.0 * M * d * f * 2
+    return {"bytes": recompute + dh + dx + dw2 + dw1, "flops": flops,
+            "min_bytes": M * d * b * 3 + w1 + w2 + E * (fr * d + d * f) * 4}
+
+
+def run_backward(args, cfg, inp, w1_host, w2_host, layer, x, stream):
+    """One timed step = the whole backward of one layer forward: dispatch
+    (X_perm for the weight gradients) and combine backward, the expert FFN
+    backward (the roofline kernel), then the shared expert, gate, router and
+    dispatch backward.  HIP events on the layer's stream bracket the three
+    parts of every timed step."""
+    import torch
+    from sparse_expert_dispatch_amd import _native as N
+    layer.forward(x)
+    rng = np.random.default_rng(7)
+    dout = torch.from_numpy(rng.normal(size=(cfg.n, cfg.d)).astype(np.float32)).cuda().to(layer.out.dtype)
+    layer.backward(x, dout)                  # allocates the gradient buffers
+    torch.cuda.synchronize()
+    b, w = layer.bw, layer.w
+
+    def pre():
+        if layer.packed:
+            layer.dispatch(x)
+        N.moe_combine_backward(dout, layer.y_perm, layer.map, b["dy_perm"], b["d_gate"])
+
+    def ffn():
+        N.moe_expert_ffn_backward(layer.x_perm, layer.map.expert_offset, w["w1"], w["w2"], layer.act, b["dy_perm"],
+                                  b["dx_perm"], b["dw1"], b["dw2"], b["ws"])
+
+    def post():
+        if layer.shared:
+            N.moe_expert_ffn_backward(x, layer.shared_offsets, w["shared_w1"], w["shared_w2"], layer.act, dout,
+                                      b["dx_shared"], b["shared_dw1"], b["shared_dw2"], b["ws"])
+        N.moe_gate_backward(layer.logits, layer.sel_idx, b["d_gate"], layer.rcfg, layer.map, cfg.lb_coef,
+                            cfg.z_coef, b["dz"])
+        N.moe_router_backward(x, w["wg"], b["dz"], layer.rcfg, dout, b["dx_r"], b["dwg"], b["d_offset"], b["ws"])
+        N.moe_dispatch_backward(b["dx_perm"], layer.map, cfg.n, b["dx_r"], b.get("dx_shared"), b["dx"])
+
+    parts = [pre, ffn, post]
+    print(f"[bench] backward warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        for p in parts:
+            p()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for ev in events:
+        ev[0].record(stream)
+        for j, p in enumerate(parts):
+            p()
+            ev[j + 1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    print(f"[bench] timed {args.steps} backward steps in {elapsed:.4f}s", file=sys.stderr, flush=True)
+    seg_ms = [float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events])) for j in range(3)]
+    M = int(layer.map.n_kept.item())
+    touched = int((layer.map.expert_offset.diff() > 0).sum().item())
+    a = ffn_backward_bytes(cfg, M, touched)
+    ffn_ms = seg_ms[1]
+    achieved = a["bytes"] / (ffn_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "moe_expert_ffn_backward (five grouped GEMMs: pre-activation recompute, dH with the "
+                          "activation derivative, dX, dW2, dW1)",
+                "algorithmic_bytes": int(a["bytes"]), "flops": a["flops"], "avg_us": round(ffn_ms * 1e3, 2),
+                "fused_minimum_bytes": int(a["min_bytes"])}
+    line = {
+        "metric": "MoE-layer bwd tokens/sec at 1 MI355X (gradients of <dOut, out> + aux losses)",
+        "value": round(cfg.n * args.steps / elapsed, 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded normals; random-init weights of the stated shapes; dOut seeded normal)",
+        "config": {"workload": cfg.name + " backward", "n": cfg.n, "d": cfg.d, "E": cfg.E, "f": cfg.f,
+                   "act": cfg.act, "direction": cfg.direction, "k": layer.k, "kept_assignments": M,
+                   "experts_touched": touched, "parallelism": "single GPU",
+                   "weight_gradients": "fp32"},
+        "roofline": roofline,
+        "parts_us": {"dispatch_combine_bwd": round(seg_ms[0] * 1e3, 2), "expert_ffn_bwd": round(ffn_ms * 1e3, 2),
+                     "gate_router_dispatch_bwd": round(seg_ms[2] * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle's backward on a sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline_backward(cfg, inp, w1_host, w2_host, layer, dout)
+    print(json.dumps(line), flush=True)
+
+
+def _host(t):
+    """Device tensor -> numpy (bf16 as its uint16 bit patterns)."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def cpu_baseline_backward(cfg, inp, w1_host, w2_host, layer, dout):
+    """The backward oracle on the host: the FFN backward of the first few
+    experts (float64), extrapolated to all experts by rows, plus the
+    combine, gate, router and dispatch backward of the whole batch."""
+    import threadpoolctl
+    from oracle import moe_backward as B
+    host = _host
+    off = host(layer.map.expert_offset).astype(np.int64)
+    M = int(off[-1])
+    x_perm = host(layer.x_perm)[:M]
+    y_perm = host(layer.y_perm)[:M]
+    rmap = {k: host(getattr(layer.map, k)) for k in ("expert_count", "expert_offset", "slot_token", "slot_gate",
+                                                     "assign_slot", "token_offset", "token_slot")}
+    rmap["slot_token"], rmap["slot_gate"] = rmap["slot_token"][:M], rmap["slot_gate"][:M]
+    z = host(layer.logits)
+    g = host(dout)
+    with threadpoolctl.threadpool_limits(16):
+        t0 = time.perf_counter()
+        dy, dg = B.combine_backward(g, y_perm, rmap)
+        rows_done, e = 0, 0
+        while e < cfg.E and (time.perf_counter() - t0 < 8.0 or rows_done == 0):
+            a0, a1 = off[e], off[e + 1]
+            if a1 > a0:
+                B.expert_backward(x_perm[a0:a1], w1_host[e], w2_host[e], cfg.act, dy[a0:a1])
+                rows_done += a1 - a0
+            e += 1
+        t_ffn = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        dz = B.gate_backward(z, dg, rmap, cfg.direction, layer.k, cfg.score,
+                             host(layer.sel_idx) if cfg.direction == "tc" else None, cfg.norm_topk,
+                             cfg.lb_coef, cfg.z_coef)
+        dx_r, _, _ = B.router_backward(inp["x"], inp["wg"], dz, g)
+        B.dispatch_backward(np.zeros((M, cfg.d)), rmap, cfg.n, dx_r)
+        t_rest = time.perf_counter() - t1
+    est = t_ffn * (M / max(rows_done, 1)) + t_rest
+    return {"value": round(cfg.n / est, 1), "unit": "tokens/s", "cores": 16, "kind": "oracle",
+            "sample": f"float64 backward oracle: FFN backward of {e} of {cfg.E} experts ({rows_done} of {M} rows, "
+                      f"{t_ffn:.1f} s) extrapolated by rows, plus the combine, gate, router and dispatch "
+                      f"backward of all {cfg.n} tokens ({t_rest:.1f} s)"}
 
 
 if __name__ == "__main__":

@@ -378,6 +378,61 @@ MOE_DEV void epi_store(const GemmArgs& a, void* Cg, int64_t r, int c, float v) {
   }
 }
 
+// Four consecutive columns c .. c+3 of row r (the row pitches are multiples
+// of 4 elements, so the accesses are 16-byte (fp32) or 8-byte (bf16)
+// aligned).
+typedef uint32_t bwu32x2_t __attribute__((ext_vector_type(2)));
+template <int kEpi>
+MOE_DEV void epi_store4(const GemmArgs& a, void* Cg, int64_t r, int c, bwf32x4_t v) {
+#pragma clang fp contract(off)
+  if (kEpi == EPI_F32) {
+    *reinterpret_cast<bwf32x4_t*>(static_cast<float*>(Cg) + r * a.ldc + c) = v;
+  } else if (kEpi == EPI_BF16) {
+    *reinterpret_cast<bwu32x2_t*>(static_cast<bf16_t*>(Cg) + r * a.ldc + c) =
+        bwu32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  } else if (kEpi == EPI_BF16_ADD) {
+    if (a.base) {
+      const bwu32x2_t b = *reinterpret_cast<const bwu32x2_t*>(a.base + r * a.ldc + c);
+      v[0] = __uint_as_float(b[0] << 16) + v[0];
+      v[1] = __uint_as_float(b[0] & 0xFFFF0000u) + v[1];
+      v[2] = __uint_as_float(b[1] << 16) + v[2];
+      v[3] = __uint_as_float(b[1] & 0xFFFF0000u) + v[3];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = 0.f + v[e];
+    }
+    *reinterpret_cast<bwu32x2_t*>(static_cast<bf16_t*>(Cg) + r * a.ldc + c) =
+        bwu32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  } else if (kEpi == EPI_GELU_BWD) {
+    const bwf32x4_t x = *reinterpret_cast<const bwf32x4_t*>(a.pre + r * a.ld_pre + c);
+    float da[4], h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      da[e] = v[e] * gelu_exact_grad(x[e]);
+      h[e] = gelu_exact(x[e]);
+    }
+    *reinterpret_cast<bwu32x2_t*>(static_cast<bf16_t*>(Cg) + r * a.ldc + c) =
+        bwu32x2_t{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])};
+    *reinterpret_cast<bwu32x2_t*>(a.h_out + r * a.ld_h + c) = bwu32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+  } else {
+    const bwf32x4_t gp = *reinterpret_cast<const bwf32x4_t*>(a.pre + r * a.ld_pre + c);
+    const bwf32x4_t up = *reinterpret_cast<const bwf32x4_t*>(a.pre + r * a.ld_pre + a.f + c);
+    float dg[4], du[4], h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float sg = sigm(gp[e]);
+      const float si = gp[e] * sg;
+      dg[e] = v[e] * up[e] * (sg * (1.f + gp[e] * (1.f - sg)));
+      du[e] = v[e] * si;
+      h[e] = si * up[e];
+    }
+    bf16_t* C = static_cast<bf16_t*>(Cg) + r * a.ldc;
+    *reinterpret_cast<bwu32x2_t*>(C + c) = bwu32x2_t{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+    *reinterpret_cast<bwu32x2_t*>(C + a.f + c) = bwu32x2_t{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+    *reinterpret_cast<bwu32x2_t*>(a.h_out + r * a.ld_h + c) = bwu32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+  }
+}
+
 // Locate row-grouped tile `bx`: group g and its 128-row tile index, or g = -1
 // past the last tile.  Lane l of wave 0 counts the tiles of a contiguous run
 // of groups; a wave scan gives every run its first tile.
@@ -404,11 +459,27 @@ MOE_DEV void locate_row_tile(const int32_t* __restrict__ offsets, int G, int bx,
   }
 }
 
+// LDS stages, laid out so that no access conflicts on the 64 banks:
+// * K-contiguous [128][32] (64-byte rows, no padding), the 16-byte chunk c
+//   of row r stored at chunk c ^ ((r / 4) % 4): a store pass (4 rows x 64
+//   bytes) and a fragment read (16 rows, one chunk each) both cover every
+//   bank once;
+// * K-strided [32][136] (272-byte rows, 4 banks apart), K row k stored at
+//   row 8 (k / 8) + 2 (k % 4) + (k % 8) / 4: the 4 K rows a 16-lane group
+//   of a transpose read touches (k0 .. k0+3, or k0+4 .. k0+7) start 8 banks
+//   apart, and the two groups of a 32-lane pass 32 banks apart.
 constexpr int kGT = 128;             // tile rows and columns
 constexpr int kGK = 32;              // K per step
-constexpr int kLdKc = kGK + 8;       // LDS stride (bf16) of a K-contiguous stage [128][40]
+constexpr int kLdKc = kGK;           // LDS stride (bf16) of a K-contiguous stage [128][32]
 constexpr int kLdKs = kGT + 8;       // LDS stride of a K-strided stage [32][136]
-constexpr int kStageElems = kGT * kLdKc;   // 5120 >= 32 * 136 = 4352
+constexpr int kStageElems = 32 * kLdKs;   // 4352 >= 128 * 32
+
+MOE_DEV int kc_lds(int r, int chunk) { return r * kLdKc + ((chunk ^ ((r >> 2) & 3)) << 3); }
+MOE_DEV int ks_row(int k) { return (k & ~7) | ((k & 3) << 1) | ((k >> 2) & 1); }
+#ifndef MOE_BW_RING
+#define MOE_BW_RING 4
+#endif
+constexpr int kBwRing = MOE_BW_RING;        // K steps of operands in registers (even)
 
 template <bool kAK, bool kBK, int kMode, int kEpi>
 __global__ __launch_bounds__(256) void bw_gemm_bf16_kernel(GemmArgs a) {
@@ -418,12 +489,15 @@ __global__ __launch_bounds__(256) void bw_gemm_bf16_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;   // 2 x 2 waves of 64 x 64
 
-  int g, i0, j0 = blockIdx.y * kGT;
+  // blockIdx.x is the column tile, so concurrent workgroups touch adjacent
+  // column bands of the same rows (weights and outputs alike) instead of one
+  // band of many rows a full row pitch apart
+  int g, i0, j0 = blockIdx.x * kGT;
   int64_t row0 = 0;       // row-grouped: first absolute row of the tile
   int rows = kGT;         // row-grouped: valid rows of the tile
   int kbeg = 0, klen = a.K;
   if (kMode == 0) {
-    if (wave == 0) locate_row_tile(a.offsets, a.groups, blockIdx.x, &s_g, &s_tile);
+    if (wave == 0) locate_row_tile(a.offsets, a.groups, blockIdx.y, &s_g, &s_tile);
     __syncthreads();
     g = s_g;
     if (g < 0) return;
@@ -432,7 +506,7 @@ __global__ __launch_bounds__(256) void bw_gemm_bf16_kernel(GemmArgs a) {
     i0 = 0;
   } else {
     g = blockIdx.z;
-    i0 = blockIdx.x * kGT;
+    i0 = blockIdx.y * kGT;
     kbeg = a.offsets[g];
     klen = a.offsets[g + 1] - kbeg;
   }
@@ -481,49 +555,56 @@ __global__ __launch_bounds__(256) void bw_gemm_bf16_kernel(GemmArgs a) {
     if (kAK) {
       const int r = c >> 2, kq = (c & 3) * 8;
       a_off[h] = (int)(((int64_t)(i0 + r) * a.lda + kq) * 2);
-      a_lds[h] = r * kLdKc + kq;
+      a_lds[h] = kc_lds(r, c & 3);
     } else {
       const int kr = c >> 4, ic = (c & 15) * 8;
       a_off[h] = (int)(((int64_t)kr * a.lda + i0 + ic) * 2);
-      a_lds[h] = kr * kLdKs + ic;
+      a_lds[h] = ks_row(kr) * kLdKs + ic;
     }
     if (kBK) {
       const int r = c >> 2, kq = (c & 3) * 8;
       b_off[h] = (int)(((int64_t)(j0 + r) * a.ldb + kq) * 2);
-      b_lds[h] = r * kLdKc + kq;
+      b_lds[h] = kc_lds(r, c & 3);
     } else {
       const int kr = c >> 4, jc = (c & 15) * 8;
       b_off[h] = (int)(((int64_t)kr * a.ldb + j0 + jc) * 2);
-      b_lds[h] = kr * kLdKs + jc;
+      b_lds[h] = ks_row(kr) * kLdKs + jc;
     }
   }
   // scalar step offsets (bytes): K-contiguous operands advance along the
   // row, K-strided ones by 32 rows
   const int a_step = kAK ? kGK * 2 : (int)(kGK * a.lda * 2);
   const int b_step = kBK ? kGK * 2 : (int)(kGK * a.ldb * 2);
-  bwu32x4_t ra[2], rb[2];
-  auto load = [&](int st) {
+  // A ring of kBwRing steps in registers: the loads of the next kBwRing - 1
+  // steps are in flight while one is multiplied.  The step count is padded
+  // to a multiple of the ring; padded steps read zeros (K-contiguous tails
+  // are zeroed below, K-strided rows past K lie outside the resource), so
+  // every round runs whole and the loop has no branch.
+  constexpr int R = kBwRing;
+  const int ns_pad = (ns + R - 1) / R * R;
+  bwu32x4_t ra[R][2], rb[R][2];
+  auto load = [&](int st, int q) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      ra[h] = __builtin_amdgcn_raw_buffer_load_b128(ar, a_off[h], st * a_step, 0);
-      rb[h] = __builtin_amdgcn_raw_buffer_load_b128(br, b_off[h], st * b_step, 0);
+      ra[q][h] = __builtin_amdgcn_raw_buffer_load_b128(ar, a_off[h], st * a_step, 0);
+      rb[q][h] = __builtin_amdgcn_raw_buffer_load_b128(br, b_off[h], st * b_step, 0);
     }
-    // K-contiguous operands: K columns past K (a tail step) must be zero
+    // K-contiguous operands: K columns past K must be zero
     if (kAK || kBK) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int kq = ((tid + 256 * h) & 3) * 8;
         const bool in = st * kGK + kq < klen;
-        if (kAK && !in) ra[h] = bwu32x4_t{0u, 0u, 0u, 0u};
-        if (kBK && !in) rb[h] = bwu32x4_t{0u, 0u, 0u, 0u};
+        if (kAK && !in) ra[q][h] = bwu32x4_t{0u, 0u, 0u, 0u};
+        if (kBK && !in) rb[q][h] = bwu32x4_t{0u, 0u, 0u, 0u};
       }
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int q, int buf) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      *reinterpret_cast<bwu32x4_t*>(&sA[buf][a_lds[h]]) = ra[h];
-      *reinterpret_cast<bwu32x4_t*>(&sB[buf][b_lds[h]]) = rb[h];
+      *reinterpret_cast<bwu32x4_t*>(&sA[buf][a_lds[h]]) = ra[q][h];
+      *reinterpret_cast<bwu32x4_t*>(&sB[buf][b_lds[h]]) = rb[q][h];
     }
   };
   bwf32x4_t acc[4][4];
@@ -531,52 +612,66 @@ __global__ __launch_bounds__(256) void bw_gemm_bf16_kernel(GemmArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = bwf32x4_t{0.f, 0.f, 0.f, 0.f};
-  // fragment offsets: K-contiguous stage -> row (lane % 16), K 8 (lane / 16);
-  // K-strided stage -> transpose read, K row 8 (lane / 16) + (lane % 16) / 4,
-  // column 4 (lane % 4)
-  const int kc_off = (lane & 15) * kLdKc + 8 * (lane >> 4);
-  const int ks_off = (8 * (lane >> 4) + ((lane >> 2) & 3)) * kLdKs + 4 * (lane & 3);
+  // fragment offsets: K-contiguous stage -> row (lane % 16), K chunk
+  // lane / 16 (row bases are multiples of 16, so the swizzle depends on the
+  // lane only); K-strided stage -> transpose reads of K rows 8 (lane / 16) +
+  // (lane % 16) / 4 (then + 4), column 4 (lane % 4), at their permuted rows
+  const int kc_off = kc_lds(lane & 15, lane >> 4);
+  const int ks_off = (8 * (lane >> 4) + 2 * ((lane >> 2) & 3)) * kLdKs + 4 * (lane & 3);
   auto frag = [&](const bf16_t* s, bool kcontig, int rowbase) -> bwbf16x8_t {
     if (kcontig) return *reinterpret_cast<const bwbf16x8_t*>(s + kc_off + rowbase * kLdKc);
     const bwv4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bw_lds_v4i16*)(s + ks_off + rowbase));
-    const bwv4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bw_lds_v4i16*)(s + ks_off + 4 * kLdKs + rowbase));
+    const bwv4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bw_lds_v4i16*)(s + ks_off + kLdKs + rowbase));
     return __builtin_bit_cast(bwbf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int st = 0; st < ns; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < ns) load(st + 1);
-    bwbf16x8_t fa[4], fb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = frag(sA[buf], kAK, 64 * wr + 16 * i);
+  for (int q = 0; q < R; ++q) load(q, q);
+  for (int st0 = 0; st0 < ns_pad; st0 += R) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[j] = frag(sB[buf], kBK, 64 * wc + 16 * j);
+    for (int q = 0; q < R; ++q) {
+      // LDS buffer q % 2 was last read by step q - 2, which every wave
+      // finished before the previous step's barrier
+      const int buf = q & 1;
+      store(q, buf);
+      __syncthreads();
+      bwbf16x8_t fa[4], fb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) fa[i] = frag(sA[buf], kAK, 64 * wr + 16 * i);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    if (st + 1 < ns) store(buf ^ 1);
-    __syncthreads();
+      for (int j = 0; j < 4; ++j) fb[j] = frag(sB[buf], kBK, 64 * wc + 16 * j);
+      // B fragments as the first operand: the result is the C^T tile, so
+      // each lane ends with 4 consecutive columns of one row of C
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+      load(st0 + q + R, q);
+    }
   }
-  // C fragment: lane holds column (lane % 16), rows 4 (lane / 16) + r
+  // C^T fragment: lane holds row (lane % 16) of its 16 x 16 subtile and
+  // columns 4 (lane / 16) .. +3; whole groups of 4 in-range columns go out
+  // as one vector access (when the row pitches allow it), the rest element
+  // by element
+  const bool vec = a.ldc % 4 == 0 && (kEpi < EPI_GELU_BWD || (a.ld_pre % 4 == 0 && a.ld_h % 4 == 0));
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      const int ti = 64 * wr + 16 * i + (lane & 15);
+      const int c = j0 + 64 * wc + 16 * j + 4 * (lane >> 4);
+      const bool row_ok = kMode == 0 ? ti < rows : i0 + ti < a.I;
+      const int64_t r = kMode == 0 ? row0 + ti : (int64_t)(i0 + ti);
+      if (!row_ok) continue;
+      if (vec && c + 3 < a.J) {
+        epi_store4<kEpi>(a, Cg, r, c, acc[i][j]);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ti = 64 * wr + 16 * i + 4 * (lane >> 4) + r;
-        const int tj = 64 * wc + 16 * j + (lane & 15);
-        const int c = j0 + tj;
-        if (kMode == 0) {
-          if (ti < rows && c < a.J) epi_store<kEpi>(a, Cg, row0 + ti, c, acc[i][j][r]);
-        } else {
-          if (i0 + ti < a.I && c < a.J) epi_store<kEpi>(a, Cg, i0 + ti, c, acc[i][j][r]);
-        }
+        for (int e = 0; e < 4; ++e)
+          if (c + e < a.J) epi_store<kEpi>(a, Cg, r, c + e, acc[i][j][e]);
       }
+    }
 }
 
 // Plain grouped GEMM, one thread per output element, fp32 accumulation in
@@ -654,9 +749,9 @@ static hipError_t run_gemm(const GemmArgs& a, int dtype, int64_t rows_bound, hip
   if (mfma) {
     dim3 grid;
     if (kMode == 0)
-      grid = dim3((unsigned)((rows_bound + kGT - 1) / kGT + a.groups), (unsigned)((a.J + kGT - 1) / kGT), 1);
+      grid = dim3((unsigned)((a.J + kGT - 1) / kGT), (unsigned)((rows_bound + kGT - 1) / kGT + a.groups), 1);
     else
-      grid = dim3((unsigned)((a.I + kGT - 1) / kGT), (unsigned)((a.J + kGT - 1) / kGT), (unsigned)a.groups);
+      grid = dim3((unsigned)((a.J + kGT - 1) / kGT), (unsigned)((a.I + kGT - 1) / kGT), (unsigned)a.groups);
     hipLaunchKernelGGL((bw_gemm_bf16_kernel<kAK, kBK, kMode, kEpi>), grid, dim3(256), 0, stream, a);
   } else {
     if (kMode == 0) {

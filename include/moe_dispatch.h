@@ -358,7 +358,8 @@ moe_status_t moe_ffn_backward_workspace_size(int64_t M_max, int32_t E, int32_t d
  * natural layout, not packed) in dtype; dW1 [E,f_rows,d] and dW2 [E,d,f]
  * fp32 (16-byte aligned), zero for experts without rows.  bf16 runs on the
  * matrix cores (16-byte aligned tensors); fp32 on a plain kernel.  Errors: invalid
- * shapes, M_max x f_rows or a weight matrix of 2^31 elements or more,
+ * shapes, M_max x d, M_max x f_rows or a weight matrix of 2^29 elements or
+ * more (byte offsets into the fp32 gradients stay below 2^31),
  * MOE_ERR_WORKSPACE when ws is short. */
 moe_status_t moe_expert_ffn_backward(const void *X_perm, int32_t dtype, const int32_t *expert_offset, int32_t E,
                                      int32_t d, int32_t f, int32_t act, const void *W1, const void *W2,

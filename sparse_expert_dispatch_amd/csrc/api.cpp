@@ -398,8 +398,10 @@ moe_status_t moe_expert_ffn_backward(const void* X_perm, int32_t dtype, const in
   REQUIRE(M_max <= INT32_MAX, "M_max must fit in int32");
   SUPPORTED(E <= moe::kMaxExperts, "expert FFN backward supports E <= %d (E=%d)", moe::kMaxExperts, E);
   const int64_t fr = act == MOE_SWIGLU ? 2 * (int64_t)f : f;
-  REQUIRE(M_max * fr <= INT32_MAX && M_max * (int64_t)d <= INT32_MAX && fr * d <= INT32_MAX,
-          "M_max x width and the weight matrices must have fewer than 2^31 elements");
+  // the bf16 kernels address every operand and the fp32 weight gradients
+  // through 32-bit byte offsets
+  REQUIRE(M_max * fr <= INT32_MAX / 4 && M_max * (int64_t)d <= INT32_MAX / 4 && fr * d <= INT32_MAX / 4,
+          "M_max x width and the weight matrices must have fewer than 2^29 elements");
   REQUIRE(aligned16(dW1) && aligned16(dW2), "dW1 and dW2 must be 16-byte aligned");
   if (dtype == MOE_BF16)
     REQUIRE(aligned16(W1) && aligned16(W2) && (M_max == 0 || (aligned16(X_perm) && aligned16(dY_perm) &&

@@ -351,6 +351,26 @@ struct GemmArgs {
 
 enum { EPI_BF16 = 0, EPI_BF16_ADD = 1, EPI_F32 = 2, EPI_GELU_BWD = 3, EPI_SWIGLU_BWD = 4 };
 
+// Which GEMM outputs are written with non-temporal stores (bit 0: the fp32
+// pre-activation, bit 1: the fp32 weight gradients, bit 2: bf16 outputs),
+// and whether a weight-gradient tile goes out through LDS in whole rows.
+#ifndef MOE_BW_NT
+#define MOE_BW_NT 3
+#endif
+#ifndef MOE_BW_STAGE_DW
+#define MOE_BW_STAGE_DW 1
+#endif
+// Weight gradients with whole-tile J on the persistent kernel
+#ifndef MOE_BW_PERSIST
+#define MOE_BW_PERSIST 1
+#endif
+
+template <bool kNT, typename V>
+MOE_DEV void vstore(V* p, V v) {
+  if (kNT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
 // Epilogue of one output element (row `r`, column `c`, value v); row-grouped
 // rows are absolute, K-grouped outputs start at the group's C.
 template <int kEpi>
@@ -382,14 +402,14 @@ MOE_DEV void epi_store(const GemmArgs& a, void* Cg, int64_t r, int c, float v) {
 // of 4 elements, so the accesses are 16-byte (fp32) or 8-byte (bf16)
 // aligned).
 typedef uint32_t bwu32x2_t __attribute__((ext_vector_type(2)));
-template <int kEpi>
+template <int kEpi, bool kNT>
 MOE_DEV void epi_store4(const GemmArgs& a, void* Cg, int64_t r, int c, bwf32x4_t v) {
 #pragma clang fp contract(off)
   if (kEpi == EPI_F32) {
-    *reinterpret_cast<bwf32x4_t*>(static_cast<float*>(Cg) + r * a.ldc + c) = v;
+    vstore<kNT>(reinterpret_cast<bwf32x4_t*>(static_cast<float*>(Cg) + r * a.ldc + c), v);
   } else if (kEpi == EPI_BF16) {
-    *reinterpret_cast<bwu32x2_t*>(static_cast<bf16_t*>(Cg) + r * a.ldc + c) =
-        bwu32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    vstore<kNT>(reinterpret_cast<bwu32x2_t*>(static_cast<bf16_t*>(Cg) + r * a.ldc + c),
+                bwu32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
   } else if (kEpi == EPI_BF16_ADD) {
     if (a.base) {
       const bwu32x2_t b = *reinterpret_cast<const bwu32x2_t*>(a.base + r * a.ldc + c);
@@ -401,8 +421,8 @@ MOE_DEV void epi_store4(const GemmArgs& a, void* Cg, int64_t r, int c, bwf32x4_t
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = 0.f + v[e];
     }
-    *reinterpret_cast<bwu32x2_t*>(static_cast<bf16_t*>(Cg) + r * a.ldc + c) =
-        bwu32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    vstore<kNT>(reinterpret_cast<bwu32x2_t*>(static_cast<bf16_t*>(Cg) + r * a.ldc + c),
+                bwu32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
   } else if (kEpi == EPI_GELU_BWD) {
     const bwf32x4_t x = *reinterpret_cast<const bwf32x4_t*>(a.pre + r * a.ld_pre + c);
     float da[4], h[4];
@@ -411,9 +431,10 @@ MOE_DEV void epi_store4(const GemmArgs& a, void* Cg, int64_t r, int c, bwf32x4_t
       da[e] = v[e] * gelu_exact_grad(x[e]);
       h[e] = gelu_exact(x[e]);
     }
-    *reinterpret_cast<bwu32x2_t*>(static_cast<bf16_t*>(Cg) + r * a.ldc + c) =
-        bwu32x2_t{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])};
-    *reinterpret_cast<bwu32x2_t*>(a.h_out + r * a.ld_h + c) = bwu32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+    vstore<kNT>(reinterpret_cast<bwu32x2_t*>(static_cast<bf16_t*>(Cg) + r * a.ldc + c),
+                bwu32x2_t{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])});
+    vstore<kNT>(reinterpret_cast<bwu32x2_t*>(a.h_out + r * a.ld_h + c),
+                bwu32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])});
   } else {
     const bwf32x4_t gp = *reinterpret_cast<const bwf32x4_t*>(a.pre + r * a.ld_pre + c);
     const bwf32x4_t up = *reinterpret_cast<const bwf32x4_t*>(a.pre + r * a.ld_pre + a.f + c);
@@ -427,9 +448,11 @@ MOE_DEV void epi_store4(const GemmArgs& a, void* Cg, int64_t r, int c, bwf32x4_t
       h[e] = si * up[e];
     }
     bf16_t* C = static_cast<bf16_t*>(Cg) + r * a.ldc;
-    *reinterpret_cast<bwu32x2_t*>(C + c) = bwu32x2_t{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
-    *reinterpret_cast<bwu32x2_t*>(C + a.f + c) = bwu32x2_t{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
-    *reinterpret_cast<bwu32x2_t*>(a.h_out + r * a.ld_h + c) = bwu32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+    vstore<kNT>(reinterpret_cast<bwu32x2_t*>(C + c), bwu32x2_t{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])});
+    vstore<kNT>(reinterpret_cast<bwu32x2_t*>(C + a.f + c),
+                bwu32x2_t{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])});
+    vstore<kNT>(reinterpret_cast<bwu32x2_t*>(a.h_out + r * a.ld_h + c),
+                bwu32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])});
   }
 }
 
@@ -483,9 +506,13 @@ constexpr int kBwRing = MOE_BW_RING;        // K steps of operands in registers 
 
 template <bool kAK, bool kBK, int kMode, int kEpi>
 __global__ __launch_bounds__(256) void bw_gemm_bf16_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][kStageElems];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][kStageElems];
+  // operand stages; a weight-gradient epilogue reuses them for half a tile
+  // of fp32 output
+  __shared__ __attribute__((aligned(16))) bf16_t sAB[4][kStageElems];
+  bf16_t(*sA)[kStageElems] = sAB;
+  bf16_t(*sB)[kStageElems] = sAB + 2;
   __shared__ int s_g, s_tile;
+  constexpr bool kNT = kEpi == EPI_F32 ? ((MOE_BW_NT >> (kMode == 1 ? 1 : 0)) & 1) != 0 : (MOE_BW_NT & 4) != 0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;   // 2 x 2 waves of 64 x 64
 
@@ -625,35 +652,81 @@ __global__ __launch_bounds__(256) void bw_gemm_bf16_kernel(GemmArgs a) {
     return __builtin_bit_cast(bwbf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
+  // one K step from ring entry q; `next` >= 0 refills the entry with that
+  // step's loads (the last round refills nothing)
+  auto step = [&](int q, int next) {
+    // LDS buffer q % 2 was last read by step q - 2, which every wave
+    // finished before the previous step's barrier
+    const int buf = q & 1;
+    store(q, buf);
+    __syncthreads();
+    bwbf16x8_t fa[4], fb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = frag(sA[buf], kAK, 64 * wr + 16 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = frag(sB[buf], kBK, 64 * wc + 16 * j);
+    // B fragments as the first operand: the result is the C^T tile, so
+    // each lane ends with 4 consecutive columns of one row of C
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    if (next >= 0) load(next, q);
+  };
 #pragma unroll
   for (int q = 0; q < R; ++q) load(q, q);
-  for (int st0 = 0; st0 < ns_pad; st0 += R) {
+  for (int st0 = 0; st0 < ns_pad - R; st0 += R) {
 #pragma unroll
-    for (int q = 0; q < R; ++q) {
-      // LDS buffer q % 2 was last read by step q - 2, which every wave
-      // finished before the previous step's barrier
-      const int buf = q & 1;
-      store(q, buf);
-      __syncthreads();
-      bwbf16x8_t fa[4], fb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = frag(sA[buf], kAK, 64 * wr + 16 * i);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j] = frag(sB[buf], kBK, 64 * wc + 16 * j);
-      // B fragments as the first operand: the result is the C^T tile, so
-      // each lane ends with 4 consecutive columns of one row of C
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-      load(st0 + q + R, q);
-    }
+    for (int q = 0; q < R; ++q) step(q, st0 + q + R);
   }
+#pragma unroll
+  for (int q = 0; q < R; ++q) step(q, -1);
   // C^T fragment: lane holds row (lane % 16) of its 16 x 16 subtile and
   // columns 4 (lane / 16) .. +3; whole groups of 4 in-range columns go out
   // as one vector access (when the row pitches allow it), the rest element
   // by element
+  if constexpr (kMode == 1 && kEpi == EPI_F32 && MOE_BW_STAGE_DW) {
+    // Weight gradient: the tile goes out in two halves of 64 rows through
+    // LDS (row stride 132 floats: the fragment writes of 16 rows land 4
+    // banks apart), read back so that 32 consecutive lanes store one
+    // 512-byte row, whole cache lines per store instead of 64-byte pieces
+    // of 16 rows.
+    float* sC = reinterpret_cast<float*>(&sAB[0][0]);
+    constexpr int kCs = kGT + 4;
+    static_assert(64 * kCs * 4 <= 4 * kStageElems * 2, "half tile fits the stages");
+    const bool vec_out = a.ldc % 4 == 0;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      __syncthreads();   // p = 0: the last step's fragment reads; p = 1: half 0's read-out
+      if (wr == p) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<bwf32x4_t*>(sC + (16 * i + (lane & 15)) * kCs + 64 * wc + 16 * j + 4 * (lane >> 4)) =
+                acc[i][j];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int e = tid + 256 * q;   // 64 rows x 32 chunks of 4
+        const int r = e >> 5, c = (e & 31) * 4;
+        const int gr = i0 + 64 * p + r, gc = j0 + c;
+        if (gr >= a.I) continue;
+        const bwf32x4_t v = *reinterpret_cast<const bwf32x4_t*>(sC + r * kCs + c);
+        float* dst = static_cast<float*>(Cg) + (int64_t)gr * a.ldc + gc;
+        if (vec_out && gc + 3 < a.J) {
+          vstore<kNT>(reinterpret_cast<bwf32x4_t*>(dst), v);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (gc + u < a.J) dst[u] = v[u];
+        }
+      }
+    }
+    return;
+  }
   const bool vec = a.ldc % 4 == 0 && (kEpi < EPI_GELU_BWD || (a.ld_pre % 4 == 0 && a.ld_h % 4 == 0));
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -665,13 +738,184 @@ __global__ __launch_bounds__(256) void bw_gemm_bf16_kernel(GemmArgs a) {
       const int64_t r = kMode == 0 ? row0 + ti : (int64_t)(i0 + ti);
       if (!row_ok) continue;
       if (vec && c + 3 < a.J) {
-        epi_store4<kEpi>(a, Cg, r, c, acc[i][j]);
+        epi_store4<kEpi, kNT>(a, Cg, r, c, acc[i][j]);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (c + e < a.J) epi_store<kEpi>(a, Cg, r, c + e, acc[i][j][e]);
       }
     }
+}
+
+// Persistent weight-gradient GEMM (K grouped by expert, both operands
+// K-strided, fp32 out): C_g[i, j] = sum over the rows k of group g of
+// A[k, i] B[k, j].  Each workgroup walks tiles t = blockIdx.x, + gridDim.x,
+// ... (column tile fastest, then row tile, then group).  The K loop of one
+// expert is short (its rows / 32 steps), so a tile is mostly load latency
+// and 64 KB of stores; here the last round of each tile refills the
+// register ring with the next tile's first steps, whose loads are in flight
+// while this tile's output is staged through LDS and stored.  The stores are
+// buffer stores bounded by the group's I x J output (whole tiles in J; rows
+// past I are dropped by the bound), so every thread issues the same count
+// and no wait for a refill load has to wait for them too.  Needs J a
+// multiple of 128 and ldc == J.
+#ifndef MOE_WG_RING
+#define MOE_WG_RING 4
+#endif
+#ifndef MOE_WG_WAVES
+#define MOE_WG_WAVES 3
+#endif
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_WG_WAVES))) void bw_wgrad_bf16_kernel(
+    GemmArgs a, int tiles_i, int tiles_j, int total) {
+  __shared__ __attribute__((aligned(16))) bf16_t sAB[4][kStageElems];
+  bf16_t(*sA)[kStageElems] = sAB;
+  bf16_t(*sB)[kStageElems] = sAB + 2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  constexpr int R = MOE_WG_RING;
+  constexpr int kCs = 68;   // fp32 LDS row stride of the staged output
+  static_assert(128 * kCs * 4 <= 4 * kStageElems * 2, "staged output fits the stages");
+  int t = blockIdx.x;
+  if (t >= total) return;
+
+  // per thread and step: two 16-byte chunks of each operand, chunk c ->
+  // K row c / 16, column offset 8 (c % 16); the tile's first column goes
+  // into the scalar offset
+  int a_off[2], b_off[2], s_lds[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = tid + 256 * h;
+    const int kr = c >> 4, cc = (c & 15) * 8;
+    a_off[h] = (int)(((int64_t)kr * a.lda + cc) * 2);
+    b_off[h] = (int)(((int64_t)kr * a.ldb + cc) * 2);
+    s_lds[h] = ks_row(kr) * kLdKs + cc;
+  }
+  const int a_step = (int)(kGK * a.lda * 2), b_step = (int)(kGK * a.ldb * 2);
+
+  struct Tile {
+    __amdgpu_buffer_rsrc_t ar, br;
+    int g, i0, j0, klen;
+  };
+  // tile coordinates and operand resources (rows past the group's K read
+  // as zero; `live` false gives empty resources, whose loads return zeros)
+  auto tile_at = [&](int tt, bool live) -> Tile {
+    Tile x;
+    x.j0 = (tt % tiles_j) * kGT;
+    x.i0 = ((tt / tiles_j) % tiles_i) * kGT;
+    x.g = tt / (tiles_j * tiles_i);
+    const int kb = live ? a.offsets[x.g] : 0;
+    x.klen = live ? a.offsets[x.g + 1] - kb : 0;
+    x.ar = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a.A + (int64_t)kb * a.lda), (short)0,
+                                             (int)((int64_t)x.klen * a.lda * 2), 0x00020000);
+    x.br = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a.B + (int64_t)kb * a.ldb), (short)0,
+                                             (int)((int64_t)x.klen * a.ldb * 2), 0x00020000);
+    return x;
+  };
+  bwu32x4_t ra[R][2], rb[R][2];
+  auto load = [&](const Tile& x, int st, int q) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ra[q][h] = __builtin_amdgcn_raw_buffer_load_b128(x.ar, a_off[h], st * a_step + x.i0 * 2, 0);
+      rb[q][h] = __builtin_amdgcn_raw_buffer_load_b128(x.br, b_off[h], st * b_step + x.j0 * 2, 0);
+    }
+  };
+  const int ks_off = (8 * (lane >> 4) + 2 * ((lane >> 2) & 3)) * kLdKs + 4 * (lane & 3);
+  auto frag = [&](const bf16_t* s, int rowbase) -> bwbf16x8_t {
+    const bwv4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bw_lds_v4i16*)(s + ks_off + rowbase));
+    const bwv4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bw_lds_v4i16*)(s + ks_off + kLdKs + rowbase));
+    return __builtin_bit_cast(bwbf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  bwf32x4_t acc[4][4];
+  // one K step from ring entry q, then refill the entry with step `st` of
+  // tile `x`
+  auto step = [&](int q, const Tile& x, int st) {
+    const int buf = q & 1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      *reinterpret_cast<bwu32x4_t*>(&sA[buf][s_lds[h]]) = ra[q][h];
+      *reinterpret_cast<bwu32x4_t*>(&sB[buf][s_lds[h]]) = rb[q][h];
+    }
+    __syncthreads();
+    bwbf16x8_t fb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = frag(sB[buf], 64 * wc + 16 * j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bwbf16x8_t fa = frag(sA[buf], 64 * wr + 16 * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa, acc[i][j], 0, 0, 0);
+    }
+    load(x, st, q);
+  };
+
+  // epilogue constants: this thread's fragment writes start at LDS float
+  // acc_lds; its read-outs are rows out_r0 + 16 q of the pass, local column
+  // lc, which is tile column 64 (lc / 32) + 32 p + lc % 32
+  const int acc_lds = (64 * wr + (lane & 15)) * kCs + 32 * wc + 4 * (lane >> 4);
+  const int out_r0 = tid >> 4, out_lc = (tid & 15) * 4;
+  const int out_lds = out_r0 * kCs + out_lc;
+  const int row_bytes = (int)(a.ldc * 4);
+  const int out_voff = out_r0 * row_bytes + (64 * (out_lc >> 5) + (out_lc & 31)) * 4;
+
+  Tile cur = tile_at(t, true);
+#pragma unroll
+  for (int q = 0; q < R; ++q) load(cur, q, q);
+  while (true) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = bwf32x4_t{0.f, 0.f, 0.f, 0.f};
+    // the previous tile's epilogue has read its LDS out
+    __syncthreads();
+    // steps padded to whole rounds of R (at least one: an expert without
+    // rows runs one round of zeros and stores a zero gradient)
+    const int ns_pad = max(R, (cur.klen + kGK * R - 1) / (kGK * R) * R);
+    for (int st0 = 0; st0 < ns_pad - R; st0 += R) {
+#pragma unroll
+      for (int q = 0; q < R; ++q) step(q, cur, st0 + q + R);
+    }
+    const int tn = t + gridDim.x;
+    const bool more = tn < total;
+    const Tile nxt = tile_at(more ? tn : t, more);
+#pragma unroll
+    for (int q = 0; q < R; ++q) step(q, nxt, q);
+
+    // C^T fragments -> LDS -> 128-byte row pieces.  Two passes, each takes
+    // the column pieces j = 2p, 2p + 1 of every wave (128 rows x 64 columns,
+    // row stride 68 floats: the 16 rows of a fragment write land 4 banks
+    // apart), so half of every wave's accumulators is free after the first
+    // pass.  Local column lc of pass p is column 64 (lc / 32) + 32 p +
+    // lc % 32 of the tile; 8 lanes store one 128-byte line.
+    float* sC = reinterpret_cast<float*>(&sAB[0][0]);
+    float* Cg = static_cast<float*>(a.C) + (size_t)cur.g * a.c_stride;
+    const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+        Cg, (short)0, (int)((int64_t)a.I * a.ldc * 4), 0x00020000);
+    // rows left in this tile for the thread's first read-out row; a row past
+    // I gets an offset beyond the resource, so its store is dropped
+    const int rows_left = a.I - cur.i0 - out_r0;
+    const int tile_soff = (int)(((int64_t)cur.i0 * a.ldc + cur.j0) * 4);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+          *reinterpret_cast<bwf32x4_t*>(sC + acc_lds + 16 * i * kCs + 16 * jj) = acc[i][2 * p + jj];
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {   // rows out_r0 + 16 q
+        const bwf32x4_t v = *reinterpret_cast<const bwf32x4_t*>(sC + out_lds + 16 * q * kCs);
+        const int off = 16 * q < rows_left ? out_voff : (int)0x80000000;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(bwu32x4_t, v), cr, off,
+                                               tile_soff + 16 * q * row_bytes + 128 * p, 2 /* nt */);
+      }
+    }
+    if (!more) break;
+    t = tn;
+    cur = nxt;
+  }
 }
 
 // Plain grouped GEMM, one thread per output element, fp32 accumulation in
@@ -747,6 +991,30 @@ template <bool kAK, bool kBK, int kMode, int kEpi>
 static hipError_t run_gemm(const GemmArgs& a, int dtype, int64_t rows_bound, hipStream_t stream) {
   const bool mfma = dtype == 1 && a.lda % 8 == 0 && a.ldb % 8 == 0 && (kMode == 1 || a.K % 8 == 0);
   if (mfma) {
+    if constexpr (kMode == 1 && kEpi == EPI_F32 && !kAK && !kBK && MOE_BW_PERSIST) {
+      // (rows up to a tile past I keep every store offset below 2^31)
+      if (a.J % kGT == 0 && a.ldc == a.J && ((int64_t)a.I + kGT) * a.ldc * 4 <= INT32_MAX) {
+        // resident workgroups per device (CUs x workgroups per CU), asked once
+        static int slots_of[64] = {};
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+        int& slots = slots_of[dev];
+        if (slots == 0) {
+          int cus = 0, per_cu = 0;
+          const hipError_t e1 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+          if (e1 != hipSuccess) return e1;
+          const hipError_t e2 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bw_wgrad_bf16_kernel, 256, 0);
+          if (e2 != hipSuccess) return e2;
+          slots = max(1, cus * max(1, per_cu));
+        }
+        const int ti = (a.I + kGT - 1) / kGT, tj = a.J / kGT;
+        const int64_t total = (int64_t)ti * tj * a.groups;
+        if (total == 0) return hipSuccess;
+        const int grid = (int)(total < slots ? total : (int64_t)slots);
+        hipLaunchKernelGGL(bw_wgrad_bf16_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a, ti, tj, (int)total);
+        return hipGetLastError();
+      }
+    }
     dim3 grid;
     if (kMode == 0)
       grid = dim3((unsigned)((a.J + kGT - 1) / kGT), (unsigned)((rows_bound + kGT - 1) / kGT + a.groups), 1);

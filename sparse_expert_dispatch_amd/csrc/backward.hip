@@ -504,6 +504,133 @@ MOE_DEV int ks_row(int k) { return (k & ~7) | ((k & 3) << 1) | ((k >> 2) & 1); }
 #endif
 constexpr int kBwRing = MOE_BW_RING;        // K steps of operands in registers (even)
 
+// One 128 x 128 output tile's K loop: acc = sum over k < klen of
+// A[i0 + i, k] B[j0 + j, k] (C^T fragments).  abase / bbase and their byte
+// bounds locate the operands (reads past the bounds return zero);
+// kAK / kBK say whether an operand is K-contiguous ([row][K], leading
+// dimension lda / ldb) or K-strided ([K][row]).  All 256 threads call it.
+template <bool kAK, bool kBK, int R = kBwRing>
+MOE_DEV void tile_mainloop(const bf16_t* abase, int64_t abytes, int64_t lda, int i0, const bf16_t* bbase,
+                           int64_t bbytes, int64_t ldb, int j0, int klen, bf16_t (*sA)[kStageElems],
+                           bf16_t (*sB)[kStageElems], bwf32x4_t (&acc)[4][4]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int ns = (klen + kGK - 1) / kGK;
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(abase), (short)0, (int)min(abytes, (int64_t)0x7FFFFFFF), 0x00020000);
+  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(bbase), (short)0, (int)min(bbytes, (int64_t)0x7FFFFFFF), 0x00020000);
+
+  // Per step each thread moves two 16-byte chunks of each operand.
+  //   K-contiguous: chunk c -> row c / 4 of the tile, K offset 8 (c % 4);
+  //   K-strided:    chunk c -> K row c / 16, column offset 8 (c % 16).
+  int a_off[2], b_off[2], a_lds[2], b_lds[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = tid + 256 * h;
+    if (kAK) {
+      const int r = c >> 2, kq = (c & 3) * 8;
+      a_off[h] = (int)(((int64_t)(i0 + r) * lda + kq) * 2);
+      a_lds[h] = kc_lds(r, c & 3);
+    } else {
+      const int kr = c >> 4, ic = (c & 15) * 8;
+      a_off[h] = (int)(((int64_t)kr * lda + i0 + ic) * 2);
+      a_lds[h] = ks_row(kr) * kLdKs + ic;
+    }
+    if (kBK) {
+      const int r = c >> 2, kq = (c & 3) * 8;
+      b_off[h] = (int)(((int64_t)(j0 + r) * ldb + kq) * 2);
+      b_lds[h] = kc_lds(r, c & 3);
+    } else {
+      const int kr = c >> 4, jc = (c & 15) * 8;
+      b_off[h] = (int)(((int64_t)kr * ldb + j0 + jc) * 2);
+      b_lds[h] = ks_row(kr) * kLdKs + jc;
+    }
+  }
+  // scalar step offsets (bytes): K-contiguous operands advance along the
+  // row, K-strided ones by 32 rows
+  const int a_step = kAK ? kGK * 2 : (int)(kGK * lda * 2);
+  const int b_step = kBK ? kGK * 2 : (int)(kGK * ldb * 2);
+  // A ring of kBwRing steps in registers: the loads of the next kBwRing - 1
+  // steps are in flight while one is multiplied.  The step count is padded
+  // to a multiple of the ring; padded steps read zeros (K-contiguous tails
+  // are zeroed below, K-strided rows past K lie outside the resource), so
+  // every round runs whole and the loop has no branch.
+  const int ns_pad = (ns + R - 1) / R * R;
+  bwu32x4_t ra[R][2], rb[R][2];
+  auto load = [&](int st, int q) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ra[q][h] = __builtin_amdgcn_raw_buffer_load_b128(ar, a_off[h], st * a_step, 0);
+      rb[q][h] = __builtin_amdgcn_raw_buffer_load_b128(br, b_off[h], st * b_step, 0);
+    }
+    // K-contiguous operands: K columns past K must be zero
+    if (kAK || kBK) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kq = ((tid + 256 * h) & 3) * 8;
+        const bool in = st * kGK + kq < klen;
+        if (kAK && !in) ra[q][h] = bwu32x4_t{0u, 0u, 0u, 0u};
+        if (kBK && !in) rb[q][h] = bwu32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store = [&](int q, int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      *reinterpret_cast<bwu32x4_t*>(&sA[buf][a_lds[h]]) = ra[q][h];
+      *reinterpret_cast<bwu32x4_t*>(&sB[buf][b_lds[h]]) = rb[q][h];
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = bwf32x4_t{0.f, 0.f, 0.f, 0.f};
+  // fragment offsets: K-contiguous stage -> row (lane % 16), K chunk
+  // lane / 16 (row bases are multiples of 16, so the swizzle depends on the
+  // lane only); K-strided stage -> transpose reads of K rows 8 (lane / 16) +
+  // (lane % 16) / 4 (then + 4), column 4 (lane % 4), at their permuted rows
+  const int kc_off = kc_lds(lane & 15, lane >> 4);
+  const int ks_off = (8 * (lane >> 4) + 2 * ((lane >> 2) & 3)) * kLdKs + 4 * (lane & 3);
+  auto frag = [&](const bf16_t* s, bool kcontig, int rowbase) -> bwbf16x8_t {
+    if (kcontig) return *reinterpret_cast<const bwbf16x8_t*>(s + kc_off + rowbase * kLdKc);
+    const bwv4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bw_lds_v4i16*)(s + ks_off + rowbase));
+    const bwv4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bw_lds_v4i16*)(s + ks_off + kLdKs + rowbase));
+    return __builtin_bit_cast(bwbf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // one K step from ring entry q; `next` >= 0 refills the entry with that
+  // step's loads (the last round refills nothing)
+  auto step = [&](int q, int next) {
+    // LDS buffer q % 2 was last read by step q - 2, which every wave
+    // finished before the previous step's barrier
+    const int buf = q & 1;
+    store(q, buf);
+    __syncthreads();
+    bwbf16x8_t fa[4], fb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = frag(sA[buf], kAK, 64 * wr + 16 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = frag(sB[buf], kBK, 64 * wc + 16 * j);
+    // B fragments as the first operand: the result is the C^T tile, so
+    // each lane ends with 4 consecutive columns of one row of C
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    if (next >= 0) load(next, q);
+  };
+#pragma unroll
+  for (int q = 0; q < R; ++q) load(q, q);
+  for (int st0 = 0; st0 < ns_pad - R; st0 += R) {
+#pragma unroll
+    for (int q = 0; q < R; ++q) step(q, st0 + q + R);
+  }
+#pragma unroll
+  for (int q = 0; q < R; ++q) step(q, -1);
+}
+
 template <bool kAK, bool kBK, int kMode, int kEpi>
 __global__ __launch_bounds__(256) void bw_gemm_bf16_kernel(GemmArgs a) {
   // operand stages; a weight-gradient epilogue reuses them for half a tile
@@ -567,121 +694,8 @@ __global__ __launch_bounds__(256) void bw_gemm_bf16_kernel(GemmArgs a) {
     bbase = a.B + (int64_t)kbeg * a.ldb;
     bbytes = (int64_t)klen * a.ldb * 2;
   }
-  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(abase), (short)0, (int)min(abytes, (int64_t)0x7FFFFFFF), 0x00020000);
-  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(bbase), (short)0, (int)min(bbytes, (int64_t)0x7FFFFFFF), 0x00020000);
-
-  // Per step each thread moves two 16-byte chunks of each operand.
-  //   K-contiguous: chunk c -> row c / 4 of the tile, K offset 8 (c % 4);
-  //   K-strided:    chunk c -> K row c / 16, column offset 8 (c % 16).
-  int a_off[2], b_off[2], a_lds[2], b_lds[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = tid + 256 * h;
-    if (kAK) {
-      const int r = c >> 2, kq = (c & 3) * 8;
-      a_off[h] = (int)(((int64_t)(i0 + r) * a.lda + kq) * 2);
-      a_lds[h] = kc_lds(r, c & 3);
-    } else {
-      const int kr = c >> 4, ic = (c & 15) * 8;
-      a_off[h] = (int)(((int64_t)kr * a.lda + i0 + ic) * 2);
-      a_lds[h] = ks_row(kr) * kLdKs + ic;
-    }
-    if (kBK) {
-      const int r = c >> 2, kq = (c & 3) * 8;
-      b_off[h] = (int)(((int64_t)(j0 + r) * a.ldb + kq) * 2);
-      b_lds[h] = kc_lds(r, c & 3);
-    } else {
-      const int kr = c >> 4, jc = (c & 15) * 8;
-      b_off[h] = (int)(((int64_t)kr * a.ldb + j0 + jc) * 2);
-      b_lds[h] = ks_row(kr) * kLdKs + jc;
-    }
-  }
-  // scalar step offsets (bytes): K-contiguous operands advance along the
-  // row, K-strided ones by 32 rows
-  const int a_step = kAK ? kGK * 2 : (int)(kGK * a.lda * 2);
-  const int b_step = kBK ? kGK * 2 : (int)(kGK * a.ldb * 2);
-  // A ring of kBwRing steps in registers: the loads of the next kBwRing - 1
-  // steps are in flight while one is multiplied.  The step count is padded
-  // to a multiple of the ring; padded steps read zeros (K-contiguous tails
-  // are zeroed below, K-strided rows past K lie outside the resource), so
-  // every round runs whole and the loop has no branch.
-  constexpr int R = kBwRing;
-  const int ns_pad = (ns + R - 1) / R * R;
-  bwu32x4_t ra[R][2], rb[R][2];
-  auto load = [&](int st, int q) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      ra[q][h] = __builtin_amdgcn_raw_buffer_load_b128(ar, a_off[h], st * a_step, 0);
-      rb[q][h] = __builtin_amdgcn_raw_buffer_load_b128(br, b_off[h], st * b_step, 0);
-    }
-    // K-contiguous operands: K columns past K must be zero
-    if (kAK || kBK) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kq = ((tid + 256 * h) & 3) * 8;
-        const bool in = st * kGK + kq < klen;
-        if (kAK && !in) ra[q][h] = bwu32x4_t{0u, 0u, 0u, 0u};
-        if (kBK && !in) rb[q][h] = bwu32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto store = [&](int q, int buf) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      *reinterpret_cast<bwu32x4_t*>(&sA[buf][a_lds[h]]) = ra[q][h];
-      *reinterpret_cast<bwu32x4_t*>(&sB[buf][b_lds[h]]) = rb[q][h];
-    }
-  };
   bwf32x4_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = bwf32x4_t{0.f, 0.f, 0.f, 0.f};
-  // fragment offsets: K-contiguous stage -> row (lane % 16), K chunk
-  // lane / 16 (row bases are multiples of 16, so the swizzle depends on the
-  // lane only); K-strided stage -> transpose reads of K rows 8 (lane / 16) +
-  // (lane % 16) / 4 (then + 4), column 4 (lane % 4), at their permuted rows
-  const int kc_off = kc_lds(lane & 15, lane >> 4);
-  const int ks_off = (8 * (lane >> 4) + 2 * ((lane >> 2) & 3)) * kLdKs + 4 * (lane & 3);
-  auto frag = [&](const bf16_t* s, bool kcontig, int rowbase) -> bwbf16x8_t {
-    if (kcontig) return *reinterpret_cast<const bwbf16x8_t*>(s + kc_off + rowbase * kLdKc);
-    const bwv4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bw_lds_v4i16*)(s + ks_off + rowbase));
-    const bwv4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bw_lds_v4i16*)(s + ks_off + kLdKs + rowbase));
-    return __builtin_bit_cast(bwbf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-
-  // one K step from ring entry q; `next` >= 0 refills the entry with that
-  // step's loads (the last round refills nothing)
-  auto step = [&](int q, int next) {
-    // LDS buffer q % 2 was last read by step q - 2, which every wave
-    // finished before the previous step's barrier
-    const int buf = q & 1;
-    store(q, buf);
-    __syncthreads();
-    bwbf16x8_t fa[4], fb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = frag(sA[buf], kAK, 64 * wr + 16 * i);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fb[j] = frag(sB[buf], kBK, 64 * wc + 16 * j);
-    // B fragments as the first operand: the result is the C^T tile, so
-    // each lane ends with 4 consecutive columns of one row of C
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-    if (next >= 0) load(next, q);
-  };
-#pragma unroll
-  for (int q = 0; q < R; ++q) load(q, q);
-  for (int st0 = 0; st0 < ns_pad - R; st0 += R) {
-#pragma unroll
-    for (int q = 0; q < R; ++q) step(q, st0 + q + R);
-  }
-#pragma unroll
-  for (int q = 0; q < R; ++q) step(q, -1);
+  tile_mainloop<kAK, kBK>(abase, abytes, a.lda, i0, bbase, bbytes, a.ldb, j0, klen, sA, sB, acc);
   // C^T fragment: lane holds row (lane % 16) of its 16 x 16 subtile and
   // columns 4 (lane / 16) .. +3; whole groups of 4 in-range columns go out
   // as one vector access (when the row pitches allow it), the rest element
@@ -743,6 +757,78 @@ __global__ __launch_bounds__(256) void bw_gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (c + e < a.J) epi_store<kEpi>(a, Cg, r, c + e, acc[i][j][e]);
+      }
+    }
+}
+
+// GELU: dH = dY W2 fused with the pre-activation recompute A = X W1^T.
+// Both contract over d into the same [rows, f] tile, so one workgroup runs
+// the two K loops into two register tiles and its epilogue forms
+// dA = dH gelu'(A) and H = gelu(A): the fp32 pre-activation never leaves
+// registers.  Row-grouped (tiles located from expert_offset as in the tiled
+// kernel); the arithmetic is that of the recompute GEMM followed by the dH
+// GEMM, bit for bit.  a: A = dY (lda = d), B = W2 (ldb = f, b_stride d f),
+// C = dA (ldc = f), h_out = H (ld_h = f), J = f, K = d.
+#ifndef MOE_BW_FUSE_DH
+#define MOE_BW_FUSE_DH 1
+#endif
+// register ring of the second K loop (the first tile is live beside it)
+#ifndef MOE_BW_FUSE_RING
+#define MOE_BW_FUSE_RING 2
+#endif
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bw_dh_gelu_fused_kernel(
+    GemmArgs a, const bf16_t* __restrict__ X,
+                                                               const bf16_t* __restrict__ W1) {
+  __shared__ __attribute__((aligned(16))) bf16_t sAB[4][kStageElems];
+  bf16_t(*sA)[kStageElems] = sAB;
+  bf16_t(*sB)[kStageElems] = sAB + 2;
+  __shared__ int s_g, s_tile;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int j0 = blockIdx.x * kGT;
+  if (wave == 0) locate_row_tile(a.offsets, a.groups, blockIdx.y, &s_g, &s_tile);
+  __syncthreads();
+  const int g = s_g;
+  if (g < 0) return;
+  const int64_t row0 = (int64_t)a.offsets[g] + (int64_t)s_tile * kGT;
+  const int rows = (int)min((int64_t)kGT, (int64_t)a.offsets[g + 1] - row0);
+  const int d = a.K, f = a.J;
+  bwf32x4_t pre[4][4], acc[4][4];
+  // A = X W1^T: X rows and W1[g] rows ([f][d]) are both K-contiguous
+  tile_mainloop<true, true>(X + row0 * d, (int64_t)rows * d * 2, d, 0, W1 + (int64_t)g * f * d,
+                            (int64_t)f * d * 2, d, j0, d, sA, sB, pre);
+  __syncthreads();
+  // dH = dY W2: W2[g] is [d][f], K-strided
+  tile_mainloop<true, false, MOE_BW_FUSE_RING>(a.A + row0 * a.lda, (int64_t)rows * a.lda * 2, a.lda, 0,
+                                               a.B + (int64_t)g * a.b_stride,
+                             (int64_t)d * a.ldb * 2, a.ldb, j0, d, sA, sB, acc);
+  bf16_t* dA = static_cast<bf16_t*>(a.C);
+  const bool vec = a.ldc % 4 == 0 && a.ld_h % 4 == 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ti = 64 * wr + 16 * i + (lane & 15);
+      const int c = j0 + 64 * wc + 16 * j + 4 * (lane >> 4);
+      if (ti >= rows) continue;
+      const int64_t r = row0 + ti;
+      float da[4], h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        da[e] = acc[i][j][e] * gelu_exact_grad(pre[i][j][e]);
+        h[e] = gelu_exact(pre[i][j][e]);
+      }
+      if (vec && c + 3 < f) {
+        *reinterpret_cast<bwu32x2_t*>(dA + r * a.ldc + c) = bwu32x2_t{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])};
+        *reinterpret_cast<bwu32x2_t*>(a.h_out + r * a.ld_h + c) =
+            bwu32x2_t{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c + e < f) {
+            dA[r * a.ldc + c + e] = f32_to_bf16(da[e]);
+            a.h_out[r * a.ld_h + c + e] = f32_to_bf16(h[e]);
+          }
       }
     }
 }
@@ -1070,8 +1156,31 @@ hipError_t launch_expert_ffn_backward(const void* X_perm, int dtype, const int32
   void* h = w + al256((size_t)M * fr * 4);
   void* da = w + al256((size_t)M * fr * 4) + al256((size_t)M * f * eb);
   hipError_t err;
+  // 1 + 2 fused (GELU on the matrix cores): dA, H straight from both products
+  const bool fuse = MOE_BW_FUSE_DH && act == 0 && dtype == 1 && d % 8 == 0 && f % 8 == 0;
+  if (fuse) {
+    GemmArgs a{};
+    a.A = static_cast<const bf16_t*>(dY_perm);
+    a.lda = d;
+    a.B = static_cast<const bf16_t*>(W2);
+    a.ldb = f;
+    a.b_stride = (int64_t)d * f;
+    a.C = da;
+    a.ldc = fr;
+    a.offsets = expert_offset;
+    a.groups = E;
+    a.J = f;
+    a.K = d;
+    a.h_out = static_cast<bf16_t*>(h);
+    a.ld_h = f;
+    a.f = f;
+    const dim3 grid((unsigned)((f + kGT - 1) / kGT), (unsigned)((M + kGT - 1) / kGT + E), 1);
+    hipLaunchKernelGGL(bw_dh_gelu_fused_kernel, grid, dim3(256), 0, stream, a, static_cast<const bf16_t*>(X_perm),
+                       static_cast<const bf16_t*>(W1));
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   // 1. pre-activation A = X W1^T  (row-grouped; W1[e] is [fr][d]: K-contiguous)
-  {
+  if (!fuse) {
     GemmArgs a{};
     a.A = static_cast<const bf16_t*>(X_perm);
     a.lda = d;
@@ -1089,7 +1198,7 @@ hipError_t launch_expert_ffn_backward(const void* X_perm, int dtype, const int32
   }
   // 2. dH = dY W2 with the activation backward in the epilogue: dA, H
   //    (W2[e] is [d][f]: K = d is its row index)
-  {
+  if (!fuse) {
     GemmArgs a{};
     a.A = static_cast<const bf16_t*>(dY_perm);
     a.lda = d;

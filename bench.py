@@ -115,7 +115,7 @@ def main():
                          "instead of the forward")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only (the library has no multi-GPU path); --gpus must be 1"}))
         sys.exit(2)
 
     import torch

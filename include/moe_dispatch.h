@@ -33,7 +33,7 @@
  *    call only.
  *  - Every call validates its arguments on the host before touching the GPU
  *    and returns MOE_ERR_INVALID_ARG (bad shape, null pointer, k > E, ...),
- *    MOE_ERR_UNSUPPORTED (a valid request this build does not implement) or
+ *    MOE_ERR_UNSUPPORTED (a valid request the library does not implement) or
  *    MOE_ERR_WORKSPACE (workspace too small) without any device work.  A HIP
  *    launch failure returns MOE_ERR_LAUNCH.  moe_last_error() returns a
  *    thread-local message for the last non-OK status.  No exception or abort

@@ -456,25 +456,51 @@ MOE_DEV void epi_store4(const GemmArgs& a, void* Cg, int64_t r, int c, bwf32x4_t
   }
 }
 
-// Locate row-grouped tile `bx`: group g and its 128-row tile index, or g = -1
-// past the last tile.  Lane l of wave 0 counts the tiles of a contiguous run
-// of groups; a wave scan gives every run its first tile.
-MOE_DEV void locate_row_tile(const int32_t* __restrict__ offsets, int G, int bx, int* s_g, int* s_tile) {
+// Workgroups are dealt to the 8 XCDs round-robin by linear id, and each XCD
+// has its own L2.  Tile t of n goes to workgroup b so that XCD b % 8 owns a
+// contiguous range of tiles (the first n % 8 XCDs one more): tiles that
+// share an operand band (the column tiles of one row tile) then share one
+// L2 instead of fetching the band once per XCD.
+#ifndef MOE_BW_XCD
+#define MOE_BW_XCD 1
+#endif
+constexpr int kBwXcds = 8;
+MOE_DEV int xcd_range_start(int n, int xcd) {
+  const int q = n / kBwXcds, r = n % kBwXcds;
+  return xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
+}
+MOE_DEV int xcd_tile(int n, int b) {
+  return MOE_BW_XCD ? xcd_range_start(n, b % kBwXcds) + b / kBwXcds : b;
+}
+
+// Locate the row-grouped tile of linear workgroup id b over nJ column
+// tiles: group g, its 128-row tile index and the column tile, or g = -1
+// past the live tiles.  Lane l of wave 0 counts the row tiles of a
+// contiguous run of groups; a wave scan gives every run its first tile and
+// the total, over which the tiles are spread across the XCDs (b < nJ x
+// total; the grid's slots beyond return at once).
+MOE_DEV void locate_row_tile(const int32_t* __restrict__ offsets, int G, int nJ, int b, int* s_g, int* s_tile,
+                             int* s_x) {
   const int lane = threadIdx.x & 63;
   const int per = (G + 63) / 64;
   const int g0 = min(G, lane * per), g1 = min(G, g0 + per);
   int cnt = 0;
   for (int g = g0; g < g1; ++g) cnt += (offsets[g + 1] - offsets[g] + 127) >> 7;
   const int incl = wave_inclusive_scan_i32(cnt);
+  const int n = nJ * __builtin_amdgcn_readlane(incl, 63);
   int base = incl - cnt;
   if (lane == 0) *s_g = -1;
   __builtin_amdgcn_wave_barrier();
+  if (b >= n) return;
+  const int t = xcd_tile(n, b);
+  const int bx = t / nJ;
   if (bx >= base && bx < incl) {
     for (int g = g0; g < g1; ++g) {
       const int tiles = (offsets[g + 1] - offsets[g] + 127) >> 7;
       if (bx < base + tiles) {
         *s_g = g;
         *s_tile = bx - base;
+        *s_x = t % nJ;
         break;
       }
       base += tiles;
@@ -638,23 +664,25 @@ __global__ __launch_bounds__(256) void bw_gemm_bf16_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t sAB[4][kStageElems];
   bf16_t(*sA)[kStageElems] = sAB;
   bf16_t(*sB)[kStageElems] = sAB + 2;
-  __shared__ int s_g, s_tile;
+  __shared__ int s_g, s_tile, s_x;
   constexpr bool kNT = kEpi == EPI_F32 ? ((MOE_BW_NT >> (kMode == 1 ? 1 : 0)) & 1) != 0 : (MOE_BW_NT & 4) != 0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;   // 2 x 2 waves of 64 x 64
 
-  // blockIdx.x is the column tile, so concurrent workgroups touch adjacent
-  // column bands of the same rows (weights and outputs alike) instead of one
-  // band of many rows a full row pitch apart
+  // column tiles fastest, so concurrent workgroups touch adjacent column
+  // bands of the same rows (weights and outputs alike) instead of one band
+  // of many rows a full row pitch apart
   int g, i0, j0 = blockIdx.x * kGT;
   int64_t row0 = 0;       // row-grouped: first absolute row of the tile
   int rows = kGT;         // row-grouped: valid rows of the tile
   int kbeg = 0, klen = a.K;
   if (kMode == 0) {
-    if (wave == 0) locate_row_tile(a.offsets, a.groups, blockIdx.y, &s_g, &s_tile);
+    if (wave == 0)
+      locate_row_tile(a.offsets, a.groups, gridDim.x, blockIdx.x + blockIdx.y * gridDim.x, &s_g, &s_tile, &s_x);
     __syncthreads();
     g = s_g;
     if (g < 0) return;
+    j0 = s_x * kGT;
     row0 = (int64_t)a.offsets[g] + (int64_t)s_tile * kGT;
     rows = min((int64_t)kGT, (int64_t)a.offsets[g + 1] - row0);
     i0 = 0;
@@ -782,14 +810,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   __shared__ __attribute__((aligned(16))) bf16_t sAB[4][kStageElems];
   bf16_t(*sA)[kStageElems] = sAB;
   bf16_t(*sB)[kStageElems] = sAB + 2;
-  __shared__ int s_g, s_tile;
+  __shared__ int s_g, s_tile, s_x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
-  const int j0 = blockIdx.x * kGT;
-  if (wave == 0) locate_row_tile(a.offsets, a.groups, blockIdx.y, &s_g, &s_tile);
+  if (wave == 0)
+    locate_row_tile(a.offsets, a.groups, gridDim.x, blockIdx.x + blockIdx.y * gridDim.x, &s_g, &s_tile, &s_x);
   __syncthreads();
   const int g = s_g;
   if (g < 0) return;
+  const int j0 = s_x * kGT;
   const int64_t row0 = (int64_t)a.offsets[g] + (int64_t)s_tile * kGT;
   const int rows = (int)min((int64_t)kGT, (int64_t)a.offsets[g + 1] - row0);
   const int d = a.K, f = a.J;
@@ -835,8 +864,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 
 // Persistent weight-gradient GEMM (K grouped by expert, both operands
 // K-strided, fp32 out): C_g[i, j] = sum over the rows k of group g of
-// A[k, i] B[k, j].  Each workgroup walks tiles t = blockIdx.x, + gridDim.x,
-// ... (column tile fastest, then row tile, then group).  The K loop of one
+// A[k, i] B[k, j].  Tiles are numbered column tile fastest, then row tile,
+// then group; each XCD owns a contiguous range of them, walked by its
+// workgroups in strides (so an operand band is fetched into one L2).  The K loop of one
 // expert is short (its rows / 32 steps), so a tile is mostly load latency
 // and 64 KB of stores; here the last round of each tile refills the
 // register ring with the next tile's first steps, whose loads are in flight
@@ -861,8 +891,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_WG_WAVE
   constexpr int R = MOE_WG_RING;
   constexpr int kCs = 68;   // fp32 LDS row stride of the staged output
   static_assert(128 * kCs * 4 <= 4 * kStageElems * 2, "staged output fits the stages");
-  int t = blockIdx.x;
-  if (t >= total) return;
+  // this workgroup's tiles: with a grid of whole XCD rounds, a strided walk
+  // over its XCD's contiguous range, else over all tiles
+  const bool by_xcd = MOE_BW_XCD && gridDim.x % kBwXcds == 0;
+  const int xcd = blockIdx.x % kBwXcds;
+  const int t_step = by_xcd ? gridDim.x / kBwXcds : gridDim.x;
+  const int t_end = by_xcd ? xcd_range_start(total, xcd + 1) : total;
+  int t = by_xcd ? xcd_range_start(total, xcd) + blockIdx.x / kBwXcds : blockIdx.x;
+  if (t >= t_end) return;
 
   // per thread and step: two 16-byte chunks of each operand, chunk c ->
   // K row c / 16, column offset 8 (c % 16); the tile's first column goes
@@ -961,8 +997,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_WG_WAVE
 #pragma unroll
       for (int q = 0; q < R; ++q) step(q, cur, st0 + q + R);
     }
-    const int tn = t + gridDim.x;
-    const bool more = tn < total;
+    const int tn = t + t_step;
+    const bool more = tn < t_end;
     const Tile nxt = tile_at(more ? tn : t, more);
 #pragma unroll
     for (int q = 0; q < R; ++q) step(q, nxt, q);

@@ -26,6 +26,8 @@
 //   derivative is fused into the dH epilogue;
 // * a plain fp32 grouped GEMM (one thread per output) for fp32 data and for
 //   shapes the bf16 tiling does not cover.
+#include <atomic>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -1117,10 +1119,11 @@ static hipError_t run_gemm(const GemmArgs& a, int dtype, int64_t rows_bound, hip
       // (rows up to a tile past I keep every store offset below 2^31)
       if (a.J % kGT == 0 && a.ldc == a.J && ((int64_t)a.I + kGT) * a.ldc * 4 <= INT32_MAX) {
         // resident workgroups per device (CUs x workgroups per CU), asked once
-        static int slots_of[64] = {};
+        // (threads that race here store the same value)
+        static std::atomic<int> slots_of[64];
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-        int& slots = slots_of[dev];
+        int slots = slots_of[dev].load(std::memory_order_relaxed);
         if (slots == 0) {
           int cus = 0, per_cu = 0;
           const hipError_t e1 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1128,6 +1131,7 @@ static hipError_t run_gemm(const GemmArgs& a, int dtype, int64_t rows_bound, hip
           const hipError_t e2 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bw_wgrad_bf16_kernel, 256, 0);
           if (e2 != hipSuccess) return e2;
           slots = max(1, cus * max(1, per_cu));
+          slots_of[dev].store(slots, std::memory_order_relaxed);
         }
         const int ti = (a.I + kGT - 1) / kGT, tj = a.J / kGT;
         const int64_t total = (int64_t)ti * tj * a.groups;

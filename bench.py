@@ -49,6 +49,7 @@ BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix cores, TFLOP/s
 FP32_PEAK_TFLOPS = 157.3
 STAGES = ("router", "select", "build_map", "dispatch", "expert_ffn", "combine", "balance_stats")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expert_ffn_traffic.json")
+BW_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expert_ffn_backward_traffic.json")
 
 
 def algorithmic(cfg, k, M, touched=None):
@@ -76,9 +77,10 @@ def algorithmic(cfg, k, M, touched=None):
     }
 
 
-def source_hash():
+def source_hash(files=("grouped_gemm.hip", "device_common.hpp", "kernels.hpp")):
+    """Hash of the kernel sources a stored traffic measurement was taken on."""
     h = hashlib.sha256()
-    for name in ("grouped_gemm.hip", "device_common.hpp", "kernels.hpp"):
+    for name in files:
         with open(os.path.join(ROOT, "sparse_expert_dispatch_amd", "csrc", name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -245,12 +247,7 @@ def main():
     ffn = alg["expert_ffn"]
     intensity = ffn["flops"] / ffn["bytes"]
     ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as fh:
-            tr = json.load(fh)
-        if tr.get("source_hash") == source_hash() and tr.get("workload") == cfg.name:
-            traffic = tr.get("bytes_per_launch")
+    traffic = stored_traffic(TRAFFIC_FILE, source_hash(), cfg.name)
     if intensity < ridge or cfg.dtype != "bf16":
         achieved = ffn["bytes"] / (ffn_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -295,6 +292,21 @@ def main():
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(cfg, inp, w1_host, w2_host)
     print(json.dumps(line), flush=True)
+
+
+def stored_traffic(path, src_hash, workload):
+    """Measured HBM bytes per call from a counter summary in profiles/, or
+    None when it was taken on other sources or another workload."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        tr = json.load(fh)
+    if tr.get("source_hash") == src_hash and tr.get("workload") == workload:
+        return tr.get("bytes_per_launch")
+    return None
+
+
+BW_SOURCES = ("backward.hip", "device_common.hpp", "kernels.hpp")
 
 
 def ffn_backward_bytes(cfg, M, touched):
@@ -376,7 +388,8 @@ def run_backward(args, cfg, inp, w1_host, w2_host, layer, x, stream):
     ffn_ms = seg_ms[1]
     achieved = a["bytes"] / (ffn_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": stored_traffic(BW_TRAFFIC_FILE, source_hash(BW_SOURCES), cfg.name),
                 "kernel": "moe_expert_ffn_backward (grouped GEMMs: pre-activation recompute and dH with the "
                           "activation derivative (one launch for GELU), dX, dW2, dW1)",
                 "algorithmic_bytes": int(a["bytes"]), "flops": a["flops"], "avg_us": round(ffn_ms * 1e3, 2),

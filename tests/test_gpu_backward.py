@@ -151,14 +151,15 @@ def test_backward_sqrtsoftplus_unnormalised_and_rank_major():
     _run(W.SMALL_CONFIGS[4].scaled("bw_rank_major", k=2, capacity_order="rank", norm_topk=True))
 
 
-@pytest.mark.parametrize("d,f", [(192, 64), (256, 192), (192, 128)])
+@pytest.mark.parametrize("d,f", [(192, 64), (256, 192), (192, 128), (100, 60)])
 def test_backward_ragged_tiles(d, f):
     """Experts of 0, 1, 31, 33, 130 and 300 rows (empty experts, K tails of
     the weight gradients, several 128-row tiles).  (192, 64): d and f not
     multiples of 128, partial column tiles everywhere, the weight gradients
     on the tiled kernel; (256, 192): dW1 (f x 256, 2f x 256) on the
     persistent weight-gradient kernel with a partial last row tile;
-    (192, 128): dW2 (192 x 128) on it likewise."""
+    (192, 128): dW2 (192 x 128) on it likewise; (100, 60): rows that are not
+    whole 16-byte chunks, so every GEMM takes the plain bf16 kernel."""
     from harness import host, log, widen
     from oracle import moe_backward as B
     from sparse_expert_dispatch_amd import _native as N

@@ -216,6 +216,21 @@ class MoELayer:
             self.forward(x, residual, stats)
         return graph
 
+    def capture_step(self, x: torch.Tensor, dout: torch.Tensor, residual: bool = True):
+        """Record one forward and its backward (one training step of the
+        layer) into a HIP graph; replays recompute every output and gradient
+        buffer from the current contents of `x` and `dout`.  An eager step
+        runs first, so the gradient buffers are allocated and the library's
+        one-time host queries happen outside the capture."""
+        self.forward(x, residual)
+        self.backward(x, dout, residual)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.forward(x, residual)
+            self.backward(x, dout, residual)
+        return graph
+
 
 def to_device(a, device="cuda") -> Optional[torch.Tensor]:
     """numpy array (float32, int32, or bf16 as uint16) -> device tensor

@@ -344,7 +344,9 @@ moe_status_t moe_combine_backward(const void *dOut, const void *Y_perm, int32_t 
 /* Workspace for moe_expert_ffn_backward: the recomputed pre-activation
  * [M_max, f_rows] in fp32, the activation H [M_max, f] and the gradient of
  * the pre-activation [M_max, f_rows] in dtype (f_rows = f, or 2f for
- * SwiGLU). */
+ * SwiGLU).  GELU on bf16 with d and f multiples of 8 keeps the
+ * pre-activation in registers (one launch computes it and dH) and leaves
+ * its part of the workspace untouched; the size is the same either way. */
 moe_status_t moe_ffn_backward_workspace_size(int64_t M_max, int32_t E, int32_t d, int32_t f, int32_t act,
                                              int32_t dtype, size_t *bytes);
 

@@ -806,6 +806,10 @@ __global__ __launch_bounds__(256) void bw_gemm_bf16_kernel(GemmArgs a) {
 #ifndef MOE_BW_FUSE_RING
 #define MOE_BW_FUSE_RING 2
 #endif
+// dA and H staged through LDS and stored as whole 16-byte row pieces
+#ifndef MOE_BW_FUSE_STAGE
+#define MOE_BW_FUSE_STAGE 1
+#endif
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bw_dh_gelu_fused_kernel(
     GemmArgs a, const bf16_t* __restrict__ X,
                                                                const bf16_t* __restrict__ W1) {
@@ -834,6 +838,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
                                                a.B + (int64_t)g * a.b_stride,
                              (int64_t)d * a.ldb * 2, a.ldb, j0, d, sA, sB, acc);
   bf16_t* dA = static_cast<bf16_t*>(a.C);
+  if (MOE_BW_FUSE_STAGE) {
+    // dA goes to LDS as it is computed, H waits in registers as bf16 pairs;
+    // each tile then leaves through LDS (row stride 136: the fragment
+    // writes of 16 rows land 4 banks apart) as 16-byte pieces of whole rows
+    // (f is a multiple of 8 here)
+    constexpr int kHs = kGT + 8;
+    static_assert(kGT * kHs <= 4 * kStageElems, "a bf16 output tile fits the stages");
+    bf16_t* sC = &sAB[0][0];
+    uint32_t ph[4][4][2];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float da[4], h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          da[e] = acc[i][j][e] * gelu_exact_grad(pre[i][j][e]);
+          h[e] = gelu_exact(pre[i][j][e]);
+        }
+        ph[i][j][0] = pack_bf16x2(h[0], h[1]);
+        ph[i][j][1] = pack_bf16x2(h[2], h[3]);
+        *reinterpret_cast<bwu32x2_t*>(sC + (64 * wr + 16 * i + (lane & 15)) * kHs + 64 * wc + 16 * j +
+                                      4 * (lane >> 4)) = bwu32x2_t{pack_bf16x2(da[0], da[1]),
+                                                                   pack_bf16x2(da[2], da[3])};
+      }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if (p == 1) {
+        __syncthreads();   // dA has been read out
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<bwu32x2_t*>(sC + (64 * wr + 16 * i + (lane & 15)) * kHs + 64 * wc + 16 * j +
+                                          4 * (lane >> 4)) = bwu32x2_t{ph[i][j][0], ph[i][j][1]};
+      }
+      __syncthreads();
+      bf16_t* dst = p == 0 ? dA : a.h_out;
+      const int64_t ld = p == 0 ? a.ldc : a.ld_h;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int e = tid + 256 * q;   // 128 rows x 16 chunks of 8
+        const int r = e >> 4, c = (e & 15) * 8;
+        if (r < rows && j0 + c < f)
+          *reinterpret_cast<bwu32x4_t*>(dst + (row0 + r) * ld + j0 + c) =
+              *reinterpret_cast<const bwu32x4_t*>(sC + r * kHs + c);
+      }
+    }
+    return;
+  }
   const bool vec = a.ldc % 4 == 0 && a.ld_h % 4 == 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i)

@@ -362,6 +362,14 @@ enum { EPI_BF16 = 0, EPI_BF16_ADD = 1, EPI_F32 = 2, EPI_GELU_BWD = 3, EPI_SWIGLU
 #ifndef MOE_BW_STAGE_DW
 #define MOE_BW_STAGE_DW 1
 #endif
+// Row-grouped GEMMs on 128 x 256 tiles when the experts average at least
+// MOE_BW_WIDE_ROWS rows (the host's row bound over the groups)
+#ifndef MOE_BW_WIDE
+#define MOE_BW_WIDE 1
+#endif
+#ifndef MOE_BW_WIDE_ROWS
+#define MOE_BW_WIDE_ROWS 512
+#endif
 // Weight gradients with whole-tile J on the persistent kernel
 #ifndef MOE_BW_PERSIST
 #define MOE_BW_PERSIST 1
@@ -1097,6 +1105,139 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_WG_WAVE
   }
 }
 
+// Row-grouped GEMM for experts with many rows (the matrix cores, not the
+// weight stream, bound the time): 128 x 256 tiles, each wave 64 x 128 (four
+// A and eight B fragments per 32-K step, a quarter fewer LDS bytes per MFMA
+// than 64 x 64), a two-step register ring.  A is K-contiguous ([rows][K]);
+// B either way, staged as in the 128-wide kernel ([256][32] swizzled, or
+// [32][264] read with transposes: 264 keeps the 4-bank row offset of 136).
+constexpr int kWideN = 256;
+constexpr int kLdKsW = kWideN + 8;
+constexpr int kStageW = 32 * kLdKsW;   // 8448 >= 256 * 32
+template <bool kBK, int kEpi>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bw_gemm_wide_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2][kStageElems];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[2][kStageW];
+  __shared__ int s_g, s_tile, s_x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  if (wave == 0)
+    locate_row_tile(a.offsets, a.groups, gridDim.x, blockIdx.x + blockIdx.y * gridDim.x, &s_g, &s_tile, &s_x);
+  __syncthreads();
+  const int g = s_g;
+  if (g < 0) return;
+  const int j0 = s_x * kWideN;
+  const int64_t row0 = (int64_t)a.offsets[g] + (int64_t)s_tile * kGT;
+  const int rows = (int)min((int64_t)kGT, (int64_t)a.offsets[g + 1] - row0);
+  const int klen = a.K, ns = (klen + kGK - 1) / kGK;
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(a.A + row0 * a.lda), (short)0, (int)((int64_t)rows * a.lda * 2), 0x00020000);
+  const bf16_t* bbase = a.B + (int64_t)g * a.b_stride;
+  const int64_t bbytes = kBK ? (int64_t)a.J * a.ldb * 2 : (int64_t)a.K * a.ldb * 2;
+  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(bbase), (short)0, (int)min(bbytes, (int64_t)0x7FFFFFFF), 0x00020000);
+  int a_off[2], a_lds[2], a_kq[2], b_off[4], b_lds[4], b_kq[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = tid + 256 * h;
+    a_kq[h] = (c & 3) * 8;
+    a_off[h] = (int)(((int64_t)(c >> 2) * a.lda + a_kq[h]) * 2);
+    a_lds[h] = kc_lds(c >> 2, c & 3);
+  }
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int c = tid + 256 * h;
+    if (kBK) {
+      b_kq[h] = (c & 3) * 8;
+      b_off[h] = (int)(((int64_t)(j0 + (c >> 2)) * a.ldb + b_kq[h]) * 2);
+      b_lds[h] = kc_lds(c >> 2, c & 3);
+    } else {
+      b_kq[h] = 0;
+      b_off[h] = (int)(((int64_t)(c >> 5) * a.ldb + j0 + (c & 31) * 8) * 2);
+      b_lds[h] = ks_row(c >> 5) * kLdKsW + (c & 31) * 8;
+    }
+  }
+  const int b_step = kBK ? kGK * 2 : (int)(kGK * a.ldb * 2);
+  constexpr int R = 2;
+  const int ns_pad = (ns + R - 1) / R * R;
+  bwu32x4_t ra[R][2], rb[R][4];
+  auto load = [&](int st, int q) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) ra[q][h] = __builtin_amdgcn_raw_buffer_load_b128(ar, a_off[h], st * kGK * 2, 0);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) rb[q][h] = __builtin_amdgcn_raw_buffer_load_b128(br, b_off[h], st * b_step, 0);
+    // K columns past K of the K-contiguous operands must be zero
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (st * kGK + a_kq[h] >= klen) ra[q][h] = bwu32x4_t{0u, 0u, 0u, 0u};
+    if (kBK) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        if (st * kGK + b_kq[h] >= klen) rb[q][h] = bwu32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  bwf32x4_t acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = bwf32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int kc_off = kc_lds(lane & 15, lane >> 4);
+  const int ks_offw = (8 * (lane >> 4) + 2 * ((lane >> 2) & 3)) * kLdKsW + 4 * (lane & 3);
+  auto step = [&](int q, int next) {
+    const int buf = q & 1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) *reinterpret_cast<bwu32x4_t*>(&sA[buf][a_lds[h]]) = ra[q][h];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) *reinterpret_cast<bwu32x4_t*>(&sB[buf][b_lds[h]]) = rb[q][h];
+    __syncthreads();
+    bwbf16x8_t fa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      fa[i] = *reinterpret_cast<const bwbf16x8_t*>(&sA[buf][kc_off + (64 * wr + 16 * i) * kLdKc]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int cb = 128 * wc + 16 * j;
+      bwbf16x8_t fb;
+      if (kBK) {
+        fb = *reinterpret_cast<const bwbf16x8_t*>(&sB[buf][kc_off + cb * kLdKc]);
+      } else {
+        const bwv4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bw_lds_v4i16*)(&sB[buf][ks_offw + cb]));
+        const bwv4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bw_lds_v4i16*)(&sB[buf][ks_offw + kLdKsW + cb]));
+        fb = __builtin_bit_cast(bwbf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa[i], acc[i][j], 0, 0, 0);
+    }
+    if (next >= 0) load(next, q);
+  };
+#pragma unroll
+  for (int q = 0; q < R; ++q) load(q, q);
+  for (int st0 = 0; st0 < ns_pad - R; st0 += R) {
+#pragma unroll
+    for (int q = 0; q < R; ++q) step(q, st0 + q + R);
+  }
+#pragma unroll
+  for (int q = 0; q < R; ++q) step(q, -1);
+  constexpr bool kNT = kEpi == EPI_F32 ? (MOE_BW_NT & 1) != 0 : (MOE_BW_NT & 4) != 0;
+  const bool vec = a.ldc % 4 == 0 && (kEpi < EPI_GELU_BWD || (a.ld_pre % 4 == 0 && a.ld_h % 4 == 0));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int ti = 64 * wr + 16 * i + (lane & 15);
+      const int c = j0 + 128 * wc + 16 * j + 4 * (lane >> 4);
+      if (ti >= rows) continue;
+      const int64_t r = row0 + ti;
+      if (vec && c + 3 < a.J) {
+        epi_store4<kEpi, kNT>(a, a.C, r, c, acc[i][j]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c + e < a.J) epi_store<kEpi>(a, a.C, r, c + e, acc[i][j][e]);
+      }
+    }
+}
+
 // Plain grouped GEMM, one thread per output element, fp32 accumulation in
 // K order; T = float or bf16.  Same argument meaning as the bf16 kernel.
 template <typename T, bool kAK, bool kBK, int kMode, int kEpi>
@@ -1193,6 +1334,14 @@ static hipError_t run_gemm(const GemmArgs& a, int dtype, int64_t rows_bound, hip
         if (total == 0) return hipSuccess;
         const int grid = (int)(total < slots ? total : (int64_t)slots);
         hipLaunchKernelGGL(bw_wgrad_bf16_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a, ti, tj, (int)total);
+        return hipGetLastError();
+      }
+    }
+    // many rows per expert (past the matrix-core ridge): the wide tiles
+    if constexpr (kMode == 0 && kAK && kEpi != EPI_BF16_ADD && kEpi != EPI_GELU_BWD) {
+      if (MOE_BW_WIDE && a.J % kWideN == 0 && rows_bound >= (int64_t)MOE_BW_WIDE_ROWS * a.groups) {
+        const dim3 grid((unsigned)(a.J / kWideN), (unsigned)((rows_bound + kGT - 1) / kGT + a.groups), 1);
+        hipLaunchKernelGGL((bw_gemm_wide_kernel<kBK, kEpi>), grid, dim3(256), 0, stream, a);
         return hipGetLastError();
       }
     }

@@ -151,21 +151,11 @@ def test_backward_sqrtsoftplus_unnormalised_and_rank_major():
     _run(W.SMALL_CONFIGS[4].scaled("bw_rank_major", k=2, capacity_order="rank", norm_topk=True))
 
 
-@pytest.mark.parametrize("d,f", [(192, 64), (256, 192), (192, 128), (100, 60)])
-def test_backward_ragged_tiles(d, f):
-    """Experts of 0, 1, 31, 33, 130 and 300 rows (empty experts, K tails of
-    the weight gradients, several 128-row tiles).  (192, 64): d and f not
-    multiples of 128, partial column tiles everywhere, the weight gradients
-    on the tiled kernel; (256, 192): dW1 (f x 256, 2f x 256) on the
-    persistent weight-gradient kernel with a partial last row tile;
-    (192, 128): dW2 (192 x 128) on it likewise; (100, 60): rows that are not
-    whole 16-byte chunks, so every GEMM takes the plain bf16 kernel."""
-    from harness import host, log, widen
+def _ffn_backward_case(rows, d, f, seed):
+    from harness import host, widen
     from oracle import moe_backward as B
     from sparse_expert_dispatch_amd import _native as N
-    log(f"[backward ragged] d={d} f={f}")
-    rng = np.random.default_rng(21 + d + f)
-    rows = [0, 1, 31, 33, 130, 300]
+    rng = np.random.default_rng(seed)
     E = len(rows)
     M = sum(rows)
     off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
@@ -189,4 +179,30 @@ def test_backward_ragged_tiles(d, f):
         for name, got, ref in (("dX", widen(host(dx)), dx_ref), ("dW1", host(dw1), dw1_ref),
                                ("dW2", host(dw2), dw2_ref)):
             assert row_err(got, ref) <= 5e-2, (act, name, row_err(got, ref))
-        assert (host(dw1)[0] == 0).all() and (host(dw2)[0] == 0).all()
+        for e in range(E):
+            if rows[e] == 0:
+                assert (host(dw1)[e] == 0).all() and (host(dw2)[e] == 0).all()
+
+
+@pytest.mark.parametrize("d,f", [(192, 64), (256, 192), (192, 128), (100, 60)])
+def test_backward_ragged_tiles(d, f):
+    """Experts of 0, 1, 31, 33, 130 and 300 rows (empty experts, K tails of
+    the weight gradients, several 128-row tiles).  (192, 64): d and f not
+    multiples of 128, partial column tiles everywhere, the weight gradients
+    on the tiled kernel; (256, 192): dW1 (f x 256, 2f x 256) on the
+    persistent weight-gradient kernel with a partial last row tile;
+    (192, 128): dW2 (192 x 128) on it likewise; (100, 60): rows that are not
+    whole 16-byte chunks, so every GEMM takes the plain bf16 kernel."""
+    from harness import log
+    log(f"[backward ragged] d={d} f={f}")
+    _ffn_backward_case([0, 1, 31, 33, 130, 300], d, f, 21 + d + f)
+
+
+def test_backward_wide_tiles():
+    """Experts averaging more than 512 rows (0, 900, 1300, 40: empty, ragged
+    last row tiles) with d = 512, f = 256: the row-grouped GEMMs whose width
+    is a multiple of 256 (recompute and dH of SwiGLU, dX of both) run on the
+    128 x 256 tiles."""
+    from harness import log
+    log("[backward wide] rows 0/900/1300/40, d=512 f=256")
+    _ffn_backward_case([0, 900, 1300, 40], 512, 256, 77)

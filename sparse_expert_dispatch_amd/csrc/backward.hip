@@ -1238,6 +1238,179 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     }
 }
 
+// Weight gradients of experts with many rows (matrix-core bound): the
+// persistent kernel above on 128 x 256 tiles, each wave 64 x 128 (eight B
+// fragments per step), a two-step register ring, B staged as [32][264] for
+// the transpose reads; the output leaves in four passes of two column
+// pieces per wave.  Needs J a multiple of 256 and ldc == J.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bw_wgrad_wide_kernel(
+    GemmArgs a, int tiles_i, int tiles_j, int total) {
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * kStageElems + 2 * kStageW];
+  bf16_t(*sA)[kStageElems] = reinterpret_cast<bf16_t(*)[kStageElems]>(smem);
+  bf16_t(*sB)[kStageW] = reinterpret_cast<bf16_t(*)[kStageW]>(smem + 2 * kStageElems);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  constexpr int R = 2;
+  constexpr int kCs = 68;   // fp32 LDS row stride of the staged output
+  static_assert(128 * kCs * 4 <= (2 * kStageElems + 2 * kStageW) * 2, "staged output fits the stages");
+  // this workgroup's tiles: with a grid of whole XCD rounds, a strided walk
+  // over its XCD's contiguous range, else over all tiles
+  const bool by_xcd = MOE_BW_XCD && gridDim.x % kBwXcds == 0;
+  const int xcd = blockIdx.x % kBwXcds;
+  const int t_step = by_xcd ? gridDim.x / kBwXcds : gridDim.x;
+  const int t_end = by_xcd ? xcd_range_start(total, xcd + 1) : total;
+  int t = by_xcd ? xcd_range_start(total, xcd) + blockIdx.x / kBwXcds : blockIdx.x;
+  if (t >= t_end) return;
+
+  // per thread and step: two 16-byte chunks of each operand, chunk c ->
+  // K row c / 16, column offset 8 (c % 16); the tile's first column goes
+  // into the scalar offset
+  int a_off[2], s_lds[2], b_off[4], sb_lds[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = tid + 256 * h;
+    const int kr = c >> 4, cc = (c & 15) * 8;
+    a_off[h] = (int)(((int64_t)kr * a.lda + cc) * 2);
+    s_lds[h] = ks_row(kr) * kLdKs + cc;
+  }
+  // B: 256 columns, four chunks per thread: K row c / 32, column 8 (c % 32)
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int c = tid + 256 * h;
+    const int kr = c >> 5, cc = (c & 31) * 8;
+    b_off[h] = (int)(((int64_t)kr * a.ldb + cc) * 2);
+    sb_lds[h] = ks_row(kr) * kLdKsW + cc;
+  }
+  const int a_step = (int)(kGK * a.lda * 2), b_step = (int)(kGK * a.ldb * 2);
+
+  struct Tile {
+    __amdgpu_buffer_rsrc_t ar, br;
+    int g, i0, j0, klen;
+  };
+  // tile coordinates and operand resources (rows past the group's K read
+  // as zero; `live` false gives empty resources, whose loads return zeros)
+  auto tile_at = [&](int tt, bool live) -> Tile {
+    Tile x;
+    x.j0 = (tt % tiles_j) * kWideN;
+    x.i0 = ((tt / tiles_j) % tiles_i) * kGT;
+    x.g = tt / (tiles_j * tiles_i);
+    const int kb = live ? a.offsets[x.g] : 0;
+    x.klen = live ? a.offsets[x.g + 1] - kb : 0;
+    x.ar = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a.A + (int64_t)kb * a.lda), (short)0,
+                                             (int)((int64_t)x.klen * a.lda * 2), 0x00020000);
+    x.br = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a.B + (int64_t)kb * a.ldb), (short)0,
+                                             (int)((int64_t)x.klen * a.ldb * 2), 0x00020000);
+    return x;
+  };
+  bwu32x4_t ra[R][2], rb[R][4];
+  auto load = [&](const Tile& x, int st, int q) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      ra[q][h] = __builtin_amdgcn_raw_buffer_load_b128(x.ar, a_off[h], st * a_step + x.i0 * 2, 0);
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      rb[q][h] = __builtin_amdgcn_raw_buffer_load_b128(x.br, b_off[h], st * b_step + x.j0 * 2, 0);
+  };
+  const int ks_off = (8 * (lane >> 4) + 2 * ((lane >> 2) & 3)) * kLdKs + 4 * (lane & 3);
+  auto frag = [&](const bf16_t* s, int rowbase) -> bwbf16x8_t {
+    const bwv4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bw_lds_v4i16*)(s + ks_off + rowbase));
+    const bwv4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bw_lds_v4i16*)(s + ks_off + kLdKs + rowbase));
+    return __builtin_bit_cast(bwbf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  const int ks_offw = (8 * (lane >> 4) + 2 * ((lane >> 2) & 3)) * kLdKsW + 4 * (lane & 3);
+  auto fragw = [&](const bf16_t* s, int rowbase) -> bwbf16x8_t {
+    const bwv4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bw_lds_v4i16*)(s + ks_offw + rowbase));
+    const bwv4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((bw_lds_v4i16*)(s + ks_offw + kLdKsW + rowbase));
+    return __builtin_bit_cast(bwbf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  bwf32x4_t acc[4][8];
+  // one K step from ring entry q, then refill the entry with step `st` of
+  // tile `x`
+  auto step = [&](int q, const Tile& x, int st) {
+    const int buf = q & 1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) *reinterpret_cast<bwu32x4_t*>(&sA[buf][s_lds[h]]) = ra[q][h];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) *reinterpret_cast<bwu32x4_t*>(&sB[buf][sb_lds[h]]) = rb[q][h];
+    __syncthreads();
+    bwbf16x8_t fa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = frag(sA[buf], 64 * wr + 16 * i);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bwbf16x8_t fb = fragw(sB[buf], 128 * wc + 16 * j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa[i], acc[i][j], 0, 0, 0);
+    }
+    load(x, st, q);
+  };
+
+  // epilogue constants: this thread's fragment writes start at LDS float
+  // acc_lds; its read-outs are rows out_r0 + 16 q of the pass, local column
+  // lc, which is tile column 128 (lc / 32) + 32 p + lc % 32
+  const int acc_lds = (64 * wr + (lane & 15)) * kCs + 32 * wc + 4 * (lane >> 4);
+  const int out_r0 = tid >> 4, out_lc = (tid & 15) * 4;
+  const int out_lds = out_r0 * kCs + out_lc;
+  const int row_bytes = (int)(a.ldc * 4);
+  const int out_voff = out_r0 * row_bytes + (128 * (out_lc >> 5) + (out_lc & 31)) * 4;
+
+  Tile cur = tile_at(t, true);
+#pragma unroll
+  for (int q = 0; q < R; ++q) load(cur, q, q);
+  while (true) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = bwf32x4_t{0.f, 0.f, 0.f, 0.f};
+    // the previous tile's epilogue has read its LDS out
+    __syncthreads();
+    // steps padded to whole rounds of R (at least one: an expert without
+    // rows runs one round of zeros and stores a zero gradient)
+    const int ns_pad = max(R, (cur.klen + kGK * R - 1) / (kGK * R) * R);
+    for (int st0 = 0; st0 < ns_pad - R; st0 += R) {
+#pragma unroll
+      for (int q = 0; q < R; ++q) step(q, cur, st0 + q + R);
+    }
+    const int tn = t + t_step;
+    const bool more = tn < t_end;
+    const Tile nxt = tile_at(more ? tn : t, more);
+#pragma unroll
+    for (int q = 0; q < R; ++q) step(q, nxt, q);
+
+    // C^T fragments -> LDS -> 128-byte row pieces, four passes of the
+    // column pieces j = 2p, 2p + 1 of every wave, as in the 128-wide kernel
+    float* sC = reinterpret_cast<float*>(smem);
+    float* Cg = static_cast<float*>(a.C) + (size_t)cur.g * a.c_stride;
+    const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+        Cg, (short)0, (int)((int64_t)a.I * a.ldc * 4), 0x00020000);
+    // rows left in this tile for the thread's first read-out row; a row past
+    // I gets an offset beyond the resource, so its store is dropped
+    const int rows_left = a.I - cur.i0 - out_r0;
+    const int tile_soff = (int)(((int64_t)cur.i0 * a.ldc + cur.j0) * 4);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+          *reinterpret_cast<bwf32x4_t*>(sC + acc_lds + 16 * i * kCs + 16 * jj) = acc[i][2 * p + jj];
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {   // rows out_r0 + 16 q
+        const bwf32x4_t v = *reinterpret_cast<const bwf32x4_t*>(sC + out_lds + 16 * q * kCs);
+        const int off = 16 * q < rows_left ? out_voff : (int)0x80000000;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(bwu32x4_t, v), cr, off,
+                                               tile_soff + 16 * q * row_bytes + 128 * p, 2 /* nt */);
+      }
+    }
+    if (!more) break;
+    t = tn;
+    cur = nxt;
+  }
+}
+
 // Plain grouped GEMM, one thread per output element, fp32 accumulation in
 // K order; T = float or bf16.  Same argument meaning as the bf16 kernel.
 template <typename T, bool kAK, bool kBK, int kMode, int kEpi>
@@ -1303,6 +1476,28 @@ __global__ __launch_bounds__(256) void bw_gemm_plain_kernel(GemmArgs a, int64_t 
   }
 }
 
+// Resident workgroups of a persistent kernel per device (CUs x workgroups
+// per CU), asked once per kernel (kId) and device; threads that race here
+// store the same value.
+template <int kId, typename K>
+static hipError_t resident_slots(K kernel, int* out) {
+  static std::atomic<int> slots_of[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  int slots = slots_of[dev].load(std::memory_order_relaxed);
+  if (slots == 0) {
+    int cus = 0, per_cu = 0;
+    const hipError_t e1 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e1 != hipSuccess) return e1;
+    const hipError_t e2 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0);
+    if (e2 != hipSuccess) return e2;
+    slots = max(1, cus * max(1, per_cu));
+    slots_of[dev].store(slots, std::memory_order_relaxed);
+  }
+  *out = slots;
+  return hipSuccess;
+}
+
 // Host side: grid and kernel choice.  bf16 on the matrix cores needs the
 // K-contiguous operands' leading dimensions to be multiples of 8 (16-byte
 // rows), K % 8 == 0, and every leading dimension a multiple of 8; anything
@@ -1314,26 +1509,19 @@ static hipError_t run_gemm(const GemmArgs& a, int dtype, int64_t rows_bound, hip
     if constexpr (kMode == 1 && kEpi == EPI_F32 && !kAK && !kBK && MOE_BW_PERSIST) {
       // (rows up to a tile past I keep every store offset below 2^31)
       if (a.J % kGT == 0 && a.ldc == a.J && ((int64_t)a.I + kGT) * a.ldc * 4 <= INT32_MAX) {
-        // resident workgroups per device (CUs x workgroups per CU), asked once
-        // (threads that race here store the same value)
-        static std::atomic<int> slots_of[64];
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-        int slots = slots_of[dev].load(std::memory_order_relaxed);
-        if (slots == 0) {
-          int cus = 0, per_cu = 0;
-          const hipError_t e1 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-          if (e1 != hipSuccess) return e1;
-          const hipError_t e2 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bw_wgrad_bf16_kernel, 256, 0);
-          if (e2 != hipSuccess) return e2;
-          slots = max(1, cus * max(1, per_cu));
-          slots_of[dev].store(slots, std::memory_order_relaxed);
-        }
-        const int ti = (a.I + kGT - 1) / kGT, tj = a.J / kGT;
+        const bool wide = MOE_BW_WIDE && a.J % kWideN == 0 && rows_bound >= (int64_t)MOE_BW_WIDE_ROWS * a.groups;
+        int slots = 0;
+        const hipError_t es = wide ? resident_slots<1>(bw_wgrad_wide_kernel, &slots)
+                                   : resident_slots<0>(bw_wgrad_bf16_kernel, &slots);
+        if (es != hipSuccess) return es;
+        const int ti = (a.I + kGT - 1) / kGT, tj = a.J / (wide ? kWideN : kGT);
         const int64_t total = (int64_t)ti * tj * a.groups;
         if (total == 0) return hipSuccess;
         const int grid = (int)(total < slots ? total : (int64_t)slots);
-        hipLaunchKernelGGL(bw_wgrad_bf16_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a, ti, tj, (int)total);
+        if (wide)
+          hipLaunchKernelGGL(bw_wgrad_wide_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a, ti, tj, (int)total);
+        else
+          hipLaunchKernelGGL(bw_wgrad_bf16_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a, ti, tj, (int)total);
         return hipGetLastError();
       }
     }
@@ -1495,7 +1683,7 @@ hipError_t launch_expert_ffn_backward(const void* X_perm, int dtype, const int32
     a.groups = E;
     a.I = d;
     a.J = f;
-    err = run_gemm<false, false, 1, EPI_F32>(a, dtype, 0, stream);
+    err = run_gemm<false, false, 1, EPI_F32>(a, dtype, M, stream);
     if (err != hipSuccess) return err;
   }
   // 5. dW1[e] = dA^T X
@@ -1512,7 +1700,7 @@ hipError_t launch_expert_ffn_backward(const void* X_perm, int dtype, const int32
     a.groups = E;
     a.I = fr;
     a.J = d;
-    err = run_gemm<false, false, 1, EPI_F32>(a, dtype, 0, stream);
+    err = run_gemm<false, false, 1, EPI_F32>(a, dtype, M, stream);
   }
   return err;
 }

@@ -5,30 +5,35 @@ router -> selection -> routing map -> dispatch -> expert FFNs (grouped GEMM)
 -> combine -> balance statistics, every stage a call into libmoe_dispatch.so
 on one HIP stream, inputs and weights resident in HBM.
 
-Default workload: expert choice, bf16, n = 4096 tokens, d = 2048, 64 experts,
-capacity factor 2 (128 tokens per expert), GELU experts d -> 4096 -> d.
+Default workload (the largest one, and the only one near the pages'
+production shapes): sigmoid gating with a selection bias, 8 expert groups
+of which each token keeps 4, top-8 of 256 SwiGLU experts (d = 7168, f =
+2048) plus one always-on shared expert, bf16, n = 4096 tokens, dropless.
 
-    python bench.py [--steps K] [--warmup W] [--config 2|1..5|decode] [--no-cpu-baseline] [--backward]
+    python bench.py [--steps K] [--warmup W] [--config 5|1..5|decode] [--no-cpu-baseline] [--backward]
 
---config decode times a decode step instead: 64 tokens, top-8 of 64 SwiGLU
-experts (d = 2048, f = 1024), where the grouped GEMM streams the weights of
-the experts the batch touches.
+--config 2 is expert choice (n = 4096, d = 2048, 64 GELU experts, c = 2),
+3 top-8 of 64 SwiGLU experts with Zipf-skewed loads (n = 8192), 4 Switch
+top-1 of 128 GELU experts with capacity 160 (n = 16384); --config decode a
+decode step (64 tokens, top-8 of 64 SwiGLU experts).
 
 --backward times the layer's backward on the same workload instead (one
 step = the gradients of <dOut, out> + the auxiliary losses for one forward:
 combine, expert FFN, shared expert, gate, router and dispatch backward), with
 the expert FFN backward as the roofline kernel; it prints its own JSON line.
 
-A timed step is three parts (routing: router .. dispatch; the expert FFN;
-combine + statistics) with a HIP event between them on the layer's stream.
+A timed step is a few parts (routing: router, select, map; the routed up
+projection; the routed down projection; the shared expert; combine +
+statistics) with a HIP event between parts on the layer's stream, so the
+dominant kernel's launches are timed on their own inside the timed region.
 By default the library calls are launched one by one; --graph replays each
-part as a captured HIP graph instead (on this stack that measured slower:
-the graph launches cost more than the direct launches they replace).
+part as a captured HIP graph instead.
 
-Prints one JSON line: tokens/s over exactly K timed steps, the roofline of the
-dominant step (the expert FFN call, timed by the events around it), per-call
-times from eager steps run before the timed region, and the CPU oracle's
-throughput on the same workload for reference.
+Prints one JSON line: tokens/s over exactly K timed steps (wall clock), the
+median and p10/p90 step time from the events, the roofline of the dominant
+kernel (the routed up projection), the other GEMMs against their own
+rooflines, per-call times from eager steps run before the timed region, and
+the CPU oracle's throughput on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -47,26 +52,38 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix cores, TFLOP/s
 FP32_PEAK_TFLOPS = 157.3
+RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)      # FLOP per byte
 STAGES = ("router", "select", "build_map", "dispatch", "expert_ffn", "combine", "balance_stats")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expert_ffn_traffic.json")
 BW_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "expert_ffn_backward_traffic.json")
+
+
+def gemm_model(cfg, M, touched, f=None, experts=None):
+    """Compulsory bytes and FLOPs of the two FFN GEMMs (every weight of the
+    experts with rows read once, the token rows read once per assignment,
+    the output written once) and the hidden activation H that the up
+    projection writes and the down projection reads (not algorithmic: a
+    fused FFN would keep it on chip)."""
+    b = 2 if cfg.dtype == "bf16" else 4
+    d = cfg.d
+    f = cfg.f if f is None else f
+    E = touched if experts is None else experts
+    fr = 2 * f if cfg.act == "swiglu" else f
+    return {"up": {"bytes": E * fr * d * b + M * d * b, "flops": 2.0 * M * d * fr, "h_bytes": M * f * b},
+            "down": {"bytes": E * d * f * b + M * d * b, "flops": 2.0 * M * f * d, "h_bytes": M * f * b}}
 
 
 def algorithmic(cfg, k, M, touched=None):
     """Compulsory HBM bytes and FLOPs of each stage (each tensor touched once;
     the FFN reads the weights of the `touched` experts, those with rows)."""
     b = 2 if cfg.dtype == "bf16" else 4
-    n, d, E, f = cfg.n, cfg.d, cfg.E, cfg.f
+    n, d, E = cfg.n, cfg.d, cfg.E
     touched = E if touched is None else touched
-    w1r = 2 * f if cfg.act == "swiglu" else f
-    flops_ffn = 2.0 * M * d * w1r + 2.0 * M * f * d
-    bytes_ffn = touched * (w1r * d + d * f) * b + M * d * b + 2 * M * f * b + M * d * b
-    if cfg.shared_f:
-        sr = 2 * cfg.shared_f if cfg.act == "swiglu" else cfg.shared_f
-        flops_ffn += 2.0 * n * d * sr + 2.0 * n * cfg.shared_f * d
-        bytes_ffn += (sr * d + d * cfg.shared_f) * b + n * d * b + 2 * n * cfg.shared_f * b + n * d * b
+    g = gemm_model(cfg, M, touched)
+    bytes_ffn = g["up"]["bytes"] + g["down"]["bytes"]
+    flops_ffn = g["up"]["flops"] + g["down"]["flops"]
     ec = cfg.direction == "ec"
-    return {
+    out = {
         "router": dict(bytes=n * d * b + d * E * b + 4 * n * E * (2 if ec else 1), flops=2.0 * n * d * E),
         "select": dict(bytes=4 * n * E + 8 * (E * k if ec else n * k), flops=0.0),
         "build_map": dict(bytes=8 * M + 16 * M + 4 * n, flops=0.0),
@@ -75,6 +92,23 @@ def algorithmic(cfg, k, M, touched=None):
         "combine": dict(bytes=M * d * b + 2 * n * d * b + (n * d * b if cfg.shared_f else 0), flops=2.0 * M * d),
         "balance_stats": dict(bytes=4 * n * E, flops=0.0),
     }
+    if cfg.shared_f:
+        s = gemm_model(cfg, n, 1, f=cfg.shared_f, experts=1)
+        out["shared_expert"] = dict(bytes=s["up"]["bytes"] + s["down"]["bytes"],
+                                    flops=s["up"]["flops"] + s["down"]["flops"])
+    return out
+
+
+def grade(bytes_, flops, seconds, dtype="bf16"):
+    """Roofline of one kernel: HBM below the ridge (or for fp32 work), the
+    bf16 matrix cores above it."""
+    if flops / bytes_ < RIDGE or dtype != "bf16":
+        a = bytes_ / seconds / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4)}
+    a = flops / seconds / 1e12
+    return {"bound": "mfma", "achieved": round(a, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(a / BF16_PEAK_TFLOPS, 4)}
 
 
 def source_hash(files=("grouped_gemm.hip", "device_common.hpp", "kernels.hpp")):
@@ -86,18 +120,41 @@ def source_hash(files=("grouped_gemm.hip", "device_common.hpp", "kernels.hpp")):
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(cfg, inp, w1_host, w2_host):
-    """The CPU oracle, as it is, on one full forward of the same workload."""
+def host_cpu():
+    """(threads this process may run on, CPU model name)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
+
+
+def cpu_baseline(cfg, inp, w1_host, w2_host, budget_s=30.0):
+    """The CPU oracle, as it is, on the same workload: one full layer forward
+    (router, selection, map, every expert's FFN with its weights widened one
+    expert at a time, shared expert, combine, statistics) on all the host
+    threads this process may use."""
     import threadpoolctl
     from oracle import moe_oracle as O
-    info = threadpoolctl.threadpool_info()
-    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-    t0 = time.perf_counter()
-    O.forward(cfg, dict(inp, w1=w1_host, w2=w2_host))
-    dt = time.perf_counter() - t0
-    return {"value": cfg.n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"one full layer forward of the same workload (n={cfg.n}), {dt:.2f} s "
-                      f"of host time, numpy/OpenBLAS float64"}
+    threads, model = host_cpu()
+    with threadpoolctl.threadpool_limits(threads):
+        t0 = time.perf_counter()
+        O.forward(cfg, dict(inp, w1=w1_host, w2=w2_host))
+        dt = time.perf_counter() - t0
+    return {"value": round(cfg.n / dt, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu": model,
+            "sample": f"one full layer forward of the same workload (all n={cfg.n} tokens), {dt:.1f} s of "
+                      f"host time, numpy float64 with {threads} BLAS threads, expert weights widened one "
+                      f"expert at a time"}
 
 
 def main():
@@ -105,11 +162,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="2",
-                    help="workload 1..5 (default 2, the headline one) or 'decode' (64 tokens, top-8)")
+    ap.add_argument("--config", default="5",
+                    help="workload 1..5 (default 5, the largest) or 'decode' (64 tokens, top-8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
-                    help="time HIP-graph replays of the three parts instead of direct launches")
+                    help="time HIP-graph replays of the parts instead of direct launches")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--backward", action="store_true",
@@ -117,7 +174,8 @@ def main():
                          "instead of the forward")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "the benchmark runs on one GPU only (the library has no multi-GPU path); --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only (the library has no multi-GPU path); "
+                                   "--gpus must be 1"}))
         sys.exit(2)
 
     import torch
@@ -163,8 +221,6 @@ def main():
 
     w = layer.w
     tc = layer.rcfg.dir == N.MOE_TOKEN_CHOICE
-    # the step in three parts: routing (router .. dispatch), the expert FFN,
-    # and combine + statistics; each part is one or more library calls
     calls_route = [
         lambda: N.moe_router(x, w["wg"], w.get("logit_offset"), layer.rcfg, layer.logits, None,
                              None if tc else layer.scores_t, layer.ws_router),
@@ -174,95 +230,126 @@ def main():
         # packed weights: the up GEMM gathers the rows itself (no call here)
         lambda: None if layer.packed else layer.dispatch(x),
     ]
-
-    def ffn_part():
-        layer.expert_ffn(x)
-
     calls_post = [lambda: layer.combine(x, residual=True), lambda: layer.balance_stats()]
-    parts = [lambda: [c() for c in calls_route], ffn_part, lambda: [c() for c in calls_post]]
+    # the step in parts, one HIP event after each: routing; on packed
+    # weights the routed up projection (the dominant kernel, one launch) and
+    # down projection (one launch) on their own, then the shared expert;
+    # combine + statistics
+    if layer.packed:
+        parts = {"route": lambda: [c() for c in calls_route],
+                 "routed_up": lambda: layer.routed_up(x),
+                 "routed_down": lambda: layer.routed_down(),
+                 "shared_expert": lambda: layer.shared_expert(x),
+                 "combine_stats": lambda: [c() for c in calls_post]}
+        if not layer.shared:
+            del parts["shared_expert"]
+    else:
+        parts = {"route": lambda: [c() for c in calls_route],
+                 "expert_ffn": lambda: layer.expert_ffn(x),
+                 "combine_stats": lambda: [c() for c in calls_post]}
+    names = list(parts)
+    fns = [parts[k] for k in names]
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        for p in parts:
+        for p in fns:
             p()
     torch.cuda.synchronize()
 
-    # per-stage breakdown: eager steps with an event after every call
+    # per-call breakdown: eager steps with an event after every call
     # (before the timed region)
     n_diag = min(args.steps, 20)
-    diag = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(n_diag)]
+    calls = calls_route + [lambda: layer.expert_ffn(x)] + calls_post
+    diag = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(n_diag)]
     for ev in diag:
         ev[0].record(stream)
-        for j, c in enumerate(calls_route + [ffn_part] + calls_post):
+        for j, c in enumerate(calls):
             c()
             ev[j + 1].record(stream)
     torch.cuda.synchronize()
     stage_ms = {s: [ev[j].elapsed_time(ev[j + 1]) for ev in diag] for j, s in enumerate(STAGES)}
 
     if args.graph:
-        # each part captured once into a HIP graph; a timed step is three
-        # graph launches
         graphs = []
-        for p in parts:
+        for p in fns:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 p()
             graphs.append(g)
-        parts = [g.replay for g in graphs]
+        fns = [g.replay for g in graphs]
         for _ in range(args.warmup):
-            for p in parts:
+            for p in fns:
                 p()
         torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for ev in events:
         ev[0].record(stream)
-        for j, p in enumerate(parts):
+        for j, p in enumerate(fns):
             p()
             ev[j + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     print(f"[bench] timed {args.steps} steps in {elapsed:.4f}s "
           f"({'HIP graphs' if args.graph else 'direct launches'})", file=sys.stderr, flush=True)
-    seg_ms = [float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events])) for j in range(3)]
+    part_ms = {k: [ev[j].elapsed_time(ev[j + 1]) for ev in events] for j, k in enumerate(names)}
+    step_ms = np.array([ev[0].elapsed_time(ev[-1]) for ev in events])
 
     k = layer.k
     M = int(layer.map.n_kept.item())
     touched = int((layer.map.expert_offset.diff() > 0).sum().item())
     alg = algorithmic(cfg, k, M, touched)
+    gm = gemm_model(cfg, M, touched)
     stages = {}
     for s in STAGES:
         if s == "dispatch" and layer.packed:
-            stages[s] = {"fused": "into expert_ffn: the up GEMM gathers X rows through slot_token"}
+            stages[s] = {"fused": "into the routed up projection: it gathers X rows through slot_token"}
             continue
-        ms = float(np.mean(stage_ms[s]))
+        ms = float(np.median(stage_ms[s]))
         a = alg[s]
         stages[s] = {"us": round(ms * 1e3, 2), "GB/s": round(a["bytes"] / (ms * 1e-3) / 1e9, 1),
                      "hbm_frac": round(a["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         if a["flops"]:
             stages[s]["TFLOP/s"] = round(a["flops"] / (ms * 1e-3) / 1e12, 1)
-    ffn_ms = seg_ms[1]                     # the FFN part of the timed steps
-    ffn = alg["expert_ffn"]
-    intensity = ffn["flops"] / ffn["bytes"]
-    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    traffic = stored_traffic(TRAFFIC_FILE, source_hash(), cfg.name)
-    if intensity < ridge or cfg.dtype != "bf16":
-        achieved = ffn["bytes"] / (ffn_ms * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
-    else:
-        achieved = ffn["flops"] / (ffn_ms * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
-    roofline["kernel"] = ("moe_expert_ffn_packed" if layer.packed else "moe_expert_ffn") + \
-        " (grouped GEMM: up projection + activation, down projection)"
-    roofline["algorithmic_bytes"] = int(ffn["bytes"])
-    roofline["flops"] = ffn["flops"]
-    roofline["avg_us"] = round(ffn_ms * 1e3, 2)
 
-    ms_per_step = elapsed / args.steps * 1e3
+    kernels = {}
+    if layer.packed:
+        # the dominant kernel: the routed up projection (one launch per step)
+        up_s = float(np.mean(part_ms["routed_up"])) * 1e-3
+        roofline = grade(gm["up"]["bytes"], gm["up"]["flops"], up_s, cfg.dtype)
+        roofline.update({
+            "traffic": stored_traffic(TRAFFIC_FILE, source_hash(), cfg.name, "routed_up"),
+            "kernel": "moe_expert_up_packed: routed experts' up projection + activation (one launch of "
+                      "the weight-streaming grouped GEMM, the dispatch gather fused into its row loads)",
+            "algorithmic_bytes": int(gm["up"]["bytes"]), "flops": gm["up"]["flops"],
+            "h_bytes_written": int(gm["up"]["h_bytes"]), "avg_us": round(up_s * 1e6, 2)})
+        dn_s = float(np.mean(part_ms["routed_down"])) * 1e-3
+        kernels["routed_down"] = dict(grade(gm["down"]["bytes"], gm["down"]["flops"], dn_s, cfg.dtype),
+                                      avg_us=round(dn_s * 1e6, 2), algorithmic_bytes=int(gm["down"]["bytes"]),
+                                      h_bytes_read=int(gm["down"]["h_bytes"]))
+        ffn_s = up_s + dn_s
+        kernels["routed_ffn"] = dict(grade(gm["up"]["bytes"] + gm["down"]["bytes"],
+                                           gm["up"]["flops"] + gm["down"]["flops"], ffn_s, cfg.dtype),
+                                     avg_us=round(ffn_s * 1e6, 2),
+                                     algorithmic_bytes=int(gm["up"]["bytes"] + gm["down"]["bytes"]),
+                                     h_round_trip_bytes=int(2 * gm["up"]["h_bytes"]))
+        if layer.shared:
+            sm = gemm_model(cfg, cfg.n, 1, f=cfg.shared_f, experts=1)
+            sh_s = float(np.mean(part_ms["shared_expert"])) * 1e-3
+            kernels["shared_expert"] = dict(grade(sm["up"]["bytes"] + sm["down"]["bytes"],
+                                                  sm["up"]["flops"] + sm["down"]["flops"], sh_s, cfg.dtype),
+                                            avg_us=round(sh_s * 1e6, 2),
+                                            flops=sm["up"]["flops"] + sm["down"]["flops"])
+    else:
+        ffn_s = float(np.mean(part_ms["expert_ffn"])) * 1e-3
+        ffn = alg["expert_ffn"]
+        roofline = grade(ffn["bytes"], ffn["flops"], ffn_s, cfg.dtype)
+        roofline.update({"traffic": None, "kernel": "moe_expert_ffn (dispatch + grouped FFN, fp32)",
+                         "algorithmic_bytes": int(ffn["bytes"]), "flops": ffn["flops"],
+                         "avg_us": round(ffn_s * 1e6, 2)})
+
     line = {
         "metric": "MoE-layer fwd tokens/sec at 1 MI355X; % peak HBM (route/dispatch) & MFMA (experts)",
         "value": round(cfg.n * args.steps / elapsed, 1),
@@ -270,23 +357,28 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded normals; random-init weights of the stated shapes)",
         "config": {"workload": cfg.name, "n": cfg.n, "d": cfg.d, "E": cfg.E, "f": cfg.f, "act": cfg.act,
-                   "direction": cfg.direction, "k": k, "kept_assignments": M, "experts_touched": touched,
-                   "parallelism": "single GPU",
+                   "direction": cfg.direction, "score": cfg.score, "k": k, "shared_f": cfg.shared_f,
+                   "kept_assignments": M, "experts_touched": touched, "parallelism": "single GPU",
                    "weights": ("packed operand order, packed once at load in %.1f ms (not timed per step)"
                                % pack_ms) if layer.packed else "natural [E, rows, K] layout"},
+        "step_ms": {"median": round(float(np.median(step_ms)), 4),
+                    "p10": round(float(np.percentile(step_ms, 10)), 4),
+                    "p90": round(float(np.percentile(step_ms, 90)), 4),
+                    "tokens_per_s_at_median": round(cfg.n / (float(np.median(step_ms)) * 1e-3), 1)},
         "roofline": roofline,
+        "kernels": kernels,
         "mode": "hip_graph" if args.graph else "eager",
-        "parts_us": {"route": round(seg_ms[0] * 1e3, 2), "expert_ffn": round(seg_ms[1] * 1e3, 2),
-                     "combine_stats": round(seg_ms[2] * 1e3, 2)},
+        "parts_us": {k_: round(float(np.mean(v)) * 1e3, 2) for k_, v in part_ms.items()},
         "stages": stages,
-        "stages_note": f"per-call breakdown from {n_diag} eager steps before the timed region",
+        "stages_note": f"per-call medians from {n_diag} eager steps before the timed region "
+                       f"(expert_ffn = routed experts + shared expert)",
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -294,14 +386,15 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def stored_traffic(path, src_hash, workload):
-    """Measured HBM bytes per call from a counter summary in profiles/, or
-    None when it was taken on other sources or another workload."""
+def stored_traffic(path, src_hash, workload, kernel=None):
+    """Measured HBM bytes per launch from a counter summary in profiles/, or
+    None when it was taken on other sources, another workload or another
+    kernel."""
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         tr = json.load(fh)
-    if tr.get("source_hash") == src_hash and tr.get("workload") == workload:
+    if tr.get("source_hash") == src_hash and tr.get("workload") == workload and tr.get("kernel") == kernel:
         return tr.get("bytes_per_launch")
     return None
 

@@ -13,6 +13,8 @@
  *   Y[e] = Expert_e(X_in[e])                            moe_expert_ffn
  *     (bf16, packed weights, dispatch fused in)         moe_pack_expert_weights,
  *                                                       moe_expert_ffn_packed
+ *     (its up and down projections one by one)          moe_expert_up_packed,
+ *                                                       moe_expert_down_packed
  *   out = residual + shared + scatter_add(G * Y, I)     moe_combine
  *   load-balance loss, z-loss, MaxVio                   moe_balance_stats
  *   loss-free balancing: bias step from the loads       moe_update_bias
@@ -281,6 +283,24 @@ moe_status_t moe_expert_ffn_packed(const void *X, int32_t n_x, const int32_t *ro
                                    const int32_t *expert_offset, int32_t E, int32_t d, int32_t f, int32_t act,
                                    const void *W1_packed, const void *W2_packed, int64_t M_max, void *Y_perm,
                                    void *ws, size_t ws_bytes, void *stream);
+
+/* The two grouped GEMMs of moe_expert_ffn_packed as separate calls (page 2
+ * "The math": Y[e] = Expert_e(X_in[e]); the expert is an up projection with
+ * its activation, then a down projection), for a caller that keeps the
+ * hidden activation or runs the projections one at a time:
+ *   moe_expert_up_packed:   H [M_max, f] = act(X_in W1_e^T) per expert, the
+ *     rows of X taken as in moe_expert_ffn_packed (through row_index when
+ *     given), fp32 accumulation, H rounded once to bf16;
+ *   moe_expert_down_packed: Y_perm [M_max, d] = H W2_e^T per expert.
+ * Rows of H / Y_perm at or past expert_offset[E] are left untouched.  The two
+ * calls in sequence write the same bits as moe_expert_ffn_packed.  bf16
+ * tensors, 16-byte aligned; the same shape rules as moe_expert_ffn_packed; H
+ * must not alias X, Y_perm must not alias H.  No workspace. */
+moe_status_t moe_expert_up_packed(const void *X, int32_t n_x, const int32_t *row_index,
+                                  const int32_t *expert_offset, int32_t E, int32_t d, int32_t f, int32_t act,
+                                  const void *W1_packed, int64_t M_max, void *H, void *stream);
+moe_status_t moe_expert_down_packed(const void *H, const int32_t *expert_offset, int32_t E, int32_t d, int32_t f,
+                                    const void *W2_packed, int64_t M_max, void *Y_perm, void *stream);
 
 /* Combine out = scatter_add(G * Y, I) (page 2 "The math"), the gate applied
  * to the expert output: for every token, out = residual + shared_out + sum

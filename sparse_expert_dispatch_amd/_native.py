@@ -32,6 +32,7 @@ EXPORTED = ("moe_ec_k", "moe_tc_capacity", "moe_max_slots", "moe_token_list_len"
             "moe_route_workspace_size", "moe_ffn_workspace_size", "moe_router", "moe_select",
             "moe_build_map", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_balance_stats",
             "moe_update_bias", "moe_pack_expert_weights", "moe_expert_ffn_packed",
+            "moe_expert_up_packed", "moe_expert_down_packed",
             "moe_combine_backward", "moe_ffn_backward_workspace_size", "moe_expert_ffn_backward",
             "moe_gate_backward", "moe_router_backward_workspace_size", "moe_router_backward",
             "moe_dispatch_backward", "moe_status_string", "moe_last_error")
@@ -90,6 +91,8 @@ def lib() -> ctypes.CDLL:
         "moe_update_bias": (I32, [P, CFG, F32, P, P]),
         "moe_pack_expert_weights": (I32, [P, I32, I32, I32, I32, P, P]),
         "moe_expert_ffn_packed": (I32, [P, I32, P, P, I32, I32, I32, I32, P, P, I64, P, P, SZ, P]),
+        "moe_expert_up_packed": (I32, [P, I32, P, P, I32, I32, I32, I32, P, I64, P, P]),
+        "moe_expert_down_packed": (I32, [P, P, I32, I32, I32, P, I64, P, P]),
         "moe_combine_backward": (I32, [P, P, I32, I32, I32, MAP, I64, P, P, P]),
         "moe_ffn_backward_workspace_size": (I32, [I64, I32, I32, I32, I32, I32, SZP]),
         "moe_expert_ffn_backward": (I32, [P, I32, P, I32, I32, I32, I32, P, P, P, I64, P, P, P, P, SZ, P]),
@@ -345,6 +348,35 @@ def moe_expert_ffn_packed(x, expert_offset, w1p, w2p, act: int, y_perm, ws, stre
                                        _ptr(w2p, "w2_packed", bf), M_max,
                                        _ptr(y_perm, "y_perm", bf), w, wb, _stream(stream)),
            "moe_expert_ffn_packed")
+
+
+def moe_expert_up_packed(x, expert_offset, w1p, act: int, h, stream=None, row_index=None, m_max=None):
+    """Up projection + activation on packed weights: h [M_max, f] (bf16).
+    row_index / m_max as in moe_expert_ffn_packed."""
+    E = expert_offset.numel() - 1
+    d = x.shape[1]
+    f = h.shape[1]
+    M_max = int(m_max if m_max is not None else (h.shape[0] if row_index is not None else x.shape[0]))
+    bf = _elem_dtypes(MOE_BF16)
+    _check(lib().moe_expert_up_packed(_ptr(x, "x", bf), int(x.shape[0]),
+                                      _ptr(row_index, "row_index", _I32) if row_index is not None else None,
+                                      _ptr(expert_offset, "expert_offset", _I32), int(E), int(d), int(f),
+                                      int(act), _ptr(w1p, "w1_packed", bf), M_max, _ptr(h, "h", bf),
+                                      _stream(stream)),
+           "moe_expert_up_packed")
+
+
+def moe_expert_down_packed(h, expert_offset, w2p, y_perm, stream=None, m_max=None):
+    """Down projection on packed weights: y_perm = h W2^T per expert."""
+    E = expert_offset.numel() - 1
+    f = h.shape[1]
+    d = y_perm.shape[1]
+    M_max = int(m_max if m_max is not None else h.shape[0])
+    bf = _elem_dtypes(MOE_BF16)
+    _check(lib().moe_expert_down_packed(_ptr(h, "h", bf), _ptr(expert_offset, "expert_offset", _I32), int(E),
+                                        int(d), int(f), _ptr(w2p, "w2_packed", bf), M_max,
+                                        _ptr(y_perm, "y_perm", bf), _stream(stream)),
+           "moe_expert_down_packed")
 
 
 def moe_combine(y_perm, rmap: RouteMap, n: int, residual, shared_out, out, stream=None):

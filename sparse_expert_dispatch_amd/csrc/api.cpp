@@ -308,6 +308,45 @@ moe_status_t moe_expert_ffn_packed(const void* X, int32_t n_x, const int32_t* ro
                   "moe_expert_ffn_packed");
 }
 
+// Shape rules shared by the packed FFN calls.
+static moe_status_t check_packed_ffn(int32_t E, int32_t d, int32_t f, int64_t M_max) {
+  REQUIRE(E > 0 && d > 0 && f > 0 && M_max >= 0, "E, d, f must be positive, M_max non-negative");
+  REQUIRE(M_max <= INT32_MAX, "M_max must fit in int32");
+  SUPPORTED(E <= moe::kMaxExperts, "bf16 expert FFN supports E <= %d (E=%d)", moe::kMaxExperts, E);
+  SUPPORTED(d % 64 == 0 && f % 64 == 0, "bf16 expert FFN needs d %% 64 == 0 and f %% 64 == 0 (d=%d f=%d)",
+            d, f);
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_up_packed(const void* X, int32_t n_x, const int32_t* row_index,
+                                  const int32_t* expert_offset, int32_t E, int32_t d, int32_t f, int32_t act,
+                                  const void* W1_packed, int64_t M_max, void* H, void* stream) {
+  moe_status_t st = check_packed_ffn(E, d, f, M_max);
+  if (st != MOE_OK) return st;
+  if (M_max == 0) return MOE_OK;
+  REQUIRE(X && expert_offset && W1_packed && H, "tensor arguments must be non-NULL");
+  REQUIRE(!row_index || n_x > 0, "n_x must be positive when row_index is given");
+  REQUIRE(act == MOE_GELU || act == MOE_SWIGLU, "act must be MOE_GELU or MOE_SWIGLU");
+  REQUIRE(aligned16(X) && aligned16(W1_packed) && aligned16(H), "bf16 tensors must be 16-byte aligned");
+  REQUIRE(H != X, "H must not alias X");
+  return launched(moe::launch_expert_gemm(1, X, row_index, n_x, expert_offset, E, d, f, act, W1_packed, M_max, H,
+                                          true, as_stream(stream)),
+                  "moe_expert_up_packed");
+}
+
+moe_status_t moe_expert_down_packed(const void* H, const int32_t* expert_offset, int32_t E, int32_t d, int32_t f,
+                                    const void* W2_packed, int64_t M_max, void* Y_perm, void* stream) {
+  moe_status_t st = check_packed_ffn(E, d, f, M_max);
+  if (st != MOE_OK) return st;
+  if (M_max == 0) return MOE_OK;
+  REQUIRE(H && expert_offset && W2_packed && Y_perm, "tensor arguments must be non-NULL");
+  REQUIRE(aligned16(H) && aligned16(W2_packed) && aligned16(Y_perm), "bf16 tensors must be 16-byte aligned");
+  REQUIRE(H != Y_perm, "Y_perm must not alias H");
+  return launched(moe::launch_expert_gemm(2, H, nullptr, (int)M_max, expert_offset, E, d, f, MOE_GELU, W2_packed,
+                                          M_max, Y_perm, true, as_stream(stream)),
+                  "moe_expert_down_packed");
+}
+
 moe_status_t moe_combine(const void* Y_perm, int32_t dtype, const moe_route_map_t* map, int32_t n,
                          int32_t d, const void* residual, const void* shared_out, void* out,
                          void* stream) {

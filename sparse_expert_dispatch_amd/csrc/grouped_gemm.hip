@@ -793,63 +793,78 @@ hipError_t launch_pack_weights(const void* W, int E, int R, int K, int gate_up, 
   return hipGetLastError();
 }
 
+// One grouped GEMM of the FFN on bf16: the up projection (stage 1: A = the
+// token rows, through row_index when given; B = W1; activation epilogue; C =
+// H [M_max, f]) or the down projection (stage 2: A = H; B = W2; C = Y_perm).
+static void launch_ffn_gemm_bf16(int stage, const bf16_t* a, const int32_t* row_index, int n_a,
+                                 const int32_t* expert_offset, int E, int d, int f, int act, const bf16_t* b,
+                                 int64_t M_max, bf16_t* c, bool packed, hipStream_t stream) {
+  // few rows per expert: the GEMMs stream weights, walk M tiles innermost
+#if MOE_GEMM_ORDER < 0
+  const int mt_inner = M_max <= (int64_t)E * 4 * kBM ? 1 : 0;
+#else
+  const int mt_inner = MOE_GEMM_ORDER;
+#endif
+  // Weight-streaming shapes (few rows per expert, M tiles innermost)
+  // measured best with 128 x 128 tiles and two double-buffered workgroups
+  // per CU; shapes with many rows per expert (matrix-core bound) with
+  // 128 x 256 tiles (a quarter fewer LDS bytes per MFMA) and one LDS copy,
+  // two workgroups per CU (8-10% faster there, slower on weight streaming).
+  const bool two_bufs = mt_inner != 0;
+  // a_index / n_a: rows of A gathered through an index (the up GEMM with a
+  // fused dispatch) or nullptr (A's rows are the slots)
+  auto gemm = [&](auto dual, auto epi, int N, int K) {
+    constexpr bool kD = decltype(dual)::value;
+    constexpr int kE = decltype(epi)::value;
+    const int nk = K / kBK;
+    if (packed && mt_inner && nk % MOE_STREAM_DEPTH == 0) {
+      launch_persistent<stream_gemm_bf16_kernel<kD, kE, MOE_STREAM_DEPTH>>(stream, a, row_index, n_a, b,
+                                                                            expert_offset, E, N, K, c);
+    } else if (two_bufs) {
+      if (packed)
+        launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 2, MOE_GEMM_NB_STREAM, true>>(
+            stream, a, row_index, n_a, b, expert_offset, E, N, K, mt_inner, c);
+      else
+        launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 2, MOE_GEMM_NB_STREAM, false>>(
+            stream, a, row_index, n_a, b, expert_offset, E, N, K, mt_inner, c);
+    } else {
+      if (packed)
+        launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 1, MOE_GEMM_NB_MFMA, true>>(
+            stream, a, row_index, n_a, b, expert_offset, E, N, K, mt_inner, c);
+      else
+        launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 1, MOE_GEMM_NB_MFMA, false>>(
+            stream, a, row_index, n_a, b, expert_offset, E, N, K, mt_inner, c);
+    }
+  };
+  using std::integral_constant;
+  if (stage == 1) {
+    if (act == 1)
+      gemm(integral_constant<bool, true>{}, integral_constant<int, kEpiSwiglu>{}, f, d);
+    else
+      gemm(integral_constant<bool, false>{}, integral_constant<int, kEpiGelu>{}, f, d);
+  } else {
+    gemm(integral_constant<bool, false>{}, integral_constant<int, kEpiNone>{}, d, f);
+  }
+}
+
+hipError_t launch_expert_gemm(int stage, const void* A, const int32_t* row_index, int n_a,
+                              const int32_t* expert_offset, int E, int d, int f, int act, const void* W,
+                              int64_t M_max, void* C, bool packed, hipStream_t stream) {
+  launch_ffn_gemm_bf16(stage, static_cast<const bf16_t*>(A), row_index, n_a, expert_offset, E, d, f, act,
+                       static_cast<const bf16_t*>(W), M_max, static_cast<bf16_t*>(C), packed, stream);
+  return hipGetLastError();
+}
+
 hipError_t launch_expert_ffn(const void* X_perm, const int32_t* row_index, int n_x, int dtype,
                              const int32_t* expert_offset, int E, int d, int f, int act, const void* W1,
                              const void* W2, int64_t M_max, void* Y_perm, void* ws, bool packed,
                              hipStream_t stream) {
-  char* w = static_cast<char*>(ws);
-  void* H = w;
+  void* H = ws;
   if (dtype == 1) {
-    const bf16_t* x = static_cast<const bf16_t*>(X_perm);
-    bf16_t* h = static_cast<bf16_t*>(H);
-    // few rows per expert: the GEMMs stream weights, walk M tiles innermost
-#if MOE_GEMM_ORDER < 0
-    const int mt_inner = M_max <= (int64_t)E * 4 * kBM ? 1 : 0;
-#else
-    const int mt_inner = MOE_GEMM_ORDER;
-#endif
-    // Weight-streaming shapes (few rows per expert, M tiles innermost)
-    // measured best with 128 x 128 tiles and two double-buffered workgroups
-    // per CU; shapes with many rows per expert (matrix-core bound) with
-    // 128 x 256 tiles (a quarter fewer LDS bytes per MFMA) and one LDS copy,
-    // two workgroups per CU (8-10% faster there, slower on weight streaming).
-    const bool two_bufs = mt_inner != 0;
-    // a_index / n_a: rows of A gathered through an index (the up GEMM with a
-    // fused dispatch) or nullptr (A's rows are the slots)
-    auto gemm = [&](auto dual, auto epi, const bf16_t* a, const int32_t* a_index, int n_a, const bf16_t* b,
-                    int N, int K, bf16_t* c) {
-      constexpr bool kD = decltype(dual)::value;
-      constexpr int kE = decltype(epi)::value;
-      const int nk = K / kBK;
-      if (packed && mt_inner && nk % MOE_STREAM_DEPTH == 0) {
-        launch_persistent<stream_gemm_bf16_kernel<kD, kE, MOE_STREAM_DEPTH>>(stream, a, a_index, n_a, b,
-                                                                              expert_offset, E, N, K, c);
-      } else if (two_bufs) {
-        if (packed)
-          launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 2, MOE_GEMM_NB_STREAM, true>>(
-              stream, a, a_index, n_a, b, expert_offset, E, N, K, mt_inner, c);
-        else
-          launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 2, MOE_GEMM_NB_STREAM, false>>(
-              stream, a, a_index, n_a, b, expert_offset, E, N, K, mt_inner, c);
-      } else {
-        if (packed)
-          launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 1, MOE_GEMM_NB_MFMA, true>>(
-              stream, a, a_index, n_a, b, expert_offset, E, N, K, mt_inner, c);
-        else
-          launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 1, MOE_GEMM_NB_MFMA, false>>(
-              stream, a, a_index, n_a, b, expert_offset, E, N, K, mt_inner, c);
-      }
-    };
-    using std::integral_constant;
-    const int n_h = (int)M_max;
-    if (act == 1)
-      gemm(integral_constant<bool, true>{}, integral_constant<int, kEpiSwiglu>{}, x, row_index, n_x,
-           static_cast<const bf16_t*>(W1), f, d, h);
-    else
-      gemm(integral_constant<bool, false>{}, integral_constant<int, kEpiGelu>{}, x, row_index, n_x,
-           static_cast<const bf16_t*>(W1), f, d, h);
-    gemm(integral_constant<bool, false>{}, integral_constant<int, kEpiNone>{}, h, nullptr, n_h,
-         static_cast<const bf16_t*>(W2), d, f, static_cast<bf16_t*>(Y_perm));
+    launch_ffn_gemm_bf16(1, static_cast<const bf16_t*>(X_perm), row_index, n_x, expert_offset, E, d, f, act,
+                         static_cast<const bf16_t*>(W1), M_max, static_cast<bf16_t*>(H), packed, stream);
+    launch_ffn_gemm_bf16(2, static_cast<const bf16_t*>(H), nullptr, (int)M_max, expert_offset, E, d, f, act,
+                         static_cast<const bf16_t*>(W2), M_max, static_cast<bf16_t*>(Y_perm), packed, stream);
   } else {
     const int64_t up = M_max * f, down = M_max * d;
     hipLaunchKernelGGL(ffn_up_f32_kernel, dim3((unsigned)((up + 255) / 256)), dim3(256), 0, stream,

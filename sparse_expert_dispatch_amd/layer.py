@@ -82,6 +82,9 @@ class MoELayer:
             if not bf16:
                 raise ValueError("packed expert weights are bf16 only")
             self.w1p, self.w2p = N.pack_ffn_weights(weights["w1"], weights["w2"], self.act)
+            # the routed experts' hidden activation H [M_max, f] (bf16), in
+            # the FFN workspace
+            self.h = self.ws_ffn.view(torch.bfloat16)[:self.M_max * cfg.f].view(self.M_max, cfg.f)
             if self.shared:
                 self.shared_w1p, self.shared_w2p = N.pack_ffn_weights(weights["shared_w1"],
                                                                       weights["shared_w2"], self.act)
@@ -111,17 +114,32 @@ class MoELayer:
             self.dispatch(x, stream)
         self.expert_ffn(x, stream)
 
+    def routed_up(self, x, stream=None):
+        """Packed weights: the routed experts' up projection + activation into
+        H, its rows gathered from x through the map's slot_token (the
+        dispatch fused in)."""
+        N.moe_expert_up_packed(x, self.map.expert_offset, self.w1p, self.act, self.h, stream,
+                               row_index=self.map.slot_token, m_max=self.M_max)
+
+    def routed_down(self, stream=None):
+        """Packed weights: the routed experts' down projection, H -> Y_perm."""
+        N.moe_expert_down_packed(self.h, self.map.expert_offset, self.w2p, self.y_perm, stream)
+
+    def shared_expert(self, x, stream=None):
+        """The always-on shared expert on every token (packed weights)."""
+        N.moe_expert_ffn_packed(x, self.shared_offsets, self.shared_w1p, self.shared_w2p, self.act,
+                                self.shared_out, self.ws_shared, stream)
+
     def expert_ffn(self, x, stream=None):
         """The routed experts (and the shared expert on x).  Packed weights:
         the up GEMM gathers its rows from x through the map's slot_token
         (dispatch fused in); otherwise it reads the dispatched X_perm."""
         w = self.w
         if self.packed:
-            N.moe_expert_ffn_packed(x, self.map.expert_offset, self.w1p, self.w2p, self.act, self.y_perm,
-                                    self.ws_ffn, stream, row_index=self.map.slot_token, m_max=self.M_max)
+            self.routed_up(x, stream)
+            self.routed_down(stream)
             if self.shared:
-                N.moe_expert_ffn_packed(x, self.shared_offsets, self.shared_w1p, self.shared_w2p, self.act,
-                                        self.shared_out, self.ws_shared, stream)
+                self.shared_expert(x, stream)
             return
         N.moe_expert_ffn(self.x_perm, self.map.expert_offset, w["w1"], w["w2"], self.act,
                          self.y_perm, self.ws_ffn, stream)

@@ -5,8 +5,10 @@ with the CPU oracle run on the same seeded inputs.
 Selection, routing maps, drop sets and permutations must match bit for bit
 given the device's fp32 logits (the oracle is run with those logits
 injected).  Logits must match within 1e-5 relative to each row's largest
-magnitude.  Expert outputs and layer outputs in bf16 must match within
-max-abs 2e-2 x RMS of the oracle's value; fp32 layers within 1e-4 x RMS."""
+magnitude.  bf16 expert outputs, the MoE branch (residual = NULL) and
+residual + branch must each lie, element by element, within the bound
+derived from the device's rounding points (tests/bounds.py); fp32 layers
+within 1e-4 x RMS of the branch."""
 from __future__ import annotations
 
 import sys
@@ -19,8 +21,9 @@ from oracle import moe_oracle as O
 from sparse_expert_dispatch_amd import _native as N
 from sparse_expert_dispatch_amd.layer import MoELayer, to_device
 
+from bounds import check_branch, check_layer_rows
+
 LOGIT_RTOL = 1e-5
-BF16_TOL = 2e-2
 F32_TOL = 1e-4
 
 
@@ -100,28 +103,6 @@ def max_rel_rms(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.abs(got - ref).max() / rms) if rms > 0 else float(np.abs(got - ref).max())
 
 
-def check_expert_rows(y_dev: np.ndarray, xe: np.ndarray, w1: np.ndarray, w2: np.ndarray, act: str,
-                      bf16: bool, what: str):
-    """Device expert outputs against the oracle, element by element, within
-    the bound of the device's arithmetic.  bf16: the hidden activation and
-    the output are each rounded once to bf16 (relative error <= 2^-8), so
-    |y_dev - y| <= 2^-8 |y| + 2^-8 (|h| |W2|^T), with 5% slack for the fp32
-    accumulations and the activation functions.  fp32: 1e-4 x RMS."""
-    h = O.expert_hidden(xe, w1, act)
-    W2 = widen(w2)
-    y = h @ W2.T
-    got = widen(y_dev)
-    if not bf16:
-        err = max_rel_rms(got, y)
-        assert err <= F32_TOL, f"{what}: max-abs / RMS = {err:.3g}"
-        return
-    u = 2.0 ** -8
-    bound = 1.05 * (u * np.abs(y) + u * (np.abs(h) @ np.abs(W2).T)) + 1e-6 * np.sqrt((y ** 2).mean())
-    excess = np.abs(got - y) - bound
-    assert excess.max() <= 0, f"{what}: error exceeds the rounding bound by {excess.max():.3g} " \
-                              f"(max-abs / RMS {max_rel_rms(got, y):.3g})"
-
-
 def check_map(g: dict, ref_map: dict):
     nk = int(ref_map["n_kept"])
     assert g["n_kept"] == nk
@@ -145,7 +126,6 @@ def compare_all(cfg, inp: dict, g: dict, full_ffn: bool = True, sample_tokens=No
     check_logits(g["logits"], z_ref)
     z = g["logits"]
     bf16 = cfg.dtype == "bf16"
-    tol = BF16_TOL if bf16 else F32_TOL
 
     if cfg.direction == "tc":
         idx, gate = O.select_token_choice(z, cfg.k, cfg.score, inp.get("sel_bias"), cfg.n_group,
@@ -171,50 +151,36 @@ def compare_all(cfg, inp: dict, g: dict, full_ffn: bool = True, sample_tokens=No
 
     w1_of = lambda e: inp["w1"][e]
     w2_of = lambda e: inp["w2"][e]
-    shared = None
     if full_ffn:
+        tokens = np.arange(cfg.n)
+    else:
+        tokens = np.asarray(sample_tokens)
+    nt = len(tokens)
+    if bf16:
+        # every expert output within the bound of its rounding points, and the
+        # branch (residual = NULL) within the bound composed from those
+        # through the gates and the combine's rounding (tests/bounds.py)
+        bb, worst = check_layer_rows(cfg, inp, rmap, tokens, g["y_perm"], g.get("shared"), progress=log)
+        if full_ffn:
+            # the composed branch is the oracle's: its grouped FFN and combine
+            y_ref = O.expert_ffn(inp["x"][rmap["slot_token"]], rmap["expert_offset"], w1_of, w2_of, cfg.act)
+            shared = (O.expert_forward(inp["x"], inp["shared_w1"], inp["shared_w2"], cfg.act)
+                      if cfg.shared_f else None)
+            branch = O.combine(y_ref, rmap["slot_gate"], rmap["token_offset"], rmap["token_slot"], cfg.n,
+                               None, shared)
+            assert np.allclose(bb.branch, branch, rtol=1e-9, atol=1e-12 * np.abs(branch).max()), "oracle branch"
+        log(f"  expert rows within their rounding bound (worst max-abs / RMS {worst:.3g})")
+    else:
         y_ref = O.expert_ffn(inp["x"][rmap["slot_token"]], rmap["expert_offset"], w1_of, w2_of, cfg.act)
         off = rmap["expert_offset"]
         for e in range(cfg.E):
             a, b = int(off[e]), int(off[e + 1])
             if b > a:
-                check_expert_rows(g["y_perm"][a:b], inp["x"][rmap["slot_token"][a:b]], w1_of(e),
-                                  w2_of(e), cfg.act, bf16, f"expert {e}")
-        if cfg.shared_f:
-            shared = O.expert_forward(inp["x"], inp["shared_w1"], inp["shared_w2"], cfg.act)
-            check_expert_rows(g["shared"], inp["x"], inp["shared_w1"], inp["shared_w2"], cfg.act, bf16,
-                              "shared expert")
+                err = max_rel_rms(widen(g["y_perm"][a:b]), y_ref[a:b])
+                assert err <= F32_TOL, f"expert {e}: max-abs / RMS = {err:.3g}"
+        shared = O.expert_forward(inp["x"], inp["shared_w1"], inp["shared_w2"], cfg.act) if cfg.shared_f else None
         branch = O.combine(y_ref, rmap["slot_gate"], rmap["token_offset"], rmap["token_slot"], cfg.n,
-                           None, shared)
-        tokens = np.arange(cfg.n)
-    else:
-        # sampled tokens: each one's branch from its own experts, the expert
-        # outputs computed one expert at a time for all sampled rows it owns
-        tokens = np.asarray(sample_tokens)
-        pairs = {}                                   # expert -> [(i, slot)]
-        for i, t in enumerate(tokens):
-            for s in kept_slots(rmap, t):
-                e = int(np.searchsorted(rmap["expert_offset"], s, side="right") - 1)
-                pairs.setdefault(e, []).append((i, s))
-        yrows = {}
-        for e, lst in sorted(pairs.items()):
-            xe = inp["x"][[tokens[i] for i, _ in lst]]
-            ys = O.expert_forward(xe, w1_of(e), w2_of(e), cfg.act)
-            slots = [s for _, s in lst]
-            check_expert_rows(g["y_perm"][slots], xe, w1_of(e), w2_of(e), cfg.act, bf16, f"expert {e}")
-            for (i, s), y in zip(lst, ys):
-                yrows[s] = y
-        shared_rows = None
-        if cfg.shared_f:
-            shared_rows = O.expert_forward(inp["x"][tokens], inp["shared_w1"], inp["shared_w2"], cfg.act)
-            check_expert_rows(g["shared"][tokens], inp["x"][tokens], inp["shared_w1"], inp["shared_w2"],
-                              cfg.act, bf16, "shared expert")
-        branch = np.zeros((len(tokens), cfg.d))
-        for i, t in enumerate(tokens):
-            for s in kept_slots(rmap, t):
-                branch[i] += float(rmap["slot_gate"][s]) * yrows[s]
-            if shared_rows is not None:
-                branch[i] += shared_rows[i]
+                           None, shared)[tokens]
     # combine on its own: the device's expert outputs summed by the oracle;
     # the only difference left is one rounding of the fp32 sum to `dtype`
     gb = widen(g["branch"][tokens])
@@ -230,17 +196,20 @@ def compare_all(cfg, inp: dict, g: dict, full_ffn: bool = True, sample_tokens=No
     cerr = np.abs(gb - comb) - ulp * np.abs(comb)
     assert cerr.max() <= 1e-6 * np.sqrt((comb ** 2).mean()) + 1e-30, \
         f"combine: worst excess {cerr.max():.3g}"
-    # the layer against the oracle end to end (the tolerance is relative to
-    # the RMS of the layer output, residual included)
+    # the layer against the oracle end to end: the MoE branch alone
+    # (residual = NULL), then residual + branch
     res = widen(inp["x"][tokens])
-    out_ref = branch + res
-    rms_out = np.sqrt((out_ref ** 2).mean())
-    err_out = np.abs(widen(g["out"][tokens]) - out_ref).max() / rms_out
-    err_branch = np.abs(gb - branch).max() / rms_out
-    log(f"  max-abs / RMS(out): out {err_out:.3g}, branch {err_branch:.3g}; "
-        f"branch vs RMS(branch) {max_rel_rms(gb, branch):.3g}")
-    assert err_out <= tol, f"layer output: max-abs / RMS(out) = {err_out:.3g}"
-    assert err_branch <= tol, f"layer branch: max-abs / RMS(out) = {err_branch:.3g}"
+    if bf16:
+        err_b, floor_b, bnd_b = check_branch(g["branch"][tokens], bb, None, "layer branch")
+        err_o, _, _ = check_branch(g["out"][tokens], bb, res, "layer output")
+        log(f"  branch: max-abs / RMS(branch) {err_b:.3g} (one bf16 rounding of the exact branch alone: "
+            f"{floor_b:.3g}; largest bound / RMS {bnd_b:.3g}); residual + branch: max-abs / RMS(out) {err_o:.3g}")
+    else:
+        err_b = max_rel_rms(gb, branch)
+        err_o = max_rel_rms(widen(g["out"][tokens]), branch + res)
+        log(f"  branch: max-abs / RMS(branch) {err_b:.3g}; residual + branch: max-abs / RMS(out) {err_o:.3g}")
+        assert err_b <= F32_TOL, f"layer branch: max-abs / RMS(branch) = {err_b:.3g}"
+        assert err_o <= F32_TOL, f"layer output: max-abs / RMS(out) = {err_o:.3g}"
     # tokens with no kept expert (and no shared expert) ride the residual bit for bit
     if not cfg.shared_f:
         empty = np.array([t for t in tokens if not kept_slots(rmap, t)], dtype=np.int64)

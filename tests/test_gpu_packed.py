@@ -136,3 +136,33 @@ def test_fused_gather_equals_dispatch_then_ffn(rows, d, f, act):
     b = y_ref.view(torch.int16).cpu().numpy()
     assert np.array_equal(a, b)
     assert (a[M:] == np.int16(0x40E0)).all()
+
+
+@pytest.mark.parametrize("act", [N.MOE_GELU, N.MOE_SWIGLU])
+def test_up_then_down_calls_equal_the_ffn_call(act):
+    # moe_expert_up_packed then moe_expert_down_packed (H in a caller buffer)
+    # write the same bits as moe_expert_ffn_packed, with the gather fused in
+    rows = [0, 1, 127, 128, 129, 300, 5, 257, 64]
+    g = torch.Generator(device="cuda").manual_seed(16)
+    n, E, M, d, f = 600, len(rows), int(sum(rows)), 256, 320
+    w1r = 2 * f if act == N.MOE_SWIGLU else f
+    x = torch.randn(n, d, device="cuda", generator=g).to(torch.bfloat16)
+    idx = torch.randint(0, n, (M + 3,), device="cuda", generator=g, dtype=torch.int32)
+    w1 = (torch.randn(E, w1r, d, device="cuda", generator=g) * d ** -0.5).to(torch.bfloat16)
+    w2 = (torch.randn(E, d, f, device="cuda", generator=g) * f ** -0.5).to(torch.bfloat16)
+    w1p, w2p = N.pack_ffn_weights(w1, w2, act)
+    off = torch.tensor(np.r_[0, np.cumsum(rows)], dtype=torch.int32, device="cuda")
+    ws = torch.empty((N.moe_ffn_workspace_size(M + 3, E, d, f, act, N.MOE_BF16) + 7) // 8,
+                     dtype=torch.float64, device="cuda")
+    y_one = torch.full((M + 3, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    y_two = y_one.clone()
+    h = torch.full((M + 3, f), 5.0, dtype=torch.bfloat16, device="cuda")
+    N.moe_expert_ffn_packed(x, off, w1p, w2p, act, y_one, ws, row_index=idx, m_max=M + 3)
+    N.moe_expert_up_packed(x, off, w1p, act, h, row_index=idx, m_max=M + 3)
+    N.moe_expert_down_packed(h, off, w2p, y_two)
+    torch.cuda.synchronize()
+    a = y_one.view(torch.int16).cpu().numpy()
+    b = y_two.view(torch.int16).cpu().numpy()
+    assert np.array_equal(a, b)
+    assert (b[M:] == np.int16(0x40E0)).all()
+    assert (h[M:].view(torch.int16).cpu().numpy() == np.int16(0x40A0)).all()    # 5.0: untouched

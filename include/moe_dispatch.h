@@ -295,12 +295,19 @@ moe_status_t moe_expert_ffn_packed(const void *X, int32_t n_x, const int32_t *ro
  * Rows of H / Y_perm at or past expert_offset[E] are left untouched.  The two
  * calls in sequence write the same bits as moe_expert_ffn_packed.  bf16
  * tensors, 16-byte aligned; the same shape rules as moe_expert_ffn_packed; H
- * must not alias X, Y_perm must not alias H.  No workspace. */
+ * must not alias X, Y_perm must not alias H.  ws: MOE_GEMM_WS_BYTES of
+ * caller-owned device memory, 16-byte aligned (the grouped GEMM's tile
+ * counters; overwritten by every call, so calls that may run at the same
+ * time need workspaces of their own); a shorter one returns
+ * MOE_ERR_WORKSPACE. */
+#define MOE_GEMM_WS_BYTES 256
 moe_status_t moe_expert_up_packed(const void *X, int32_t n_x, const int32_t *row_index,
                                   const int32_t *expert_offset, int32_t E, int32_t d, int32_t f, int32_t act,
-                                  const void *W1_packed, int64_t M_max, void *H, void *stream);
+                                  const void *W1_packed, int64_t M_max, void *H, void *ws, size_t ws_bytes,
+                                  void *stream);
 moe_status_t moe_expert_down_packed(const void *H, const int32_t *expert_offset, int32_t E, int32_t d, int32_t f,
-                                    const void *W2_packed, int64_t M_max, void *Y_perm, void *stream);
+                                    const void *W2_packed, int64_t M_max, void *Y_perm, void *ws, size_t ws_bytes,
+                                    void *stream);
 
 /* Combine out = scatter_add(G * Y, I) (page 2 "The math"), the gate applied
  * to the expert output: for every token, out = residual + shared_out + sum

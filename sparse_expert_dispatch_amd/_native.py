@@ -24,6 +24,7 @@ MOE_TOKEN_MAJOR, MOE_RANK_MAJOR = 0, 1
 MOE_TOKEN_CHOICE, MOE_EXPERT_CHOICE = 0, 1
 MOE_GELU, MOE_SWIGLU = 0, 1
 MOE_NSTATS = 8
+MOE_GEMM_WS_BYTES = 256
 STAT_NAMES = ("lb_loss", "z_loss", "max_vio", "max_load_share", "n_kept", "n_dropped",
               "tokens_without_expert", "max_experts_per_token")
 
@@ -91,8 +92,8 @@ def lib() -> ctypes.CDLL:
         "moe_update_bias": (I32, [P, CFG, F32, P, P]),
         "moe_pack_expert_weights": (I32, [P, I32, I32, I32, I32, P, P]),
         "moe_expert_ffn_packed": (I32, [P, I32, P, P, I32, I32, I32, I32, P, P, I64, P, P, SZ, P]),
-        "moe_expert_up_packed": (I32, [P, I32, P, P, I32, I32, I32, I32, P, I64, P, P]),
-        "moe_expert_down_packed": (I32, [P, P, I32, I32, I32, P, I64, P, P]),
+        "moe_expert_up_packed": (I32, [P, I32, P, P, I32, I32, I32, I32, P, I64, P, P, SZ, P]),
+        "moe_expert_down_packed": (I32, [P, P, I32, I32, I32, P, I64, P, P, SZ, P]),
         "moe_combine_backward": (I32, [P, P, I32, I32, I32, MAP, I64, P, P, P]),
         "moe_ffn_backward_workspace_size": (I32, [I64, I32, I32, I32, I32, I32, SZP]),
         "moe_expert_ffn_backward": (I32, [P, I32, P, I32, I32, I32, I32, P, P, P, I64, P, P, P, P, SZ, P]),
@@ -350,32 +351,35 @@ def moe_expert_ffn_packed(x, expert_offset, w1p, w2p, act: int, y_perm, ws, stre
            "moe_expert_ffn_packed")
 
 
-def moe_expert_up_packed(x, expert_offset, w1p, act: int, h, stream=None, row_index=None, m_max=None):
+def moe_expert_up_packed(x, expert_offset, w1p, act: int, h, ws, stream=None, row_index=None, m_max=None):
     """Up projection + activation on packed weights: h [M_max, f] (bf16).
-    row_index / m_max as in moe_expert_ffn_packed."""
+    row_index / m_max as in moe_expert_ffn_packed; ws: MOE_GEMM_WS_BYTES of
+    device memory."""
     E = expert_offset.numel() - 1
     d = x.shape[1]
     f = h.shape[1]
     M_max = int(m_max if m_max is not None else (h.shape[0] if row_index is not None else x.shape[0]))
     bf = _elem_dtypes(MOE_BF16)
+    w, wb = _ws(ws)
     _check(lib().moe_expert_up_packed(_ptr(x, "x", bf), int(x.shape[0]),
                                       _ptr(row_index, "row_index", _I32) if row_index is not None else None,
                                       _ptr(expert_offset, "expert_offset", _I32), int(E), int(d), int(f),
-                                      int(act), _ptr(w1p, "w1_packed", bf), M_max, _ptr(h, "h", bf),
+                                      int(act), _ptr(w1p, "w1_packed", bf), M_max, _ptr(h, "h", bf), w, wb,
                                       _stream(stream)),
            "moe_expert_up_packed")
 
 
-def moe_expert_down_packed(h, expert_offset, w2p, y_perm, stream=None, m_max=None):
+def moe_expert_down_packed(h, expert_offset, w2p, y_perm, ws, stream=None, m_max=None):
     """Down projection on packed weights: y_perm = h W2^T per expert."""
     E = expert_offset.numel() - 1
     f = h.shape[1]
     d = y_perm.shape[1]
     M_max = int(m_max if m_max is not None else h.shape[0])
     bf = _elem_dtypes(MOE_BF16)
+    w, wb = _ws(ws)
     _check(lib().moe_expert_down_packed(_ptr(h, "h", bf), _ptr(expert_offset, "expert_offset", _I32), int(E),
                                         int(d), int(f), _ptr(w2p, "w2_packed", bf), M_max,
-                                        _ptr(y_perm, "y_perm", bf), _stream(stream)),
+                                        _ptr(y_perm, "y_perm", bf), w, wb, _stream(stream)),
            "moe_expert_down_packed")
 
 

@@ -318,9 +318,19 @@ static moe_status_t check_packed_ffn(int32_t E, int32_t d, int32_t f, int64_t M_
   return MOE_OK;
 }
 
+static_assert(MOE_GEMM_WS_BYTES == moe::kGemmWsBytes, "header and kernels agree on the GEMM workspace");
+
+static moe_status_t check_gemm_ws(void* ws, size_t ws_bytes, const char* who) {
+  if (!ws || ws_bytes < MOE_GEMM_WS_BYTES)
+    return fail(MOE_ERR_WORKSPACE, "%s needs %d workspace bytes, got %zu", who, (int)MOE_GEMM_WS_BYTES, ws_bytes);
+  REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
+  return MOE_OK;
+}
+
 moe_status_t moe_expert_up_packed(const void* X, int32_t n_x, const int32_t* row_index,
                                   const int32_t* expert_offset, int32_t E, int32_t d, int32_t f, int32_t act,
-                                  const void* W1_packed, int64_t M_max, void* H, void* stream) {
+                                  const void* W1_packed, int64_t M_max, void* H, void* ws, size_t ws_bytes,
+                                  void* stream) {
   moe_status_t st = check_packed_ffn(E, d, f, M_max);
   if (st != MOE_OK) return st;
   if (M_max == 0) return MOE_OK;
@@ -329,21 +339,24 @@ moe_status_t moe_expert_up_packed(const void* X, int32_t n_x, const int32_t* row
   REQUIRE(act == MOE_GELU || act == MOE_SWIGLU, "act must be MOE_GELU or MOE_SWIGLU");
   REQUIRE(aligned16(X) && aligned16(W1_packed) && aligned16(H), "bf16 tensors must be 16-byte aligned");
   REQUIRE(H != X, "H must not alias X");
+  if ((st = check_gemm_ws(ws, ws_bytes, "moe_expert_up_packed")) != MOE_OK) return st;
   return launched(moe::launch_expert_gemm(1, X, row_index, n_x, expert_offset, E, d, f, act, W1_packed, M_max, H,
-                                          true, as_stream(stream)),
+                                          true, ws, as_stream(stream)),
                   "moe_expert_up_packed");
 }
 
 moe_status_t moe_expert_down_packed(const void* H, const int32_t* expert_offset, int32_t E, int32_t d, int32_t f,
-                                    const void* W2_packed, int64_t M_max, void* Y_perm, void* stream) {
+                                    const void* W2_packed, int64_t M_max, void* Y_perm, void* ws, size_t ws_bytes,
+                                    void* stream) {
   moe_status_t st = check_packed_ffn(E, d, f, M_max);
   if (st != MOE_OK) return st;
   if (M_max == 0) return MOE_OK;
   REQUIRE(H && expert_offset && W2_packed && Y_perm, "tensor arguments must be non-NULL");
   REQUIRE(aligned16(H) && aligned16(W2_packed) && aligned16(Y_perm), "bf16 tensors must be 16-byte aligned");
   REQUIRE(H != Y_perm, "Y_perm must not alias H");
+  if ((st = check_gemm_ws(ws, ws_bytes, "moe_expert_down_packed")) != MOE_OK) return st;
   return launched(moe::launch_expert_gemm(2, H, nullptr, (int)M_max, expert_offset, E, d, f, MOE_GELU, W2_packed,
-                                          M_max, Y_perm, true, as_stream(stream)),
+                                          M_max, Y_perm, true, ws, as_stream(stream)),
                   "moe_expert_down_packed");
 }
 

@@ -649,6 +649,330 @@ stream_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict_
   }
 }
 
+// ---------------------------------------------------------------- paired weight-streaming kernel
+// Weight streaming with two 4-wave halves per workgroup (8 waves, two per
+// SIMD), so that no weight byte is fetched twice and each SIMD has a second
+// wave to issue matrix work while the first waits on memory.  A tile is
+// chosen per expert from its row count m:
+//  - wide (m <= 128): 128 rows x 2 kNW output columns; half h takes the
+//    columns n0 + h kNW ..: twice the distinct weight bytes in flight per CU;
+//  - tall (m > 128): 256 rows x kNW columns; half h takes rows 128 h ..
+//    of the same columns, so both halves load the same weight chunks at the
+//    same K stage (the second load is served by the cache): an expert of up
+//    to 256 rows streams its weights from memory once.
+// Each wave owns 128 rows and two 32-row weight blocks (64 output columns,
+// or the gate and up blocks of 32 SwiGLU outputs) as in the 4-wave kernel;
+// the weights stream from memory straight into registers, kDepth K stages
+// ahead, and only A (the token rows) goes through LDS.  All global loads are
+// buffer loads: the uniform part of an address is scalar and each lane keeps
+// a 32-bit offset.
+constexpr int kPairThreads = 512;
+
+// Tile plan of the paired kernel, two lists in expert order: the wide tiles
+// (ceil(N / (2 kNW)) per expert of 1..128 rows; wide_off[e] = wide tiles of
+// experts before e) and the tall tiles (ceil(m / 256) * ceil(N / kNW) per
+// expert of more than 128 rows, M tiles innermost; tall_off[e]).
+// wide_off[E], tall_off[E] are the totals.
+template <int kNW>
+MOE_DEV void pair_tile_plan(const int32_t* __restrict__ expert_offset, int E, int N, int32_t* wide_off,
+                            int32_t* tall_off) {
+  __shared__ int scratch[kPairThreads / 64];
+  static_assert(kMaxExperts <= kPairThreads, "one expert per thread");
+  const int ntw = (N + 2 * kNW - 1) / (2 * kNW), ntn = (N + kNW - 1) / kNW;
+  const int e = threadIdx.x;
+  const int m = e < E ? expert_offset[e + 1] - expert_offset[e] : 0;
+  const int cw = (m > 0 && m <= 128) ? ntw : 0;
+  const int ct = m > 128 ? ((m + 255) / 256) * ntn : 0;
+  int tot_w = 0, tot_t = 0;
+  const int rw = block_exclusive_scan<kPairThreads>(cw, scratch, &tot_w);
+  const int rt = block_exclusive_scan<kPairThreads>(ct, scratch, &tot_t);
+  if (e < E) {
+    wide_off[e] = rw;
+    tall_off[e] = rt;
+  }
+  if (threadIdx.x == 0) {
+    wide_off[E] = tot_w;
+    tall_off[E] = tot_t;
+  }
+  __syncthreads();
+}
+
+template <bool kDual, int kEpi, int kDepth>
+__global__ __launch_bounds__(kPairThreads, 1) void
+stream_pair_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ row_index, int n_a,
+                             const bf16_t* __restrict__ Bp, const int32_t* __restrict__ expert_offset, int E,
+                             int N, int K, bf16_t* __restrict__ C, int32_t* __restrict__ tile_ctr) {
+  static_assert(kBK == 64, "a stage is four 16-K operand chunks");
+  constexpr int kNW = kDual ? 128 : 256;           // output columns per half
+  constexpr int kCStride = kNW + 8;                // bf16 per output row in LDS
+  constexpr int kATile = 256 * kLdsStride;
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2 * kATile];
+  __shared__ __attribute__((aligned(16))) bf16_t sC[128 * kCStride];   // one half per pass
+  __shared__ int32_t wide_off[kMaxExperts + 1], tall_off[kMaxExperts + 1];
+  // A row offsets (bytes) of this thread's staging loads, one table per tile
+  // parity; each thread reads and writes only its own entries
+  __shared__ __attribute__((aligned(16))) uint32_t row_off[2][kPairThreads][4];
+  pair_tile_plan<kNW>(expert_offset, E, N, wide_off, tall_off);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hw = wave >> 2, qw = wave & 3;         // half, wave within the half
+  // Schedule: XCD x (workgroups b with b % 8 == x share its L2) takes an
+  // eighth of the wide list and an eighth of the tall list, in that order.
+  // Wide tiles carry twice the weight bytes of tall ones, and tall tiles
+  // whose halves both hold rows twice the matrix work, so tiles differ in
+  // cost and a static deal leaves some workgroups with far more work than
+  // others.  Each workgroup therefore takes its first two tiles round-robin
+  // (positions w and w + 32 of its XCD's sequence) and every further tile
+  // from the XCD's counter tile_ctr[x] (zero at launch): whoever finishes
+  // first takes the next tile.  Neighbouring workgroups of an XCD still work
+  // on neighbouring tiles of the same expert (shared A rows, and for an
+  // expert's M tiles shared weights, in that L2).
+  const int xcd = blockIdx.x % kXcds;
+  const int per_xcd_blocks = gridDim.x / kXcds;
+  const int n_wide = wide_off[E], n_tall = tall_off[E];
+  const int wl = (int)((int64_t)n_wide * xcd / kXcds), wh = (int)((int64_t)n_wide * (xcd + 1) / kXcds);
+  const int tl = (int)((int64_t)n_tall * xcd / kXcds), th = (int)((int64_t)n_tall * (xcd + 1) / kXcds);
+  const int len = (wh - wl) + (th - tl);
+  // Positions of this workgroup's tiles, three ahead of the one being
+  // computed (the load pipeline locates tile j + 1 during tile j and gathers
+  // the A rows of tile j + 2): slot j % 4 holds the j-th position; once the
+  // sequence is exhausted a slot repeats the last valid position with
+  // valid = 0.  Thread 0 writes a slot at the top of tile j - 3; the K loop's
+  // barriers publish it long before it is read.
+  __shared__ int tpos[4], tval[4];
+  auto take = [&](int slot, int prev) {            // thread 0 only
+    int p = len;
+    if (tval[prev]) p = 2 * per_xcd_blocks + atomicAdd(&tile_ctr[xcd], 1);
+    tpos[slot] = p < len ? p : tpos[prev];
+    tval[slot] = p < len;
+  };
+  if (tid == 0) {
+    const int w0 = blockIdx.x / kXcds;
+    tpos[0] = w0;
+    tval[0] = w0 < len;
+    tval[1] = w0 + per_xcd_blocks < len;
+    tpos[1] = tval[1] ? w0 + per_xcd_blocks : w0;
+    take(2, 1);
+  }
+  __syncthreads();
+  if (!tval[0]) return;
+  auto valid = [&](int j) { return tval[j & 3] != 0; };
+  const int nk = K / kBK;
+  const int P = kDual ? 2 * N / 32 : N / 32;       // weight row blocks per expert
+  const int last_pb = N / 32 - 1;
+  const size_t stage_bytes = (size_t)E * P * 4096;  // packed bytes per K stage, all experts
+  const int ld_row = tid >> 3, ld_chunk = (tid & 7) * 8;
+
+  struct Place {
+    int row_base, m_valid, n0, e, wide;
+  };
+  auto find = [&](const int32_t* off, int g) {     // expert holding list entry g
+    int e_lo = 0, e_hi = E - 1;
+    while (e_lo < e_hi) {
+      const int mid = (e_lo + e_hi + 1) >> 1;
+      if (off[mid] <= g) e_lo = mid; else e_hi = mid - 1;
+    }
+    return __builtin_amdgcn_readfirstlane(e_lo);
+  };
+  auto locate = [&](int j) {
+    const int pos = tpos[j & 3];
+    Place p;
+    if (pos < wh - wl) {
+      const int g = wl + pos;
+      p.e = find(wide_off, g);
+      p.wide = 1;
+      p.row_base = __builtin_amdgcn_readfirstlane(expert_offset[p.e]);
+      p.m_valid = __builtin_amdgcn_readfirstlane(expert_offset[p.e + 1] - p.row_base);
+      p.n0 = __builtin_amdgcn_readfirstlane((g - wide_off[p.e]) * 2 * kNW);
+    } else {
+      const int g = tl + pos - (wh - wl);
+      p.e = find(tall_off, g);
+      const int base = expert_offset[p.e];
+      const int m = expert_offset[p.e + 1] - base;
+      const int mt = (m + 255) / 256;
+      const int local = g - tall_off[p.e];
+      p.wide = 0;
+      p.row_base = __builtin_amdgcn_readfirstlane(base + (local % mt) * 256);
+      p.m_valid = __builtin_amdgcn_readfirstlane(min(256, m - (local % mt) * 256));
+      p.n0 = __builtin_amdgcn_readfirstlane((local / mt) * kNW);
+    }
+    return p;
+  };
+
+  // the A rows of tile j this thread stages (rows past the tile's last
+  // repeat it; they feed only output rows that are never stored)
+  auto rows_of = [&](int j) {
+    const Place p = locate(j);
+    uint32_t r4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = p.row_base + min(ld_row + 64 * i, p.m_valid - 1);
+      const int r = row_index ? min(max(row_index[s], 0), n_a - 1) : s;
+      r4[i] = (uint32_t)r * (uint32_t)(K * 2) + (uint32_t)(ld_chunk * 2);
+    }
+    *reinterpret_cast<u32x4_t*>(&row_off[j & 1][tid][0]) = (u32x4_t){r4[0], r4[1], r4[2], r4[3]};
+  };
+
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(A), (short)0, (int)min((int64_t)n_a * K * 2, (int64_t)0x7FFFFFFF), 0x00020000);
+  const uint32_t b_lane = (uint32_t)lane * 16;
+
+  // Load cursor (as in the 4-wave kernel): past the last tile it re-reads the
+  // last stage of the last tile (locate() of an exhausted slot gives that
+  // tile), so every iteration issues the same loads.
+  int l_j = 0, l_kt = 0;
+  const char* l_b = reinterpret_cast<const char*>(Bp);   // this wave's first row block, stage 0
+  int l_b1 = 0;                                           // byte offset of its second row block
+  auto load_tile = [&](int j) {
+    const Place p = locate(j);
+    rows_of(j + 1);
+    const int nc = p.n0 + (p.wide ? hw * kNW : 0);        // this half's first output column
+    int pb0, pb1;
+    if (kDual) {
+      const int ob = min(nc / 32 + qw, last_pb);
+      pb0 = 2 * ob;
+      pb1 = 2 * ob + 1;
+    } else {
+      pb0 = min(nc / 32 + 2 * qw, last_pb);
+      pb1 = min(nc / 32 + 2 * qw + 1, last_pb);
+    }
+    l_b = reinterpret_cast<const char*>(Bp) + ((size_t)p.e * P + pb0) * 4096;
+    l_b1 = __builtin_amdgcn_readfirstlane((pb1 - pb0) * 4096);
+  };
+  u32x4_t ra[kDepth][4], rb[kDepth][2][4];
+  auto issue = [&](auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
+    const int kt = valid(l_j) ? l_kt : nk - 1;
+    const u32x4_t ro = *reinterpret_cast<const u32x4_t*>(&row_off[l_j & 1][tid][0]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      ra[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, ro[i], kt * 128, 0));
+    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(l_b + (size_t)kt * stage_bytes), (short)0, 0x7FFFFFFF, 0x00020000);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      rb[slot][0][s] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_lane + s * 1024, 0, 0));
+      rb[slot][1][s] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_lane + s * 1024, l_b1, 0));
+    }
+    if (++l_kt == nk) {
+      l_kt = 0;
+      ++l_j;
+      load_tile(l_j);
+    }
+  };
+  int buf = 0;
+  auto store_a = [&](auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4_t*>(&sA[buf * kATile + (ld_row + 64 * i) * kLdsStride + ld_chunk]) = ra[slot][i];
+  };
+
+  using std::integral_constant;
+  rows_of(0);
+  load_tile(0);
+  static_for<0, kDepth>([&](auto u) { issue(u); });
+  store_a(integral_constant<int, 0>{});
+  __syncthreads();
+
+  for (int j = 0; valid(j); ++j) {
+    if (tid == 0) take((j + 3) & 3, (j + 2) & 3);
+    const Place pj = locate(j);
+    const int r0 = pj.wide ? 0 : 128 * hw;         // this wave's first row in the tile
+    // 32-row blocks of this wave holding rows of the expert (0..4, uniform
+    // per wave): the matrix work follows the row count rounded up to 32
+    const int nbw = min(4, max(0, (pj.m_valid - r0 + 31) >> 5));
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][b][v] = 0.f;
+    for (int kt0 = 0; kt0 < nk; kt0 += kDepth) {
+      static_for<0, kDepth>([&](auto uc) {
+        constexpr int U = decltype(uc)::value;
+        const bf16_t* pa = sA + buf * kATile + r0 * kLdsStride;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i < nbw) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              const int kc = s * 16 + ((lane >> 5) << 3);
+              const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(pa + (i * 32 + (lane & 31)) * kLdsStride + kc);
+              acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8_t, rb[U][0][s]),
+                                                                  acc[i][0], 0, 0, 0);
+              acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8_t, rb[U][1][s]),
+                                                                  acc[i][1], 0, 0, 0);
+            }
+          }
+        }
+        buf ^= 1;
+        store_a(integral_constant<int, (U + 1) % kDepth>{});
+        issue(integral_constant<int, U>{});
+        __syncthreads();
+      });
+    }
+
+    // Epilogue, one half per pass: the half's waves apply the activation,
+    // round to bf16 and write their rows into LDS; then every thread stores
+    // whole 16-byte chunks of output rows (non-temporal).  Wide tiles: pass
+    // h covers columns n0 + h kNW ..; tall tiles: rows 128 h ...  32x32
+    // accumulator layout: lane holds column (lane % 32), element v -> row
+    // (v / 4) * 8 + (lane / 32) * 4 + v % 4.
+#pragma unroll
+    for (int ph = 0; ph < 2; ++ph) {
+      const int prow = pj.wide ? 0 : 128 * ph;      // first tile row of this pass
+      const int pcol = pj.n0 + (pj.wide ? ph * kNW : 0);
+      const int m_pass = min(128, pj.m_valid - prow);
+      if (m_pass <= 0 || pcol >= N) break;         // uniform
+      if (ph > 0) __syncthreads();                 // the previous pass has been read out
+      if (hw == ph) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int v = 0; v < 16; v += 2) {       // elements v, v + 1: rows r, r + 1 of one column
+            const int r = i * 32 + (v >> 2) * 8 + ((lane >> 5) << 2) + (v & 3);
+            if (kDual) {
+              const int col = qw * 32 + (lane & 31);
+              const uint32_t h = bf16x2_rne(epi_value<kEpi>(acc[i][0][v], acc[i][1][v]),
+                                            epi_value<kEpi>(acc[i][0][v + 1], acc[i][1][v + 1]));
+              sC[r * kCStride + col] = (bf16_t)h;
+              sC[(r + 1) * kCStride + col] = (bf16_t)(h >> 16);
+            } else {
+#pragma unroll
+              for (int b = 0; b < 2; ++b) {
+                const int col = qw * 64 + b * 32 + (lane & 31);
+                const uint32_t h =
+                    bf16x2_rne(epi_value<kEpi>(acc[i][b][v], 0.f), epi_value<kEpi>(acc[i][b][v + 1], 0.f));
+                sC[r * kCStride + col] = (bf16_t)h;
+                sC[(r + 1) * kCStride + col] = (bf16_t)(h >> 16);
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();
+      constexpr int kOutChunksRow = kNW / 8;
+      for (int q = tid; q < 128 * kOutChunksRow; q += kPairThreads) {
+        const int r = q / kOutChunksRow, c = (q % kOutChunksRow) * 8;
+        if (r < m_pass && pcol + c < N)
+          __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(sC + r * kCStride + c),
+                                      reinterpret_cast<u32x4_t*>(C + (size_t)(pj.row_base + prow + r) * N + pcol + c));
+      }
+    }
+  }
+}
+
+// Clears the paired kernel's tile counters before a launch (a kernel rather
+// than a memset, so that a captured graph replays it as it runs eagerly).
+__global__ void zero_i32_kernel(int32_t* __restrict__ p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
+}
+
 // ---------------------------------------------------------------- weight packing
 // Packed operand order of the expert weights W [E, R, K] (bf16,
 // K-contiguous; R % 32 == 0, K % 64 == 0).  Row block p of an expert holds
@@ -752,6 +1076,9 @@ __global__ __launch_bounds__(256) void ffn_down_f32_kernel(const float* __restri
 #ifndef MOE_STREAM_DEPTH
 #define MOE_STREAM_DEPTH 2       // K stages of packed weights in flight per wave, weight streaming
 #endif
+#ifndef MOE_STREAM_PAIR
+#define MOE_STREAM_PAIR 1        // weight streaming on the paired (8-wave) kernel
+#endif
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -759,30 +1086,32 @@ size_t ffn_workspace_bytes(int64_t M_max, int E, int d, int f, int act, int dtyp
   (void)d;
   (void)act;
   const size_t elem = dtype == 1 ? 2 : 4;
-  return align256((size_t)M_max * f * elem);
+  // H, then the grouped GEMMs' tile counters (bf16); nothing without rows
+  if (M_max <= 0) return 0;
+  return align256((size_t)M_max * f * elem) + (dtype == 1 ? kGemmWsBytes : 0);
 }
 
 // Persistent grid: as many workgroups as fit on the device at once (so every
 // one of them is resident and walks its share of the tile list), rounded
 // down to a multiple of the XCD count.
 template <typename Kern>
-static int persistent_blocks(Kern kernel) {
+static int persistent_blocks(Kern kernel, int threads = kGemmThreads) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel),
-                                                   kGemmThreads, 0) != hipSuccess || per_cu <= 0)
+                                                   threads, 0) != hipSuccess || per_cu <= 0)
     per_cu = 1;
   return ((per_cu * cus) / kXcds) * kXcds;
 }
 
 // One launch of a persistent kernel; the grid size is computed once per
 // kernel (its occupancy does not change).
-template <auto kKernel, typename... Args>
+template <auto kKernel, int kThreads = kGemmThreads, typename... Args>
 static void launch_persistent(hipStream_t stream, Args... args) {
-  static const int blocks = persistent_blocks(kKernel);
-  hipLaunchKernelGGL(kKernel, dim3(blocks), dim3(kGemmThreads), 0, stream, args...);
+  static const int blocks = persistent_blocks(kKernel, kThreads);
+  hipLaunchKernelGGL(kKernel, dim3(blocks), dim3(kThreads), 0, stream, args...);
 }
 
 hipError_t launch_pack_weights(const void* W, int E, int R, int K, int gate_up, void* P,
@@ -796,9 +1125,11 @@ hipError_t launch_pack_weights(const void* W, int E, int R, int K, int gate_up, 
 // One grouped GEMM of the FFN on bf16: the up projection (stage 1: A = the
 // token rows, through row_index when given; B = W1; activation epilogue; C =
 // H [M_max, f]) or the down projection (stage 2: A = H; B = W2; C = Y_perm).
+// ctr: kGemmWsBytes of device memory for the paired kernel's tile counters
+// (cleared here before the launch).
 static void launch_ffn_gemm_bf16(int stage, const bf16_t* a, const int32_t* row_index, int n_a,
                                  const int32_t* expert_offset, int E, int d, int f, int act, const bf16_t* b,
-                                 int64_t M_max, bf16_t* c, bool packed, hipStream_t stream) {
+                                 int64_t M_max, bf16_t* c, bool packed, int32_t* ctr, hipStream_t stream) {
   // few rows per expert: the GEMMs stream weights, walk M tiles innermost
 #if MOE_GEMM_ORDER < 0
   const int mt_inner = M_max <= (int64_t)E * 4 * kBM ? 1 : 0;
@@ -817,7 +1148,12 @@ static void launch_ffn_gemm_bf16(int stage, const bf16_t* a, const int32_t* row_
     constexpr bool kD = decltype(dual)::value;
     constexpr int kE = decltype(epi)::value;
     const int nk = K / kBK;
-    if (packed && mt_inner && nk % MOE_STREAM_DEPTH == 0) {
+    if (packed && mt_inner && nk % MOE_STREAM_DEPTH == 0 && MOE_STREAM_PAIR &&
+        (int64_t)n_a * K * 2 <= (int64_t)0x7FFFFFFF) {
+      hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, stream, ctr, kXcds);
+      launch_persistent<stream_pair_gemm_bf16_kernel<kD, kE, MOE_STREAM_DEPTH>, kPairThreads>(
+          stream, a, row_index, n_a, b, expert_offset, E, N, K, c, ctr);
+    } else if (packed && mt_inner && nk % MOE_STREAM_DEPTH == 0) {
       launch_persistent<stream_gemm_bf16_kernel<kD, kE, MOE_STREAM_DEPTH>>(stream, a, row_index, n_a, b,
                                                                             expert_offset, E, N, K, c);
     } else if (two_bufs) {
@@ -849,9 +1185,10 @@ static void launch_ffn_gemm_bf16(int stage, const bf16_t* a, const int32_t* row_
 
 hipError_t launch_expert_gemm(int stage, const void* A, const int32_t* row_index, int n_a,
                               const int32_t* expert_offset, int E, int d, int f, int act, const void* W,
-                              int64_t M_max, void* C, bool packed, hipStream_t stream) {
+                              int64_t M_max, void* C, bool packed, void* ws, hipStream_t stream) {
   launch_ffn_gemm_bf16(stage, static_cast<const bf16_t*>(A), row_index, n_a, expert_offset, E, d, f, act,
-                       static_cast<const bf16_t*>(W), M_max, static_cast<bf16_t*>(C), packed, stream);
+                       static_cast<const bf16_t*>(W), M_max, static_cast<bf16_t*>(C), packed,
+                       static_cast<int32_t*>(ws), stream);
   return hipGetLastError();
 }
 
@@ -861,10 +1198,11 @@ hipError_t launch_expert_ffn(const void* X_perm, const int32_t* row_index, int n
                              hipStream_t stream) {
   void* H = ws;
   if (dtype == 1) {
+    int32_t* ctr = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align256((size_t)M_max * f * 2));
     launch_ffn_gemm_bf16(1, static_cast<const bf16_t*>(X_perm), row_index, n_x, expert_offset, E, d, f, act,
-                         static_cast<const bf16_t*>(W1), M_max, static_cast<bf16_t*>(H), packed, stream);
+                         static_cast<const bf16_t*>(W1), M_max, static_cast<bf16_t*>(H), packed, ctr, stream);
     launch_ffn_gemm_bf16(2, static_cast<const bf16_t*>(H), nullptr, (int)M_max, expert_offset, E, d, f, act,
-                         static_cast<const bf16_t*>(W2), M_max, static_cast<bf16_t*>(Y_perm), packed, stream);
+                         static_cast<const bf16_t*>(W2), M_max, static_cast<bf16_t*>(Y_perm), packed, ctr, stream);
   } else {
     const int64_t up = M_max * f, down = M_max * d;
     hipLaunchKernelGGL(ffn_up_f32_kernel, dim3((unsigned)((up + 255) / 256)), dim3(256), 0, stream,

@@ -93,10 +93,12 @@ hipError_t launch_expert_ffn(const void* X_perm, const int32_t* row_index, int n
 hipError_t launch_pack_weights(const void* W, int E, int R, int K, int gate_up, void* P, hipStream_t stream);
 // One bf16 grouped GEMM of the FFN: stage 1 the up projection (A = token rows
 // through row_index when given, W = W1, C = H [M_max, f]), stage 2 the down
-// projection (A = H, W = W2, C = Y_perm).
+// projection (A = H, W = W2, C = Y_perm).  ws: kGemmWsBytes of device memory
+// (tile counters of the weight-streaming kernel).
+constexpr size_t kGemmWsBytes = 256;
 hipError_t launch_expert_gemm(int stage, const void* A, const int32_t* row_index, int n_a,
                               const int32_t* expert_offset, int E, int d, int f, int act, const void* W,
-                              int64_t M_max, void* C, bool packed, hipStream_t stream);
+                              int64_t M_max, void* C, bool packed, void* ws, hipStream_t stream);
 
 // backward.hip
 hipError_t launch_combine_backward(const void* dout, const void* Y, int dtype, int d, const int32_t* slot_token,

@@ -85,6 +85,7 @@ class MoELayer:
             # the routed experts' hidden activation H [M_max, f] (bf16), in
             # the FFN workspace
             self.h = self.ws_ffn.view(torch.bfloat16)[:self.M_max * cfg.f].view(self.M_max, cfg.f)
+            self.ws_gemm = _bytes(N.MOE_GEMM_WS_BYTES, dev)     # the split GEMM calls' tile counters
             if self.shared:
                 self.shared_w1p, self.shared_w2p = N.pack_ffn_weights(weights["shared_w1"],
                                                                       weights["shared_w2"], self.act)
@@ -118,12 +119,12 @@ class MoELayer:
         """Packed weights: the routed experts' up projection + activation into
         H, its rows gathered from x through the map's slot_token (the
         dispatch fused in)."""
-        N.moe_expert_up_packed(x, self.map.expert_offset, self.w1p, self.act, self.h, stream,
+        N.moe_expert_up_packed(x, self.map.expert_offset, self.w1p, self.act, self.h, self.ws_gemm, stream,
                                row_index=self.map.slot_token, m_max=self.M_max)
 
     def routed_down(self, stream=None):
         """Packed weights: the routed experts' down projection, H -> Y_perm."""
-        N.moe_expert_down_packed(self.h, self.map.expert_offset, self.w2p, self.y_perm, stream)
+        N.moe_expert_down_packed(self.h, self.map.expert_offset, self.w2p, self.y_perm, self.ws_gemm, stream)
 
     def shared_expert(self, x, stream=None):
         """The always-on shared expert on every token (packed weights)."""

@@ -157,18 +157,30 @@ def test_packed_weight_validation(L):
     assert ffn(FAKE, 0, FAKE, FAKE, 8, 128, 128, N.MOE_GELU, FAKE, FAKE, 64, FAKE, FAKE, 1 << 30, None) == \
         N.MOE_ERR_INVALID_ARG
     up, down = L.moe_expert_up_packed, L.moe_expert_down_packed
-    assert up(None, 0, None, None, 8, 128, 128, N.MOE_GELU, None, 0, None, None) == N.MOE_OK
-    assert down(None, None, 8, 128, 128, None, 0, None, None) == N.MOE_OK
-    assert up(FAKE, 0, None, FAKE, 8, 100, 128, N.MOE_GELU, FAKE, 64, FAKE + 4096, None) == N.MOE_ERR_UNSUPPORTED
-    assert up(FAKE, 0, FAKE, FAKE, 8, 128, 128, N.MOE_GELU, FAKE, 64, FAKE + 4096, None) == N.MOE_ERR_INVALID_ARG
-    assert up(FAKE, 0, None, FAKE, 8, 128, 128, 3, FAKE, 64, FAKE + 4096, None) == N.MOE_ERR_INVALID_ARG
-    assert up(FAKE, 0, None, FAKE, 8, 128, 128, N.MOE_GELU, FAKE, 64, FAKE, None) == N.MOE_ERR_INVALID_ARG  # H = X
-    assert up(FAKE + 8, 0, None, FAKE, 8, 128, 128, N.MOE_GELU, FAKE, 64, FAKE + 4096, None) == \
+    W = FAKE + 8192                                          # a workspace
+    wsb = N.MOE_GEMM_WS_BYTES
+    assert up(None, 0, None, None, 8, 128, 128, N.MOE_GELU, None, 0, None, None, 0, None) == N.MOE_OK
+    assert down(None, None, 8, 128, 128, None, 0, None, None, 0, None) == N.MOE_OK
+    assert up(FAKE, 0, None, FAKE, 8, 100, 128, N.MOE_GELU, FAKE, 64, FAKE + 4096, W, wsb, None) == \
+        N.MOE_ERR_UNSUPPORTED
+    assert up(FAKE, 0, FAKE, FAKE, 8, 128, 128, N.MOE_GELU, FAKE, 64, FAKE + 4096, W, wsb, None) == \
+        N.MOE_ERR_INVALID_ARG
+    assert up(FAKE, 0, None, FAKE, 8, 128, 128, 3, FAKE, 64, FAKE + 4096, W, wsb, None) == N.MOE_ERR_INVALID_ARG
+    assert up(FAKE, 0, None, FAKE, 8, 128, 128, N.MOE_GELU, FAKE, 64, FAKE, W, wsb, None) == \
+        N.MOE_ERR_INVALID_ARG                                                                     # H = X
+    assert up(FAKE + 8, 0, None, FAKE, 8, 128, 128, N.MOE_GELU, FAKE, 64, FAKE + 4096, W, wsb, None) == \
         N.MOE_ERR_INVALID_ARG                                                                     # misaligned
-    assert down(FAKE, None, 8, 128, 128, FAKE, 64, FAKE + 4096, None) == N.MOE_ERR_INVALID_ARG   # offsets
-    assert down(FAKE, FAKE, 8, 128, 96, FAKE, 64, FAKE + 4096, None) == N.MOE_ERR_UNSUPPORTED    # f % 64
-    assert down(FAKE, FAKE, 8, 128, 128, FAKE, 64, FAKE, None) == N.MOE_ERR_INVALID_ARG          # Y = H
-    assert down(FAKE, FAKE, 8, 128, 128, FAKE, -1, FAKE + 4096, None) == N.MOE_ERR_INVALID_ARG
+    assert up(FAKE, 0, None, FAKE, 8, 128, 128, N.MOE_GELU, FAKE, 64, FAKE + 4096, W, wsb - 1, None) == \
+        N.MOE_ERR_WORKSPACE
+    assert up(FAKE, 0, None, FAKE, 8, 128, 128, N.MOE_GELU, FAKE, 64, FAKE + 4096, None, wsb, None) == \
+        N.MOE_ERR_WORKSPACE
+    assert down(FAKE, None, 8, 128, 128, FAKE, 64, FAKE + 4096, W, wsb, None) == N.MOE_ERR_INVALID_ARG   # offsets
+    assert down(FAKE, FAKE, 8, 128, 96, FAKE, 64, FAKE + 4096, W, wsb, None) == N.MOE_ERR_UNSUPPORTED    # f % 64
+    assert down(FAKE, FAKE, 8, 128, 128, FAKE, 64, FAKE, W, wsb, None) == N.MOE_ERR_INVALID_ARG          # Y = H
+    assert down(FAKE, FAKE, 8, 128, 128, FAKE, -1, FAKE + 4096, W, wsb, None) == N.MOE_ERR_INVALID_ARG
+    assert down(FAKE, FAKE, 8, 128, 128, FAKE, 64, FAKE + 4096, W + 4, wsb, None) == \
+        N.MOE_ERR_INVALID_ARG                                                                     # ws misaligned
+    assert down(FAKE, FAKE, 8, 128, 128, FAKE, 64, FAKE + 4096, W, 16, None) == N.MOE_ERR_WORKSPACE
 
 
 def test_workspace_checks(L):

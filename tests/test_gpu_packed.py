@@ -158,8 +158,9 @@ def test_up_then_down_calls_equal_the_ffn_call(act):
     y_two = y_one.clone()
     h = torch.full((M + 3, f), 5.0, dtype=torch.bfloat16, device="cuda")
     N.moe_expert_ffn_packed(x, off, w1p, w2p, act, y_one, ws, row_index=idx, m_max=M + 3)
-    N.moe_expert_up_packed(x, off, w1p, act, h, row_index=idx, m_max=M + 3)
-    N.moe_expert_down_packed(h, off, w2p, y_two)
+    wsg = torch.empty(N.MOE_GEMM_WS_BYTES // 8, dtype=torch.float64, device="cuda")
+    N.moe_expert_up_packed(x, off, w1p, act, h, wsg, row_index=idx, m_max=M + 3)
+    N.moe_expert_down_packed(h, off, w2p, y_two, wsg)
     torch.cuda.synchronize()
     a = y_one.view(torch.int16).cpu().numpy()
     b = y_two.view(torch.int16).cpu().numpy()

@@ -143,7 +143,7 @@ moe_status_t moe_router_workspace_size(const moe_route_cfg_t* cfg, int32_t dtype
   if (st != MOE_OK) return st;
   REQUIRE(bytes != nullptr, "bytes is NULL");
   REQUIRE(dtype == MOE_F32 || dtype == MOE_BF16, "dtype must be MOE_F32 or MOE_BF16");
-  *bytes = moe::router_workspace_bytes(cfg->n, cfg->d, cfg->E, dtype);
+  *bytes = moe::router_workspace_bytes(cfg->n, cfg->d, cfg->E, dtype, cfg->score);
   return MOE_OK;
 }
 
@@ -175,7 +175,7 @@ moe_status_t moe_router(const void* X, const void* Wg, int32_t dtype, const floa
   REQUIRE(!noise || std::isfinite(noise_std), "noise_std must be finite");
   if (dtype == MOE_BF16 && cfg->d % 64 == 0 && cfg->E % 16 == 0)   // the matrix-core path
     REQUIRE(aligned16(X) && aligned16(Wg), "X and Wg must be 16-byte aligned");
-  const size_t need = moe::router_workspace_bytes(cfg->n, cfg->d, cfg->E, dtype);
+  const size_t need = moe::router_workspace_bytes(cfg->n, cfg->d, cfg->E, dtype, cfg->score);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(MOE_ERR_WORKSPACE, "router needs %zu workspace bytes, got %zu", need, ws_bytes);
   return launched(moe::launch_router(X, Wg, dtype, logit_offset, noise, noise ? noise_std : 0.f, cfg->n,

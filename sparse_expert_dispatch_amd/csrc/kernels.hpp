@@ -36,7 +36,7 @@ __device__ __forceinline__ float row_tree_sum(const float (&row)[R], int P) {
 #endif
 
 // router.hip
-size_t router_workspace_bytes(int n, int d, int E, int dtype);
+size_t router_workspace_bytes(int n, int d, int E, int dtype, int score);
 hipError_t launch_router(const void* X, const void* Wg, int dtype, const float* offset,
                          const float* noise, float noise_std, int n, int d, int E, int score,
                          float* logits, float* scores, float* scores_t, void* ws, hipStream_t stream);

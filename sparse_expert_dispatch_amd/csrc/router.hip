@@ -206,8 +206,6 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-constexpr int kFusedLdw = 72;     // bf16 per LDS row of a W_g step (64 experts + 16 bytes)
-constexpr int kFusedRedLd = 68;   // floats per LDS row of the cross-wave sums
 #ifndef MOE_ROUTER_AHEAD
 #define MOE_ROUTER_AHEAD 4
 #endif
@@ -219,28 +217,37 @@ constexpr int kFusedRedLd = 68;   // floats per LDS row of the cross-wave sums
 #endif
 constexpr int kFusedAhead = MOE_ROUTER_AHEAD;   // K steps in flight per wave
 
-template <int KW, int RT>
+// LDS of the fused kernel with NT 16-expert tiles per workgroup (expert
+// tile of 16 NT experts): the waves' W_g steps during the K loop, reused for
+// the cross-wave sums after it, plus the transpose tile of the scores.
+template <int KW, int RT, int NT = 4>
 constexpr size_t router_fused_lds() {
-  constexpr size_t w = (size_t)KW * 32 * kFusedLdw * 2;
-  constexpr size_t r = (size_t)KW * 16 * RT * kFusedRedLd * 4;
-  return (w > r ? w : r) + (size_t)16 * RT * 65 * 4;
+  constexpr int kEt = 16 * NT;
+  constexpr size_t w = (size_t)KW * 32 * (kEt + 8) * 2;
+  constexpr size_t r = (size_t)KW * 16 * RT * (kEt + 4) * 4;
+  return (w > r ? w : r) + (size_t)16 * RT * (kEt + 1) * 4;
 }
 
-template <int KW, int RT, int AHEAD>
-__global__ __launch_bounds__(64 * KW) void router_fused_bf16_kernel(
+template <int KW, int RT, int AHEAD, int NT = 4>
+__global__ __launch_bounds__(64 * KW, KW <= 4 ? 2 : 1) void router_fused_bf16_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ Wg, int n, int d, int E,
     const float* __restrict__ offset, const float* __restrict__ noise, float noise_std, int score,
     float* __restrict__ logits, float* __restrict__ scores, float* __restrict__ scores_t) {
 #pragma clang fp contract(off)
   extern __shared__ __attribute__((aligned(16))) char router_lds[];
   constexpr int kRows = 16 * RT;
-  constexpr size_t kMain = router_fused_lds<KW, RT>() - (size_t)kRows * 65 * 4;
-  bf16_t* sW = reinterpret_cast<bf16_t*>(router_lds);   // [KW][32][kFusedLdw], during the K loop
-  float* red = reinterpret_cast<float*>(router_lds);    // [KW][kRows][kFusedRedLd], after it
+  constexpr int kEt = 16 * NT;                          // experts per workgroup (expert tile)
+  constexpr int kLdw = kEt + 8;                         // bf16 per LDS row of a W_g step
+  constexpr int kRedLd = kEt + 4;                       // floats per LDS row of the cross-wave sums
+  constexpr size_t kMain = router_fused_lds<KW, RT, NT>() - (size_t)kRows * (kEt + 1) * 4;
+  bf16_t* sW = reinterpret_cast<bf16_t*>(router_lds);   // [KW][32][kLdw], during the K loop
+  float* red = reinterpret_cast<float*>(router_lds);    // [KW][kRows][kRedLd], after it
   float* sT = reinterpret_cast<float*>(router_lds + kMain);   // [kRows][E + 1]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r0 = blockIdx.x * kRows;
+  const int e0 = blockIdx.y * kEt;                      // first expert of this workgroup's tile
+  const int et = min(kEt, E - e0);                      // its experts
   const int ksl = d / KW;
   const int kbeg = wave * ksl;
   const int ns = ksl / 32;
@@ -254,32 +261,35 @@ __global__ __launch_bounds__(64 * KW) void router_fused_bf16_kernel(
   int xoff[RT];
 #pragma unroll
   for (int i = 0; i < RT; ++i) xoff[i] = ((16 * i + (lane & 15)) * d + kl) * 2;
-  // W_g step loads: rows 8 h + lane / 8, experts 8 (lane % 8) .. +7 (clamped
-  // to the last whole chunk when E < 64; those LDS columns are never read)
-  const int wr = lane >> 3, wc = (lane & 7) << 3;
+  // W_g step loads, NT 16-byte chunks per lane: chunk lane + 64 h is row
+  // kRstep h + lane / kCpr, experts e0 + 8 (lane % kCpr) .. +7 of the tile
+  // (clamped to the last whole chunk of W_g past E; those LDS columns are
+  // never read)
+  constexpr int kCpr = kEt / 8;                         // 16-byte chunks per W_g row of the tile
+  constexpr int kRstep = 64 / kCpr;                     // rows per chunk round
+  const int wr = lane / kCpr, wc = (lane % kCpr) << 3;
   const __amdgpu_buffer_rsrc_t wr_src = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16_t*>(Wg + (size_t)kbeg * E), (short)0, ksl * E * 2, 0x00020000);
-  const int woff = (wr * E + min(wc, E - 8)) * 2;
-  bf16_t* sw = sW + wave * 32 * kFusedLdw;
-  const int tr_off = (8 * (lane >> 4) + ((lane >> 2) & 3)) * kFusedLdw + 4 * (lane & 3);
+  const int woff = (wr * E + min(e0 + wc, E - 8)) * 2;
+  bf16_t* sw = sW + wave * 32 * kLdw;
+  const int tr_off = (8 * (lane >> 4) + ((lane >> 2) & 3)) * kLdw + 4 * (lane & 3);
 
-  // Always four 16-expert tiles: with E < 64 the extra tiles multiply LDS
-  // columns past E (clamped copies) and their sums are never read.
-  constexpr int NT = 4;
+  // Always NT 16-expert tiles: past E the extra tiles multiply LDS columns
+  // of clamped copies and their sums are never read.
   f32x4_t acc[RT][NT];
 #pragma unroll
   for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   bf16x8_t xr[AHEAD][RT];
-  u32x4_t wv[AHEAD][4];
+  u32x4_t wv[AHEAD][NT];
   auto load = [&](int st, int q) {
 #pragma unroll
     for (int i = 0; i < RT; ++i)
       xr[q][i] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(xr_src, xoff[i], st * 64, 0));
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
-      wv[q][h] = __builtin_amdgcn_raw_buffer_load_b128(wr_src, woff, (st * 32 + 8 * h) * E * 2, 0);
+    for (int h = 0; h < NT; ++h)
+      wv[q][h] = __builtin_amdgcn_raw_buffer_load_b128(wr_src, woff, (st * 32 + kRstep * h) * E * 2, 0);
   };
   // AHEAD divides ns, so every round of the ring runs whole; loads are
   // issued unconditionally (the last round re-reads step ns - 1), which
@@ -292,12 +302,12 @@ __global__ __launch_bounds__(64 * KW) void router_fused_bf16_kernel(
       // one wave's LDS operations execute in order: these stores land after
       // the previous step's transpose reads
 #pragma unroll
-      for (int h = 0; h < 4; ++h) *reinterpret_cast<u32x4_t*>(sw + (8 * h + wr) * kFusedLdw + wc) = wv[q][h];
+      for (int h = 0; h < NT; ++h) *reinterpret_cast<u32x4_t*>(sw + (kRstep * h + wr) * kLdw + wc) = wv[q][h];
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(sw + tr_off + 16 * j));
         const v4i16 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(sw + tr_off + 4 * kFusedLdw + 16 * j));
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(sw + tr_off + 4 * kLdw + 16 * j));
         const bf16x8_t b = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int i = 0; i < RT; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xr[q][i], b, acc[i][j], 0, 0, 0);
@@ -307,44 +317,57 @@ __global__ __launch_bounds__(64 * KW) void router_fused_bf16_kernel(
   }
   __syncthreads();   // every wave is done with its W_g rows; the sums reuse the space
   // C fragment: lane holds column (lane % 16), rows 4 (lane / 16) + r
-  float* rw = red + wave * kRows * kFusedRedLd;
+  float* rw = red + wave * kRows * kRedLd;
 #pragma unroll
   for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        rw[(16 * i + 4 * (lane >> 4) + r) * kFusedRedLd + 16 * j + (lane & 15)] = acc[i][j][r];
+        rw[(16 * i + 4 * (lane >> 4) + r) * kRedLd + 16 * j + (lane & 15)] = acc[i][j][r];
   __syncthreads();
-  const int ld = E + 1;
+  // Rows finish one per wave: lane l holds tile experts l + 64 jj.  A softmax
+  // needs the whole row, so it runs only on workgroups that hold every
+  // expert (the launcher keeps the expert tile at E); the per-expert scores
+  // need no other expert.
+  constexpr int kJ = (kEt + 63) / 64;
+  constexpr int ld = kEt + 1;                           // odd stride: conflict-free both ways
   for (int rr = wave; rr < kRows; rr += KW) {
     const int row = r0 + rr;
     if (row >= n) break;
-    const int e = lane;
-    float z[1] = {0.f};
-    if (e < E) {
-      float v = red[rr * kFusedRedLd + e];
+    float z[kJ];
 #pragma unroll
-      for (int w = 1; w < KW; ++w) v = v + red[(w * kRows + rr) * kFusedRedLd + e];
-      if (offset) v = v + offset[e];
-      if (noise) v = v + noise_std * noise[(size_t)row * E + e];
-      z[0] = v;
-      if (logits) logits[(size_t)row * E + e] = v;
+    for (int jj = 0; jj < kJ; ++jj) {
+      const int e = lane + 64 * jj;
+      z[jj] = 0.f;
+      if (e < et) {
+        float v = red[rr * kRedLd + e];
+#pragma unroll
+        for (int w = 1; w < KW; ++w) v = v + red[(w * kRows + rr) * kRedLd + e];
+        if (offset) v = v + offset[e0 + e];
+        if (noise) v = v + noise_std * noise[(size_t)row * E + e0 + e];
+        z[jj] = v;
+        if (logits) logits[(size_t)row * E + e0 + e] = v;
+      }
     }
     if (!scores && !scores_t) continue;
-    float p[1];
-    row_scores(z, 1, E, score, p);
-    if (e < E) {
-      if (scores) scores[(size_t)row * E + e] = p[0];
-      if (scores_t) sT[rr * ld + e] = p[0];
+    float p[kJ];
+    row_scores(z, kJ, et, score, p);
+#pragma unroll
+    for (int jj = 0; jj < kJ; ++jj) {
+      const int e = lane + 64 * jj;
+      if (e < et) {
+        if (scores) scores[(size_t)row * E + e0 + e] = p[jj];
+        if (scores_t) sT[rr * ld + e] = p[jj];
+      }
     }
   }
   if (!scores_t) return;
   __syncthreads();
   const int rows = min(kRows, n - r0);
-  for (int item = tid; item < E * kRows; item += 64 * KW) {
+  for (int item = tid; item < et * kRows; item += 64 * KW) {
     const int e = item / kRows, rr = item % kRows;
-    if (rr < rows) scores_t[(size_t)e * n + r0 + rr] = sT[rr * ld + e];
+    if (rr < rows) scores_t[(size_t)(e0 + e) * n + r0 + rr] = sT[rr * ld + e];
   }
 }
 
@@ -440,22 +463,42 @@ static int router_splits(int n, int d, int E) {
   return s;
 }
 
-// Fused path: up to 64 experts (the workgroup holds all of them), K in
-// 32-wide steps per wave.  Shapes: RT = 2 when there are at least 512
-// 16-row tiles, else 1; MOE_ROUTER_KW_SMALL waves per workgroup when there
-// are fewer than 64 workgroups (short batches: more K slices in flight),
-// else MOE_ROUTER_KW_BIG.
+// Fused path, K in 32-wide steps per wave.
+//  - Up to 64 experts (NT = 4, the workgroup holds all of them): RT = 2 when
+//    there are at least 512 16-row tiles, else 1; MOE_ROUTER_KW_SMALL waves
+//    per workgroup when there are fewer than 64 workgroups (short batches:
+//    more K slices in flight), else MOE_ROUTER_KW_BIG.
+//  - 65 to 128 experts (NT = 8, all experts in one workgroup, so softmax
+//    rows stay whole): 4 waves, RT = 2.
+//  - More experts with a per-expert score (sigmoid, sqrtsoftplus): 64-expert
+//    tiles across workgroups (blockIdx.y), 4 waves, RT = 4 (or less when
+//    that leaves fewer than 256 workgroups).
+// Softmax rows over more than 128 experts take the split-K path.
 struct FusedShape {
   bool ok;
-  int kw, rt;
+  int kw, rt, nt, etiles;
 };
-static FusedShape router_fused_shape(int n, int d, int E, int dtype) {
-  FusedShape f{false, MOE_ROUTER_KW_BIG, 1};
-  if (dtype != 1 || E % 16 != 0 || E > 64 || n < 1) return f;
+static FusedShape router_fused_shape(int n, int d, int E, int dtype, int score) {
+  FusedShape f{false, MOE_ROUTER_KW_BIG, 1, 4, 1};
+  if (dtype != 1 || E % 16 != 0 || n < 1) return f;
   const int tiles = (n + 15) / 16;
-  f.rt = tiles >= 512 ? 2 : 1;
-  const int blocks = (n + 16 * f.rt - 1) / (16 * f.rt);
-  f.kw = blocks < 64 && d % (32 * MOE_ROUTER_KW_SMALL) == 0 ? MOE_ROUTER_KW_SMALL : MOE_ROUTER_KW_BIG;
+  if (E <= 64) {
+    f.rt = tiles >= 512 ? 2 : 1;
+    const int blocks = (n + 16 * f.rt - 1) / (16 * f.rt);
+    f.kw = blocks < 64 && d % (32 * MOE_ROUTER_KW_SMALL) == 0 ? MOE_ROUTER_KW_SMALL : MOE_ROUTER_KW_BIG;
+  } else if (E <= 128 && (score == 0 || E % 64 != 0)) {
+    f.kw = 4;
+    f.rt = 2;
+    f.nt = 8;
+  } else if (score != 0) {
+    f.kw = 4;
+    f.nt = 4;
+    f.etiles = (E + 63) / 64;
+    f.rt = 4;
+    while (f.rt > 1 && ((n + 16 * f.rt - 1) / (16 * f.rt)) * f.etiles < 256) f.rt /= 2;
+  } else {
+    return f;
+  }
   f.ok = d % (32 * f.kw) == 0;
   return f;
 }
@@ -471,8 +514,8 @@ static hipError_t lds_limit_once() {
   return status;
 }
 
-size_t router_workspace_bytes(int n, int d, int E, int dtype) {
-  if (router_fused_shape(n, d, E, dtype).ok) return 0;
+size_t router_workspace_bytes(int n, int d, int E, int dtype, int score) {
+  if (router_fused_shape(n, d, E, dtype, score).ok) return 0;
   if (!router_uses_mfma(dtype, d, E)) return 0;
   const int s = router_splits(n, d, E);
   return s > 1 ? (size_t)s * n * E * sizeof(float) : 0;
@@ -481,28 +524,32 @@ size_t router_workspace_bytes(int n, int d, int E, int dtype) {
 hipError_t launch_router(const void* X, const void* Wg, int dtype, const float* offset,
                          const float* noise, float noise_std, int n, int d, int E, int score,
                          float* logits, float* scores, float* scores_t, void* ws, hipStream_t stream) {
-  const FusedShape fs = router_fused_shape(n, d, E, dtype);
+  const FusedShape fs = router_fused_shape(n, d, E, dtype, score);
   if (fs.ok) {
     const bf16_t* x = static_cast<const bf16_t*>(X);
     const bf16_t* w = static_cast<const bf16_t*>(Wg);
     auto go = [&](auto kern, hipError_t limit, size_t lds, int rows, int threads) -> hipError_t {
       if (limit != hipSuccess) return limit;
-      hipLaunchKernelGGL(kern, dim3((unsigned)((n + rows - 1) / rows)), dim3(threads), lds, stream, x, w, n, d,
-                         E, offset, noise, noise_std, score, logits, scores, scores_t);
+      hipLaunchKernelGGL(kern, dim3((unsigned)((n + rows - 1) / rows), fs.etiles), dim3(threads), lds, stream, x, w,
+                         n, d, E, offset, noise, noise_std, score, logits, scores, scores_t);
       return hipGetLastError();
     };
-#define MOE_FUSED(KW, RT, A)                                                                             \
-  go(router_fused_bf16_kernel<KW, RT, A>,                                                                \
-     lds_limit_once<router_fused_bf16_kernel<KW, RT, A>, router_fused_lds<KW, RT>()>(),                   \
-     router_fused_lds<KW, RT>(), 16 * RT, 64 * KW)
-#define MOE_FUSED_RING(KW, RT)                                                                      \
-  (ns % kFusedAhead == 0 ? MOE_FUSED(KW, RT, kFusedAhead) : ns % 2 == 0 ? MOE_FUSED(KW, RT, 2) \
-                                                                         : MOE_FUSED(KW, RT, 1))
+#define MOE_FUSED(KW, RT, A, NT)                                                                         \
+  go(router_fused_bf16_kernel<KW, RT, A, NT>,                                                            \
+     lds_limit_once<router_fused_bf16_kernel<KW, RT, A, NT>, router_fused_lds<KW, RT, NT>()>(),           \
+     router_fused_lds<KW, RT, NT>(), 16 * RT, 64 * KW)
+#define MOE_FUSED_RING(KW, RT, NT)                                                                    \
+  (ns % kFusedAhead == 0 ? MOE_FUSED(KW, RT, kFusedAhead, NT) : ns % 2 == 0 ? MOE_FUSED(KW, RT, 2, NT) \
+                                                                           : MOE_FUSED(KW, RT, 1, NT))
     const int ns = d / fs.kw / 32;   // K steps per wave
     hipError_t err;
-    if (fs.kw == MOE_ROUTER_KW_SMALL && MOE_ROUTER_KW_SMALL != MOE_ROUTER_KW_BIG) err = MOE_FUSED_RING(MOE_ROUTER_KW_SMALL, 1);
-    else if (fs.rt == 2) err = MOE_FUSED_RING(MOE_ROUTER_KW_BIG, 2);
-    else err = MOE_FUSED_RING(MOE_ROUTER_KW_BIG, 1);
+    if (fs.nt == 8) err = ns % 2 == 0 ? MOE_FUSED(4, 2, 2, 8) : MOE_FUSED(4, 2, 1, 8);
+    else if (fs.etiles > 1 && fs.rt == 4) err = MOE_FUSED_RING(4, 4, 4);
+    else if (fs.etiles > 1 && fs.rt == 2) err = MOE_FUSED_RING(4, 2, 4);
+    else if (fs.etiles > 1) err = MOE_FUSED_RING(4, 1, 4);
+    else if (fs.kw == MOE_ROUTER_KW_SMALL && MOE_ROUTER_KW_SMALL != MOE_ROUTER_KW_BIG) err = MOE_FUSED_RING(MOE_ROUTER_KW_SMALL, 1, 4);
+    else if (fs.rt == 2) err = MOE_FUSED_RING(MOE_ROUTER_KW_BIG, 2, 4);
+    else err = MOE_FUSED_RING(MOE_ROUTER_KW_BIG, 1, 4);
 #undef MOE_FUSED_RING
 #undef MOE_FUSED
     return err;

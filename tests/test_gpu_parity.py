@@ -146,3 +146,33 @@ def test_repeat_runs_are_bitwise_identical():
     for key in ("logits", "sel_idx", "sel_gate", "slot_token", "token_slot", "y_perm", "branch",
                 "out", "stats", "hist"):
         assert np.array_equal(np.asarray(a[key]).view(np.uint8), np.asarray(b[key]).view(np.uint8)), key
+
+
+def test_expert_choice_column_select_beyond_lds():
+    # 40000 tokens: a column of keys no longer fits the select kernel's LDS
+    # staging (more than 32768 tokens), so the column select reads its keys
+    # from memory on every radix pass; selection, map and layer end to end
+    cfg = W.SMALL_CONFIGS[2].scaled("ec_n40000", n=40000, d=128, E=64, f=64)
+    rmap, g, _ = _run(cfg)
+    assert g["k"] == 1250
+
+
+def test_expert_choice_select_beyond_lds_with_ties():
+    """moe_select straight on 40000 tokens of quantised logits (most keys of
+    a column tie): every expert's k tokens and gates bit for bit, ties to the
+    lower token index."""
+    from oracle import moe_oracle as O
+    from sparse_expert_dispatch_amd import _native as N
+    rng = np.random.default_rng(6)
+    n, E = 40000, 64
+    z = (np.round(rng.normal(size=(n, E)) * 2) / 2).astype(np.float32)
+    k = O.ec_k(n, 2.0, E)
+    cfg = N.make_cfg(n, 64, E, k, N.MOE_EXPERT_CHOICE)
+    ws = torch.empty(N.moe_route_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+    I = torch.empty((E, k), dtype=torch.int32, device="cuda")
+    G = torch.empty((E, k), dtype=torch.float32, device="cuda")
+    N.moe_select(torch.from_numpy(z).cuda(), None, None, cfg, I, G, ws)
+    torch.cuda.synchronize()
+    rI, rG = O.select_expert_choice(z, k)
+    assert np.array_equal(I.cpu().numpy(), rI)
+    assert np.array_equal(G.cpu().numpy().view(np.uint32), rG.view(np.uint32))

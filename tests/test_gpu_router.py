@@ -6,8 +6,11 @@ softmax(X W_g); page 5 "MoE routing strategies explained", strategy 4 for
 the sigmoid scores; page 4 "How MoE routing strategies ...", section
 "Pitfalls" for the noise).  For bf16 inputs with at most 64 experts one
 fused kernel does it all (workgroups of 16 or 32 rows, K split over 4 or 16
-waves); more experts, or K not a multiple of the step, take the split-K
-GEMM and its finalize kernel.  Every case checks the logits against the
+waves).  65 to 128 experts: the same fused kernel with a 128-expert tile
+(every softmax row whole in one workgroup).  More experts with a per-expert
+score (sigmoid, sqrtsoftplus): the fused kernel on 64-expert tiles spread
+over workgroups.  Softmax over more than 128 experts, or K not a multiple
+of the step, takes the split-K GEMM and its finalize kernel.  Every case checks the logits against the
 oracle's float64 product (within 1e-5 of each row's largest magnitude) and
 the scores, row-major and transposed, bit for bit against the oracle's
 score functions applied to the device's own logits."""
@@ -82,7 +85,19 @@ def test_fused_router_offset_and_noise():
 
 
 @pytest.mark.parametrize("n,d,E,score", [
-    (500, 512, 128, "softmax"),       # more than 64 experts: split-K GEMM + finalize
+    (500, 512, 128, "softmax"),       # 128-expert tile, 32-row workgroups, ragged last one
+    (33, 1024, 96, "sigmoid"),        # 128-expert tile with 32 columns past E
+    (2100, 4096, 128, "softmax"),     # the Switch workload's router shape (d, E), fewer rows
+    (700, 7168, 256, "sigmoid"),      # four 64-expert tiles: the DeepSeek-V3-shaped router (d, E)
+    (129, 512, 192, "sqrtsoftplus"),  # three 64-expert tiles, ragged rows
+    (4000, 256, 128, "sigmoid"),      # two 64-expert tiles, 64-row workgroups
+])
+def test_expert_tiled_router(n, d, E, score):
+    _run_router(n, d, E, score, with_offset=True, with_noise=score == "sigmoid", seed=n)
+
+
+@pytest.mark.parametrize("n,d,E,score", [
+    (500, 512, 256, "softmax"),       # softmax over more than 128 experts: split-K GEMM + finalize
     (300, 96, 64, "softmax"),         # K not a multiple of 64: scalar GEMM + finalize
 ])
 def test_other_router_paths(n, d, E, score):

@@ -528,10 +528,13 @@ hipError_t launch_router(const void* X, const void* Wg, int dtype, const float* 
   if (fs.ok) {
     const bf16_t* x = static_cast<const bf16_t*>(X);
     const bf16_t* w = static_cast<const bf16_t*>(Wg);
+    // the transpose tile at the end of the LDS only when scores_t is
+    // requested: without it two workgroups fit on a CU
     auto go = [&](auto kern, hipError_t limit, size_t lds, int rows, int threads) -> hipError_t {
       if (limit != hipSuccess) return limit;
-      hipLaunchKernelGGL(kern, dim3((unsigned)((n + rows - 1) / rows), fs.etiles), dim3(threads), lds, stream, x, w,
-                         n, d, E, offset, noise, noise_std, score, logits, scores, scores_t);
+      const size_t lds_used = scores_t ? lds : lds - (size_t)rows * (16 * fs.nt + 1) * 4;
+      hipLaunchKernelGGL(kern, dim3((unsigned)((n + rows - 1) / rows), fs.etiles), dim3(threads), lds_used, stream,
+                         x, w, n, d, E, offset, noise, noise_std, score, logits, scores, scores_t);
       return hipGetLastError();
     };
 #define MOE_FUSED(KW, RT, A, NT)                                                                         \

@@ -284,6 +284,23 @@ moe_status_t moe_expert_ffn_packed(const void *X, int32_t n_x, const int32_t *ro
                                    const void *W1_packed, const void *W2_packed, int64_t M_max, void *Y_perm,
                                    void *ws, size_t ws_bytes, void *stream);
 
+/* moe_expert_ffn_packed for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments, kernels and results, without `ws`.  The
+ * workspace is a fixed array of MOE_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends; the call allocates
+ * and frees nothing.  It serves M_max * f * 2 + MOE_GEMM_WS_BYTES (rounded
+ * up to 256) <= MOE_NOALLOC_SCRATCH_BYTES, e.g. M_max * f <= 33 million;
+ * larger shapes return MOE_ERR_WORKSPACE (use moe_expert_ffn_packed).  Every
+ * call on a GPU uses that GPU's one array, so calls that overlap on one GPU
+ * (other streams, other threads) race on it and must be serialised by the
+ * caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64 << 20)
+moe_status_t moe_expert_ffn_packed_noalloc(const void *X, int32_t n_x, const int32_t *row_index,
+                                           const int32_t *expert_offset, int32_t E, int32_t d, int32_t f,
+                                           int32_t act, const void *W1_packed, const void *W2_packed,
+                                           int64_t M_max, void *Y_perm, void *stream);
+
 /* The two grouped GEMMs of moe_expert_ffn_packed as separate calls (page 2
  * "The math": Y[e] = Expert_e(X_in[e]); the expert is an up projection with
  * its activation, then a down projection), for a caller that keeps the

@@ -25,6 +25,7 @@ MOE_TOKEN_CHOICE, MOE_EXPERT_CHOICE = 0, 1
 MOE_GELU, MOE_SWIGLU = 0, 1
 MOE_NSTATS = 8
 MOE_GEMM_WS_BYTES = 256
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 STAT_NAMES = ("lb_loss", "z_loss", "max_vio", "max_load_share", "n_kept", "n_dropped",
               "tokens_without_expert", "max_experts_per_token")
 
@@ -33,7 +34,7 @@ EXPORTED = ("moe_ec_k", "moe_tc_capacity", "moe_max_slots", "moe_token_list_len"
             "moe_route_workspace_size", "moe_ffn_workspace_size", "moe_router", "moe_select",
             "moe_build_map", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_balance_stats",
             "moe_update_bias", "moe_pack_expert_weights", "moe_expert_ffn_packed",
-            "moe_expert_up_packed", "moe_expert_down_packed",
+            "moe_expert_up_packed", "moe_expert_down_packed", "moe_expert_ffn_packed_noalloc",
             "moe_combine_backward", "moe_ffn_backward_workspace_size", "moe_expert_ffn_backward",
             "moe_gate_backward", "moe_router_backward_workspace_size", "moe_router_backward",
             "moe_dispatch_backward", "moe_status_string", "moe_last_error")
@@ -94,6 +95,7 @@ def lib() -> ctypes.CDLL:
         "moe_expert_ffn_packed": (I32, [P, I32, P, P, I32, I32, I32, I32, P, P, I64, P, P, SZ, P]),
         "moe_expert_up_packed": (I32, [P, I32, P, P, I32, I32, I32, I32, P, I64, P, P, SZ, P]),
         "moe_expert_down_packed": (I32, [P, P, I32, I32, I32, P, I64, P, P, SZ, P]),
+        "moe_expert_ffn_packed_noalloc": (I32, [P, I32, P, P, I32, I32, I32, I32, P, P, I64, P, P]),
         "moe_combine_backward": (I32, [P, P, I32, I32, I32, MAP, I64, P, P, P]),
         "moe_ffn_backward_workspace_size": (I32, [I64, I32, I32, I32, I32, I32, SZP]),
         "moe_expert_ffn_backward": (I32, [P, I32, P, I32, I32, I32, I32, P, P, P, I64, P, P, P, P, SZ, P]),
@@ -349,6 +351,24 @@ def moe_expert_ffn_packed(x, expert_offset, w1p, w2p, act: int, y_perm, ws, stre
                                        _ptr(w2p, "w2_packed", bf), M_max,
                                        _ptr(y_perm, "y_perm", bf), w, wb, _stream(stream)),
            "moe_expert_ffn_packed")
+
+
+def moe_expert_ffn_packed_noalloc(x, expert_offset, w1p, w2p, act: int, y_perm, stream=None, row_index=None,
+                                  m_max=None):
+    """moe_expert_ffn_packed without a workspace argument: the library's
+    fixed per-GPU array serves as the workspace (calls overlapping on one GPU
+    race on it)."""
+    E = expert_offset.numel() - 1
+    d = x.shape[1]
+    f = w2p.shape[-1]
+    M_max = int(m_max if m_max is not None else (y_perm.shape[0] if row_index is not None else x.shape[0]))
+    bf = _elem_dtypes(MOE_BF16)
+    _check(lib().moe_expert_ffn_packed_noalloc(_ptr(x, "x", bf), int(x.shape[0]),
+                                               _ptr(row_index, "row_index", _I32) if row_index is not None else None,
+                                               _ptr(expert_offset, "expert_offset", _I32), int(E), int(d), int(f),
+                                               int(act), _ptr(w1p, "w1_packed", bf), _ptr(w2p, "w2_packed", bf),
+                                               M_max, _ptr(y_perm, "y_perm", bf), _stream(stream)),
+           "moe_expert_ffn_packed_noalloc")
 
 
 def moe_expert_up_packed(x, expert_offset, w1p, act: int, h, ws, stream=None, row_index=None, m_max=None):

@@ -22,7 +22,7 @@ LIBNAME = "libmoe_dispatch.so"
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["api.cpp", "router.hip", "select.hip", "route_map.hip", "permute.hip", "grouped_gemm.hip",
-           "stats.hip", "backward.hip"]
+           "stats.hip", "backward.hip", "noalloc.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -284,12 +284,11 @@ moe_status_t moe_pack_expert_weights(const void* W, int32_t E, int32_t rows, int
                   "moe_pack_expert_weights");
 }
 
-moe_status_t moe_expert_ffn_packed(const void* X, int32_t n_x, const int32_t* row_index,
-                                   const int32_t* expert_offset, int32_t E, int32_t d, int32_t f, int32_t act,
-                                   const void* W1_packed, const void* W2_packed, int64_t M_max, void* Y_perm,
-                                   void* ws, size_t ws_bytes, void* stream) {
-  REQUIRE(E > 0 && d > 0 && f > 0 && M_max >= 0, "E, d, f must be positive, M_max non-negative");
-  if (M_max == 0) return MOE_OK;                  // no rows: nothing to compute
+// Arguments of the packed FFN other than its workspace (M_max > 0).
+static moe_status_t check_ffn_packed(const void* X, int32_t n_x, const int32_t* row_index,
+                                     const int32_t* expert_offset, int32_t E, int32_t d, int32_t f, int32_t act,
+                                     const void* W1_packed, const void* W2_packed, int64_t M_max,
+                                     void* Y_perm) {
   REQUIRE(X && expert_offset && W1_packed && W2_packed && Y_perm, "tensor arguments must be non-NULL");
   REQUIRE(!row_index || n_x > 0, "n_x must be positive when row_index is given");
   REQUIRE(act == MOE_GELU || act == MOE_SWIGLU, "act must be MOE_GELU or MOE_SWIGLU");
@@ -299,6 +298,43 @@ moe_status_t moe_expert_ffn_packed(const void* X, int32_t n_x, const int32_t* ro
             d, f);
   REQUIRE(aligned16(X) && aligned16(W1_packed) && aligned16(W2_packed) && aligned16(Y_perm),
           "bf16 tensors must be 16-byte aligned");
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_ffn_packed_noalloc(const void* X, int32_t n_x, const int32_t* row_index,
+                                           const int32_t* expert_offset, int32_t E, int32_t d, int32_t f,
+                                           int32_t act, const void* W1_packed, const void* W2_packed,
+                                           int64_t M_max, void* Y_perm, void* stream) {
+  REQUIRE(E > 0 && d > 0 && f > 0 && M_max >= 0, "E, d, f must be positive, M_max non-negative");
+  if (M_max == 0) return MOE_OK;                  // no rows: nothing to compute
+  moe_status_t st = check_ffn_packed(X, n_x, row_index, expert_offset, E, d, f, act, W1_packed, W2_packed,
+                                     M_max, Y_perm);
+  if (st != MOE_OK) return st;
+  const size_t need = moe::ffn_workspace_bytes(M_max, E, d, f, act, MOE_BF16);
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_expert_ffn_packed_noalloc: M_max x f = %lld x %d needs %zu bytes of workspace, more than "
+                "its fixed %d-byte array; use moe_expert_ffn_packed with a caller workspace",
+                (long long)M_max, f, need, (int)MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const hipError_t err = moe::noalloc_scratch(&ws);
+  if (err != hipSuccess)
+    return fail(MOE_ERR_LAUNCH, "moe_expert_ffn_packed_noalloc: the library's workspace array: %s",
+                hipGetErrorString(err));
+  return launched(moe::launch_expert_ffn(X, row_index, n_x, MOE_BF16, expert_offset, E, d, f, act, W1_packed,
+                                         W2_packed, M_max, Y_perm, ws, true, as_stream(stream)),
+                  "moe_expert_ffn_packed_noalloc");
+}
+
+moe_status_t moe_expert_ffn_packed(const void* X, int32_t n_x, const int32_t* row_index,
+                                   const int32_t* expert_offset, int32_t E, int32_t d, int32_t f, int32_t act,
+                                   const void* W1_packed, const void* W2_packed, int64_t M_max, void* Y_perm,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(E > 0 && d > 0 && f > 0 && M_max >= 0, "E, d, f must be positive, M_max non-negative");
+  if (M_max == 0) return MOE_OK;                  // no rows: nothing to compute
+  moe_status_t st = check_ffn_packed(X, n_x, row_index, expert_offset, E, d, f, act, W1_packed, W2_packed,
+                                     M_max, Y_perm);
+  if (st != MOE_OK) return st;
   const size_t need = moe::ffn_workspace_bytes(M_max, E, d, f, act, MOE_BF16);
   if (!ws || ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "expert_ffn needs %zu workspace bytes, got %zu", need, ws_bytes);

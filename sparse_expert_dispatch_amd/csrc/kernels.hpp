@@ -100,6 +100,11 @@ hipError_t launch_expert_gemm(int stage, const void* A, const int32_t* row_index
                               const int32_t* expert_offset, int E, int d, int f, int act, const void* W,
                               int64_t M_max, void* C, bool packed, void* ws, hipStream_t stream);
 
+// noalloc.hip: the device address of this library's fixed workspace array
+// on the current device (MOE_NOALLOC_SCRATCH_BYTES), looked up once per
+// device.
+hipError_t noalloc_scratch(void** ptr);
+
 // backward.hip
 hipError_t launch_combine_backward(const void* dout, const void* Y, int dtype, int d, const int32_t* slot_token,
                                    const float* slot_gate, const int32_t* n_kept, int64_t M_max, void* dY,

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 28
+    assert len(names) == 29
     for name in names:
         assert hasattr(L, name), name
     assert sorted(N.EXPORTED) == names
@@ -181,6 +181,22 @@ def test_packed_weight_validation(L):
     assert down(FAKE, FAKE, 8, 128, 128, FAKE, 64, FAKE + 4096, W + 4, wsb, None) == \
         N.MOE_ERR_INVALID_ARG                                                                     # ws misaligned
     assert down(FAKE, FAKE, 8, 128, 128, FAKE, 64, FAKE + 4096, W, 16, None) == N.MOE_ERR_WORKSPACE
+
+
+def test_noalloc_ffn_argument_checks(L):
+    """The no-alloc FFN rejects what moe_expert_ffn_packed rejects, and shapes
+    whose workspace exceeds its fixed array, before touching a device."""
+    na = L.moe_expert_ffn_packed_noalloc
+    assert na(None, 0, None, None, 8, 128, 128, N.MOE_GELU, None, None, 0, None, None) == N.MOE_OK
+    assert na(FAKE, 0, None, FAKE, 8, 100, 128, N.MOE_GELU, FAKE, FAKE, 64, FAKE, None) == N.MOE_ERR_UNSUPPORTED
+    assert na(FAKE, 0, None, None, 8, 128, 128, N.MOE_GELU, FAKE, FAKE, 64, FAKE, None) == N.MOE_ERR_INVALID_ARG
+    assert na(FAKE, 0, None, FAKE, 8, 128, 128, 5, FAKE, FAKE, 64, FAKE, None) == N.MOE_ERR_INVALID_ARG
+    assert na(FAKE, 0, FAKE, FAKE, 8, 128, 128, N.MOE_GELU, FAKE, FAKE, 64, FAKE, None) == N.MOE_ERR_INVALID_ARG
+    assert na(FAKE + 2, 0, None, FAKE, 8, 128, 128, N.MOE_GELU, FAKE, FAKE, 64, FAKE, None) == N.MOE_ERR_INVALID_ARG
+    # M_max x f x 2 bytes beyond the 64 MiB array
+    assert na(FAKE, 0, None, FAKE, 8, 128, 4096, N.MOE_GELU, FAKE, FAKE, 8193, FAKE, None) == N.MOE_ERR_WORKSPACE
+    assert b"fixed" in L.moe_last_error()
+    assert N.MOE_NOALLOC_SCRATCH_BYTES == 64 << 20
 
 
 def test_workspace_checks(L):

@@ -842,25 +842,36 @@ stream_pair_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
     l_b1 = __builtin_amdgcn_readfirstlane((pb1 - pb0) * 4096);
   };
   u32x4_t ra[kDepth][4], rb[kDepth][2][4];
-  auto issue = [&](auto slot_c) {
+  // The loads of the stage at the cursor come in two parts: issue_b(slot, s)
+  // fetches the weight chunks of K step s, as soon as this stage's MFMAs of
+  // step s have read that register pair, so the weight stream never waits
+  // for the whole stage; issue_a then fetches the A rows and advances the
+  // cursor.
+  auto issue_b = [&](auto slot_c, auto step_c) {
+    constexpr int slot = decltype(slot_c)::value;
+    constexpr int s = decltype(step_c)::value;
+    const int kt = valid(l_j) ? l_kt : nk - 1;
+    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(l_b + (size_t)kt * stage_bytes), (short)0, 0x7FFFFFFF, 0x00020000);
+    rb[slot][0][s] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_lane + s * 1024, 0, 0));
+    rb[slot][1][s] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_lane + s * 1024, l_b1, 0));
+  };
+  auto issue_a = [&](auto slot_c) {
     constexpr int slot = decltype(slot_c)::value;
     const int kt = valid(l_j) ? l_kt : nk - 1;
     const u32x4_t ro = *reinterpret_cast<const u32x4_t*>(&row_off[l_j & 1][tid][0]);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       ra[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, ro[i], kt * 128, 0));
-    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(l_b + (size_t)kt * stage_bytes), (short)0, 0x7FFFFFFF, 0x00020000);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      rb[slot][0][s] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_lane + s * 1024, 0, 0));
-      rb[slot][1][s] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_lane + s * 1024, l_b1, 0));
-    }
     if (++l_kt == nk) {
       l_kt = 0;
       ++l_j;
       load_tile(l_j);
     }
+  };
+  auto issue = [&](auto slot_c) {
+    static_for<0, 4>([&](auto sc) { issue_b(slot_c, sc); });
+    issue_a(slot_c);
   };
   int buf = 0;
   auto store_a = [&](auto slot_c) {
@@ -895,12 +906,14 @@ stream_pair_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
       static_for<0, kDepth>([&](auto uc) {
         constexpr int U = decltype(uc)::value;
         const bf16_t* pa = sA + buf * kATile + r0 * kLdsStride;
+        // K step s of every row block, then step s's weight registers of
+        // this ring slot are refilled for the stage kDepth ahead
+        static_for<0, 4>([&](auto sc) {
+          constexpr int s = decltype(sc)::value;
+          const int kc = s * 16 + ((lane >> 5) << 3);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (i < nbw) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const int kc = s * 16 + ((lane >> 5) << 3);
+          for (int i = 0; i < 4; ++i) {
+            if (i < nbw) {
               const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(pa + (i * 32 + (lane & 31)) * kLdsStride + kc);
               acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8_t, rb[U][0][s]),
                                                                   acc[i][0], 0, 0, 0);
@@ -908,10 +921,11 @@ stream_pair_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
                                                                   acc[i][1], 0, 0, 0);
             }
           }
-        }
+          issue_b(integral_constant<int, U>{}, sc);
+        });
         buf ^= 1;
         store_a(integral_constant<int, (U + 1) % kDepth>{});
-        issue(integral_constant<int, U>{});
+        issue_a(integral_constant<int, U>{});
         __syncthreads();
       });
     }

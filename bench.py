@@ -111,6 +111,14 @@ def grade(bytes_, flops, seconds, dtype="bf16"):
             "frac": round(a / BF16_PEAK_TFLOPS, 4)}
 
 
+def gemm_kernel_kind(m_max, E, bm=128):
+    """Which grouped GEMM the library launches for the routed experts: the
+    same rule as its launcher (few slots per expert, at most four 128-row
+    tiles on average: the weight-streaming kernel; otherwise the LDS-tiled
+    matrix-core kernel)."""
+    return "weight-streaming" if m_max <= E * 4 * bm else "LDS-tiled matrix-core"
+
+
 def source_hash(files=("grouped_gemm.hip", "device_common.hpp", "kernels.hpp")):
     """Hash of the kernel sources a stored traffic measurement was taken on."""
     h = hashlib.sha256()
@@ -322,7 +330,8 @@ def main():
         roofline.update({
             "traffic": stored_traffic(TRAFFIC_FILE, source_hash(), cfg.name, "routed_up"),
             "kernel": "moe_expert_up_packed: routed experts' up projection + activation (one launch of "
-                      "the weight-streaming grouped GEMM, the dispatch gather fused into its row loads)",
+                      f"the {gemm_kernel_kind(layer.M_max, cfg.E)} grouped GEMM, the dispatch gather fused "
+                      "into its row loads)",
             "algorithmic_bytes": int(gm["up"]["bytes"]), "flops": gm["up"]["flops"],
             "h_bytes_written": int(gm["up"]["h_bytes"]), "avg_us": round(up_s * 1e6, 2)})
         dn_s = float(np.mean(part_ms["routed_down"])) * 1e-3

@@ -16,20 +16,22 @@
 //   max_vio = (max_e load_e - mean load) / mean load,  load = kept rows,
 // plus kept / dropped counts and the experts-per-token histogram.
 //
-// Two kernels.  The row kernel (16 tokens per workgroup, one per wave) adds
-// up each block's normalised scores, squared log-sum-exps and experts-per-
-// token histogram; the final kernel (one workgroup) reduces the block
-// partials in a fixed order, so the floats are reproducible bit for bit.
+// Two kernels.  The row kernel (16 waves, R tokens per wave) adds up each
+// block's normalised scores, squared log-sum-exps and experts-per-token
+// histogram; the final kernel (one workgroup) reduces the block partials in
+// a fixed order, so the floats are reproducible bit for bit.  R = 1 unless
+// the final workgroup would then need more than two load rounds (many
+// blocks, or many experts: each column takes a thread); R = 4 cuts its
+// partial rows fourfold.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 
-constexpr int kStatRowsPerWave = 1;
-constexpr int kStatRows = 16 * kStatRowsPerWave;   // rows per block
+constexpr int kStatRows = 16;   // rows per block at one row per wave (the workspace bound)
 
-// NJ = expert registers per lane (experts e = lane + 64 j, j < NJ).
-template <int NJ>
+// NJ = expert registers per lane (experts e = lane + 64 j, j < NJ); R = rows per wave.
+template <int NJ, int R>
 __global__ __launch_bounds__(1024) void stats_rows_kernel(const float* __restrict__ logits,
                                                          const int32_t* __restrict__ token_offset,
                                                          const int32_t* __restrict__ token_slot,
@@ -38,7 +40,6 @@ __global__ __launch_bounds__(1024) void stats_rows_kernel(const float* __restric
                                                          float* __restrict__ part_Z,
                                                          int32_t* __restrict__ part_H) {
 #pragma clang fp contract(off)
-  constexpr int R = kStatRowsPerWave;
   __shared__ float sP[16][64 * NJ];
   __shared__ float sZ[16];
   __shared__ int sH[kMaxExperts + 1];
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(1024) void stats_rows_kernel(const float* __restric
   const int wave = threadIdx.x >> 6;
   const int P2 = next_pow2(E);
   for (int i = threadIdx.x; i <= E; i += 1024) sH[i] = 0;
-  const int row0 = blockIdx.x * kStatRows + wave * R;
+  const int row0 = blockIdx.x * 16 * R + wave * R;
   // every row's list bounds and logits, loaded before the first wait
   int q0[R], q1[R];
   float z[R][NJ];
@@ -255,16 +256,26 @@ size_t stats_workspace_bytes(int n, int E) {
 hipError_t launch_balance_stats(const float* logits, const MapPtrs& m, int n, int E, int k, int dir,
                                 int score, float lb_coef, float z_coef, float* stats, int32_t* hist,
                                 void* ws, hipStream_t stream) {
-  const int nb = (n + kStatRows - 1) / kStatRows;
+  // final-kernel load rounds at one row per wave: partial rows / (thread
+  // groups x kFinRows), thread groups = 1024 / (power of two >= E + 2)
+  const int nb1 = (n + kStatRows - 1) / kStatRows;
+  int cp = 32;
+  while (cp < E + 2) cp <<= 1;
+  const bool four = (int64_t)nb1 * cp > 2LL * kFinThreads * kFinRows;
+  const int nb = four ? (n + 4 * kStatRows - 1) / (4 * kStatRows) : nb1;
   char* w = static_cast<char*>(ws);
   float* part_P = reinterpret_cast<float*>(w);
   float* part_Z = reinterpret_cast<float*>(w + align256((size_t)nb * E * sizeof(float)));
   int32_t* part_H = reinterpret_cast<int32_t*>(w + align256((size_t)nb * E * sizeof(float)) +
                                                align256((size_t)nb * sizeof(float)));
-  const auto rows = E <= 64 ? stats_rows_kernel<1>
-                    : E <= 128 ? stats_rows_kernel<2>
-                    : E <= 256 ? stats_rows_kernel<4>
-                               : stats_rows_kernel<8>;
+  const auto rows = four ? (E <= 64 ? stats_rows_kernel<1, 4>
+                            : E <= 128 ? stats_rows_kernel<2, 4>
+                            : E <= 256 ? stats_rows_kernel<4, 4>
+                                       : stats_rows_kernel<8, 4>)
+                     : (E <= 64 ? stats_rows_kernel<1, 1>
+                            : E <= 128 ? stats_rows_kernel<2, 1>
+                            : E <= 256 ? stats_rows_kernel<4, 1>
+                                       : stats_rows_kernel<8, 1>);
   hipLaunchKernelGGL(rows, dim3(nb), dim3(1024), 0, stream, logits, m.token_offset, m.token_slot, n, E,
                      score, part_P, part_Z, part_H);
   hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(kFinThreads), 0, stream, part_P, part_Z, part_H,

@@ -17,7 +17,8 @@ of which each token keeps 4, top-8 of 256 SwiGLU experts (d = 7168, f =
 top-1 of 128 GELU experts with capacity 160 (n = 16384); --config decode a
 decode step (64 tokens, top-8 of 64 SwiGLU experts).
 
---backward times the layer's backward on the same workload instead (one
+--backward times the layer's backward instead, on --config 2 unless another
+workload is named (one
 step = the gradients of <dOut, out> + the auxiliary losses for one forward:
 combine, expert FFN, shared expert, gate, router and dispatch backward), with
 the expert FFN backward as the roofline kernel; it prints its own JSON line.
@@ -170,8 +171,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="5",
-                    help="workload 1..5 (default 5, the largest) or 'decode' (64 tokens, top-8)")
+    ap.add_argument("--config", default=None,
+                    help="workload 1..5 or 'decode' (64 tokens, top-8); default 5 (the largest), "
+                         "or 2 (expert choice) with --backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="time HIP-graph replays of the parts instead of direct launches")
@@ -193,6 +195,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     N.lib()
+    if args.config is None:
+        args.config = "2" if args.backward else "5"
     cfg = W.FULL_CONFIGS[int(args.config)] if args.config.isdigit() else W.EXTRA_CONFIGS[args.config]
     print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     inp = W.gen_inputs(cfg)

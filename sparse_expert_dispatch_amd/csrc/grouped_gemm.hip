@@ -105,10 +105,11 @@ MOE_DEV float epi_value(float g, float u) {
 
 // Tile list, built by every workgroup in LDS at kernel start (no separate
 // launch, no host synchronisation): tile_off[e] = sum over e' < e of
-// ceil(m_e' / kBM), tile_off[E] = all M tiles.  E <= kMaxExperts.
+// ceil(m_e' / kRows), tile_off[E] = all M tiles.  E <= kMaxExperts.
+template <int kThreads = kGemmThreads, int kRows = kBM>
 MOE_DEV void block_tile_plan(const int32_t* __restrict__ expert_offset, int E, int32_t* tile_off) {
-  __shared__ int scratch[kGemmThreads / 64];
-  constexpr int kPer = (kMaxExperts + kGemmThreads - 1) / kGemmThreads;
+  __shared__ int scratch[kThreads / 64];
+  constexpr int kPer = (kMaxExperts + kThreads - 1) / kThreads;
   const int e0 = threadIdx.x * kPer;
   int cnt[kPer];
   int sum = 0;
@@ -116,11 +117,11 @@ MOE_DEV void block_tile_plan(const int32_t* __restrict__ expert_offset, int E, i
   for (int i = 0; i < kPer; ++i) {
     const int e = e0 + i;
     const int m = e < E ? expert_offset[e + 1] - expert_offset[e] : 0;
-    cnt[i] = (m + kBM - 1) / kBM;
+    cnt[i] = (m + kRows - 1) / kRows;
     sum += cnt[i];
   }
   int total = 0;
-  int run = block_exclusive_scan<kGemmThreads>(sum, scratch, &total);
+  int run = block_exclusive_scan<kThreads>(sum, scratch, &total);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     if (e0 + i < E) tile_off[e0 + i] = run;
@@ -151,29 +152,36 @@ MOE_DEV int b_row_of(int r, int n0, int N) {
 // (each K stage of 32 weight rows is one contiguous 4 KB block; LDS holds
 // the blocks unpadded and every fragment read is 64 consecutive 16-byte
 // chunks); otherwise B is the natural [rows, K] layout.
-template <bool kDual, int kEpi, int kLdsBufs, int kNB, bool kPacked>
-__global__ __launch_bounds__(kGemmThreads, kNB == 4 ? 2 : (kLdsBufs == 1 ? 3 : 1)) void
+// kWM: waves in M (2: 4 waves, 128-row tiles; 4: 8 waves, 256-row tiles,
+// one workgroup per CU with two waves per SIMD, double-buffered LDS: the
+// same 64 x 128 wave tiles, with a quarter fewer global and LDS-write bytes
+// per MFMA than two 128-row workgroups and one barrier per K stage).
+template <bool kDual, int kEpi, int kLdsBufs, int kNB, bool kPacked, int kWM = 2>
+__global__ __launch_bounds__(kWM * 128, kWM == 4 ? 1 : (kNB == 4 ? 2 : (kLdsBufs == 1 ? 3 : 1))) void
 grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ row_index, int n_a,
                          const bf16_t* __restrict__ B, const int32_t* __restrict__ expert_offset, int E,
                          int N, int K, int mt_inner, bf16_t* __restrict__ C) {
+  constexpr int kT = kWM * 128;                    // threads
+  constexpr int kTM = kWM * 64;                    // rows per tile
   constexpr int kBRows = 2 * kNB * 32;             // weight rows per tile
   constexpr int kBNout = kDual ? kBRows / 2 : kBRows;
-  constexpr int kTileA = 128 * kLdsStride;
+  constexpr int kTileA = kTM * kLdsStride;
   constexpr int kTileB = kPacked ? kBRows * kBK : kBRows * kLdsStride;
   static_assert(!kPacked || kBK == 64, "a packed K stage is 4 row-block chunks of 16 K");
   constexpr int kStageElems = kTileA + kTileB;
   constexpr int kChunksRow = kBK / 8;              // 16-byte chunks per operand row
-  constexpr int kRowsPass = kGemmThreads / kChunksRow;
-  constexpr int kLoadsA = 128 / kRowsPass;         // 16-byte loads per thread per stage
+  constexpr int kRowsPass = kT / kChunksRow;
+  constexpr int kLoadsA = kTM / kRowsPass;         // 16-byte loads per thread per stage
   constexpr int kLoadsB = kBRows / kRowsPass;
   constexpr int kPassCols = kBNout < 128 ? kBNout : 128;   // output columns per epilogue pass
   constexpr int kPasses = kBNout / kPassCols;
   constexpr int kCStride = kPassCols + 8;          // bf16 per output row in LDS
-  static_assert(128 * kCStride <= kLdsBufs * kStageElems, "an epilogue pass must fit the LDS stages");
+  static_assert(kTM * kCStride <= kLdsBufs * kStageElems, "an epilogue pass must fit the LDS stages");
+  static_assert(kWM == 2 || kPacked, "256-row tiles: packed weights");
   // LDS: the K stage(s); reused for the output tile.
   __shared__ __attribute__((aligned(16))) bf16_t smem[kLdsBufs * kStageElems];
   __shared__ int32_t tile_off[kMaxExperts + 1];
-  block_tile_plan(expert_offset, E, tile_off);
+  block_tile_plan<kT, kTM>(expert_offset, E, tile_off);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -223,8 +231,8 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
     const int local = (int)(t - (int64_t)tile_off[p.e] * ntn);
     const int mloc = mt_inner ? local % mtiles : local / ntn;
     const int nt = mt_inner ? local / mtiles : local % ntn;
-    p.row_base = __builtin_amdgcn_readfirstlane(expert_offset[p.e] + mloc * kBM);
-    p.m_valid = __builtin_amdgcn_readfirstlane(min(kBM, expert_offset[p.e + 1] - p.row_base));
+    p.row_base = __builtin_amdgcn_readfirstlane(expert_offset[p.e] + mloc * kTM);
+    p.m_valid = __builtin_amdgcn_readfirstlane(min(kTM, expert_offset[p.e + 1] - p.row_base));
     p.n0 = __builtin_amdgcn_readfirstlane(nt * kBNout);
     return p;
   };
@@ -233,7 +241,7 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
   // the GEMM); tail rows repeat the last valid one.  The rows of the next
   // tile are fetched one tile ahead (parked in LDS, which is cheaper than
   // registers here), so a gathered index is never waited on.
-  __shared__ int nx_row[kLoadsA][kGemmThreads];
+  __shared__ int nx_row[kLoadsA][kT];
   auto rows_of = [&](int64_t t) {
     const Place p = place(min(t, hi - 1));
 #pragma unroll
@@ -278,11 +286,14 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
 #pragma unroll
     for (int i = 0; i < kLoadsB; ++i) {
       if (kPacked) {
-        // load i fetches tile-local row block i (columns past N re-read the last block)
+        // load i fetches tile-local row block i (with 512 threads, blocks
+        // 2i and 2i + 1, one per 256 threads; columns past N re-read the
+        // last block)
         const int last = N / 32 - 1;
-        const int pb = kDual ? 2 * min(n0 / 32 + (i >> 1), last) + (i & 1) : min(n0 / 32 + i, last);
+        const int bi = kT == 256 ? i : i * (kT / 256) + (tid >> 8);
+        const int pb = kDual ? 2 * min(n0 / 32 + (bi >> 1), last) + (bi & 1) : min(n0 / 32 + bi, last);
         rb[i] = *reinterpret_cast<const u32x4_t*>(b_tile + ((size_t)st * E * (nbrows / 32) + pb) * 2048 +
-                                                  tid * 8);
+                                                  (tid & 255) * 8);
       } else {
         rb[i] = *reinterpret_cast<const u32x4_t*>(b_src[i] + koff);
       }
@@ -297,7 +308,7 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
 #pragma unroll
     for (int i = 0; i < kLoadsB; ++i) {
       if (kPacked)
-        *reinterpret_cast<u32x4_t*>(&sB[i * kBK * 32 + tid * 8]) = rb[i];
+        *reinterpret_cast<u32x4_t*>(&sB[i * kT * 8 + tid * 8]) = rb[i];
       else
         *reinterpret_cast<u32x4_t*>(&sB[(ld_row + kRowsPass * i) * kLdsStride + ld_chunk]) = rb[i];
     }
@@ -410,7 +421,7 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
       __syncthreads();
       constexpr int kOutChunksRow = kPassCols / 8;
       const int pc0 = c_n0 + p * kPassCols;
-      for (int q = tid; q < 128 * kOutChunksRow; q += kGemmThreads) {
+      for (int q = tid; q < kTM * kOutChunksRow; q += kT) {
         const int r = q / kOutChunksRow, c = (q % kOutChunksRow) * 8;
         if (r < c_m_valid && pc0 + c < N)
           __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(sC + r * kCStride + c),
@@ -1086,6 +1097,9 @@ __global__ __launch_bounds__(256) void ffn_down_f32_kernel(const float* __restri
 #ifndef MOE_GEMM_NB_MFMA
 #define MOE_GEMM_NB_MFMA 4       // N blocks per wave, shapes with many rows per expert
 #endif
+#ifndef MOE_GEMM_WM_MFMA
+#define MOE_GEMM_WM_MFMA 4       // waves in M there, packed weights (4: 256-row tiles, 8 waves)
+#endif
 
 #ifndef MOE_STREAM_DEPTH
 #define MOE_STREAM_DEPTH 2       // K stages of packed weights in flight per wave, weight streaming
@@ -1178,7 +1192,14 @@ static void launch_ffn_gemm_bf16(int stage, const bf16_t* a, const int32_t* row_
         launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 2, MOE_GEMM_NB_STREAM, false>>(
             stream, a, row_index, n_a, b, expert_offset, E, N, K, mt_inner, c);
     } else {
-      if (packed)
+      // 256-row tiles once experts average 2048 rows or more (the
+      // always-on shared expert: one expert with every token): there the
+      // 8-wave tile measured 7% faster; with fewer rows per expert its
+      // coarser tail per expert costs more than that (2.5% slower at 1024)
+      if (packed && MOE_GEMM_WM_MFMA == 4 && M_max >= (int64_t)2048 * E)
+        launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 2, MOE_GEMM_NB_MFMA, true, 4>, 512>(
+            stream, a, row_index, n_a, b, expert_offset, E, N, K, mt_inner, c);
+      else if (packed)
         launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 1, MOE_GEMM_NB_MFMA, true>>(
             stream, a, row_index, n_a, b, expert_offset, E, N, K, mt_inner, c);
       else

@@ -92,6 +92,17 @@ def test_packed_ffn_equals_natural_matrix_core_order(act):
     assert (b[M:] == np.int16(0x40E0)).all()
 
 
+@pytest.mark.parametrize("act", [N.MOE_GELU, N.MOE_SWIGLU])
+def test_packed_ffn_equals_natural_large_experts(act):
+    # experts averaging 2048 rows or more (the shared expert's shape): the
+    # packed path takes 256-row tiles of 8 waves, the natural one 128-row
+    # tiles; ragged last tiles (4100 = 16 x 256 + 4, 2100 = 8 x 256 + 52)
+    rows = [4100, 0, 2100]
+    a, b, M = _ffn_pair(rows, 192, 384, act, 16)
+    assert np.array_equal(a, b)
+    assert (b[M:] == np.int16(0x40E0)).all()
+
+
 def test_packed_ffn_benchmark_shape_sample():
     # the expert-choice benchmark's per-expert shape (128 rows, d 2048, f 4096), 4 experts
     a, b, M = _ffn_pair([128] * 4, 2048, 4096, N.MOE_GELU, 13)
@@ -110,7 +121,8 @@ def test_packed_ffn_equals_natural_several_tiles_per_workgroup(act):
 
 
 @pytest.mark.parametrize("rows,d,f", [([0, 3, 128, 129, 300, 64, 5, 200], 256, 512),     # weight streaming
-                                      ([1500, 0, 700], 192, 384)])                    # matrix-core order
+                                      ([1500, 0, 700], 192, 384),                     # matrix-core order
+                                      ([4100, 0, 2100], 192, 384)])                   # 256-row tiles
 @pytest.mark.parametrize("act", [N.MOE_GELU, N.MOE_SWIGLU])
 def test_fused_gather_equals_dispatch_then_ffn(rows, d, f, act):
     # row_index = a routing map's slot_token: the up GEMM reads X[row_index[s]]

@@ -18,11 +18,12 @@
 //  2. one workgroup turns them into per-chunk starting positions per expert
 //     (a scan over chunks in chunk order) and expert offsets of the kept
 //     rows (a scan over experts),
-//  3. one wave per chunk walks its arrivals in order, 64 at a time: lanes
+//  3. one workgroup per chunk, one wave per 64 consecutive arrivals: lanes
 //     with the same expert find each other with one ballot per expert-id
-//     bit, their rank inside the wave is a popcount, and a per-expert LDS
-//     counter carries the running position across iterations.  A position
-//     below the capacity is kept; its slot is offset[e] + position.
+//     bit, their rank inside the wave is a popcount, each wave's count per
+//     expert goes to LDS, and a scan over the waves in order (thread e for
+//     expert e) gives every wave its experts' starting positions.  A
+//     position below the capacity is kept; its slot is offset[e] + position.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -57,6 +58,11 @@ __global__ __launch_bounds__(256) void map_chunk_hist_kernel(const int32_t* __re
 
 // One workgroup: thread e scans expert e's chunk counts in chunk order; then
 // a workgroup scan over experts of the kept counts gives the slot offsets.
+// The counts are loaded kScanBatch chunks at a time, every load from a
+// clamped address and issued before the first add, so a batch costs one
+// memory latency rather than one per chunk.
+constexpr int kScanBatch = 16;
+
 __global__ __launch_bounds__(kScanThreads) void map_scan_kernel(
     const int32_t* __restrict__ chunk_hist, int nchunks, int E, int capacity,
     int32_t* __restrict__ chunk_base, int32_t* __restrict__ expert_count,
@@ -66,10 +72,17 @@ __global__ __launch_bounds__(kScanThreads) void map_scan_kernel(
   int kept = 0;
   if (e < E) {
     int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = chunk_hist[(size_t)c * E + e];
-      chunk_base[(size_t)c * E + e] = run;
-      run += v;
+    for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) v[u] = chunk_hist[(size_t)min(c0 + u, nchunks - 1) * E + e];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) {
+        if (c0 + u < nchunks) {
+          chunk_base[(size_t)(c0 + u) * E + e] = run;
+          run += v[u];
+        }
+      }
     }
     expert_count[e] = run;
     kept = capacity < 0 ? run : min(run, capacity);
@@ -85,71 +98,65 @@ __global__ __launch_bounds__(kScanThreads) void map_scan_kernel(
 
 // Token choice also writes the token-side lists: token t's entries are its
 // k assignments in rank order (token_offset[t] = t*k), -1 for a dropped one.
-// The chunk's expert ids and gates are loaded into registers up front (all
-// kMapChunk / 64 loads per lane in flight at once) and the expert offsets
-// into LDS, so the in-order walk below waits on no global load.
-constexpr int kScatterIters = kMapChunk / 64;
+// Wave w of chunk c takes arrivals c*kMapChunk + 64 w + lane, one per lane.
+constexpr int kScatterWaves = kMapChunk / 64;
 
-__global__ __launch_bounds__(64) void map_scatter_kernel(
+__global__ __launch_bounds__(kMapChunk) void map_scatter_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ gate, int64_t M, int n, int k, int E,
     int rank_major, int nbits, int capacity, const int32_t* __restrict__ chunk_base,
     const int32_t* __restrict__ expert_offset, MapPtrs m) {
-  extern __shared__ int cnt[];                      // [E] running positions, then [E] offsets
-  int* eoff = cnt + E;
-  const int lane = threadIdx.x;
+  extern __shared__ int sm[];                       // [kScatterWaves][E] wave counts, then [E] offsets
+  int* eoff = sm + kScatterWaves * E;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
   const int c = blockIdx.x;
-  for (int e = lane; e < E; e += 64) {
-    cnt[e] = chunk_base[(size_t)c * E + e];
-    eoff[e] = expert_offset[e];
-  }
+  for (int i = threadIdx.x; i < kScatterWaves * E; i += kMapChunk) sm[i] = 0;
+  for (int e = threadIdx.x; e < E; e += kMapChunk) eoff[e] = expert_offset[e];
   // 32-bit indices (the host checks n k < 2^31): a 64-bit division per
-  // element would cost more than the walk itself
+  // element would cost more than the rest of the work
   const int Mi = (int)M;
-  const int a0 = c * kMapChunk;
-  int q_all[kScatterIters], e_all[kScatterIters];
-  float g_all[kScatterIters];
+  const int a = c * kMapChunk + 64 * w + lane;
+  const bool inrange = a < Mi;
+  const int q = inrange ? (rank_major ? (a % n) * k + a / n : a) : 0;   // element of idx arriving a-th
+  const int e_raw = inrange ? idx[q] : 0;
+  const float g = inrange ? gate[q] : 0.f;
+  const bool valid = inrange && (unsigned)e_raw < (unsigned)E;
+  const int e = valid ? e_raw : 0;
+  // lanes of this wave with the same expert, and this lane's rank among them
+  uint64_t match = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bal = __ballot(bit);
+    match &= bit ? bal : ~bal;
+  }
+  const int rank = __popcll(match & ((1ull << lane) - 1ull));
+  __syncthreads();                                  // counts cleared, offsets staged
+  if (valid && (match >> lane) == 1ull) sm[w * E + e] = __popcll(match);   // the expert's last lane
+  __syncthreads();
+  // thread x < E: expert x's running position through the waves in order,
+  // from the chunk's starting position
+  if ((int)threadIdx.x < E) {
+    int run = chunk_base[(size_t)c * E + threadIdx.x];
 #pragma unroll
-  for (int i = 0; i < kScatterIters; ++i) {
-    const int a = a0 + 64 * i + lane;
-    const int q = a < Mi ? (rank_major ? (a % n) * k + a / n : a) : 0;   // element of idx arriving a-th
-    q_all[i] = q;
-    e_all[i] = a < Mi ? idx[q] : 0;
-    g_all[i] = a < Mi ? gate[q] : 0.f;
+    for (int v = 0; v < kScatterWaves; ++v) {
+      const int cnt = sm[v * E + threadIdx.x];
+      sm[v * E + threadIdx.x] = run;
+      run += cnt;
+    }
   }
   __syncthreads();
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
-  if (c == 0 && lane == 0) m.token_offset[Mi / k] = Mi;
-#pragma unroll
-  for (int i = 0; i < kScatterIters; ++i) {
-    const bool inrange = a0 + 64 * i + lane < Mi;
-    const int q = q_all[i];                                   // (t, r) = (q / k, q % k)
-    const int e_raw = e_all[i];
-    const bool valid = inrange && (unsigned)e_raw < (unsigned)E;
-    const int e = valid ? e_raw : 0;
-    uint64_t match = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t bal = __ballot(bit);
-      match &= bit ? bal : ~bal;
+  if (c == 0 && threadIdx.x == 0) m.token_offset[Mi / k] = Mi;
+  if (inrange) {
+    const int pos = valid ? sm[w * E + e] + rank : 0;
+    int32_t s = -1;
+    if (valid && (capacity < 0 || pos < capacity)) {
+      s = eoff[e] + pos;
+      m.slot_token[s] = q / k;
+      m.slot_gate[s] = g;
     }
-    // every lane reads its expert's running position before any lane of
-    // this wave updates it (the update below depends on the value read)
-    const int base = valid ? cnt[e] : 0;
-    const int rank = __popcll(match & lt_mask);
-    const int pos = base + rank;
-    const bool last = valid && (match >> lane) == 1ull;
-    if (last) cnt[e] = base + __popcll(match);
-    if (inrange) {
-      int32_t s = -1;
-      if (valid && (capacity < 0 || pos < capacity)) {
-        s = eoff[e] + pos;
-        m.slot_token[s] = q / k;
-        m.slot_gate[s] = g_all[i];
-      }
-      m.assign_slot[q] = s;
-      m.token_slot[q] = s;
-      if (q % k == 0) m.token_offset[q / k] = (int32_t)q;
-    }
+    m.assign_slot[q] = s;
+    m.token_slot[q] = s;
+    if (q % k == 0) m.token_offset[q / k] = (int32_t)q;
   }
 }
 
@@ -362,8 +369,8 @@ hipError_t launch_build_map_tc(const int32_t* idx, const float* gate, int n, int
                      E, rank_major, chunk_hist);
   hipLaunchKernelGGL(map_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, chunk_hist, nch, E,
                      capacity, chunk_base, m.expert_count, m.expert_offset, m.n_kept);
-  hipLaunchKernelGGL(map_scatter_kernel, dim3(nch), dim3(64), 2 * E * sizeof(int), stream, idx, gate, M,
-                     n, k, E, rank_major, nbits, capacity, chunk_base, m.expert_offset, m);
+  hipLaunchKernelGGL(map_scatter_kernel, dim3(nch), dim3(kMapChunk), (kScatterWaves + 1) * E * sizeof(int),
+                     stream, idx, gate, M, n, k, E, rank_major, nbits, capacity, chunk_base, m.expert_offset, m);
   return hipGetLastError();
 }
 

@@ -110,15 +110,33 @@ MOE_DEV float spec_expert_score(float z, int score) {
 
 // ---------------------------------------------------------------- wave64 helpers
 
+// One step of the maximum through the DPP lane network: each lane takes
+// the value of the lane kCtrl names (0 where there is none, or in rows
+// outside kRowMask), so no LDS round trip as with a shuffle.
+template <int kCtrl, int kRowMask>
+MOE_DEV uint64_t dpp_max_step_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, kCtrl, kRowMask, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), kCtrl, kRowMask, 0xf, false);
+  const uint64_t w = ((uint64_t)hi << 32) | lo;
+  return w > v ? w : v;
+}
+
+// Maximum over the 64 lanes of a wave (all lanes active; 0 is the identity:
+// every key this serves is an unsigned composite).  Lanes shifted right by
+// 1, 2, 4, 8 within each 16-lane row give lane 15 of a row the row's
+// maximum; broadcasts of lane 15 into rows 1 and 3 and of lane 31 into rows
+// 2 and 3 bring the whole wave's into lane 63, which every lane reads.  The
+// maximum does not depend on the order of comparisons.
 MOE_DEV uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)(v & 0xFFFFFFFFull), o, 64);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
-    uint64_t w = ((uint64_t)hi << 32) | lo;
-    v = w > v ? w : v;
-  }
-  return v;
+  v = dpp_max_step_u64<0x111, 0xf>(v);   // row_shr:1
+  v = dpp_max_step_u64<0x112, 0xf>(v);   // row_shr:2
+  v = dpp_max_step_u64<0x114, 0xf>(v);   // row_shr:4
+  v = dpp_max_step_u64<0x118, 0xf>(v);   // row_shr:8
+  v = dpp_max_step_u64<0x142, 0xa>(v);   // row_bcast:15 into rows 1, 3
+  v = dpp_max_step_u64<0x143, 0xc>(v);   // row_bcast:31 into rows 2, 3
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 MOE_DEV float wave_max_f32(float v) {

@@ -20,6 +20,9 @@ namespace moe {
 // one wave-wide unsigned max per round yields the best remaining expert with
 // the lower index winning ties.  Group scores: lane g < n_group scans its
 // contiguous group in LDS for the top-m keys.
+// NJ = expert registers per lane (experts lane + 64 j, j < NJ): the per-lane
+// loops run exactly as many times as the row needs.
+template <int NJ>
 __global__ __launch_bounds__(256) void select_tc_kernel(const float* __restrict__ logits,
                                                         const float* __restrict__ bias, SelectArgs a,
                                                         int32_t* __restrict__ idx_out,
@@ -36,9 +39,9 @@ __global__ __launch_bounds__(256) void select_tc_kernel(const float* __restrict_
   const int nj = (E + 63) >> 6;
   const float kNegInf = -__builtin_huge_valf();
 
-  float z[kMaxExpertRegs], key[kMaxExpertRegs];
+  float z[NJ], key[NJ];
 #pragma unroll
-  for (int j = 0; j < kMaxExpertRegs; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
     const bool valid = active && j < nj && e < E;
     z[j] = valid ? logits[(size_t)t * E + e] : 0.f;
@@ -85,15 +88,15 @@ __global__ __launch_bounds__(256) void select_tc_kernel(const float* __restrict_
       if ((uint32_t)lane == g) gk = 0;
     }
 #pragma unroll
-    for (int j = 0; j < kMaxExpertRegs; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int e = lane + 64 * j;
       if (j < nj && e < E && !((keep >> (e / gsz)) & 1ull)) key[j] = kNegInf;
     }
   }
 
-  uint64_t ck[kMaxExpertRegs];
+  uint64_t ck[NJ];
 #pragma unroll
-  for (int j = 0; j < kMaxExpertRegs; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
     ck[j] = (active && j < nj && e < E) ? rank_key(key[j], (uint32_t)e) : 0ull;
   }
@@ -101,11 +104,11 @@ __global__ __launch_bounds__(256) void select_tc_kernel(const float* __restrict_
   for (int r = 0; r < a.k; ++r) {
     uint64_t best = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxExpertRegs; ++j) best = ck[j] > best ? ck[j] : best;
+    for (int j = 0; j < NJ; ++j) best = ck[j] > best ? ck[j] : best;
     const uint64_t w = wave_max_u64(best);
     const int e = (int)rank_key_index(w);
 #pragma unroll
-    for (int j = 0; j < kMaxExpertRegs; ++j)
+    for (int j = 0; j < NJ; ++j)
       if (lane + 64 * j == e) ck[j] = 0ull;
     if (lane == r) my_sel = e;
   }
@@ -125,12 +128,12 @@ __global__ __launch_bounds__(256) void select_tc_kernel(const float* __restrict_
       // the full-row softmax probability
       float m = kNegInf;
 #pragma unroll
-      for (int j = 0; j < kMaxExpertRegs; ++j)
+      for (int j = 0; j < NJ; ++j)
         if (j < nj && lane + 64 * j < E) m = fmaxf(m, z[j]);
       m = wave_max_f32(m);
-      float tt[kMaxExpertRegs];
+      float tt[NJ];
 #pragma unroll
-      for (int j = 0; j < kMaxExpertRegs; ++j)
+      for (int j = 0; j < NJ; ++j)
         tt[j] = (j < nj && lane + 64 * j < E) ? spec_exp(z[j] - m) : 0.f;
       const float s = row_tree_sum(tt, next_pow2(E));
       gate = spec_exp(sz[my_sel] - m) / s;
@@ -154,8 +157,10 @@ __global__ __launch_bounds__(256) void select_tc_kernel(const float* __restrict_
 hipError_t launch_select_tc(const float* logits, const float* bias, const SelectArgs& a, int32_t* idx,
                             float* gate, hipStream_t stream) {
   const size_t lds = (size_t)4 * 2 * a.E * sizeof(float);
-  hipLaunchKernelGGL(select_tc_kernel, dim3((a.n + 3) / 4), dim3(256), lds, stream, logits, bias, a,
-                     idx, gate);
+  const int nj = (a.E + 63) / 64;
+  const auto kern = nj <= 1 ? select_tc_kernel<1> : nj <= 2 ? select_tc_kernel<2>
+                  : nj <= 4 ? select_tc_kernel<4> : select_tc_kernel<8>;
+  hipLaunchKernelGGL(kern, dim3((a.n + 3) / 4), dim3(256), lds, stream, logits, bias, a, idx, gate);
   return hipGetLastError();
 }
 

@@ -14,21 +14,25 @@
 // the MFMA operand layout wants: every lane feeds 8 consecutive K values of
 // one row (A) or one column (B).
 //
-// Two bf16 kernels, both on v_mfma_f32_32x32x16_bf16:
-//  - grouped_gemm_bf16_kernel (LDS kernel): a workgroup (4 waves) owns a
-//    128-row output tile, 128 or 256 columns wide (SwiGLU: half as many
-//    outputs from as many gate + up weight rows, so the gate and up
-//    accumulators of one output land in the same lane); each wave computes
-//    64 x 64 or 64 x 128.  K advances 64 at a time through LDS tiles; the
-//    next K tile is fetched from HBM into registers while the matrix cores
-//    work on the current one.  Weights in the natural layout or packed.
-//  - stream_gemm_bf16_kernel (weight streaming, packed weights only): the
-//    weights bypass LDS and stream into registers several K stages ahead
-//    (see the kernel).
-// The launcher picks the streaming kernel for packed weights when every
-// expert has few rows (the GEMMs are bound by the weight stream), the LDS
-// kernel with 128 x 256 tiles when experts have many rows (matrix-core
-// bound), and the LDS kernel for the natural layout.
+// bf16 kernels, all on v_mfma_f32_32x32x16_bf16:
+//  - grouped_gemm_bf16_kernel (LDS kernel): each wave computes 64 x 64 or
+//    64 x 128 (SwiGLU: half as many outputs from as many gate + up weight
+//    rows, so the gate and up accumulators of one output land in the same
+//    lane); K advances 64 at a time through LDS tiles, the next K tile
+//    fetched from HBM into registers while the matrix cores work on the
+//    current one.  A workgroup of 4 waves owns a 128-row tile, 128 or 256
+//    columns wide; with packed weights and experts averaging 2048 rows or
+//    more, a workgroup of 8 waves owns a 256 x 256 tile.  Weights in the
+//    natural layout or packed.
+//  - stream_pair_gemm_bf16_kernel (weight streaming, packed weights): the
+//    weights bypass LDS and stream into registers two K stages ahead, two
+//    4-wave halves per workgroup (see the kernel);
+//    stream_gemm_bf16_kernel, its 4-wave predecessor, serves A operands of
+//    more than 2 GiB (the paired kernel addresses A through 32-bit offsets).
+// The launcher picks weight streaming for packed weights when every expert
+// has few rows (the GEMMs are bound by the weight stream), the LDS kernel
+// when experts have many rows (matrix-core bound), and the LDS kernel for
+// the natural layout.
 //
 // Scheduling: the per-expert tile counts are prefix-summed on the device
 // (no host synchronisation), and a persistent grid walks the resulting tile

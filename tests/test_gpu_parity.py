@@ -86,6 +86,17 @@ def test_wide_expert_counts():
     _run(W.SMALL_CONFIGS[4].scaled("softmax_e128_top1", E=128, n=1100, d=128, f=128))
 
 
+def test_max_expert_count():
+    # E = 512, the largest the library takes: eight expert registers per lane
+    # in the token-choice select and the statistics, nine expert-id bits in
+    # the map's ballot match, the expert-tiled router (sigmoid, 8 tiles) and
+    # the split-K router (softmax over more than 128 experts), the tile plans
+    # of the grouped GEMMs at their expert limit
+    _run(W.SMALL_CONFIGS[5].scaled("sigmoid_groups_e512", E=512, n=300, d=128, f=64, shared_f=64))
+    _run(W.SMALL_CONFIGS[3].scaled("softmax_top8_e512", E=512, n=700, d=128, f=64))
+    _run(W.SMALL_CONFIGS[2].scaled("ec_e512", E=512, n=2048, d=128, f=64))
+
+
 def test_group_limited_sum_of_top2():
     _run(W.SMALL_CONFIGS[5].scaled("groups_top2", group_topm=2))
 

@@ -99,8 +99,14 @@ __global__ __launch_bounds__(kScanThreads) void map_scan_kernel(
 // Token choice also writes the token-side lists: token t's entries are its
 // k assignments in rank order (token_offset[t] = t*k), -1 for a dropped one.
 // Wave w of chunk c takes arrivals c*kMapChunk + 64 w + lane, one per lane.
+// kSingle: the whole batch is one chunk (n k <= kMapChunk, decode-sized
+// batches), and this one workgroup also does the histogram and scans of
+// steps 1 and 2: the chunk starts every expert at 0, the per-expert totals
+// are its counts, and a workgroup scan of the kept counts gives the
+// offsets.  One launch instead of three, with the same slots.
 constexpr int kScatterWaves = kMapChunk / 64;
 
+template <bool kSingle>
 __global__ __launch_bounds__(kMapChunk) void map_scatter_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ gate, int64_t M, int n, int k, int E,
     int rank_major, int nbits, int capacity, const int32_t* __restrict__ chunk_base,
@@ -111,7 +117,8 @@ __global__ __launch_bounds__(kMapChunk) void map_scatter_kernel(
   const int w = threadIdx.x >> 6;
   const int c = blockIdx.x;
   for (int i = threadIdx.x; i < kScatterWaves * E; i += kMapChunk) sm[i] = 0;
-  for (int e = threadIdx.x; e < E; e += kMapChunk) eoff[e] = expert_offset[e];
+  if (!kSingle)
+    for (int e = threadIdx.x; e < E; e += kMapChunk) eoff[e] = expert_offset[e];
   // 32-bit indices (the host checks n k < 2^31): a 64-bit division per
   // element would cost more than the rest of the work
   const int Mi = (int)M;
@@ -135,13 +142,31 @@ __global__ __launch_bounds__(kMapChunk) void map_scatter_kernel(
   __syncthreads();
   // thread x < E: expert x's running position through the waves in order,
   // from the chunk's starting position
+  int kept = 0;
   if ((int)threadIdx.x < E) {
-    int run = chunk_base[(size_t)c * E + threadIdx.x];
+    int run = kSingle ? 0 : chunk_base[(size_t)c * E + threadIdx.x];
 #pragma unroll
     for (int v = 0; v < kScatterWaves; ++v) {
       const int cnt = sm[v * E + threadIdx.x];
       sm[v * E + threadIdx.x] = run;
       run += cnt;
+    }
+    if (kSingle) {
+      m.expert_count[threadIdx.x] = run;
+      kept = capacity < 0 ? run : min(run, capacity);
+    }
+  }
+  if (kSingle) {
+    __shared__ int scratch[kMapChunk / 64];
+    int total = 0;
+    const int off = block_exclusive_scan<kMapChunk>(kept, scratch, &total);
+    if ((int)threadIdx.x < E) {
+      eoff[threadIdx.x] = off;
+      m.expert_offset[threadIdx.x] = off;
+    }
+    if (threadIdx.x == 0) {
+      m.expert_offset[E] = total;
+      *m.n_kept = total;
     }
   }
   __syncthreads();
@@ -365,12 +390,18 @@ hipError_t launch_build_map_tc(const int32_t* idx, const float* gate, int n, int
   int32_t* chunk_base = chunk_hist + (size_t)nch * E;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
+  const size_t lds = (kScatterWaves + 1) * E * sizeof(int);
+  if (nch == 1) {
+    hipLaunchKernelGGL(map_scatter_kernel<true>, dim3(1), dim3(kMapChunk), lds, stream, idx, gate, M, n, k, E,
+                       rank_major, nbits, capacity, chunk_base, m.expert_offset, m);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(map_chunk_hist_kernel, dim3(nch), dim3(256), E * sizeof(int), stream, idx, M, n, k,
                      E, rank_major, chunk_hist);
   hipLaunchKernelGGL(map_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, chunk_hist, nch, E,
                      capacity, chunk_base, m.expert_count, m.expert_offset, m.n_kept);
-  hipLaunchKernelGGL(map_scatter_kernel, dim3(nch), dim3(kMapChunk), (kScatterWaves + 1) * E * sizeof(int),
-                     stream, idx, gate, M, n, k, E, rank_major, nbits, capacity, chunk_base, m.expert_offset, m);
+  hipLaunchKernelGGL(map_scatter_kernel<false>, dim3(nch), dim3(kMapChunk), lds, stream, idx, gate, M, n, k, E,
+                     rank_major, nbits, capacity, chunk_base, m.expert_offset, m);
   return hipGetLastError();
 }
 

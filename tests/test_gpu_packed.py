@@ -103,6 +103,18 @@ def test_packed_ffn_equals_natural_large_experts(act):
     assert (b[M:] == np.int16(0x40E0)).all()
 
 
+def test_packed_ffn_operand_beyond_2gib():
+    # 512 experts of 511 rows (M tiles innermost, weight streaming) with
+    # f = 4224: the down projection's A operand, H [261639, 4224] in bf16,
+    # is 2.2 GB, past the 32-bit byte offsets of the paired streaming kernel,
+    # so that GEMM runs on the 4-wave streaming kernel (64-bit row
+    # addresses); both must match the natural layout's bits
+    a, b, M = _ffn_pair([511] * 512, 128, 4224, N.MOE_GELU, 17)
+    assert (M + 7) * 4224 * 2 > 2 ** 31
+    assert np.array_equal(a, b)
+    assert (b[M:] == np.int16(0x40E0)).all()
+
+
 def test_packed_ffn_benchmark_shape_sample():
     # the expert-choice benchmark's per-expert shape (128 rows, d 2048, f 4096), 4 experts
     a, b, M = _ffn_pair([128] * 4, 2048, 4096, N.MOE_GELU, 13)

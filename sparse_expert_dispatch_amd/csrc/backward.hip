@@ -643,6 +643,7 @@ MOE_DEV void tile_mainloop(const bf16_t* abase, int64_t abytes, int64_t lda, int
     const int buf = q & 1;
     store(q, buf);
     __syncthreads();
+    if (next >= 0) load(next, q);
     bwbf16x8_t fa[4], fb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[i] = frag(sA[buf], kAK, 64 * wr + 16 * i);
@@ -655,7 +656,6 @@ MOE_DEV void tile_mainloop(const bf16_t* abase, int64_t abytes, int64_t lda, int
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-    if (next >= 0) load(next, q);
   };
 #pragma unroll
   for (int q = 0; q < R; ++q) load(q, q);
@@ -1023,6 +1023,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_WG_WAVE
       *reinterpret_cast<bwu32x4_t*>(&sB[buf][s_lds[h]]) = rb[q][h];
     }
     __syncthreads();
+    load(x, st, q);
     bwbf16x8_t fb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) fb[j] = frag(sB[buf], 64 * wc + 16 * j);
@@ -1033,7 +1034,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_WG_WAVE
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa, acc[i][j], 0, 0, 0);
     }
-    load(x, st, q);
   };
 
   // epilogue constants: this thread's fragment writes start at LDS float
@@ -1190,6 +1190,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
     for (int h = 0; h < 4; ++h) *reinterpret_cast<bwu32x4_t*>(&sB[buf][b_lds[h]]) = rb[q][h];
     __syncthreads();
+    if (next >= 0) load(next, q);
     bwbf16x8_t fa[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -1208,7 +1209,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa[i], acc[i][j], 0, 0, 0);
     }
-    if (next >= 0) load(next, q);
   };
 #pragma unroll
   for (int q = 0; q < R; ++q) load(q, q);
@@ -1333,6 +1333,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
     for (int h = 0; h < 4; ++h) *reinterpret_cast<bwu32x4_t*>(&sB[buf][sb_lds[h]]) = rb[q][h];
     __syncthreads();
+    load(x, st, q);
     bwbf16x8_t fa[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[i] = frag(sA[buf], 64 * wr + 16 * i);
@@ -1343,7 +1344,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
       for (int i = 0; i < 4; ++i)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa[i], acc[i][j], 0, 0, 0);
     }
-    load(x, st, q);
   };
 
   // epilogue constants: this thread's fragment writes start at LDS float

@@ -349,6 +349,9 @@ struct GemmArgs {
   bf16_t* h_out;       // activation backward: act(pre) [rows, ld_h]
   int64_t ld_h;
   int f;               // activation backward: hidden size (SwiGLU up columns start at f)
+  // weight gradients: per-XCD expert lists from wgrad_plan_kernel, or
+  // nullptr for equal tile counts per XCD
+  const int32_t* plan;
 };
 
 enum { EPI_BF16 = 0, EPI_BF16_ADD = 1, EPI_F32 = 2, EPI_GELU_BWD = 3, EPI_SWIGLU_BWD = 4 };
@@ -482,6 +485,87 @@ MOE_DEV int xcd_range_start(int n, int xcd) {
 MOE_DEV int xcd_tile(int n, int b) {
   return MOE_BW_XCD ? xcd_range_start(n, b % kBwXcds) + b / kBwXcds : b;
 }
+
+// Schedule of the persistent weight-gradient kernels.  A tile's time grows
+// with its expert's row count (the K of its product), and routed loads are
+// skewed (the top-8 Zipf workload's largest expert has 8x the mean), so an
+// equal count of tiles per XCD and per workgroup leaves most of the chip
+// idle while a few workgroups finish the largest experts.  This kernel (one
+// workgroup, before the weight gradients) deals whole experts to the 8 XCDs,
+// longest first, each to the XCD with the least work so far, so that an
+// expert's operand bands stay in one L2.  In the kernels the k workgroups of
+// an XCD take the tiles of its list round-robin (positions w, w + k, ...),
+// longest experts first: within a few percent of an even split, with no
+// atomics (whose returns would have to wait behind the loads in flight).
+// Cost of a tile: its 32-row K steps (rounds of two, at least one) plus 16
+// for the output.  plan[x * groups + k]: k-th expert of XCD x;
+// plan[8 groups + x]: their count.
+constexpr int kPlanThreads = kMaxExperts;
+__global__ __launch_bounds__(kPlanThreads) void wgrad_plan_kernel(const int32_t* __restrict__ offsets, int groups,
+                                                                  int32_t* __restrict__ plan) {
+  __shared__ int cost[kPlanThreads], order[kPlanThreads];
+  const int e = threadIdx.x;
+  int c = 0;
+  if (e < groups) {
+    const int k = offsets[e + 1] - offsets[e];
+    c = 2 * max(1, (k + 63) / 64) + 16;
+  }
+  cost[e] = c;
+  __syncthreads();
+  if (e < groups) {
+    int rank = 0;                                  // longest first, lower index first among equals
+    for (int o = 0; o < groups; ++o) {
+      const int co = cost[o];
+      rank += (co > c || (co == c && o < e)) ? 1 : 0;
+    }
+    order[rank] = e;
+  }
+  __syncthreads();
+  if (e == 0) {
+    int64_t load[kBwXcds];
+    int cnt[kBwXcds];
+    for (int x = 0; x < kBwXcds; ++x) load[x] = 0, cnt[x] = 0;
+    for (int r = 0; r < groups; ++r) {
+      const int g = order[r];
+      int best = 0;
+      for (int x = 1; x < kBwXcds; ++x)
+        if (load[x] < load[best]) best = x;
+      plan[best * groups + cnt[best]++] = g;
+      load[best] += cost[g];
+    }
+    for (int x = 0; x < kBwXcds; ++x) plan[8 * groups + x] = cnt[x];
+  }
+}
+
+// A weight-gradient workgroup's tile sequence.  With a plan: position p of
+// its XCD's list (copied to LDS once, so that no wait in the tile loop is a
+// memory wait) is tile (list[p / per_group], p % per_group), in the global
+// numbering (g tiles_i + ti) tiles_j + tj; positions w, w + k, ... for the
+// w-th of the XCD's k workgroups.  Without: the equal split by tile count.
+struct WgradSchedule {
+  int* list;                                       // LDS, kMaxExperts entries
+  int n, per_group, step, t_end;
+  bool dyn;
+  MOE_DEV int first(const GemmArgs& a, int total) {
+    const int xcd = blockIdx.x % kBwXcds;
+    const bool by_xcd = MOE_BW_XCD && gridDim.x % kBwXcds == 0;
+    dyn = a.plan != nullptr && by_xcd;
+    if (dyn) {
+      const int cnt = a.plan[8 * a.groups + xcd];
+      for (int i = threadIdx.x; i < cnt; i += blockDim.x) list[i] = a.plan[xcd * a.groups + i];
+      __syncthreads();
+      n = cnt * per_group;
+      step = gridDim.x / kBwXcds;
+      return at((int)blockIdx.x / kBwXcds);
+    }
+    step = by_xcd ? gridDim.x / kBwXcds : gridDim.x;
+    t_end = by_xcd ? xcd_range_start(total, xcd + 1) : total;
+    const int t = by_xcd ? xcd_range_start(total, xcd) + blockIdx.x / kBwXcds : blockIdx.x;
+    return t < t_end ? t : -1;
+  }
+  // tile at position p (dyn) or -1 past the end
+  MOE_DEV int at(int p) const { return p < n ? list[p / per_group] * per_group + p % per_group : -1; }
+};
 
 // Locate the row-grouped tile of linear workgroup id b over nJ column
 // tiles: group g, its 128-row tile index and the column tile, or g = -1
@@ -958,12 +1042,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_WG_WAVE
   static_assert(128 * kCs * 4 <= 4 * kStageElems * 2, "staged output fits the stages");
   // this workgroup's tiles: with a grid of whole XCD rounds, a strided walk
   // over its XCD's contiguous range, else over all tiles
-  const bool by_xcd = MOE_BW_XCD && gridDim.x % kBwXcds == 0;
-  const int xcd = blockIdx.x % kBwXcds;
-  const int t_step = by_xcd ? gridDim.x / kBwXcds : gridDim.x;
-  const int t_end = by_xcd ? xcd_range_start(total, xcd + 1) : total;
-  int t = by_xcd ? xcd_range_start(total, xcd) + blockIdx.x / kBwXcds : blockIdx.x;
-  if (t >= t_end) return;
+  __shared__ int s_list[kMaxExperts];
+  WgradSchedule sched;
+  sched.list = s_list;
+  sched.per_group = tiles_i * tiles_j;
+  int t = sched.first(a, total);                   // uniform
+  int pos = blockIdx.x / kBwXcds;                  // list position of tile t (plan)
+  if (t < 0) return;
 
   // per thread and step: two 16-byte chunks of each operand, chunk c ->
   // K row c / 16, column offset 8 (c % 16); the tile's first column goes
@@ -1062,8 +1147,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_WG_WAVE
 #pragma unroll
       for (int q = 0; q < R; ++q) step(q, cur, st0 + q + R);
     }
-    const int tn = t + t_step;
-    const bool more = tn < t_end;
+    const int tn = sched.dyn ? sched.at(pos + sched.step) : t + sched.step;
+    const bool more = sched.dyn ? tn >= 0 : tn < sched.t_end;
     const Tile nxt = tile_at(more ? tn : t, more);
 #pragma unroll
     for (int q = 0; q < R; ++q) step(q, nxt, q);
@@ -1101,6 +1186,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_WG_WAVE
     }
     if (!more) break;
     t = tn;
+    pos += sched.step;
     cur = nxt;
   }
 }
@@ -1255,12 +1341,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
   static_assert(128 * kCs * 4 <= (2 * kStageElems + 2 * kStageW) * 2, "staged output fits the stages");
   // this workgroup's tiles: with a grid of whole XCD rounds, a strided walk
   // over its XCD's contiguous range, else over all tiles
-  const bool by_xcd = MOE_BW_XCD && gridDim.x % kBwXcds == 0;
-  const int xcd = blockIdx.x % kBwXcds;
-  const int t_step = by_xcd ? gridDim.x / kBwXcds : gridDim.x;
-  const int t_end = by_xcd ? xcd_range_start(total, xcd + 1) : total;
-  int t = by_xcd ? xcd_range_start(total, xcd) + blockIdx.x / kBwXcds : blockIdx.x;
-  if (t >= t_end) return;
+  __shared__ int s_list[kMaxExperts];
+  WgradSchedule sched;
+  sched.list = s_list;
+  sched.per_group = tiles_i * tiles_j;
+  int t = sched.first(a, total);                   // uniform
+  int pos = blockIdx.x / kBwXcds;                  // list position of tile t (plan)
+  if (t < 0) return;
 
   // per thread and step: two 16-byte chunks of each operand, chunk c ->
   // K row c / 16, column offset 8 (c % 16); the tile's first column goes
@@ -1372,8 +1459,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
       for (int q = 0; q < R; ++q) step(q, cur, st0 + q + R);
     }
-    const int tn = t + t_step;
-    const bool more = tn < t_end;
+    const int tn = sched.dyn ? sched.at(pos + sched.step) : t + sched.step;
+    const bool more = sched.dyn ? tn >= 0 : tn < sched.t_end;
     const Tile nxt = tile_at(more ? tn : t, more);
 #pragma unroll
     for (int q = 0; q < R; ++q) step(q, nxt, q);
@@ -1407,6 +1494,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     }
     if (!more) break;
     t = tn;
+    pos += sched.step;
     cur = nxt;
   }
 }
@@ -1517,11 +1605,15 @@ static hipError_t run_gemm(const GemmArgs& a, int dtype, int64_t rows_bound, hip
         const int ti = (a.I + kGT - 1) / kGT, tj = a.J / (wide ? kWideN : kGT);
         const int64_t total = (int64_t)ti * tj * a.groups;
         if (total == 0) return hipSuccess;
-        const int grid = (int)(total < slots ? total : (int64_t)slots);
+        int grid = (int)(total < slots ? total : (int64_t)slots);
+        // a plan needs every XCD to hold a workgroup: whole rounds of 8
+        // (without them the kernels fall back to the equal split)
+        if (grid >= kBwXcds) grid -= grid % kBwXcds;
+        const GemmArgs& ap = a;
         if (wide)
-          hipLaunchKernelGGL(bw_wgrad_wide_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a, ti, tj, (int)total);
+          hipLaunchKernelGGL(bw_wgrad_wide_kernel, dim3((unsigned)grid), dim3(256), 0, stream, ap, ti, tj, (int)total);
         else
-          hipLaunchKernelGGL(bw_wgrad_bf16_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a, ti, tj, (int)total);
+          hipLaunchKernelGGL(bw_wgrad_bf16_kernel, dim3((unsigned)grid), dim3(256), 0, stream, ap, ti, tj, (int)total);
         return hipGetLastError();
       }
     }
@@ -1566,14 +1658,15 @@ static hipError_t run_gemm(const GemmArgs& a, int dtype, int64_t rows_bound, hip
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace: the pre-activation in fp32 (it feeds act' and act, so it is
-// not rounded to bf16), H and dA in the activation type.
+// not rounded to bf16), H and dA in the activation type, then the weight
+// gradients' schedule (wgrad_plan_kernel: 8 E + 8 int32).
+static size_t plan_bytes(int E) { return al256(((size_t)8 * E + 8) * 4); }
 size_t ffn_backward_workspace_bytes(int64_t M_max, int E, int d, int f, int act, int dtype) {
-  (void)E;
   (void)d;
   const size_t eb = dtype == 1 ? 2 : 4;
   const int64_t fr = act == 1 ? 2 * (int64_t)f : f;
   const int64_t M = M_max > 0 ? M_max : 0;
-  return al256((size_t)M * fr * 4) + al256((size_t)M * f * eb) + al256((size_t)M * fr * eb);
+  return al256((size_t)M * fr * 4) + al256((size_t)M * f * eb) + al256((size_t)M * fr * eb) + plan_bytes(E);
 }
 
 hipError_t launch_expert_ffn_backward(const void* X_perm, int dtype, const int32_t* expert_offset, int E, int d,
@@ -1587,6 +1680,7 @@ hipError_t launch_expert_ffn_backward(const void* X_perm, int dtype, const int32
   float* pre = reinterpret_cast<float*>(w);
   void* h = w + al256((size_t)M * fr * 4);
   void* da = w + al256((size_t)M * fr * 4) + al256((size_t)M * f * eb);
+  int32_t* plan = reinterpret_cast<int32_t*>(static_cast<char*>(da) + al256((size_t)M * fr * eb));
   hipError_t err;
   // 1 + 2 fused (GELU on the matrix cores): dA, H straight from both products
   const bool fuse = MOE_BW_FUSE_DH && act == 0 && dtype == 1 && d % 8 == 0 && f % 8 == 0;
@@ -1669,9 +1763,13 @@ hipError_t launch_expert_ffn_backward(const void* X_perm, int dtype, const int32
     err = run_gemm<true, false, 0, EPI_BF16>(a, dtype, M, stream);
     if (err != hipSuccess) return err;
   }
-  // 4. dW2[e] = dY^T H  (K-grouped over the expert's rows)
+  // 4. dW2[e] = dY^T H  (K-grouped over the expert's rows), after the
+  //    weight gradients' schedule
+  hipLaunchKernelGGL(wgrad_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, expert_offset, E, plan);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   {
     GemmArgs a{};
+    a.plan = plan;
     a.A = static_cast<const bf16_t*>(dY_perm);
     a.lda = d;
     a.B = static_cast<const bf16_t*>(h);
@@ -1689,6 +1787,7 @@ hipError_t launch_expert_ffn_backward(const void* X_perm, int dtype, const int32
   // 5. dW1[e] = dA^T X
   {
     GemmArgs a{};
+    a.plan = plan;
     a.A = static_cast<const bf16_t*>(da);
     a.lda = fr;
     a.B = static_cast<const bf16_t*>(X_perm);

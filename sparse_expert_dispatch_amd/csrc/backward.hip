@@ -521,19 +521,43 @@ __global__ __launch_bounds__(kPlanThreads) void wgrad_plan_kernel(const int32_t*
     order[rank] = e;
   }
   __syncthreads();
-  if (e == 0) {
-    int64_t load[kBwXcds];
-    int cnt[kBwXcds];
-    for (int x = 0; x < kBwXcds; ++x) load[x] = 0, cnt[x] = 0;
-    for (int r = 0; r < groups; ++r) {
-      const int g = order[r];
-      int best = 0;
-      for (int x = 1; x < kBwXcds; ++x)
-        if (load[x] < load[best]) best = x;
-      plan[best * groups + cnt[best]++] = g;
-      load[best] += cost[g];
+  if (e < 64) {
+    // wave 0 deals the experts in rank order.  Lane l holds ranks l, l + 64,
+    // ...; lanes 0..7 hold the running work and list length of XCDs 0..7.
+    // Per expert: the least-loaded XCD (lowest index among equals) by a
+    // minimum of load * 8 + x over lanes 0..7 (three row shifts: lane 7 ends
+    // with the minimum), then that lane adds the expert's cost.  Loads stay
+    // below 2^28 (the costs sum to at most M_max / 32 + 16 E).
+    constexpr int kChunks = kPlanThreads / 64;
+    int og[kChunks], oc[kChunks], myx[kChunks], myp[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int r = c * 64 + e;
+      og[c] = r < groups ? order[r] : 0;
+      oc[c] = r < groups ? cost[og[c]] : 0;
+      myx[c] = 0;
+      myp[c] = 0;
     }
-    for (int x = 0; x < kBwXcds; ++x) plan[8 * groups + x] = cnt[x];
+    int ld = 0, cn = 0;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int lim = min(64, groups - c * 64);
+      for (int l = 0; l < lim; ++l) {
+        const int cg = __builtin_amdgcn_readlane(oc[c], l);
+        int key = e < kBwXcds ? ld * kBwXcds + e : INT32_MAX;
+        key = min(key, __builtin_amdgcn_update_dpp(INT32_MAX, key, 0x111, 0xf, 0xf, false));   // row_shr:1
+        key = min(key, __builtin_amdgcn_update_dpp(INT32_MAX, key, 0x112, 0xf, 0xf, false));   // row_shr:2
+        key = min(key, __builtin_amdgcn_update_dpp(INT32_MAX, key, 0x114, 0xf, 0xf, false));   // row_shr:4
+        const int best = __builtin_amdgcn_readlane(key, kBwXcds - 1) & (kBwXcds - 1);
+        const int pos = __builtin_amdgcn_readlane(cn, best);
+        if (e == best) ld += cg, cn += 1;
+        if (e == l) myx[c] = best, myp[c] = pos;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c)
+      if (c * 64 + e < groups) plan[myx[c] * groups + myp[c]] = og[c];
+    if (e < kBwXcds) plan[8 * groups + e] = cn;
   }
 }
 

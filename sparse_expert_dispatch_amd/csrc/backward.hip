@@ -1743,7 +1743,11 @@ hipError_t launch_expert_ffn_backward(const void* X_perm, int dtype, const int32
     a.groups = E;
     a.J = fr;
     a.K = d;
-    err = run_gemm<true, true, 0, EPI_F32>(a, dtype, M, stream);
+    // bf16 with d a multiple of 64: the forward's LDS-tiled grouped GEMM
+    // (32x32x16 products, 64-wide K stages) with an fp32 epilogue
+    err = dtype == 1 && d % 64 == 0 && M > 0
+              ? launch_rows_gemm_f32(X_perm, expert_offset, E, W1, fr, d, M, pre, stream)
+              : run_gemm<true, true, 0, EPI_F32>(a, dtype, M, stream);
     if (err != hipSuccess) return err;
   }
   // 2. dH = dY W2 with the activation backward in the epilogue: dA, H

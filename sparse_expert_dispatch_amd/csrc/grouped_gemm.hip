@@ -65,7 +65,9 @@ constexpr int kXcds = 8;
 #define MOE_GEMM_ORDER -1                        // tile order: -1 by shape, 0 N inner, 1 M inner
 #endif
 
-enum { kEpiNone = 0, kEpiGelu = 1, kEpiSwiglu = 2 };
+// kEpiF32: no activation, fp32 output (C is float*; the backward's
+// pre-activation recompute)
+enum { kEpiNone = 0, kEpiGelu = 1, kEpiSwiglu = 2, kEpiF32 = 3 };
 
 // GELU x * Phi(x) with erf from Abramowitz & Stegun formula 7.1.26
 // (|error| <= 1.5e-7 over the real line, far below the bf16 rounding of the
@@ -392,6 +394,39 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
     // contending for L2.
     // 32x32 accumulator layout: lane holds column (lane % 32), element v ->
     // row (v / 4) * 8 + (lane / 32) * 4 + v % 4.
+    if constexpr (kEpi == kEpiF32) {
+      // fp32 through LDS, 64 columns per pass (row stride 72 floats: the
+      // fragment writes of rows r and r + 4 land 32 banks apart), then
+      // 16-byte pieces of output rows
+      constexpr int kFC = 64, kFS = kFC + 8;
+      static_assert(kTM * kFS * 4 <= kLdsBufs * kStageElems * 2, "an fp32 pass fits the LDS stages");
+      float* sCf = reinterpret_cast<float*>(smem);
+      float* Cf = reinterpret_cast<float*>(C);
+#pragma unroll
+      for (int p = 0; p < kBNout / kFC; ++p) {
+        if (p > 0) __syncthreads();                // the previous pass has been read out
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) {
+          const int cb = wn * kNB * 32 + j * 32;   // this block's first tile column
+          if (cb / kFC != p) continue;             // uniform
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int r = wm * 64 + i * 32 + (v >> 2) * 8 + ((lane >> 5) << 2) + (v & 3);
+              sCf[r * kFS + cb - p * kFC + (lane & 31)] = acc[i][j][v];
+            }
+        }
+        __syncthreads();
+        const int pc0 = c_n0 + p * kFC;
+        for (int q = tid; q < kTM * (kFC / 4); q += kT) {
+          const int r = q / (kFC / 4), c = (q % (kFC / 4)) * 4;
+          if (r < c_m_valid && pc0 + c < N)
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(sCf + r * kFS + c),
+                                        reinterpret_cast<u32x4_t*>(Cf + (size_t)(c_row_base + r) * N + pc0 + c));
+        }
+      }
+    } else {
     bf16_t* sC = smem;
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
@@ -431,6 +466,7 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
           __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(sC + r * kCStride + c),
                                       reinterpret_cast<u32x4_t*>(C + (size_t)(c_row_base + r) * N + pc0 + c));
       }
+    }
     }
     __syncthreads();
     if (tn >= hi) break;
@@ -1220,6 +1256,25 @@ static void launch_ffn_gemm_bf16(int stage, const bf16_t* a, const int32_t* row_
   } else {
     gemm(integral_constant<bool, false>{}, integral_constant<int, kEpiNone>{}, d, f);
   }
+}
+
+// The backward's pre-activation recompute C = A W^T per expert (rows
+// grouped by expert_offset; A [rows, K], W [E, N, K] natural layout, both
+// bf16; C [rows, N] fp32), on the LDS-tiled kernel with the same tile
+// choice as the forward on natural weights.  K % 64 == 0.
+hipError_t launch_rows_gemm_f32(const void* A, const int32_t* expert_offset, int E, const void* W, int N, int K,
+                                int64_t M_max, float* C, hipStream_t stream) {
+  const int mt_inner = M_max <= (int64_t)E * 4 * kBM ? 1 : 0;
+  const bf16_t* a = static_cast<const bf16_t*>(A);
+  const bf16_t* b = static_cast<const bf16_t*>(W);
+  bf16_t* c = reinterpret_cast<bf16_t*>(C);
+  if (mt_inner)
+    launch_persistent<grouped_gemm_bf16_kernel<false, kEpiF32, 2, MOE_GEMM_NB_STREAM, false>>(
+        stream, a, nullptr, (int)M_max, b, expert_offset, E, N, K, mt_inner, c);
+  else
+    launch_persistent<grouped_gemm_bf16_kernel<false, kEpiF32, 1, MOE_GEMM_NB_MFMA, false>>(
+        stream, a, nullptr, (int)M_max, b, expert_offset, E, N, K, mt_inner, c);
+  return hipGetLastError();
 }
 
 hipError_t launch_expert_gemm(int stage, const void* A, const int32_t* row_index, int n_a,

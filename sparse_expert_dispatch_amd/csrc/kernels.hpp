@@ -100,6 +100,11 @@ hipError_t launch_expert_gemm(int stage, const void* A, const int32_t* row_index
                               const int32_t* expert_offset, int E, int d, int f, int act, const void* W,
                               int64_t M_max, void* C, bool packed, void* ws, hipStream_t stream);
 
+// The backward's pre-activation recompute: C [rows, N] fp32 = A W^T per
+// expert (A [rows, K] bf16, W [E, N, K] bf16 natural layout), K % 64 == 0.
+hipError_t launch_rows_gemm_f32(const void* A, const int32_t* expert_offset, int E, const void* W, int N, int K,
+                                int64_t M_max, float* C, hipStream_t stream);
+
 // noalloc.hip: the device address of this library's fixed workspace array
 // on the current device (MOE_NOALLOC_SCRATCH_BYTES), looked up once per
 // device.

@@ -1788,7 +1788,11 @@ hipError_t launch_expert_ffn_backward(const void* X_perm, int dtype, const int32
     a.groups = E;
     a.J = d;
     a.K = fr;
-    err = run_gemm<true, false, 0, EPI_BF16>(a, dtype, M, stream);
+    // bf16 with f_rows a multiple of 64: the forward's LDS-tiled grouped
+    // GEMM reading W1 K-major through transposing LDS reads
+    err = dtype == 1 && fr % 64 == 0 && d % 8 == 0 && M > 0
+              ? launch_rows_gemm_kmajor(da, expert_offset, E, W1, d, fr, M, dX_perm, stream)
+              : run_gemm<true, false, 0, EPI_BF16>(a, dtype, M, stream);
     if (err != hipSuccess) return err;
   }
   // 4. dW2[e] = dY^T H  (K-grouped over the expert's rows), after the

@@ -162,7 +162,17 @@ MOE_DEV int b_row_of(int r, int n0, int N) {
 // one workgroup per CU with two waves per SIMD, double-buffered LDS: the
 // same 64 x 128 wave tiles, with a quarter fewer global and LDS-write bytes
 // per MFMA than two 128-row workgroups and one barrier per K stage).
-template <bool kDual, int kEpi, int kLdsBufs, int kNB, bool kPacked, int kWM = 2>
+// kBKs: B is stored K-major, W [E, K, N] (the backward's dX = dA W1: K runs
+// down W1's rows), natural layout only, not SwiGLU.  A stage of B is staged
+// as [64 K rows][tile columns + 8] with each group of 8 K rows permuted
+// (logical row 8 g + 4 h + q at 8 g + 2 q + h), and a fragment is two
+// ds_read_b64_tr_b16: within each 16-lane group the lanes address 4 rows x
+// 16 columns (lane 4 a + b: row a, columns 4 b ..) and the transpose hands
+// lane c column c of those rows, i.e. four consecutive K; lanes 32 .. 63
+// take the next 8 K and lanes 16 .. 31 / 48 .. 63 the next 16 columns,
+// which is the 32x32x16 B operand.  The row stride (tile columns + 8) keeps
+// the rows a fragment read touches 4 banks apart.
+template <bool kDual, int kEpi, int kLdsBufs, int kNB, bool kPacked, int kWM = 2, bool kBKs = false>
 __global__ __launch_bounds__(kWM * 128, kWM == 4 ? 1 : (kNB == 4 ? 2 : (kLdsBufs == 1 ? 3 : 1))) void
 grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ row_index, int n_a,
                          const bf16_t* __restrict__ B, const int32_t* __restrict__ expert_offset, int E,
@@ -172,8 +182,10 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
   constexpr int kBRows = 2 * kNB * 32;             // weight rows per tile
   constexpr int kBNout = kDual ? kBRows / 2 : kBRows;
   constexpr int kTileA = kTM * kLdsStride;
-  constexpr int kTileB = kPacked ? kBRows * kBK : kBRows * kLdsStride;
+  constexpr int kLdB = kBRows + 8;                 // K-major B: bf16 per LDS K row
+  constexpr int kTileB = kPacked ? kBRows * kBK : (kBKs ? kBK * kLdB : kBRows * kLdsStride);
   static_assert(!kPacked || kBK == 64, "a packed K stage is 4 row-block chunks of 16 K");
+  static_assert(!kBKs || (!kPacked && !kDual && kBK == 64 && kWM == 2), "K-major B: natural, not SwiGLU");
   constexpr int kStageElems = kTileA + kTileB;
   constexpr int kChunksRow = kBK / 8;              // 16-byte chunks per operand row
   constexpr int kRowsPass = kT / kChunksRow;
@@ -263,7 +275,12 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
   int row_base = 0, m_valid = 0, n0 = 0;
   int a_row[kLoadsA];
   const bf16_t* b_tile = B;
-  const bf16_t* b_src[kPacked ? 1 : kLoadsB];
+  const bf16_t* b_src[kPacked || kBKs ? 1 : kLoadsB];
+  // K-major B: buffer loads from the expert's W with one 32-bit byte offset
+  // per load (K row and column inside the stage); the stage goes into the
+  // scalar offset
+  uint32_t b_voff[kBKs ? kLoadsB : 1];
+  __amdgpu_buffer_rsrc_t b_rsrc;
   auto setup = [&](int64_t t) {
     const Place p = place(t);
     const int e = p.e;
@@ -275,7 +292,18 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
     rows_of(t + per_xcd_blocks);
     // packed: expert e's row blocks in the first K stage's slab; natural: its matrix
     b_tile = kPacked ? B + (size_t)e * (nbrows / 32) * 2048 : B + (size_t)e * nbrows * K;
-    if (!kPacked) {
+    if (kBKs) {
+      // K row c / (kBRows / 8) of the stage, columns 8 (c % (kBRows / 8)) ..
+      // (past N: the last 8 columns again, never stored)
+      b_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(b_tile), (short)0,
+                                                 (int)min((int64_t)K * N * 2, (int64_t)0x7FFFFFFF), 0x00020000);
+#pragma unroll
+      for (int i = 0; i < kLoadsB; ++i) {
+        const int c = tid + kT * i;
+        const int kr = c / (kBRows / 8), cc = (c % (kBRows / 8)) * 8;
+        b_voff[i] = (uint32_t)(kr * N + min(n0 + cc, N - 8)) * 2u;
+      }
+    } else if (!kPacked) {
 #pragma unroll
       for (int i = 0; i < kLoadsB; ++i) {
         const int r = ld_row + kRowsPass * i;
@@ -300,6 +328,8 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
         const int pb = kDual ? 2 * min(n0 / 32 + (bi >> 1), last) + (bi & 1) : min(n0 / 32 + bi, last);
         rb[i] = *reinterpret_cast<const u32x4_t*>(b_tile + ((size_t)st * E * (nbrows / 32) + pb) * 2048 +
                                                   (tid & 255) * 8);
+      } else if (kBKs) {
+        rb[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_voff[i], koff * N * 2, 0));
       } else {
         rb[i] = *reinterpret_cast<const u32x4_t*>(b_src[i] + koff);
       }
@@ -313,10 +343,16 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
       *reinterpret_cast<u32x4_t*>(&sA[(ld_row + kRowsPass * i) * kLdsStride + ld_chunk]) = ra[i];
 #pragma unroll
     for (int i = 0; i < kLoadsB; ++i) {
-      if (kPacked)
+      if (kPacked) {
         *reinterpret_cast<u32x4_t*>(&sB[i * kT * 8 + tid * 8]) = rb[i];
-      else
+      } else if (kBKs) {
+        const int c = tid + kT * i;
+        const int kr = c / (kBRows / 8);
+        const int pr = (kr & ~7) | ((kr & 3) << 1) | ((kr >> 2) & 1);
+        *reinterpret_cast<u32x4_t*>(&sB[pr * kLdB + (c % (kBRows / 8)) * 8]) = rb[i];
+      } else {
         *reinterpret_cast<u32x4_t*>(&sB[(ld_row + kRowsPass * i) * kLdsStride + ld_chunk]) = rb[i];
+      }
     }
   };
 
@@ -350,10 +386,21 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
         for (int i = 0; i < 2; ++i)
           af[i] = *reinterpret_cast<const bf16x8_t*>(pa + (wm * 64 + i * 32 + (lane & 31)) * kLdsStride + kc);
 #pragma unroll
-        for (int j = 0; j < kNB; ++j)
-          bfr[j] = kPacked
-                       ? *reinterpret_cast<const bf16x8_t*>(pb + (b_block_packed(j) * (kBK / 16) + s) * 512 + lane * 8)
-                       : *reinterpret_cast<const bf16x8_t*>(pb + (b_block_row(j) + (lane & 31)) * kLdsStride + kc);
+        for (int j = 0; j < kNB; ++j) {
+          if (kBKs) {
+            const bf16_t* q = pb + (s * 16 + 8 * (lane >> 5) + 2 * ((lane >> 2) & 3)) * kLdB + b_block_row(j) +
+                              16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+            typedef short v4i16_t __attribute__((ext_vector_type(4)));
+            typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+            const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)q);
+            const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(q + kLdB));
+            bfr[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          } else {
+            bfr[j] = kPacked
+                         ? *reinterpret_cast<const bf16x8_t*>(pb + (b_block_packed(j) * (kBK / 16) + s) * 512 + lane * 8)
+                         : *reinterpret_cast<const bf16x8_t*>(pb + (b_block_row(j) + (lane & 31)) * kLdsStride + kc);
+          }
+        }
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -1273,6 +1320,24 @@ hipError_t launch_rows_gemm_f32(const void* A, const int32_t* expert_offset, int
         stream, a, nullptr, (int)M_max, b, expert_offset, E, N, K, mt_inner, c);
   else
     launch_persistent<grouped_gemm_bf16_kernel<false, kEpiF32, 1, MOE_GEMM_NB_MFMA, false>>(
+        stream, a, nullptr, (int)M_max, b, expert_offset, E, N, K, mt_inner, c);
+  return hipGetLastError();
+}
+
+// The backward's dX = dA W per expert with W stored K-major ([E, K, N]: the
+// natural W1 read down its rows), bf16 out, on the LDS-tiled kernel.
+// K % 64 == 0, N % 8 == 0.
+hipError_t launch_rows_gemm_kmajor(const void* A, const int32_t* expert_offset, int E, const void* W, int N, int K,
+                                   int64_t M_max, void* C, hipStream_t stream) {
+  const int mt_inner = M_max <= (int64_t)E * 4 * kBM ? 1 : 0;
+  const bf16_t* a = static_cast<const bf16_t*>(A);
+  const bf16_t* b = static_cast<const bf16_t*>(W);
+  bf16_t* c = static_cast<bf16_t*>(C);
+  if (mt_inner)
+    launch_persistent<grouped_gemm_bf16_kernel<false, kEpiNone, 2, MOE_GEMM_NB_STREAM, false, 2, true>>(
+        stream, a, nullptr, (int)M_max, b, expert_offset, E, N, K, mt_inner, c);
+  else
+    launch_persistent<grouped_gemm_bf16_kernel<false, kEpiNone, 1, MOE_GEMM_NB_MFMA, false, 2, true>>(
         stream, a, nullptr, (int)M_max, b, expert_offset, E, N, K, mt_inner, c);
   return hipGetLastError();
 }

@@ -105,6 +105,11 @@ hipError_t launch_expert_gemm(int stage, const void* A, const int32_t* row_index
 hipError_t launch_rows_gemm_f32(const void* A, const int32_t* expert_offset, int E, const void* W, int N, int K,
                                 int64_t M_max, float* C, hipStream_t stream);
 
+// The backward's dX: C [rows, N] bf16 = A W per expert with W [E, K, N]
+// bf16 (K-major), A [rows, K] bf16; K % 64 == 0, N % 8 == 0.
+hipError_t launch_rows_gemm_kmajor(const void* A, const int32_t* expert_offset, int E, const void* W, int N, int K,
+                                   int64_t M_max, void* C, hipStream_t stream);
+
 // noalloc.hip: the device address of this library's fixed workspace array
 // on the current device (MOE_NOALLOC_SCRATCH_BYTES), looked up once per
 // device.

@@ -206,3 +206,17 @@ def test_backward_wide_tiles():
     from harness import log
     log("[backward wide] rows 0/900/1300/40, d=512 f=256")
     _ffn_backward_case([0, 900, 1300, 40], 512, 256, 77)
+
+
+@pytest.mark.parametrize("E", [300, 512])
+def test_backward_many_experts(E):
+    """More experts than one wave has lanes: the weight gradients' plan deals
+    them in 5 or 8 lane chunks (a fifth of the experts empty, the rest 1 to
+    60 rows).  d = 256, f = 128: both weight gradients on the persistent
+    kernel with the plan (output widths 256 and 128), the recompute and dX
+    on the forward's LDS-tiled kernel (few rows per expert)."""
+    from harness import log
+    log(f"[backward many experts] E={E}")
+    rng = np.random.default_rng(E)
+    rows = [int(r) if rng.random() > 0.2 else 0 for r in rng.integers(1, 61, E)]
+    _ffn_backward_case(rows, 256, 128, E + 5)

@@ -1743,9 +1743,11 @@ hipError_t launch_expert_ffn_backward(const void* X_perm, int dtype, const int32
     a.groups = E;
     a.J = fr;
     a.K = d;
-    // bf16 with d a multiple of 64: the forward's LDS-tiled grouped GEMM
-    // (32x32x16 products, 64-wide K stages) with an fp32 epilogue
-    err = dtype == 1 && d % 64 == 0 && M > 0
+    // bf16 with d and f_rows multiples of 64 (the shapes the forward's
+    // kernel serves: whole 16-byte pieces of every output row): its
+    // LDS-tiled grouped GEMM (32x32x16 products, 64-wide K stages) with an
+    // fp32 epilogue
+    err = dtype == 1 && d % 64 == 0 && fr % 64 == 0 && M > 0
               ? launch_rows_gemm_f32(X_perm, expert_offset, E, W1, fr, d, M, pre, stream)
               : run_gemm<true, true, 0, EPI_F32>(a, dtype, M, stream);
     if (err != hipSuccess) return err;
@@ -1788,11 +1790,11 @@ hipError_t launch_expert_ffn_backward(const void* X_perm, int dtype, const int32
     a.groups = E;
     a.J = d;
     a.K = fr;
-    // bf16 with f_rows a multiple of 64 and experts averaging fewer rows
+    // bf16 with f_rows and d multiples of 64 and experts averaging fewer rows
     // than the wide tiles take: the forward's LDS-tiled grouped GEMM reading
     // W1 K-major through transposing LDS reads (expert choice: 294 -> 242
     // us; with many rows per expert the wide kernel measured 8% faster)
-    err = dtype == 1 && fr % 64 == 0 && d % 8 == 0 && M > 0 && M < (int64_t)MOE_BW_WIDE_ROWS * E
+    err = dtype == 1 && fr % 64 == 0 && d % 64 == 0 && M > 0 && M < (int64_t)MOE_BW_WIDE_ROWS * E
               ? launch_rows_gemm_kmajor(da, expert_offset, E, W1, d, fr, M, dX_perm, stream)
               : run_gemm<true, false, 0, EPI_BF16>(a, dtype, M, stream);
     if (err != hipSuccess) return err;

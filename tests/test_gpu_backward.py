@@ -184,7 +184,7 @@ def _ffn_backward_case(rows, d, f, seed):
                 assert (host(dw1)[e] == 0).all() and (host(dw2)[e] == 0).all()
 
 
-@pytest.mark.parametrize("d,f", [(192, 64), (256, 192), (192, 128), (100, 60)])
+@pytest.mark.parametrize("d,f", [(192, 64), (256, 192), (192, 128), (100, 60), (128, 102)])
 def test_backward_ragged_tiles(d, f):
     """Experts of 0, 1, 31, 33, 130 and 300 rows (empty experts, K tails of
     the weight gradients, several 128-row tiles).  (192, 64): d and f not
@@ -192,7 +192,10 @@ def test_backward_ragged_tiles(d, f):
     on the tiled kernel; (256, 192): dW1 (f x 256, 2f x 256) on the
     persistent weight-gradient kernel with a partial last row tile;
     (192, 128): dW2 (192 x 128) on it likewise; (100, 60): rows that are not
-    whole 16-byte chunks, so every GEMM takes the plain bf16 kernel."""
+    whole 16-byte chunks, so every GEMM takes the plain bf16 kernel;
+    (128, 102): d a multiple of 64 but f_rows not, so the recompute and dX
+    stay off the forward's kernel (whose stores are whole 16-byte pieces of
+    rows) and W2's 102-element rows take the plain kernel."""
     from harness import log
     log(f"[backward ragged] d={d} f={f}")
     _ffn_backward_case([0, 1, 31, 33, 130, 300], d, f, 21 + d + f)

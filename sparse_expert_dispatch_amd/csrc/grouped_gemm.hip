@@ -21,18 +21,22 @@
 //    lane); K advances 64 at a time through LDS tiles, the next K tile
 //    fetched from HBM into registers while the matrix cores work on the
 //    current one.  A workgroup of 4 waves owns a 128-row tile, 128 or 256
-//    columns wide; with packed weights and experts averaging 2048 rows or
-//    more, a workgroup of 8 waves owns a 256 x 256 tile.  Weights in the
-//    natural layout or packed.
+//    columns wide; with packed weights, experts averaging 2048 rows or more
+//    and an A operand past 2 GiB, a workgroup of 8 waves owns a 256 x 256
+//    tile.  Weights in the natural layout or packed.
+//  - grouped_gemm_dma_kernel (packed weights, many rows per expert): the
+//    same 128 x 256 tiles with both operands moved into LDS by the buffer
+//    loads' LDS mode, 32-K stages three deep, every fragment of a stage
+//    read ahead of its matrix work (see the kernel);
 //  - stream_pair_gemm_bf16_kernel (weight streaming, packed weights): the
 //    weights bypass LDS and stream into registers two K stages ahead, two
 //    4-wave halves per workgroup (see the kernel);
 //    stream_gemm_bf16_kernel, its 4-wave predecessor, serves A operands of
 //    more than 2 GiB (the paired kernel addresses A through 32-bit offsets).
 // The launcher picks weight streaming for packed weights when every expert
-// has few rows (the GEMMs are bound by the weight stream), the LDS kernel
-// when experts have many rows (matrix-core bound), and the LDS kernel for
-// the natural layout.
+// has few rows (the GEMMs are bound by the weight stream), the LDS-DMA
+// kernel when experts have many rows (matrix-core bound), and the LDS
+// kernel for the natural layout.
 //
 // Scheduling: the per-expert tile counts are prefix-summed on the device
 // (no host synchronisation), and a persistent grid walks the resulting tile
@@ -519,6 +523,317 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
     if (tn >= hi) break;
     t = tn;
   }
+}
+
+
+// ---------------------------------------------------------------- LDS-DMA kernel
+// The matrix-core-bound shapes (many rows per expert, packed weights) on
+// 128 x 256 tiles of 4 waves, two workgroups per CU, with the operands
+// moved from memory straight into LDS by the buffer loads' LDS mode (each
+// 16-byte lane load lands at the wave's LDS base + 16 x lane) instead of
+// through registers.  That frees the 48 registers the staged kernel keeps
+// for the next K tile, and both K steps' fragments of a stage are read
+// before its matrix work.  Stages are 32 K deep; three LDS stages rotate: at
+// the top of stage g (after its barrier) the loads of stage g + 2 are
+// issued into the buffer that stage g - 1 used, so two stages are always in
+// flight, and a tile's first stages are fetched during the previous tile's
+// last stages and epilogue (a load cursor that runs across tiles, as in the
+// weight-streaming kernel).
+//   A: 128 rows x 64 bytes per stage; row r, 16-byte chunk c is stored at
+//      slot c ^ swz(r), swz(r) = ((r >> 1) ^ (r >> 3)) & 3, so that the 32
+//      rows a fragment read touches at one K chunk fall on distinct banks
+//      (the loads pick their source chunk to match).
+//   B: the packed operand order's 1 KB chunks (32 weight rows x 16 K), in
+//      the staged kernel's tile-local block order.
+// Waits are explicit: the compiler does not order LDS reads after the LDS
+// mode's writes, so each stage waits for its own loads (vmcnt, in order)
+// and a barrier publishes them; compiler-only memory clobbers keep the LDS
+// reads on their side of the barrier.
+constexpr int kDmaBK = 32;
+constexpr int kDmaBufs = 3;
+constexpr int kDmaStageA = kBM * kDmaBK * 2;        // bytes
+constexpr int kDmaStageB = 256 * kDmaBK * 2;
+constexpr int kDmaStage = kDmaStageA + kDmaStageB;  // 24 KB
+constexpr int kDmaPerWave = 6;                      // LDS-mode loads per wave and stage (2 A, 4 B)
+
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+// Buffer resource for 32-bit offsets from base (raw, no swizzle).
+MOE_DEV i32x4_t dma_rsrc(const void* base, uint32_t num_records) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return (i32x4_t){(int32_t)(uint32_t)a, (int32_t)((uint32_t)(a >> 32) & 0xFFFFu), (int32_t)num_records,
+                   0x00020000};
+}
+// One LDS-mode buffer load: every lane's 16 bytes at rsrc + soff + voff land
+// at LDS byte lds + 16 x lane.  Written as assembly so that the compiler
+// neither sees an LDS write (it would otherwise wait for every such load
+// before any LDS read) nor counts the load: the kernel waits for it with
+// explicit s_waitcnt.  No register output (nothing the compiler could take
+// as written early); M0 is set in the same block, with the one wait state
+// an LDS-mode load needs after an M0 write (the kernels that use it keep
+// nothing else in M0).
+MOE_DEV void dma16(i32x4_t rsrc, uint32_t voff, int32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
+               : "m0");
+}
+// The same with 4 bytes per lane (LDS byte lds + 4 x lane).
+MOE_DEV void dma4(i32x4_t rsrc, uint32_t voff, int32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
+               : "m0");
+}
+MOE_DEV uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const lds_char_t*)p);
+}
+
+MOE_DEV int dma_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// s_waitcnt with vmcnt(n) (n < 64) and lgkmcnt(0), expcnt left alone
+template <int n>
+MOE_DEV void wait_vm_lgkm0() {
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));
+}
+MOE_DEV void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <bool kDual, int kEpi>
+__global__ __launch_bounds__(kGemmThreads, 2) void
+grouped_gemm_dma_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ row_index, int n_a,
+                        const bf16_t* __restrict__ B, const int32_t* __restrict__ expert_offset, int E, int N,
+                        int K, int mt_inner, bf16_t* __restrict__ C) {
+  constexpr int kT = kGemmThreads, kTM = kBM, kNB = 4, kBRows = 256;
+  constexpr int kBNout = kDual ? kBRows / 2 : kBRows;
+  constexpr int kPassCols = 64, kCStride = kPassCols + 8;
+  static_assert(kTM * kCStride * 2 <= kDmaStage, "an epilogue pass fits one LDS stage");
+  __shared__ __attribute__((aligned(1024))) char smem[kDmaBufs * kDmaStage];
+  __shared__ int32_t tile_off[kMaxExperts + 1];
+  block_tile_plan<kT, kTM>(expert_offset, E, tile_off);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ntn = (N + kBNout - 1) / kBNout;
+  const int64_t n_tiles = (int64_t)__builtin_amdgcn_readfirstlane(tile_off[E]) * ntn;
+  const int xcd = blockIdx.x % kXcds;
+  const int per_xcd_blocks = gridDim.x / kXcds;
+  const int64_t lo = n_tiles * xcd / kXcds, hi = n_tiles * (xcd + 1) / kXcds;
+  const int P = kDual ? 2 * N / 32 : N / 32;      // packed row blocks per expert
+  const int last_pb = N / 32 - 1;
+  const int nk = K / kDmaBK;
+
+  // packed tile-local row block of this wave's B block j (as the staged kernel)
+  auto b_block_packed = [&](int j) __attribute__((always_inline)) {
+    if (!kDual) return wn * kNB + j;
+    constexpr int half = kNB / 2;
+    return j < half ? 2 * (wn * half + j) : 2 * (wn * half + j - half) + 1;
+  };
+  struct Place {
+    int row_base, m_valid, n0, e;
+  };
+  auto place = [&](int64_t t) __attribute__((always_inline)) {
+    int e_lo = 0, e_hi = E - 1;
+    while (e_lo < e_hi) {
+      const int mid = (e_lo + e_hi + 1) >> 1;
+      if ((int64_t)tile_off[mid] * ntn <= t) e_lo = mid; else e_hi = mid - 1;
+    }
+    Place p;
+    p.e = __builtin_amdgcn_readfirstlane(e_lo);
+    const int mtiles = tile_off[p.e + 1] - tile_off[p.e];
+    const int local = (int)(t - (int64_t)tile_off[p.e] * ntn);
+    const int mloc = mt_inner ? local % mtiles : local / ntn;
+    const int nt = mt_inner ? local / mtiles : local % ntn;
+    p.row_base = __builtin_amdgcn_readfirstlane(expert_offset[p.e] + mloc * kTM);
+    p.m_valid = __builtin_amdgcn_readfirstlane(min(kTM, expert_offset[p.e + 1] - p.row_base));
+    p.n0 = __builtin_amdgcn_readfirstlane(nt * kBNout);
+    return p;
+  };
+  // The gathered A rows of the cursor's tile j sit in s_idx[j & 1]: the
+  // index entries of a tile's 128 rows, loaded in LDS mode by waves 0 and 1
+  // when the cursor enters the tile before it (at least two stages, hence
+  // two waits and barriers, before they are read; the slot refilled was
+  // last read at least one barrier earlier), so no index load is ever
+  // waited on at once.  The first two tiles' entries are loaded up front.
+  __shared__ __attribute__((aligned(16))) int32_t s_idx[2][kTM];
+  const i32x4_t idx_rsrc = dma_rsrc(row_index, (uint32_t)__builtin_amdgcn_readfirstlane(expert_offset[E]) * 4u);
+  const i32x4_t a_rsrc = dma_rsrc(A, (uint32_t)min((int64_t)n_a * K * 2, (int64_t)0x7FFFFFFF));
+  const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+  const uint32_t idx_base = __builtin_amdgcn_readfirstlane(lds_addr(&s_idx[0][0]));
+  auto fetch_idx = [&](int64_t tt, int slot) __attribute__((always_inline)) {
+    if (row_index && wave < 2) {
+      const Place p = place(min(tt, hi - 1));
+      dma4(idx_rsrc, (uint32_t)(p.row_base + wave * 64 + lane) * 4u, 0, idx_base + slot * kTM * 4 + wave * 256);
+    }
+  };
+  // Load cursor: tile d_t (the d_j-th of this workgroup), stage d_kt.  Past
+  // the workgroup's last tile it stays on that tile's last stage and
+  // re-reads it, so every stage issues the same loads.
+  int64_t d_t = lo + blockIdx.x / kXcds;
+  if (d_t >= hi) return;
+  int d_kt = 0, d_e = 0, d_n0 = 0, d_j = 0;
+  uint32_t a_voff[2];
+  auto cursor_tile = [&](int fetch) __attribute__((always_inline)) {
+    const Place p = place(d_t);
+    d_e = p.e;
+    d_n0 = p.n0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 16 * (4 * i + wave) + (lane >> 2);
+      const int c = (lane & 3) ^ dma_swz(r);
+      const int rr = min(r, p.m_valid - 1);
+      const int row = row_index ? min(max(s_idx[d_j & 1][rr], 0), n_a - 1) : p.row_base + rr;
+      a_voff[i] = (uint32_t)row * (uint32_t)(K * 2) + (uint32_t)(c * 16);
+    }
+    if (fetch) fetch_idx(d_t + per_xcd_blocks, (d_j + 1) & 1);
+    ++d_j;
+  };
+  auto issue = [&](int dbuf) __attribute__((always_inline)) {
+    const int kt = __builtin_amdgcn_readfirstlane(d_kt);
+    const int de = __builtin_amdgcn_readfirstlane(d_e), dn0 = __builtin_amdgcn_readfirstlane(d_n0);
+    const uint32_t base = smem_base + dbuf * kDmaStage;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(a_rsrc, a_voff[i], kt * kDmaBK * 2, base + (4 * i + wave) * 1024);
+    // packed B: 64-K stage kt / 2 of expert d_e, chunks 2 (kt & 1) + s
+    const i32x4_t b_rsrc = dma_rsrc(B + ((size_t)(kt >> 1) * E + de) * P * 2048, 0x7FFFFFFF);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = 4 * i + wave, bi = q >> 1, s = q & 1;
+      const int pb = kDual ? 2 * min(dn0 / 32 + (bi >> 1), last_pb) + (bi & 1) : min(dn0 / 32 + bi, last_pb);
+      dma16(b_rsrc, (uint32_t)lane * 16, pb * 4096 + ((kt & 1) * 2 + s) * 1024, base + kDmaStageA + q * 1024);
+    }
+    if (d_kt + 1 < nk) {
+      ++d_kt;
+    } else if (d_t + per_xcd_blocks < hi) {
+      d_kt = 0;
+      d_t += per_xcd_blocks;
+      cursor_tile(1);
+    }
+  };
+
+  fetch_idx(d_t, 0);
+  fetch_idx(d_t + per_xcd_blocks, 1);
+  wait_vm_lgkm0<0>();
+  lds_barrier();
+  cursor_tile(0);
+  int64_t t = d_t;                                 // the first tile computed (the cursor may pass it below)
+  int cbuf = 0;
+  issue(0);
+  lds_barrier();                                   // s_idx[0] read by every wave before it is refilled
+  issue(1);
+  const int sw = dma_swz(lane & 31);
+  while (true) {
+    const Place pc = place(t);
+    f32x16_t acc[2][kNB];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < kNB; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    for (int kt = 0; kt < nk; ++kt) {
+      // this stage's loads done (the next stage's may still be in flight),
+      // every wave's reads of the buffer about to be refilled done
+      wait_vm_lgkm0<kDmaPerWave>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue(cbuf == 0 ? 2 : cbuf - 1);
+      const char* pa = smem + cbuf * kDmaStage;
+      const char* pb = pa + kDmaStageA;
+      bf16x8_t af[2][2], bfr[2][kNB];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int c = (2 * s + (lane >> 5)) ^ sw;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          af[s][i] = *reinterpret_cast<const bf16x8_t*>(pa + (wm * 64 + i * 32 + (lane & 31)) * 64 + c * 16);
+#pragma unroll
+        for (int j = 0; j < kNB; ++j)
+          bfr[s][j] = *reinterpret_cast<const bf16x8_t*>(pb + (b_block_packed(j) * 2 + s) * 1024 + lane * 16);
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < kNB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s][i], bfr[s][j], acc[i][j], 0, 0, 0);
+      cbuf = cbuf == 2 ? 0 : cbuf + 1;
+    }
+
+    // Epilogue in the last stage's buffer (the next tile's first two stages
+    // are landing in the other two): activation, bf16 rounding, 64 output
+    // columns per pass through LDS, whole 16-byte chunks of output rows
+    // stored non-temporally.  32x32 accumulator layout: lane holds column
+    // (lane % 32), element v -> row (v / 4) * 8 + (lane / 32) * 4 + v % 4.
+    bf16_t* sC = reinterpret_cast<bf16_t*>(smem + (cbuf == 0 ? 2 : cbuf - 1) * kDmaStage);
+    if (!kDual && kEpi != kEpiNone) {
+      // the activation in place, one 32 x 32 block at a time
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) {
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[i][j][v] = epi_value<kEpi>(acc[i][j][v], 0.f);
+        }
+    }
+    constexpr int kEpiPack = kDual ? kEpi : kEpiNone;
+#pragma unroll
+    for (int p = 0; p < kBNout / kPassCols; ++p) {
+      lds_barrier();                               // the stage (or the previous pass) has been read
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        __builtin_amdgcn_sched_barrier(0);         // one row block's activations at a time
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const int r = wm * 64 + i * 32 + (v >> 2) * 8 + ((lane >> 5) << 2) + (v & 3);
+          if (kDual) {
+            if (wn != p) continue;                 // uniform: a wave's 64 outputs are one pass
+#pragma unroll
+            for (int j = 0; j < kNB / 2; ++j) {
+              const int col = j * 32 + (lane & 31);
+              const uint32_t h = bf16x2_rne(epi_value<kEpi>(acc[i][j][v], acc[i][j + kNB / 2][v]),
+                                            epi_value<kEpi>(acc[i][j][v + 1], acc[i][j + kNB / 2][v + 1]));
+              sC[r * kCStride + col] = (bf16_t)h;
+              sC[(r + 1) * kCStride + col] = (bf16_t)(h >> 16);
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < kNB; ++j) {
+              if (wn * 2 + (j >> 1) != p) continue;  // uniform
+              const int col = (j & 1) * 32 + (lane & 31);
+              const uint32_t h = bf16x2_rne(epi_value<kEpiPack>(acc[i][j][v], 0.f),
+                                            epi_value<kEpiPack>(acc[i][j][v + 1], 0.f));
+              sC[r * kCStride + col] = (bf16_t)h;
+              sC[(r + 1) * kCStride + col] = (bf16_t)(h >> 16);
+            }
+          }
+        }
+      }
+      lds_barrier();
+      const int pc0 = pc.n0 + p * kPassCols;
+#pragma unroll
+      for (int q = tid; q < kTM * (kPassCols / 8); q += kT) {
+        const int r = q / (kPassCols / 8), c = (q % (kPassCols / 8)) * 8;
+        if (r < pc.m_valid && pc0 + c < N)
+          __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(sC + r * kCStride + c),
+                                      reinterpret_cast<u32x4_t*>(C + (size_t)(pc.row_base + r) * N + pc0 + c));
+      }
+    }
+    if (t + per_xcd_blocks >= hi) break;
+    t += per_xcd_blocks;
+  }
+  // the cursor's re-reads of the last stage are still landing
+  __builtin_amdgcn_s_waitcnt(0x0070 | 0xF00);     // vmcnt(0)
 }
 
 
@@ -1191,6 +1506,9 @@ __global__ __launch_bounds__(256) void ffn_down_f32_kernel(const float* __restri
 #ifndef MOE_STREAM_DEPTH
 #define MOE_STREAM_DEPTH 2       // K stages of packed weights in flight per wave, weight streaming
 #endif
+#ifndef MOE_GEMM_DMA
+#define MOE_GEMM_DMA 1           // many rows per expert, packed: operands into LDS by the loads' LDS mode
+#endif
 #ifndef MOE_STREAM_PAIR
 #define MOE_STREAM_PAIR 1        // weight streaming on the paired (8-wave) kernel
 #endif
@@ -1279,11 +1597,18 @@ static void launch_ffn_gemm_bf16(int stage, const bf16_t* a, const int32_t* row_
         launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 2, MOE_GEMM_NB_STREAM, false>>(
             stream, a, row_index, n_a, b, expert_offset, E, N, K, mt_inner, c);
     } else {
-      // 256-row tiles once experts average 2048 rows or more (the
-      // always-on shared expert: one expert with every token): there the
-      // 8-wave tile measured 7% faster; with fewer rows per expert its
-      // coarser tail per expert costs more than that (2.5% slower at 1024)
-      if (packed && MOE_GEMM_WM_MFMA == 4 && M_max >= (int64_t)2048 * E)
+      // Packed weights: the LDS-DMA kernel (A addressed through 32-bit
+      // offsets); it measured 4-7% faster than the register-staged kernel on
+      // the dropless top-8 projections and 5% faster than the 256 x 256
+      // tiles on the always-on shared expert.  Past 2 GiB of A: 256-row
+      // tiles once experts average 2048 rows or more (the shared expert's
+      // shape: there the 8-wave tile measured 7% faster than 128-row
+      // tiles; with fewer rows per expert its coarser tail per expert costs
+      // more than that), else the staged 128 x 256 kernel.
+      if (packed && MOE_GEMM_DMA && (int64_t)n_a * K * 2 <= (int64_t)0x7FFFFFFF)
+        launch_persistent<grouped_gemm_dma_kernel<kD, kE>>(stream, a, row_index, n_a, b, expert_offset, E, N, K,
+                                                           mt_inner, c);
+      else if (packed && MOE_GEMM_WM_MFMA == 4 && M_max >= (int64_t)2048 * E)
         launch_persistent<grouped_gemm_bf16_kernel<kD, kE, 2, MOE_GEMM_NB_MFMA, true, 4>, 512>(
             stream, a, row_index, n_a, b, expert_offset, E, N, K, mt_inner, c);
       else if (packed)

@@ -93,10 +93,24 @@ def test_packed_ffn_equals_natural_matrix_core_order(act):
 
 
 @pytest.mark.parametrize("act", [N.MOE_GELU, N.MOE_SWIGLU])
+@pytest.mark.parametrize("d,f", [(64, 64), (64, 128)])
+def test_packed_ffn_equals_natural_two_stage_tiles(act, d, f):
+    # many rows per expert with K = 64: a tile is two 32-K LDS stages, so the
+    # matrix-core kernel's load cursor leaves a tile within its first two
+    # loads; more tiles than resident workgroups (48 experts of 1000-2000
+    # rows, 530+ row tiles), so workgroups compute several tiles each
+    rows = [int(r) for r in np.random.default_rng(17).integers(1000, 2001, 48)]
+    rows[5] = 0
+    a, b, M = _ffn_pair(rows, d, f, act, 18)
+    assert np.array_equal(a, b)
+    assert (b[M:] == np.int16(0x40E0)).all()
+
+
+@pytest.mark.parametrize("act", [N.MOE_GELU, N.MOE_SWIGLU])
 def test_packed_ffn_equals_natural_large_experts(act):
     # experts averaging 2048 rows or more (the shared expert's shape): the
-    # packed path takes 256-row tiles of 8 waves, the natural one 128-row
-    # tiles; ragged last tiles (4100 = 16 x 256 + 4, 2100 = 8 x 256 + 52)
+    # packed path on the LDS-DMA kernel, the natural one on the staged
+    # kernel; ragged last tiles (4100 = 32 x 128 + 4, 2100 = 16 x 128 + 52)
     rows = [4100, 0, 2100]
     a, b, M = _ffn_pair(rows, 192, 384, act, 16)
     assert np.array_equal(a, b)

@@ -59,6 +59,9 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 #ifndef MOE_GEMM_BK
 #define MOE_GEMM_BK 64
 #endif
+#ifndef MOE_PAIR_TALL_MAX
+#define MOE_PAIR_TALL_MAX 192    // experts of 129 .. this many rows on tall tiles, the others on wide tiles
+#endif
 constexpr int kBM = 128;
 constexpr int kBK = MOE_GEMM_BK;             // K per stage
 constexpr int kLdsStride = kBK + 8;          // bf16 per LDS row
@@ -1067,12 +1070,20 @@ stream_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict_
 // SIMD), so that no weight byte is fetched twice and each SIMD has a second
 // wave to issue matrix work while the first waits on memory.  A tile is
 // chosen per expert from its row count m:
-//  - wide (m <= 128): 128 rows x 2 kNW output columns; half h takes the
-//    columns n0 + h kNW ..: twice the distinct weight bytes in flight per CU;
-//  - tall (m > 128): 256 rows x kNW columns; half h takes rows 128 h ..
-//    of the same columns, so both halves load the same weight chunks at the
-//    same K stage (the second load is served by the cache): an expert of up
-//    to 256 rows streams its weights from memory once.
+//  - wide: 128 rows x 2 kNW output columns; half h takes the columns
+//    n0 + h kNW ..: twice the distinct weight bytes in flight per CU.  An
+//    expert of more rows takes ceil(m / 128) row tiles per column block,
+//    adjacent in the list, so neighbouring workgroups of one XCD stream the
+//    same weights at about the same time and the re-reads meet in the cache;
+//  - tall (128 < m <= MOE_PAIR_TALL_MAX): 256 rows x kNW columns; half h
+//    takes rows 128 h .. of the same columns, so both halves load the same
+//    weight chunks at the same K stage (the second load is served by the
+//    cache) and the expert streams its weights once, from one CU.  This
+//    pays while the second half is sparse; an expert whose second 128 rows
+//    are mostly full, or of more than 256 rows (two tall row tiles far
+//    apart in the list), measured faster on wide row tiles (top-8-of-256
+//    routing: up 3450 -> 3076 us, down 1790 -> 1699 us; Switch top-1 with
+//    160-row experts unchanged).
 // Each wave owns 128 rows and two 32-row weight blocks (64 output columns,
 // or the gate and up blocks of 32 SwiGLU outputs) as in the 4-wave kernel;
 // the weights stream from memory straight into registers, kDepth K stages
@@ -1082,10 +1093,11 @@ stream_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict_
 constexpr int kPairThreads = 512;
 
 // Tile plan of the paired kernel, two lists in expert order: the wide tiles
-// (ceil(N / (2 kNW)) per expert of 1..128 rows; wide_off[e] = wide tiles of
-// experts before e) and the tall tiles (ceil(m / 256) * ceil(N / kNW) per
-// expert of more than 128 rows, M tiles innermost; tall_off[e]).
-// wide_off[E], tall_off[E] are the totals.
+// (ceil(m / 128) * ceil(N / (2 kNW)) per expert not on tall tiles, M tiles
+// innermost; wide_off[e] = wide tiles of experts before e) and the tall
+// tiles (ceil(m / 256) * ceil(N / kNW) per expert of 129 ..
+// MOE_PAIR_TALL_MAX rows, M tiles innermost; tall_off[e]).  wide_off[E],
+// tall_off[E] are the totals.
 template <int kNW>
 MOE_DEV void pair_tile_plan(const int32_t* __restrict__ expert_offset, int E, int N, int32_t* wide_off,
                             int32_t* tall_off) {
@@ -1094,8 +1106,9 @@ MOE_DEV void pair_tile_plan(const int32_t* __restrict__ expert_offset, int E, in
   const int ntw = (N + 2 * kNW - 1) / (2 * kNW), ntn = (N + kNW - 1) / kNW;
   const int e = threadIdx.x;
   const int m = e < E ? expert_offset[e + 1] - expert_offset[e] : 0;
-  const int cw = (m > 0 && m <= 128) ? ntw : 0;
-  const int ct = m > 128 ? ((m + 255) / 256) * ntn : 0;
+  const bool tall = m > 128 && m <= MOE_PAIR_TALL_MAX;
+  const int cw = (m > 0 && !tall) ? ((m + 127) / 128) * ntw : 0;
+  const int ct = tall ? ((m + 255) / 256) * ntn : 0;
   int tot_w = 0, tot_t = 0;
   const int rw = block_exclusive_scan<kPairThreads>(cw, scratch, &tot_w);
   const int rt = block_exclusive_scan<kPairThreads>(ct, scratch, &tot_t);
@@ -1196,9 +1209,13 @@ stream_pair_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __rest
       const int g = wl + pos;
       p.e = find(wide_off, g);
       p.wide = 1;
-      p.row_base = __builtin_amdgcn_readfirstlane(expert_offset[p.e]);
-      p.m_valid = __builtin_amdgcn_readfirstlane(expert_offset[p.e + 1] - p.row_base);
-      p.n0 = __builtin_amdgcn_readfirstlane((g - wide_off[p.e]) * 2 * kNW);
+      const int base = expert_offset[p.e];
+      const int m = expert_offset[p.e + 1] - base;
+      const int mt = (m + 127) / 128;
+      const int local = g - wide_off[p.e];
+      p.row_base = __builtin_amdgcn_readfirstlane(base + (local % mt) * 128);
+      p.m_valid = __builtin_amdgcn_readfirstlane(min(128, m - (local % mt) * 128));
+      p.n0 = __builtin_amdgcn_readfirstlane((local / mt) * 2 * kNW);
     } else {
       const int g = tl + pos - (wh - wl);
       p.e = find(tall_off, g);

@@ -83,6 +83,18 @@ def test_packed_ffn_equals_natural_streaming_order(act):
 
 
 @pytest.mark.parametrize("act", [N.MOE_GELU, N.MOE_SWIGLU])
+def test_packed_ffn_equals_natural_tile_class_edges(act):
+    # weight streaming across the tile classes' edges: 128 / 129 rows (wide
+    # to tall), 192 / 193 (tall to two wide row tiles), 256 / 257 and 384 /
+    # 385 (two, three and four adjacent wide row tiles), 427 (the largest
+    # expert of the top-8-of-256 routing)
+    rows = [0, 1, 128, 129, 192, 193, 256, 257, 384, 385, 427, 64]
+    a, b, M = _ffn_pair(rows, 256, 384, act, 19)
+    assert np.array_equal(a, b)
+    assert (b[M:] == np.int16(0x40E0)).all()
+
+
+@pytest.mark.parametrize("act", [N.MOE_GELU, N.MOE_SWIGLU])
 def test_packed_ffn_equals_natural_matrix_core_order(act):
     # many rows per expert: N tiles innermost, 128 x 256 tiles; d = 192 is
     # narrower than one down tile, f = 384 ends mid-tile

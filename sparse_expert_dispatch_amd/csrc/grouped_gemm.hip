@@ -548,10 +548,13 @@ grouped_gemm_bf16_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict
 //      (the loads pick their source chunk to match).
 //   B: the packed operand order's 1 KB chunks (32 weight rows x 16 K), in
 //      the staged kernel's tile-local block order.
-// Waits are explicit: the compiler does not order LDS reads after the LDS
-// mode's writes, so each stage waits for its own loads (vmcnt, in order)
-// and a barrier publishes them; compiler-only memory clobbers keep the LDS
-// reads on their side of the barrier.
+// Waits are explicit: the LDS-mode loads are assembly the compiler does
+// not see, so nothing but the kernel's own waits orders the LDS reads after
+// them.  Each stage waits until at most the next stage's six loads per wave
+// are outstanding (vmcnt counts in issue order; the epilogue's stores and
+// the compiler's own loads only make that wait stricter), then a barrier
+// publishes the stage; compiler-only memory clobbers keep the LDS reads on
+// their side of the barrier.
 constexpr int kDmaBK = 32;
 constexpr int kDmaBufs = 3;
 constexpr int kDmaStageA = kBM * kDmaBK * 2;        // bytes

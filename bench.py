@@ -113,11 +113,12 @@ def grade(bytes_, flops, seconds, dtype="bf16"):
 
 
 def gemm_kernel_kind(m_max, E, bm=128):
-    """Which grouped GEMM the library launches for the routed experts on
-    packed weights: the same rule as its launcher (few slots per expert, at
-    most four 128-row tiles on average: the weight-streaming kernel;
-    otherwise the matrix-core kernel whose operands reach LDS by LDS-mode
-    loads)."""
+    """Which grouped GEMM the library launches for the routed experts' up
+    projection on packed weights: the same rule as its launcher (few slots
+    per expert, at most four 128-row tiles on average: the weight-streaming
+    kernel; otherwise the matrix-core kernel whose operands reach LDS by
+    LDS-mode loads).  The down projection streams weights up to eight tiles
+    per expert."""
     return "weight-streaming" if m_max <= E * 4 * bm else "matrix-core (LDS-mode loads)"
 
 
